@@ -1,0 +1,100 @@
+/*
+ * ss2d.h -- C ABI of the MI355X (gfx950) SS2D forward library, libss2d.so.
+ *
+ * One call computes the whole SS2D forward hot path of a VMamba block:
+ *   CrossScan  -- the H x W map is read as four sequences of length L = H*W:
+ *                 row by row (direction 0), column by column (direction 1),
+ *                 and both of those reversed (directions 2 and 3);
+ *   selective scan over each sequence, per channel c = k*D + d and state n:
+ *                 delta = softplus(dt + dt_bias[c]), A = -exp(A_log[c, n]),
+ *                 h = exp(delta*A) * h + delta * Bs[n] * u  (h starts at 0),
+ *                 out = sum_n Cs[n] * h + Ds[c] * u;
+ *   CrossMerge -- the four directional outputs are mapped back to the map and
+ *                 summed (accumulated in fp32, rounded once to `dtype`).
+ * Passages that define it, on the page [SS2D] "深入解析VMamba中的SS2D模块从理论到
+ * 代码实现": §3.1 (the four sequences), §3.2 (the selective_scan call: -exp of
+ * A_logs, delta_bias, delta_softplus, shared per-direction B/C), §3.3 (the
+ * merge), §4 (direction table).  Zero initial state: [DAMamba] page §3.1.
+ *
+ * All functions are plain C; no HIP or torch types appear in the signatures.
+ */
+#ifndef SS2D_H_
+#define SS2D_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of x, dt, Bs, Cs and y.  A_log, dt_bias and Ds are always fp32,
+ * and the scan state and every accumulation are fp32 for both types. */
+typedef enum { SS2D_F32 = 0, SS2D_BF16 = 1 } ss2d_dtype;
+
+typedef enum {
+  SS2D_OK = 0,
+  SS2D_ERR_NULL = -1,           /* a required pointer is NULL                     */
+  SS2D_ERR_SHAPE = -2,          /* B, D, H or W < 1, or a size overflows int64    */
+  SS2D_ERR_UNSUPPORTED_N = -3,  /* N outside 1..16                                */
+  SS2D_ERR_DTYPE = -4,          /* dtype is not an ss2d_dtype value               */
+  SS2D_ERR_ALIAS = -5,          /* y overlaps one of the inputs                   */
+  SS2D_ERR_ALIGN = -6,          /* a pointer is not aligned to its element size   */
+  SS2D_ERR_NO_DEVICE = -7,      /* no HIP device, or the device query failed      */
+  SS2D_ERR_HIP = -8             /* a HIP call or kernel launch failed             */
+} ss2d_status;
+
+/*
+ * ss2d_forward -- enqueue one SS2D forward on `stream`.
+ *
+ * Every pointer is DEVICE memory owned by the caller; all tensors are dense and
+ * row-major (C order).  L = H*W.  "dtype" below means the storage type chosen by
+ * `dtype` (fp32 or bf16).
+ *   x       [B, D, H, W]   dtype  channel-first feature map.
+ *   dt      [B, 4, D, L]   dtype  step input of direction k, channel d, in the
+ *                                 order direction k visits the map (its scan order).
+ *   A_log   [4*D, N]       fp32   row c = k*D + d.
+ *   dt_bias [4*D]          fp32
+ *   Bs, Cs  [B, 4, N, L]   dtype  per-direction projections in scan order, shared
+ *                                 by all D channels of that direction.
+ *   Ds      [4*D]          fp32
+ *   y       [B, D, H, W]   dtype  output; fully overwritten, never read.  Must not
+ *                                 overlap any input.
+ *   N       number of states, 1..16.
+ *   stream  a hipStream_t (NULL = the default stream).
+ *
+ * Behaviour: arguments are validated before any device work (codes above).  On
+ * SS2D_OK the work has been enqueued asynchronously; execution faults surface at
+ * the caller's next synchronisation.  Nothing is printed, thrown or aborted.  The
+ * library keeps no state between calls besides cached device properties, except
+ * that a bf16 call whose per-channel plane exceeds on-chip memory uses a
+ * stream-ordered temporary fp32 buffer (allocated and freed on `stream`).
+ * NaN and Inf propagate.  Thread-safe.
+ */
+int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
+                 const void* Bs, const void* Cs, const float* Ds, void* y,
+                 int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                 int dtype, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* ss2d_status_string(int status);
+
+/* Text of the last HIP error seen by this thread (for SS2D_ERR_HIP); "" if none. */
+const char* ss2d_last_hip_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int ss2d_version(void);
+
+/*
+ * ss2d_describe -- write a one-line, NUL-terminated description of how
+ * ss2d_forward would run this shape (kernel variant, lanes per sequence,
+ * channels per workgroup, chunk plan, where the merge plane lives) into
+ * buf[0..len).  Host only; no device work.  Returns SS2D_OK or a validation code.
+ */
+int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+                  char* buf, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS2D_H_ */

@@ -1,0 +1,139 @@
+"""MI355X-native SS2D forward (VMamba CrossScan -> selective scan -> CrossMerge).
+
+Thin Python binding over the C ABI of libss2d.so (include/ss2d.h).  It only
+marshals arguments: every step of the forward runs in the HIP kernels.  PyTorch
+provides device memory and the stream.  There is no CPU fallback: if the
+library is missing or the tensors are not on a ROCm device, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["forward", "ss2d_forward", "describe", "status_string", "version", "library_path", "lib",
+           "SS2D_F32", "SS2D_BF16", "SS2DError"]
+
+SS2D_F32 = 0
+SS2D_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libss2d.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class SS2DError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"ss2d_forward failed ({code}): {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libss2d.so (ctypes), with argument types declared."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+                                  "python -m selective_scan_crossscan_amd._build")
+            L = ctypes.CDLL(_LIB_PATH)
+            vp, i64 = ctypes.c_void_p, ctypes.c_int64
+            L.ss2d_forward.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
+            L.ss2d_forward.restype = ctypes.c_int
+            L.ss2d_status_string.argtypes = [ctypes.c_int]
+            L.ss2d_status_string.restype = ctypes.c_char_p
+            L.ss2d_last_hip_error.argtypes = []
+            L.ss2d_last_hip_error.restype = ctypes.c_char_p
+            L.ss2d_version.argtypes = []
+            L.ss2d_version.restype = ctypes.c_int
+            L.ss2d_describe.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.c_char_p, i64]
+            L.ss2d_describe.restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().ss2d_status_string(int(code)).decode()
+
+
+def version() -> int:
+    return lib().ss2d_version()
+
+
+def describe(B, D, H, W, N, dtype=SS2D_F32) -> str:
+    buf = ctypes.create_string_buffer(512)
+    rc = lib().ss2d_describe(B, D, H, W, N, int(dtype), buf, len(buf))
+    if rc != 0:
+        raise SS2DError(rc, status_string(rc))
+    return buf.value.decode()
+
+
+def ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, stream) -> int:
+    """Raw C-ABI call with integer device addresses; returns the status code."""
+    return lib().ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype), stream)
+
+
+def _raise(rc: int):
+    msg = status_string(rc)
+    if rc == -8:
+        msg += ": " + lib().ss2d_last_hip_error().decode()
+    raise SS2DError(rc, msg)
+
+
+def forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, out=None, stream=None):
+    """SS2D forward on torch tensors.
+
+    x (B,D,H,W), dt (B,4,D,H*W), Bs/Cs (B,4,N,H*W): float32 or bfloat16, all the same;
+    A_log (4D,N), dt_bias (4D,), Ds (4D,): float32.  All contiguous, on one ROCm device.
+    Returns y (B,D,H,W) in x's dtype (written into `out` if given).
+    """
+    import torch
+
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    B, D, H, W = x.shape
+    N = A_log.shape[-1]
+    if x.dtype == torch.float32:
+        code = SS2D_F32
+    elif x.dtype == torch.bfloat16:
+        code = SS2D_BF16
+    else:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    io = (x, dt, Bs, Cs)
+    params = (A_log, dt_bias, Ds)
+    for t in io + params:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU fallback)")
+        if t.device != x.device:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    for t in io:
+        if t.dtype != x.dtype:
+            raise TypeError("x, dt, Bs, Cs must share one dtype")
+    for t in params:
+        if t.dtype != torch.float32:
+            raise TypeError("A_log, dt_bias, Ds must be float32")
+    L = H * W
+    if tuple(dt.shape) != (B, 4, D, L) or tuple(Bs.shape) != (B, 4, N, L) or tuple(Cs.shape) != (B, 4, N, L):
+        raise ValueError("dt must be (B,4,D,L) and Bs, Cs (B,4,N,L)")
+    if tuple(A_log.shape) != (4 * D, N) or tuple(dt_bias.shape) != (4 * D,) or tuple(Ds.shape) != (4 * D,):
+        raise ValueError("A_log must be (4D,N); dt_bias and Ds (4D,)")
+    if out is None:
+        out = torch.empty((B, D, H, W), dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != (B, D, H, W) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B,D,H,W) tensor of x's dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        rc = ss2d_forward(x.data_ptr(), dt.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(), Bs.data_ptr(),
+                          Cs.data_ptr(), Ds.data_ptr(), out.data_ptr(), B, D, H, W, N, code,
+                          stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out

@@ -1,0 +1,186 @@
+// C ABI of libss2d.so: argument validation, planning, launch, error reporting.
+// The declarations and their contract are in include/ss2d.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "ss2d.h"
+#include "ss2d_internal.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;  // 1.0.0
+thread_local char g_last_hip_error[256] = "";
+
+void remember(hipError_t e) {
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Shape checks shared by ss2d_forward and ss2d_describe.
+int check_shape(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
+  if (B < 1 || D < 1 || H < 1 || W < 1) return SS2D_ERR_SHAPE;
+  int64_t L, t;
+  // Every element count and byte count must fit comfortably: the kernels use
+  // 32-bit in-row offsets and 32-bit channel/batch indices.
+  if (!mul_ok(H, W, &L) || L > INT32_MAX / 4) return SS2D_ERR_SHAPE;
+  if (!mul_ok(B, 4, &t) || !mul_ok(t, D, &t) || !mul_ok(t, L, &t) || !mul_ok(t, 4, &t)) return SS2D_ERR_SHAPE;
+  if (B > INT32_MAX / 4 || D > INT32_MAX / 4) return SS2D_ERR_SHAPE;
+  if (N < 1 || N > 16) return SS2D_ERR_UNSUPPORTED_N;
+  if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_DTYPE;
+  return SS2D_OK;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+struct DeviceInfo {
+  int device = -1;
+  size_t lds_limit = 0;
+  hipError_t err = hipSuccess;
+};
+
+// Per-device LDS limit, queried once per device and cached.
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[64];
+
+int device_info(DeviceInfo* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    if (e != hipSuccess) remember(e);
+    return SS2D_ERR_NO_DEVICE;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mutex);
+  if (g_dev[dev].device != dev) {
+    int lds = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) {
+      remember(e);
+      return SS2D_ERR_NO_DEVICE;
+    }
+    g_dev[dev].device = dev;
+    g_dev[dev].lds_limit = (size_t)lds;
+  }
+  *out = g_dev[dev];
+  return SS2D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss2d_version(void) { return kVersion; }
+
+const char* ss2d_last_hip_error(void) { return g_last_hip_error; }
+
+const char* ss2d_status_string(int status) {
+  switch (status) {
+    case SS2D_OK: return "ok";
+    case SS2D_ERR_NULL: return "a required pointer is NULL";
+    case SS2D_ERR_SHAPE: return "invalid shape: B, D, H, W must be >= 1 and sizes must fit";
+    case SS2D_ERR_UNSUPPORTED_N: return "unsupported state size N (supported: 1..16)";
+    case SS2D_ERR_DTYPE: return "unknown dtype (0 = fp32, 1 = bf16)";
+    case SS2D_ERR_ALIAS: return "output y overlaps an input";
+    case SS2D_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case SS2D_ERR_NO_DEVICE: return "no usable HIP device";
+    case SS2D_ERR_HIP: return "a HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, char* buf,
+                  int64_t len) {
+  if (!buf || len < 1) return SS2D_ERR_NULL;
+  const int rc = check_shape(B, D, H, W, N, dtype);
+  if (rc != SS2D_OK) return rc;
+  // Planning uses the gfx950 LDS size (160 KiB) so it works without a device.
+  const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, 160 * 1024);
+  snprintf(buf, (size_t)len,
+           "kernel=chunked_dpp_scan lanes_per_seq=%d waves=%d chans_per_block=%d blocks=%lld "
+           "plane=%s lds_bytes=%zu",
+           pl.lanes_per_seq, pl.waves, pl.chans_per_block, (long long)pl.blocks,
+           pl.lds_plane ? "lds" : (pl.needs_scratch ? "global_scratch" : "global_y"), pl.lds_bytes);
+  return SS2D_OK;
+}
+
+int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                 const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W,
+                 int64_t N, int dtype, void* stream) {
+  if (!x || !dt || !A_log || !dt_bias || !Bs || !Cs || !Ds || !y) return SS2D_ERR_NULL;
+  int rc = check_shape(B, D, H, W, N, dtype);
+  if (rc != SS2D_OK) return rc;
+  const int64_t L = H * W;
+  const int64_t s = dtype == SS2D_BF16 ? 2 : 4;
+  const int64_t xbytes = B * D * L * s, dtbytes = B * 4 * D * L * s, bcbytes = B * 4 * N * L * s;
+  const int64_t pbytes = 4 * D * N * 4, vbytes = 4 * D * 4;
+  if (overlaps(y, xbytes, x, xbytes) || overlaps(y, xbytes, dt, dtbytes) || overlaps(y, xbytes, Bs, bcbytes) ||
+      overlaps(y, xbytes, Cs, bcbytes) || overlaps(y, xbytes, A_log, pbytes) ||
+      overlaps(y, xbytes, dt_bias, vbytes) || overlaps(y, xbytes, Ds, vbytes))
+    return SS2D_ERR_ALIAS;
+  const uintptr_t m = (uintptr_t)(s - 1);
+  if (((uintptr_t)x & m) || ((uintptr_t)dt & m) || ((uintptr_t)Bs & m) || ((uintptr_t)Cs & m) ||
+      ((uintptr_t)y & m) || ((uintptr_t)A_log & 3) || ((uintptr_t)dt_bias & 3) || ((uintptr_t)Ds & 3))
+    return SS2D_ERR_ALIGN;
+  // Vector paths need 16-byte (fp32) or 8-byte (bf16) aligned bases; torch
+  // allocations are, and anything else takes the same path with the rows
+  // re-based, so insist on it here rather than silently slowing down.
+  const uintptr_t vm = (uintptr_t)(4 * s - 1);
+  if (L % 4 == 0 && (((uintptr_t)x & vm) || ((uintptr_t)dt & vm) || ((uintptr_t)Bs & vm) ||
+                     ((uintptr_t)Cs & vm) || ((uintptr_t)y & vm)))
+    return SS2D_ERR_ALIGN;
+
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc != SS2D_OK) return rc;
+  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, di.lds_limit);
+
+  ss2d::LaunchArgs a;
+  a.x = x;
+  a.dt = dt;
+  a.A_log = A_log;
+  a.dt_bias = dt_bias;
+  a.Bs = Bs;
+  a.Cs = Cs;
+  a.Ds = Ds;
+  a.y = y;
+  a.B = B;
+  a.D = D;
+  a.H = H;
+  a.W = W;
+  a.N = N;
+  a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+
+  float* scratch = nullptr;
+  if (plan.needs_scratch) {
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), (size_t)(B * D * L * 4), a.stream);
+    if (e != hipSuccess) {
+      remember(e);
+      return SS2D_ERR_HIP;
+    }
+  }
+  hipError_t e = ss2d::launch_forward(a, plan, scratch);
+  if (scratch) {
+    hipError_t e2 = hipFreeAsync(scratch, a.stream);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  return SS2D_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal interface between the C ABI layer (ss2d_api.hip) and the kernels
+// (ss2d_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss2d {
+
+// Everything a forward launch needs, already validated by the ABI layer.
+struct LaunchArgs {
+  const void* x;
+  const void* dt;
+  const float* A_log;
+  const float* dt_bias;
+  const void* Bs;
+  const void* Cs;
+  const float* Ds;
+  void* y;
+  int64_t B, D, H, W, N;
+  int dtype;  // 0 = fp32, 1 = bf16
+  hipStream_t stream;
+};
+
+// How a shape is mapped onto the machine.
+struct Plan {
+  int lanes_per_seq;     // G: lanes that share one (b, k, d) sequence per chunk
+  int waves;             // waves per workgroup
+  int chans_per_block;   // D channels one workgroup owns
+  int64_t blocks;        // workgroups in the grid
+  bool lds_plane;        // merge plane in LDS (else in an fp32 global buffer)
+  bool needs_scratch;    // global plane is a temporary (bf16 output) rather than y
+  size_t lds_bytes;      // dynamic LDS per workgroup
+};
+
+Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, size_t lds_limit);
+
+// Enqueue the forward.  Returns hipSuccess or the first HIP error.
+hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch_plane);
+
+}  // namespace ss2d

@@ -1,0 +1,114 @@
+"""C-ABI contract of libss2d.so, checked on the CPU (no device work).
+
+The library must load without a GPU, export every function include/ss2d.h
+declares, and reject bad arguments with the documented codes before touching
+the device.  Fake (never dereferenced) addresses are used for pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_scan_crossscan_amd as ss2d
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss2d.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ss2d_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert names == sorted(["ss2d_forward", "ss2d_status_string", "ss2d_last_hip_error", "ss2d_version",
+                            "ss2d_describe"])
+    lib = ctypes.CDLL(ss2d.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    assert ss2d.version() >= 10000
+    for code in range(0, -9, -1):
+        s = ss2d.status_string(code)
+        assert isinstance(s, str) and s
+    assert ss2d.status_string(123) == "unknown status"
+    assert ss2d.lib().ss2d_last_hip_error() is not None
+
+
+def test_describe_plans_the_workloads():
+    s = ss2d.describe(32, 192, 56, 56, 16, ss2d.SS2D_F32)
+    assert "lanes_per_seq=64" in s and "plane=lds" in s
+    s = ss2d.describe(2, 192, 256, 256, 16, ss2d.SS2D_F32)
+    assert "plane=global_y" in s
+    s = ss2d.describe(2, 8, 256, 256, 16, ss2d.SS2D_BF16)
+    assert "plane=global_scratch" in s
+    s = ss2d.describe(32, 768, 14, 14, 16, ss2d.SS2D_F32)
+    assert "lanes_per_seq=16" in s
+
+
+# fake, well-aligned, non-overlapping addresses (never dereferenced: validation fails first)
+BASE = 1 << 40
+X, DT, AL, BI, BS, CS, DS, Y = (BASE + i * (1 << 34) for i in range(8))
+
+
+def _call(x=X, dt=DT, al=AL, bi=BI, bs=BS, cs=CS, ds=DS, y=Y, B=2, D=3, H=4, W=5, N=16, dtype=0):
+    return ss2d.ss2d_forward(x, dt, al, bi, bs, cs, ds, y, B, D, H, W, N, dtype, None)
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_null_pointer(which):
+    args = [X, DT, AL, BI, BS, CS, DS, Y]
+    args[which] = None
+    assert _call(*args) == -1
+
+
+@pytest.mark.parametrize("shape", [(0, 3, 4, 5), (2, 0, 4, 5), (2, 3, 0, 5), (2, 3, 4, 0), (-1, 3, 4, 5),
+                                   (1, 1, 1 << 31, 1 << 31), (1 << 40, 1 << 20, 8, 8)])
+def test_bad_shape(shape):
+    B, D, H, W = shape
+    assert _call(B=B, D=D, H=H, W=W) == -2
+
+
+@pytest.mark.parametrize("N", [0, -1, 17, 256])
+def test_unsupported_state_size(N):
+    assert _call(N=N) == -3
+
+
+@pytest.mark.parametrize("dtype", [2, -1, 7])
+def test_bad_dtype(dtype):
+    assert _call(dtype=dtype) == -4
+
+
+def test_output_aliasing_an_input():
+    assert _call(y=X) == -5
+    assert _call(y=DT + 64) == -5
+    assert _call(y=CS - 16) == -5   # y's range reaches into Cs
+    assert _call(y=AL) == -5
+
+
+def test_misaligned_pointers():
+    assert _call(x=X + 2) == -6
+    assert _call(al=AL + 1) == -6
+    # bf16 elements need 2-byte alignment; with L % 4 == 0 rows need 8-byte alignment
+    assert _call(x=X + 1, dtype=1) == -6
+    assert _call(x=X + 4, dtype=1, H=4, W=4) == -6
+    # fp32 with L % 4 == 0 needs 16-byte aligned bases
+    assert _call(dt=DT + 4, H=4, W=4) == -6
+
+
+def _no_device_here():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_device_here(), reason="only meaningful where no GPU is present")
+def test_valid_call_without_device_reports_no_device():
+    assert _call() == -7

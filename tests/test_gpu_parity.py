@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path against the fp64 CPU oracle, element by element.
+
+Tolerances (fp32 storage): relative L2 <= 1e-5 and max |err| <= 1e-4 * max|y|.
+bf16 storage (fp32 state): relative L2 <= 2e-2 on y.  As a sharper diagnostic,
+the scan part alone (Ds = 0, so y carries no skip term) is held to 1e-4 (fp32)
+and 5e-3 (bf16, output rounding only).  Every call goes through the C ABI.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import ss2d_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _lib():
+    import selective_scan_crossscan_amd as ss2d
+    return ss2d
+
+
+def _dev(inp, dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {}
+    for k, v in inp.items():
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        if k in ("x", "dt", "Bs", "Cs"):
+            t = t.to(tdt)
+        out[k] = t.cuda()
+    return out
+
+
+def gpu_forward(inp, dtype, stream=None):
+    d = _dev(inp, dtype)
+    y = _lib().forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], stream=stream)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def errors(y, ref):
+    diff = y - ref
+    rel_l2 = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    return rel_l2, max_abs, float(np.max(np.abs(ref))) if ref.size else 0.0
+
+
+def check(y, ref, dtype, label=""):
+    assert y.shape == ref.shape
+    assert np.all(np.isfinite(y)), f"{label}: non-finite GPU output"
+    rel_l2, max_abs, ymax = errors(y, ref)
+    print(f"[parity] {label} dtype={dtype} rel_l2={rel_l2:.3e} max_abs={max_abs:.3e} max|y|={ymax:.3e}",
+          flush=True)
+    if dtype == "bf16":
+        assert rel_l2 <= 2e-2, (label, rel_l2)
+    else:
+        assert rel_l2 <= 1e-5, (label, rel_l2)
+        assert max_abs <= 1e-4 * ymax, (label, max_abs, ymax)
+    return rel_l2
+
+
+def check_scan_only(y, ref, dtype, label=""):
+    rel_l2, max_abs, ymax = errors(y, ref)
+    print(f"[parity] {label} scan-only dtype={dtype} rel_l2={rel_l2:.3e}", flush=True)
+    assert rel_l2 <= (5e-3 if dtype == "bf16" else 1e-4), (label, rel_l2)
+
+
+def slice_planes(inp, bsel, dsel):
+    """Inputs of the sub-problem made of batches bsel and channels dsel (exact: planes are independent)."""
+    D = inp["x"].shape[1]
+    N = inp["A_log"].shape[1]
+    bsel, dsel = np.asarray(bsel), np.asarray(dsel)
+    cidx = (np.arange(4)[:, None] * D + dsel[None, :]).reshape(-1)
+    return dict(x=inp["x"][bsel][:, dsel], dt=inp["dt"][bsel][:, :, dsel], A_log=inp["A_log"][cidx],
+                dt_bias=inp["dt_bias"][cidx], Ds=inp["Ds"][cidx], Bs=inp["Bs"][bsel], Cs=inp["Cs"][bsel])
+
+
+# ------------------------------------------------------------------ the five workloads
+@pytest.mark.parametrize("ci", range(5))
+def test_workload_parity(ci):
+    shape = ss2d_inputs.CONFIGS[ci]
+    print(f"[case] workload {ci} {shape}", flush=True)
+    inp = ss2d_inputs.generate(shape, seed=0)
+    y = gpu_forward(inp, shape.dtype)
+    full = shape.updates <= 2e9 and (os.cpu_count() or 1) >= 8
+    if full:
+        ref = oracle.ss2d_inputs_f64(inp)
+        check(y, ref, shape.dtype, f"workload{ci} full")
+    else:
+        rng = np.random.default_rng(ci)
+        bsel = sorted(set([0, shape.B - 1] + list(rng.integers(0, shape.B, 2))))
+        dsel = sorted(set([0, 1, shape.D - 1] + list(rng.integers(0, shape.D, 5))))
+        ref = oracle.ss2d_inputs_f64(slice_planes(inp, bsel, dsel))
+        check(y[np.ix_(bsel, dsel)], ref, shape.dtype, f"workload{ci} sampled")
+        assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("ci", [0, 1, 3])
+def test_workload_scan_only(ci):
+    """Ds = 0: y is the scan output alone, ~6x more sensitive than y with the skip term."""
+    shape = ss2d_inputs.CONFIGS[ci]
+    inp = ss2d_inputs.generate(shape, seed=1)
+    inp["Ds"][:] = 0.0
+    y = gpu_forward(inp, shape.dtype)
+    if ci == 0:
+        ref, yy = oracle.ss2d_inputs_f64(inp), y
+    else:
+        bsel, dsel = [0, shape.B - 1], [0, 7, shape.D - 1]
+        ref, yy = oracle.ss2d_inputs_f64(slice_planes(inp, bsel, dsel)), y[np.ix_(bsel, dsel)]
+    check_scan_only(yy, ref, shape.dtype, f"workload{ci}")
+
+
+# ------------------------------------------------------------------ edge shapes and values
+EDGE = [
+    # B, D, H, W, N, dtype
+    (1, 1, 1, 1, 16, "f32"),      # L = 1
+    (2, 3, 3, 5, 16, "f32"),      # non-square, L % 4 != 0 (scalar paths)
+    (2, 5, 5, 3, 7, "f32"),       # transposed shape, odd N
+    (1, 16, 7, 9, 1, "f32"),      # N = 1, L = 63
+    (3, 17, 8, 8, 16, "f32"),     # D not a multiple of the channel block
+    (1, 4, 1, 37, 16, "f32"),     # H = 1
+    (1, 4, 37, 1, 16, "f32"),     # W = 1
+    (2, 6, 16, 16, 16, "f32"),    # 32-lane groups
+    (2, 5, 24, 32, 16, "f32"),    # 64-lane groups, tail chunks
+    (1, 3, 33, 31, 16, "f32"),    # ragged tail, odd L
+    (1, 2, 100, 90, 16, "f32"),   # several full chunks + tails
+    (1, 2, 128, 128, 16, "f32"),  # plane in global memory (y)
+    (1, 3, 128, 128, 5, "bf16"),  # plane in a global fp32 temporary
+    (2, 3, 5, 7, 16, "bf16"),
+    (2, 9, 28, 28, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,D,H,W,N,dtype", EDGE)
+def test_edge_shapes(B, D, H, W, N, dtype):
+    print(f"[case] edge B={B} D={D} H={H} W={W} N={N} {dtype}", flush=True)
+    inp = ss2d_inputs.tiny_random(B, D, H, W, N, seed=B * 1000 + D * 100 + H * 10 + W, dtype=dtype)
+    y = gpu_forward(inp, dtype)
+    check(y, oracle.ss2d_inputs_f64(inp), dtype, f"edge {B}x{D}x{H}x{W} N={N}")
+    inp["Ds"][:] = 0.0
+    y = gpu_forward(inp, dtype)
+    check_scan_only(y, oracle.ss2d_inputs_f64(inp), dtype, f"edge {B}x{D}x{H}x{W} N={N}")
+
+
+@pytest.mark.parametrize("bias", [-14.0, -6.0, 0.0, 3.0, 12.0, 25.0])
+def test_step_size_range(bias):
+    """Tiny to large delta: softplus in both branches, decays from ~1 to ~0."""
+    inp = ss2d_inputs.tiny_random(1, 4, 9, 11, 16, seed=7)
+    inp["dt_bias"][:] = bias
+    y = gpu_forward(inp, "f32")
+    check(y, oracle.ss2d_inputs_f64(inp), "f32", f"bias={bias}")
+
+
+def test_softplus_accuracy():
+    """L = 1, N = 1, B = C = 1, D = 0, x = 1: every direction contributes exactly delta."""
+    v = np.linspace(-20, 20, 4 * 401).astype(np.float32).reshape(4, 401)
+    D = v.shape[1]
+    inp = dict(x=np.ones((1, D, 1, 1), np.float32), dt=np.zeros((1, 4, D, 1), np.float32),
+               A_log=np.zeros((4 * D, 1), np.float32), dt_bias=v.reshape(-1), Bs=np.ones((1, 4, 1, 1), np.float32),
+               Cs=np.ones((1, 4, 1, 1), np.float32), Ds=np.zeros(4 * D, np.float32))
+    y = gpu_forward(inp, "f32").reshape(-1)
+    ref = oracle.ss2d_inputs_f64(inp).reshape(-1)
+    rel = np.abs(y - ref) / np.abs(ref)
+    print(f"[softplus] max rel err {rel.max():.3e}", flush=True)
+    assert rel.max() < 2e-6
+
+
+def test_deterministic_and_stream():
+    inp = ss2d_inputs.tiny_random(2, 8, 20, 24, 16, seed=11)
+    y1 = gpu_forward(inp, "f32")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y2 = gpu_forward(inp, "f32", stream=s)
+    assert np.array_equal(y1, y2)
+
+
+def test_nan_propagates_like_the_oracle():
+    inp = ss2d_inputs.tiny_random(1, 2, 4, 6, 16, seed=13)
+    inp["x"][0, 1, 2, 3] = np.nan
+    y = gpu_forward(inp, "f32")
+    ref = oracle.ss2d_inputs_f64(inp)
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    if ok.any():
+        np.testing.assert_allclose(y[ok], ref[ok], rtol=1e-5, atol=1e-5)
+
+
+def test_output_fully_overwritten():
+    inp = ss2d_inputs.tiny_random(1, 3, 6, 6, 16, seed=17)
+    d = _dev(inp, "f32")
+    out = torch.full((1, 3, 6, 6), float("nan"), device="cuda")
+    _lib().forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], out=out)
+    torch.cuda.synchronize()
+    check(out.double().cpu().numpy(), oracle.ss2d_inputs_f64(inp), "f32", "overwrite")
