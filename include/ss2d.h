@@ -64,11 +64,11 @@ typedef enum {
  *
  * Behaviour: arguments are validated before any device work (codes above).  On
  * SS2D_OK the work has been enqueued asynchronously; execution faults surface at
- * the caller's next synchronisation.  Nothing is printed, thrown or aborted.  The
- * library keeps no state between calls besides cached device properties, except
- * that a bf16 call whose per-channel plane exceeds on-chip memory uses a
- * stream-ordered temporary fp32 buffer (allocated and freed on `stream`).
- * NaN and Inf propagate.  Thread-safe.
+ * the caller's next synchronisation.  Nothing is printed, thrown or aborted.
+ * Each call takes a stream-ordered temporary of B*D*H*W fp32 values (2*B*D*H*W
+ * for bf16) for the merge, allocated and freed on `stream` from the device's
+ * default memory pool (whose release threshold the library raises so freed
+ * blocks are reused).  NaN and Inf propagate.  Thread-safe.
  */
 int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
                  const void* Bs, const void* Cs, const float* Ds, void* y,
@@ -87,11 +87,19 @@ int ss2d_version(void);
 /*
  * ss2d_describe -- write a one-line, NUL-terminated description of how
  * ss2d_forward would run this shape (kernel variant, lanes per sequence,
- * channels per workgroup, chunk plan, where the merge plane lives) into
+ * channels per workgroup, grid size, LDS and temporary sizes) into
  * buf[0..len).  Host only; no device work.  Returns SS2D_OK or a validation code.
  */
 int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
                   char* buf, int64_t len);
+
+/*
+ * ss2d_set_lanes_per_seq -- benchmarking knob: force the number of lanes that
+ * share one sequence chunk (16, 32 or 64), or 0 to restore the automatic choice.
+ * Process-wide; affects later ss2d_forward and ss2d_describe calls.  Returns
+ * SS2D_OK, or SS2D_ERR_SHAPE for any other value.
+ */
+int ss2d_set_lanes_per_seq(int lanes);
 
 #ifdef __cplusplus
 }

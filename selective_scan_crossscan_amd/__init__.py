@@ -11,7 +11,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["forward", "ss2d_forward", "describe", "status_string", "version", "library_path", "lib",
+__all__ = ["forward", "ss2d_forward", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
            "SS2D_F32", "SS2D_BF16", "SS2DError"]
 
 SS2D_F32 = 0
@@ -53,6 +53,8 @@ def lib():
             L.ss2d_version.restype = ctypes.c_int
             L.ss2d_describe.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.c_char_p, i64]
             L.ss2d_describe.restype = ctypes.c_int
+            L.ss2d_set_lanes_per_seq.argtypes = [ctypes.c_int]
+            L.ss2d_set_lanes_per_seq.restype = ctypes.c_int
             _lib = L
     return _lib
 
@@ -71,6 +73,13 @@ def describe(B, D, H, W, N, dtype=SS2D_F32) -> str:
     if rc != 0:
         raise SS2DError(rc, status_string(rc))
     return buf.value.decode()
+
+
+def set_lanes_per_seq(lanes: int) -> None:
+    """Benchmarking knob: force 16/32/64 lanes per sequence chunk (0 = automatic)."""
+    rc = lib().ss2d_set_lanes_per_seq(int(lanes))
+    if rc != 0:
+        raise SS2DError(rc, status_string(rc))
 
 
 def ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, stream) -> int:

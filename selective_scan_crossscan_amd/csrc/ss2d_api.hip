@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "ss2d.h"
@@ -47,13 +48,11 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 struct DeviceInfo {
   int device = -1;
-  size_t lds_limit = 0;
-  hipError_t err = hipSuccess;
 };
 
-// Per-device LDS limit, queried once per device and cached.
+// Per-device one-time setup (stream-ordered memory pool keeps freed scratch).
 std::mutex g_dev_mutex;
-DeviceInfo g_dev[64];
+bool g_dev_ready[64];
 
 int device_info(DeviceInfo* out) {
   int dev = -1;
@@ -63,25 +62,39 @@ int device_info(DeviceInfo* out) {
     return SS2D_ERR_NO_DEVICE;
   }
   std::lock_guard<std::mutex> lk(g_dev_mutex);
-  if (g_dev[dev].device != dev) {
-    int lds = 0;
-    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (!g_dev_ready[dev]) {
+    hipMemPool_t pool;
+    e = hipDeviceGetDefaultMemPool(&pool, dev);
     if (e != hipSuccess) {
       remember(e);
       return SS2D_ERR_NO_DEVICE;
     }
-    g_dev[dev].device = dev;
-    g_dev[dev].lds_limit = (size_t)lds;
+    // Keep freed scratch in the pool between calls instead of returning it to the system.
+    uint64_t threshold = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    if (e != hipSuccess) {
+      remember(e);
+      return SS2D_ERR_NO_DEVICE;
+    }
+    g_dev_ready[dev] = true;
   }
-  *out = g_dev[dev];
+  out->device = dev;
   return SS2D_OK;
 }
+
+std::atomic<int> g_lanes_override{0};
 
 }  // namespace
 
 extern "C" {
 
 int ss2d_version(void) { return kVersion; }
+
+int ss2d_set_lanes_per_seq(int lanes) {
+  if (lanes != 0 && lanes != 16 && lanes != 32 && lanes != 64) return SS2D_ERR_SHAPE;
+  g_lanes_override.store(lanes);
+  return SS2D_OK;
+}
 
 const char* ss2d_last_hip_error(void) { return g_last_hip_error; }
 
@@ -105,13 +118,12 @@ int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dty
   if (!buf || len < 1) return SS2D_ERR_NULL;
   const int rc = check_shape(B, D, H, W, N, dtype);
   if (rc != SS2D_OK) return rc;
-  // Planning uses the gfx950 LDS size (160 KiB) so it works without a device.
-  const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, 160 * 1024);
+  const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
   snprintf(buf, (size_t)len,
            "kernel=chunked_dpp_scan lanes_per_seq=%d waves=%d chans_per_block=%d blocks=%lld "
-           "plane=%s lds_bytes=%zu",
-           pl.lanes_per_seq, pl.waves, pl.chans_per_block, (long long)pl.blocks,
-           pl.lds_plane ? "lds" : (pl.needs_scratch ? "global_scratch" : "global_y"), pl.lds_bytes);
+           "lds_bytes=%zu scratch_bytes=%zu",
+           pl.lanes_per_seq, pl.waves, pl.chans_per_block, (long long)pl.blocks, pl.lds_bytes,
+           pl.scratch_bytes);
   return SS2D_OK;
 }
 
@@ -144,7 +156,7 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
   DeviceInfo di;
   rc = device_info(&di);
   if (rc != SS2D_OK) return rc;
-  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, di.lds_limit);
+  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
 
   ss2d::LaunchArgs a;
   a.x = x;
@@ -164,18 +176,16 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
   a.stream = static_cast<hipStream_t>(stream);
 
   float* scratch = nullptr;
-  if (plan.needs_scratch) {
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), (size_t)(B * D * L * 4), a.stream);
+  {
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), plan.scratch_bytes, a.stream);
     if (e != hipSuccess) {
       remember(e);
       return SS2D_ERR_HIP;
     }
   }
   hipError_t e = ss2d::launch_forward(a, plan, scratch);
-  if (scratch) {
-    hipError_t e2 = hipFreeAsync(scratch, a.stream);
-    if (e == hipSuccess) e = e2;
-  }
+  hipError_t e2 = hipFreeAsync(scratch, a.stream);
+  if (e == hipSuccess) e = e2;
   if (e != hipSuccess) {
     remember(e);
     return SS2D_ERR_HIP;

@@ -28,14 +28,15 @@ struct Plan {
   int waves;             // waves per workgroup
   int chans_per_block;   // D channels one workgroup owns
   int64_t blocks;        // workgroups in the grid
-  bool lds_plane;        // merge plane in LDS (else in an fp32 global buffer)
-  bool needs_scratch;    // global plane is a temporary (bf16 output) rather than y
   size_t lds_bytes;      // dynamic LDS per workgroup
+  size_t scratch_bytes;  // fp32 merge planes in device memory (temporary)
 };
 
-Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, size_t lds_limit);
+// lanes_override: 0 = automatic, else 16, 32 or 64 lanes per sequence.
+Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override);
 
-// Enqueue the forward.  Returns hipSuccess or the first HIP error.
-hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch_plane);
+// Enqueue the forward.  `scratch` holds plan.scratch_bytes.  Returns hipSuccess
+// or the first HIP error.
+hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch);
 
 }  // namespace ss2d

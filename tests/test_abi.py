@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["ss2d_forward", "ss2d_status_string", "ss2d_last_hip_error", "ss2d_version",
-                            "ss2d_describe"])
+                            "ss2d_describe", "ss2d_set_lanes_per_seq"])
     lib = ctypes.CDLL(ss2d.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -42,13 +42,23 @@ def test_version_and_strings():
 
 def test_describe_plans_the_workloads():
     s = ss2d.describe(32, 192, 56, 56, 16, ss2d.SS2D_F32)
-    assert "lanes_per_seq=64" in s and "plane=lds" in s
-    s = ss2d.describe(2, 192, 256, 256, 16, ss2d.SS2D_F32)
-    assert "plane=global_y" in s
-    s = ss2d.describe(2, 8, 256, 256, 16, ss2d.SS2D_BF16)
-    assert "plane=global_scratch" in s
+    assert "lanes_per_seq=32" in s and "chans_per_block=8" in s and "blocks=768" in s
+    assert f"scratch_bytes={32 * 192 * 3136 * 4}" in s
+    s = ss2d.describe(64, 384, 28, 28, 16, ss2d.SS2D_BF16)
+    assert f"scratch_bytes={2 * 64 * 384 * 784 * 4}" in s
     s = ss2d.describe(32, 768, 14, 14, 16, ss2d.SS2D_F32)
-    assert "lanes_per_seq=16" in s
+    assert "lanes_per_seq=16" in s and "chans_per_block=16" in s
+
+
+def test_lanes_override_knob():
+    lib = ss2d.lib()
+    assert lib.ss2d_set_lanes_per_seq(64) == 0
+    try:
+        assert "lanes_per_seq=64" in ss2d.describe(32, 192, 56, 56, 16)
+        assert lib.ss2d_set_lanes_per_seq(48) == -2
+    finally:
+        assert lib.ss2d_set_lanes_per_seq(0) == 0
+    assert "lanes_per_seq=32" in ss2d.describe(32, 192, 56, 56, 16)
 
 
 # fake, well-aligned, non-overlapping addresses (never dereferenced: validation fails first)

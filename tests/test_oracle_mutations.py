@@ -21,7 +21,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ss2d_oracle.c")
 MUTATIONS = {
     "drop_skip_term": ("out[l] = Ds[c] * u[l];", "out[l] = 0.0;"),
     "wrong_sign_of_A": ("const double A = -exp(", "const double A = -1.0 + 0.0 * exp("),
-    "column_walk_swapped": ("return row * W + col;", "return (step % W) * W + step / W;"),
+    "column_walk_as_row_walk": ("return row * W + col;", "return col * H + row;"),
     "reverse_not_reversed": ("(k >= 2) ? (L - 1 - l) : l", "l"),
     "softplus_is_exp": ("return log1p(exp(v));", "return exp(v);"),
     "output_before_update": ("h = exp(delta[l] * A) * h + delta[l] * Bp[l] * u[l];\n          out[l] += Cp[l] * h;",
