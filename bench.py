@@ -17,6 +17,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -41,7 +42,12 @@ PEAK_UPDATES_PER_S = CUS * CLOCK_HZ * VALU_LANES_PER_CLK / SLOTS_PER_UPDATE  # 9
 KERNEL_SOURCES = ["selective_scan_crossscan_amd/csrc/ss2d_kernels.hip",
                   "selective_scan_crossscan_amd/csrc/ss2d_api.hip",
                   "selective_scan_crossscan_amd/csrc/ss2d_internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_PREFIX = "ss2d_forward_kernel"
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"ss2d_forward_kernel_{workload}_hbm_traffic.md")
 
 
 def kernel_source_hash() -> str:
@@ -56,16 +62,15 @@ def measured_traffic(workload: str):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
     scaled by the copy-kernel calibration; None when absent or the kernel changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+        with open(traffic_file(workload)) as f:
+            text = f.read()
+        m = re.search(r"```json\n(.*?)\n```", text, re.S)
+        rec = json.loads(m.group(1)) if m else {}
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload:
         return None
-    w = rec.get("workloads", {}).get(workload)
-    if not w:
-        return None
-    return w.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_model() -> str:
@@ -79,6 +84,106 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+# The profiling commands whose output --summarize-profile turns into the text summaries under profiles/.
+# Each runs from the repository root; {d} is the output folder and {c} the workload index.
+PROFILE_COMMANDS = {
+    "stats": "rocprofv3 --kernel-trace --stats -f csv -d {d} -o stats -- "
+             "python bench.py --config {c} --steps 20 --warmup 5 --no-cpu-baseline > {d}/stats_bench.json",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d} -o fetch -- "
+             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mib 512",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d} -o write -- "
+             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mib 512",
+}
+COPY_PROBE_MIB = 512
+
+
+def _find(folder: str, suffix: str) -> str:
+    import glob
+    hits = sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {folder}")
+    return hits[0]
+
+
+def _counter_rows(folder: str, prefix: str):
+    import csv
+    with open(_find(folder, f"{prefix}_counter_collection.csv")) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(folder: str, cfg: int) -> int:
+    """Write the rocprofv3 summaries of one workload into profiles/ (text only)."""
+    import csv
+    shape = ss2d_inputs.CONFIGS[cfg]
+    os.makedirs(PROFILES, exist_ok=True)
+    cmds = {k: v.format(d=folder, c=cfg) for k, v in PROFILE_COMMANDS.items()}
+
+    # Kernel-trace statistics, next to the bench line printed by the same run.
+    with open(_find(folder, "stats_kernel_stats.csv")) as f:
+        stats = list(csv.DictReader(f))
+    with open(os.path.join(folder, "stats_bench.json")) as f:
+        bench_line = [ln for ln in f.read().splitlines() if ln.startswith("{")][-1]
+    bench = json.loads(bench_line)
+    lines = [f"# ss2d_forward_kernel — {shape.name} — rocprofv3 kernel trace", "",
+             f"Workload: {shape}.  Updates per launch: {shape.updates:.4e}; "
+             f"algorithmic bytes per launch: {shape.algorithmic_bytes:.4e}.", "",
+             "Command (from the repository root):", "", "```", cmds["stats"], "```", "",
+             "| kernel | calls | average µs | min µs | max µs | share |", "|---|---|---|---|---|---|"]
+    kern_avg = None
+    for r in stats:
+        name = r["Name"]
+        if len(name) > 90:
+            name = name[:87] + "..."
+        avg = float(r["AverageNs"]) / 1e3
+        if KERNEL_PREFIX in r["Name"]:
+            kern_avg = avg
+        lines.append(f"| `{name}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    lines += ["", f"bench.py's own HIP-event average over the timed steps of this run: "
+                  f"{bench['kernel_us']:.1f} µs per launch (roofline frac {bench['roofline']['frac']:.3f}).",
+              f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs.", "",
+              "Bench line of this run:", "", "```json", bench_line, "```", ""]
+    with open(os.path.join(PROFILES, f"ss2d_forward_kernel_{shape.name}_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines))
+
+    # HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), calibrated on a plain device copy.
+    per = {}
+    for counter, prefix in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = [r for r in _counter_rows(folder, prefix) if r["Counter_Name"] == counter]
+        kern = [float(r["Counter_Value"]) for r in rows if KERNEL_PREFIX in r["Kernel_Name"]]
+        other = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if KERNEL_PREFIX not in r["Kernel_Name"]]
+        probe_kib, probe_name = max(other)
+        expected_kib = COPY_PROBE_MIB * 1024.0
+        per[counter] = {"kernel_kib_per_dispatch": sum(kern) / len(kern), "dispatches": len(kern),
+                        "copy_probe_kib": probe_kib, "copy_probe_kernel": probe_name,
+                        "copy_expected_kib": expected_kib, "scale": expected_kib / probe_kib}
+    fetch_b = per["FETCH_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["FETCH_SIZE"]["scale"]
+    write_b = per["WRITE_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["WRITE_SIZE"]["scale"]
+    rec = {"workload": shape.name, "kernel_source_hash": kernel_source_hash(),
+           "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
+           "algorithmic_bytes": shape.algorithmic_bytes, "counters": per}
+    lines = [f"# ss2d_forward_kernel — {shape.name} — HBM traffic (rocprofv3 counters)", "",
+             "Two counter runs, one counter each, from the repository root:", "", "```", cmds["fetch"],
+             cmds["write"], "```", "",
+             f"Each run also performs one {COPY_PROBE_MIB} MiB device-to-device copy; the scale factor is the "
+             "copy's known size divided by what the same counter reads for it.", "",
+             "| counter | kernel KiB / dispatch | copy probe KiB | copy expected KiB | scale | kernel bytes |",
+             "|---|---|---|---|---|---|"]
+    for counter, b in (("FETCH_SIZE", fetch_b), ("WRITE_SIZE", write_b)):
+        c = per[counter]
+        lines.append(f"| {counter} | {c['kernel_kib_per_dispatch']:.0f} | {c['copy_probe_kib']:.0f} | "
+                     f"{c['copy_expected_kib']:.0f} | {c['scale']:.4f} | {b / 1e6:.1f} MB |")
+    lines += ["", f"HBM traffic per launch: {(fetch_b + write_b) / 1e6:.1f} MB against "
+                  f"{shape.algorithmic_bytes / 1e6:.1f} MB algorithmic "
+                  f"(ratio {(fetch_b + write_b) / shape.algorithmic_bytes:.2f}).", "",
+              "Record read by bench.py (valid only while the kernel sources hash to the value below):", "",
+              "```json", json.dumps(rec, indent=1), "```", ""]
+    with open(traffic_file(shape.name), "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote profiles for {shape.name}: kernel avg {kern_avg:.1f} us, traffic {(fetch_b + write_b) / 1e6:.1f} MB")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,7 +194,11 @@ def main() -> int:
     ap.add_argument("--lanes", type=int, default=0, help="force lanes per sequence chunk (16/32/64; 0 = auto)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="turn the rocprofv3 output of PROFILE_COMMANDS in DIR into the summaries under profiles/")
     args = ap.parse_args()
+    if args.summarize_profile:
+        return summarize_profile(args.summarize_profile, args.config)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
