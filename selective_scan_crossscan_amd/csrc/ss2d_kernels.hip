@@ -10,7 +10,7 @@
 //   §3.3     y[p] = sum over the four directions of out at the step visiting p.
 //
 // How it runs.  One workgroup owns one batch b and a block of CH channels and
-// does the four directions one after the other, in the order 0, 2, 1, 3.
+// does the four directions one after the other, in the order 1, 3, 0, 2.
 //   * A sequence (b, k, d) is cut into chunks of G*T steps; a group of G lanes
 //     owns one channel's chunk, T consecutive steps per lane.
 //   * Per state n a lane turns its T steps into decays a_i = 2^(delta_i*A*log2 e)
@@ -23,17 +23,17 @@
 //     (A2 A1, A2 B1 + B2) is associative, so this equals the sequential loop up
 //     to rounding order.
 //   * Bs/Cs of a chunk are shared by every channel of the workgroup.  They are
-//     staged through LDS in groups of NG states: while the lanes work through
-//     one group, each thread holds its share of the next group in registers
-//     (coalesced 16-byte loads issued a whole group ahead), writes it to the
-//     other LDS buffer, and the workgroup synchronises once per group.  Lanes
-//     read their steps back with conflict-free 16-byte LDS loads.
-//   * Merge: directions 0 and 2 accumulate into a row-major fp32 plane (y itself
-//     for fp32 output), directions 1 and 3 into a column-major fp32 plane, so
-//     every access is contiguous along the lane's steps; a final pass adds the
-//     column plane into y through 32x32 LDS-tiled transposes.  The order of
-//     additions is fixed, y = (y0 + y2) + (y1 + y3): deterministic, no atomics.
-//     (Four separate store-only planes summed at the end measured slower.)
+//     copied global -> LDS by DMA (the vector load's LDS form: no registers, no
+//     wait) in groups of NG states, one group ahead into a two-buffer ring, and
+//     dt one chunk ahead; the workgroup synchronises once per group.  The LDS
+//     rows are XOR-swizzled so lanes read their steps with conflict-free
+//     16-byte loads.
+//   * Merge: directions 1 and 3 accumulate into a column-major fp32 plane and
+//     direction 0 into a row-major one (y itself for fp32 output), so every
+//     access is contiguous along the lane's steps.  Direction 2, last, reads
+//     both and writes y = (y0 + y2) + (y1 + y3), rounded once: the order of
+//     additions is fixed, so results are deterministic, with no atomics and no
+//     separate merge pass.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,6 +77,9 @@ struct Io<float> {
     return *reinterpret_cast<const float4*>(p + i);
   }
   static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
+  static __device__ __forceinline__ void st4(float* p, int64_t i, float4 v) {  // i % 4 == 0
+    *reinterpret_cast<float4*>(p + i) = v;
+  }
 };
 
 template <>
@@ -88,6 +91,12 @@ struct Io<uint16_t> {
                        bf16_to_f32(v.y >> 16));
   }
   static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_rne(v); }
+  static __device__ __forceinline__ void st4(uint16_t* p, int64_t i, float4 v) {  // i % 4 == 0
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+    u.y = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+    *reinterpret_cast<uint2*>(p + i) = u;
+  }
 };
 
 // Four values at positions i..i+3 of a row of length L, zero past the end.
@@ -178,10 +187,136 @@ struct Cfg {
   static constexpr int kChans = kWaves * (64 / G);  // channels per workgroup
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kSS = seg_stride<T>();
-  static constexpr int kArr = G * kSS;               // LDS floats of one staged (state, B or C)
-  static constexpr int kBuf = NG * 2 * kArr;         // one staging buffer
-  static constexpr int kLds = 2 * kBuf + 2 * kChans * kMaxN + 2 * kChans;  // floats
+  static constexpr int kArr = G * kSS;               // LDS floats of one register-staged (state, B or C)
+  static constexpr int kBuf = NG * 2 * kArr;         // one register-staged buffer
 };
+
+// LDS of a workgroup (bytes), for storage type S.  Separate arrays, so the
+// compiler can tell a DMA copy into one from reads of another and does not
+// make those reads wait for the copy.
+//   ring0, ring1  one Bs/Cs group each, copied in by DMA: [NG][B|C][G*T] of S;
+//                 ring0 also holds the register-staged group of a remainder
+//                 chunk and the tile of the final transpose
+//   dtb           dt of the next full chunk, copied in by DMA: [kChans][G*T] of S
+//   par           A*log2(e) and the carried state per (channel, state), then
+//                 dt_bias and Ds per channel
+template <typename S, int G, int T, int NG, bool VEC>
+struct Layout {
+  using C = Cfg<G, T, NG>;
+  static constexpr int kGT = G * T;
+  static constexpr int kGroupBytes = NG * 2 * kGT * (int)sizeof(S);
+  // one register-staged group: remainder chunks (at most 8 steps per lane), or
+  // every chunk when rows are not aligned for the DMA copy
+  static constexpr int kStagedBytes = NG * 2 * G * seg_stride<VEC ? 8 : T>() * 4;
+  static constexpr int kTileBytes = 32 * 33 * 4;
+  static constexpr int kRing0Bytes = kGroupBytes > kStagedBytes ? (kGroupBytes > kTileBytes ? kGroupBytes : kTileBytes)
+                                                                : (kStagedBytes > kTileBytes ? kStagedBytes : kTileBytes);
+  static constexpr int kDtBytes = C::kChans * kGT * (int)sizeof(S);
+  static constexpr int kParFloats = 2 * C::kChans * kMaxN + 2 * C::kChans;
+  static constexpr int kBytes = kRing0Bytes + kGroupBytes + kDtBytes + 4 * kParFloats;
+};
+
+// ------------------------------------------------------------------ DMA staging
+// Rows of G*T elements are copied global -> LDS with the DMA form of the vector
+// load (each lane's element goes straight to LDS; no registers, no wait until
+// the data is needed).  One wave-wide copy writes 64 consecutive granules, so
+// bank-conflict avoidance cannot use padding; instead the 16-byte slots of a
+// lane segment (T elements) are XOR-swizzled: slot q of segment s is stored at
+// s*SP + (q ^ ((s / (16/SP)) & (SP-1))), SP = slots per segment.  Sixteen
+// consecutive segments read at the same q then land on sixteen different
+// 16-byte bank groups.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <typename S, int T>
+struct Swz {
+  static constexpr int kEps = 16 / (int)sizeof(S);  // elements per 16-byte slot
+  static constexpr int kSP = T / kEps;              // slots per segment
+  static constexpr int kSpan = 16 / kSP;            // segments per sweep of the 16 bank groups
+  static_assert(kSP >= 1 && (kSP & (kSP - 1)) == 0, "segment must be a power-of-two number of slots");
+  static __device__ __forceinline__ int swz(int seg) { return (seg / kSpan) & (kSP - 1); }
+};
+
+// Wait until this wave's outstanding vector-memory operations (DMA copies
+// included) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// A copy of R rows of G*T elements into LDS, swizzled, split over the
+// workgroup: each lane moves GB bytes per copy instruction (16: fp32 rows
+// 16-byte aligned, else 4), a wave 64*GB bytes, which never straddle two rows.
+// The swizzle repeats every kPeriod = 16*SP slots, and a wave's copies all
+// start at the same offset inside that period, so a lane's element offset is a
+// per-lane constant plus a wave-uniform part: the address is a scalar row base
+// plus one 32-bit lane offset computed once.
+template <typename S, int G, int T, int R, int GB>
+struct DmaPlan {
+  using Z = Swz<S, T>;
+  static constexpr int kRowBytes = G * T * (int)sizeof(S);
+  static constexpr int kNth = kWaves * 64;
+  static constexpr int kGranules = R * kRowBytes / GB;
+  static constexpr int kIters = kGranules / kNth;
+  static constexpr int kPeriod = 16 * Z::kSP * 16;  // bytes
+  static_assert(kGranules % kNth == 0, "DMA copy must split evenly over the workgroup");
+  static_assert(kRowBytes % (64 * GB) == 0, "a wave's copy must stay inside one row");
+  static_assert((kNth * GB) % kPeriod == 0 && kRowBytes % kPeriod == 0,
+                "a wave's copies must sit at one offset inside the swizzle period");
+  int wave;
+  uint32_t lane_elem;
+
+  __device__ __forceinline__ explicit DmaPlan(int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rb = (wave * 64 * GB) % kPeriod + (tid & 63) * GB;  // lane's byte inside its period
+    const int slot = rb >> 4;
+    const int seg = slot / Z::kSP;
+    const int q = (slot % Z::kSP) ^ Z::swz(seg);
+    lane_elem = seg * T + q * Z::kEps + (rb & 15) / (int)sizeof(S);
+  }
+
+  // Every thread of the workgroup calls it; row r starts at src(r) + c0.
+  template <typename RowFn>
+  __device__ __forceinline__ void copy(char* dst, RowFn src, int c0) const {
+    // Opaque copies of the plan: the addresses are cheap to form here, and
+    // hoisted out of the main loop they would hold registers through it.
+    int w = wave;
+    uint32_t le = lane_elem;
+    asm volatile("" : "+s"(w), "+v"(le));
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int wbyte = (it * kNth + w * 64) * GB;  // first byte of this wave's copy
+      const int rowb = wbyte % kRowBytes;
+      const S* base = src(wbyte / kRowBytes) + c0 + (rowb - rowb % kPeriod) / (int)sizeof(S);
+      const S* g = base + le;
+      if constexpr (GB == 16)
+        __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + wbyte), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + wbyte), 4, 0, 0);
+    }
+  }
+};
+
+// The T elements of segment `seg` of a swizzled row, as floats.
+template <typename S, int T>
+__device__ __forceinline__ void read_seg(const char* row, int seg, float (&v)[T]) {
+  using Z = Swz<S, T>;
+  const int sw = Z::swz(seg);
+#pragma unroll
+  for (int q = 0; q < Z::kSP; ++q) {
+    const uint4 r = *reinterpret_cast<const uint4*>(row + (seg * Z::kSP + (q ^ sw)) * 16);
+    if constexpr (sizeof(S) == 4) {
+      v[q * 4 + 0] = __uint_as_float(r.x);
+      v[q * 4 + 1] = __uint_as_float(r.y);
+      v[q * 4 + 2] = __uint_as_float(r.z);
+      v[q * 4 + 3] = __uint_as_float(r.w);
+    } else {
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[q * 8 + 2 * j] = __uint_as_float(w[j] << 16);
+        v[q * 8 + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    }
+  }
+}
 
 // Walk index (row-major index for row walks, w*H+h for column walks) of step l.
 __device__ __forceinline__ int walk_index(bool rev, int l, int L) { return rev ? (L - 1 - l) : l; }
@@ -189,19 +324,9 @@ __device__ __forceinline__ int walk_index(bool rev, int l, int L) { return rev ?
 // dt and u for T consecutive steps from l0.  FULL: all steps exist (no bounds
 // checks).  VEC: rows are aligned for 16-byte (fp32) / 8-byte (bf16) loads.
 template <typename S, int T, bool VEC, bool FULL>
-__device__ __forceinline__ void load_inputs(const S* dtrow, const S* xrow, bool rev, bool col, int l0, int L, int H,
-                                            int W, float (&dtv)[T], float (&uv)[T]) {
+__device__ __forceinline__ void load_x(const S* xrow, bool rev, bool col, int l0, int L, int H, int W,
+                                       float (&uv)[T]) {
   constexpr bool V4 = VEC && FULL && (T % 4 == 0);
-  if constexpr (V4) {
-#pragma unroll
-    for (int i = 0; i < T; i += 4) {
-      const float4 q = Io<S>::ld4(dtrow, l0 + i);
-      dtv[i] = q.x; dtv[i + 1] = q.y; dtv[i + 2] = q.z; dtv[i + 3] = q.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < T; ++i) dtv[i] = (FULL || l0 + i < L) ? Io<S>::ld(dtrow, l0 + i) : 0.f;
-  }
   if (!col) {
     if constexpr (V4) {
       if (!rev) {
@@ -240,6 +365,22 @@ __device__ __forceinline__ void load_inputs(const S* dtrow, const S* xrow, bool 
   }
 }
 
+template <typename S, int T, bool VEC, bool FULL>
+__device__ __forceinline__ void load_inputs(const S* dtrow, const S* xrow, bool rev, bool col, int l0, int L, int H,
+                                            int W, float (&dtv)[T], float (&uv)[T]) {
+  if constexpr (VEC && FULL && (T % 4 == 0)) {
+#pragma unroll
+    for (int i = 0; i < T; i += 4) {
+      const float4 q = Io<S>::ld4(dtrow, l0 + i);
+      dtv[i] = q.x; dtv[i + 1] = q.y; dtv[i + 2] = q.z; dtv[i + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < T; ++i) dtv[i] = (FULL || l0 + i < L) ? Io<S>::ld(dtrow, l0 + i) : 0.f;
+  }
+  load_x<S, T, VEC, FULL>(xrow, rev, col, l0, L, H, W, uv);
+}
+
 // Raw dt/u -> delta, delta*u and the output's skip term D*u; returns sum(delta).
 template <int T>
 __device__ __forceinline__ float prepare_steps(const float (&dtv)[T], const float (&uv)[T], float bias, float dsk,
@@ -257,7 +398,12 @@ __device__ __forceinline__ float prepare_steps(const float (&dtv)[T], const floa
   return sdelta;
 }
 
-// One state n of one chunk; this lane's staged B/C are at Bst/Cst.
+template <int G, int T>
+__device__ __forceinline__ void state_core(const float (&Bv)[T], const float (&Cv)[T], float A2n, float* carry_slot,
+                                           int seg, const float (&delta)[T], const float (&du)[T], float sdelta,
+                                           float (&yv)[T]);
+
+// One state n of one chunk; this lane's register-staged B/C are at Bst/Cst.
 template <int G, int T>
 __device__ __forceinline__ void state_step(const float* Bst, const float* Cst, float A2n, float* carry_slot,
                                            int seg, const float (&delta)[T], const float (&du)[T], float sdelta,
@@ -278,14 +424,23 @@ __device__ __forceinline__ void state_step(const float* Bst, const float* Cst, f
       Cv[i] = Cst[i];
     }
   }
+  state_core<G, T>(Bv, Cv, A2n, carry_slot, seg, delta, du, sdelta, yv);
+}
+
+// One state n of one chunk from this lane's B/C values.
+template <int G, int T>
+__device__ __forceinline__ void state_core(const float (&Bv)[T], const float (&Cv)[T], float A2n, float* carry_slot,
+                                           int seg, const float (&delta)[T], const float (&du)[T], float sdelta,
+                                           float (&yv)[T]) {
   float a[T], bb[T];
-  float Bl = 0.f;
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     a[i] = __builtin_amdgcn_exp2f(delta[i] * A2n);
     bb[i] = du[i] * Bv[i];
-    Bl = fmaf(a[i], Bl, bb[i]);
   }
+  float Bl = bb[0];
+#pragma unroll
+  for (int i = 1; i < T; ++i) Bl = fmaf(a[i], Bl, bb[i]);
   float Al = __builtin_amdgcn_exp2f(A2n * sdelta);
   scan_inclusive<G>(Al, Bl);
   float h = incoming_state<G>(Al, Bl, *carry_slot, seg);
@@ -320,6 +475,54 @@ __device__ __forceinline__ void store_outputs(float* plane, bool rev, bool add, 
         float* q = plane + walk_index(rev, l0 + i, L);
         *q = add ? (*q + yv[i]) : yv[i];
       }
+    }
+  }
+}
+
+// The last direction (2, the reversed row walk) finishes the merge in place of a
+// separate pass: y[p] = (row plane[p] + out) + column plane[w*H + h] for the
+// lane's T pixels p = h*W + w, rounded once to the storage type.  Step l0 + i
+// visits pixel L-1-l0-i.  The row plane holds direction 0 (it is y itself for
+// fp32 output: each element is read, then written, by the same lane), the
+// column plane directions 1 + 3, so y = (y0 + y2) + (y1 + y3).
+template <typename S, int T, bool VEC, bool FULL>
+__device__ __forceinline__ void store_final(const float* prow, const float* pcol, S* y, int l0, int L, int H, int W,
+                                            const float (&yv)[T]) {
+  if constexpr (VEC && FULL && (T % 4 == 0)) {
+    const int s_lo = L - l0 - T;  // pixels s_lo .. s_lo+T-1; pixel s_lo+j holds yv[T-1-j]
+    float v[T];
+#pragma unroll
+    for (int j = 0; j < T; j += 4) {
+      const float4 o = *reinterpret_cast<const float4*>(prow + s_lo + j);
+      v[j] = o.x + yv[T - 1 - j];
+      v[j + 1] = o.y + yv[T - 2 - j];
+      v[j + 2] = o.z + yv[T - 3 - j];
+      v[j + 3] = o.w + yv[T - 4 - j];
+    }
+    int h = s_lo / W;
+    int w = s_lo - h * W;
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      v[j] += pcol[w * H + h];
+      ++w;
+      const bool wrap = w == W;
+      w = wrap ? 0 : w;
+      h += wrap ? 1 : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < T; j += 4) Io<S>::st4(y, s_lo + j, make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]));
+  } else {
+    int pix = L - 1 - (FULL ? l0 : min(l0, L - 1));
+    int h = pix / W;
+    int w = pix - h * W;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      if (FULL || l0 + i < L) Io<S>::st(y, pix, (prow[pix] + yv[i]) + pcol[w * H + h]);
+      --pix;
+      --w;
+      const bool wrap = w < 0;
+      w = wrap ? W - 1 : w;
+      h -= wrap ? 1 : 0;
     }
   }
 }
@@ -381,18 +584,16 @@ struct Lane {
 // inlining it would make the register allocator budget its arrays on top of the
 // main loop's.
 template <typename S, int G, int T, int NG, int TT, bool VEC>
-__device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, const S* dtrow,
-                                        const S* xrow, const S* Bbase, const S* Cbase, float* plane, bool rev,
-                                        bool col, bool add, float bias, float dsk, int c0, int L, int H, int W,
-                                        int N) {
+__device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, float* a2s, float* carry,
+                                        const S* dtrow, const S* xrow, const S* Bbase, const S* Cbase, float* plane,
+                                        const float* pcol, S* yout, bool rev, bool col, bool add, bool last, float bias,
+                                        float dsk, int c0, int L, int H, int W, int N) {
   Lane ln;
   ln.tid = tid;
   ln.seg = seg;
   ln.dl = dl;
   ln.dvalid = dvalid;
   using C = Cfg<G, T, NG>;
-  float* a2s = smem + 2 * C::kBuf;
-  float* carry = a2s + C::kChans * kMaxN;
   constexpr int SS = seg_stride<TT>();
   const int l0 = c0 + ln.seg * TT;
   float dtv[TT], uv[TT];
@@ -413,17 +614,28 @@ __device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, f
     }
     __syncthreads();
   }
-  if (ln.dvalid) store_outputs<TT, VEC, false>(plane, rev, add, l0, L, yv);
+  if (ln.dvalid) {
+    if (last)
+      store_final<S, TT, VEC, false>(plane, pcol, yout, l0, L, H, W, yv);
+    else
+      store_outputs<TT, VEC, false>(plane, rev, add, l0, L, yv);
+  }
 }
 
 template <typename S, int G, int T, int NG, bool VEC>
 __global__ __launch_bounds__(kWaves * 64, 3) void ss2d_forward_kernel(Params p) {
   using C = Cfg<G, T, NG>;
+  using Y = Layout<S, G, T, NG, VEC>;
   constexpr int CH = C::kChans;
   constexpr int NTH = C::kThreads;
-  constexpr int SS = C::kSS;
-  extern __shared__ float smem[];
-  float* a2s = smem + 2 * C::kBuf;
+  constexpr int GT = G * T;
+  constexpr int GB = (sizeof(S) == 4 && VEC) ? 16 : 4;  // bytes per lane of one DMA copy
+  __shared__ __align__(16) char ring0[Y::kRing0Bytes];
+  __shared__ __align__(16) char ring1[Y::kGroupBytes];
+  __shared__ __align__(16) char dtb[Y::kDtBytes];
+  __shared__ float par[Y::kParFloats];
+  float* smem = reinterpret_cast<float*>(ring0);
+  float* a2s = par;
   float* carry = a2s + CH * kMaxN;
   float* biass = carry + CH * kMaxN;
   float* dss = biass + CH;
@@ -445,122 +657,145 @@ __global__ __launch_bounds__(kWaves * 64, 3) void ss2d_forward_kernel(Params p) 
   ln.d0 = (work - ln.b * nbd) * CH;
   ln.dvalid = ln.d0 + ln.dl < p.D;
   ln.dsafe = ln.dvalid ? ln.d0 + ln.dl : 0;
-  const int L = p.L, N = p.N, H = p.H, W = p.W;
-  const int64_t plane_off = ((int64_t)ln.b * p.D + ln.dsafe) * L;
+  const int L = p.L, N = p.N, H = p.H, W = p.W, D = p.D;
+  const int64_t plane_off = ((int64_t)ln.b * D + ln.dsafe) * L;
   const S* xrow = static_cast<const S*>(p.x) + plane_off;
+  const DmaPlan<S, G, T, 2 * NG, GB> bpl(ln.tid);  // one Bs/Cs group
+  const DmaPlan<S, G, T, CH, GB> dpl(ln.tid);      // dt of one chunk
 
 #pragma unroll 1
   for (int kk = 0; kk < 4; ++kk) {
-    const int k = (kk == 0) ? 0 : (kk == 1) ? 2 : (kk == 2) ? 1 : 3;  // row pair, then column pair
+    const int k = (kk == 0) ? 1 : (kk == 1) ? 3 : (kk == 2) ? 0 : 2;  // column pair, then row pair
     // per-direction parameters of the block's channels
     for (int i = ln.tid; i < CH * kMaxN; i += NTH) {
       const int dd = i / kMaxN, n = i - dd * kMaxN;
       const int dg = ln.d0 + dd;
       float v = 0.f;
-      if (dg < p.D && n < N) v = -expf(p.A_log[(int64_t)(k * p.D + dg) * N + n]) * kLog2e;
+      if (dg < D && n < N) v = -expf(p.A_log[(int64_t)(k * D + dg) * N + n]) * kLog2e;
       a2s[i] = v;
       carry[i] = 0.f;
     }
     for (int i = ln.tid; i < CH; i += NTH) {
       const int dg = ln.d0 + i;
-      biass[i] = dg < p.D ? p.dt_bias[k * p.D + dg] : 0.f;
-      dss[i] = dg < p.D ? p.Ds[k * p.D + dg] : 0.f;
+      biass[i] = dg < D ? p.dt_bias[k * D + dg] : 0.f;
+      dss[i] = dg < D ? p.Ds[k * D + dg] : 0.f;
     }
     __syncthreads();
 
-    const bool rev = k >= 2, col = (k & 1) != 0, add = k >= 2;
+    const bool rev = k >= 2, col = (k & 1) != 0, add = k == 3, last = k == 2;
     float* plane = (col ? p.pcol : p.prow) + plane_off;
-    const S* dtrow = static_cast<const S*>(p.dt) + ((int64_t)(ln.b * 4 + k) * p.D + ln.dsafe) * L;
+    const float* pcol = p.pcol + plane_off;
+    S* yout = static_cast<S*>(p.y) + plane_off;
+    const S* dtdir = static_cast<const S*>(p.dt) + (int64_t)(ln.b * 4 + k) * D * L;
+    const S* dtrow = dtdir + (int64_t)ln.dsafe * L;
     const S* Bbase = static_cast<const S*>(p.Bs) + (int64_t)(ln.b * 4 + k) * N * L;
     const S* Cbase = static_cast<const S*>(p.Cs) + (int64_t)(ln.b * 4 + k) * N * L;
     const float bias = biass[ln.dl];
     const float dsk = dss[ln.dl];
-
-    // ---------------- full chunks, Bs/Cs staged one group ahead
-    constexpr int GT = G * T;
     const int nmain = L / GT;
     const int ngrp = (N + NG - 1) / NG;
-    if (nmain > 0) {
-      float dtn[T], un[T];
-      Stager<S, G, T, NG, T, VEC, true> st;
-      st.fetch(Bbase, Cbase, ln.tid, 0, N, 0, L);
-      st.commit(smem, ln.tid);
-      __syncthreads();
-      int gflat = 0;
+    int c0 = 0;
+
+    if constexpr (VEC) {
+      // ---------------- full chunks: Bs/Cs one group ahead and dt one chunk ahead, by DMA
+      const int d0 = ln.d0;
+      auto dt_rows = [=](int r) {  // channel r of the block (a valid row stands in past D)
+        const int dg = d0 + r < D ? d0 + r : d0;
+        return dtdir + (int64_t)dg * L;
+      };
+      auto bc_rows = [=](int g) {  // row 2*nn + {0: B, 1: C} of state g*NG + nn (state 0 stands in past N)
+        return [=](int r) {
+          const int n = g * NG + (r >> 1);
+          return ((r & 1) ? Cbase : Bbase) + (int64_t)(n < N ? n : 0) * L;
+        };
+      };
+      if (nmain > 0) {
+        dpl.copy(dtb, dt_rows, 0);
+        bpl.copy(ring0, bc_rows(0), 0);
+        wait_vmem();
+        __syncthreads();
+      }
+      // Group g of every chunk lives in ring(g & 1); the next chunk's group 0 is
+      // copied during this chunk's last group when that group is in ring1.
+      const bool cross = (ngrp & 1) == 0;
       for (int c = 0; c < nmain; ++c) {
+        float dtn[T], un[T];
+        read_seg<S, T>(dtb + ln.dl * GT * (int)sizeof(S), ln.seg, dtn);
+        load_x<S, T, VEC, true>(xrow, rev, col, c * GT + ln.seg * T, L, H, W, un);
         float delta[T], du[T], yv[T];
-        // dt/x of this chunk (a prefetch a chunk ahead would cost 2*T registers and
-        // drop the kernel to two waves per SIMD, which measured slower)
-        load_inputs<S, T, VEC, true>(dtrow, xrow, rev, col, c * GT + ln.seg * T, L, H, W, dtn, un);
-        const float sdelta = prepare_steps<T>(dtn, un, bias, dsk, ln.dvalid, T, delta, du, yv);
-        for (int g = 0; g < ngrp; ++g, ++gflat) {
+        // Lanes of a channel past D work on channel d0's data and store nothing; a
+        // group of G lanes never mixes channels, so no masking is needed here.
+        const float sdelta = prepare_steps<T>(dtn, un, bias, dsk, true, T, delta, du, yv);
+        auto group = [&](const char* cur, char* nxt, int g) {
           const bool more_states = g + 1 < ngrp;
-          const bool has_next = more_states || c + 1 < nmain;
-          if (has_next) st.fetch(Bbase, Cbase, ln.tid, more_states ? (g + 1) * NG : 0, N,
-                                 (more_states ? c : c + 1) * GT, L);
-          const float* base = smem + (gflat & 1) * C::kBuf;
+          // nxt was last read before the previous barrier
+          if (more_states)
+            bpl.copy(nxt, bc_rows(g + 1), c * GT);
+          else if (cross && c + 1 < nmain)
+            bpl.copy(nxt, bc_rows(0), (c + 1) * GT);
+          if (g == 1 && c + 1 < nmain)  // every lane has read this chunk's dt (barrier after group 0)
+            dpl.copy(dtb, dt_rows, (c + 1) * GT);
 #pragma unroll 1
           for (int nn = 0; nn < NG; ++nn) {
             const int n = g * NG + nn;
-            if (n < N)
-              state_step<G, T>(base + (nn * 2) * C::kArr + ln.seg * SS, base + (nn * 2 + 1) * C::kArr + ln.seg * SS,
-                               a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du, sdelta, yv);
+            if (n < N) {
+              float Bv[T], Cv[T];
+              read_seg<S, T>(cur + (2 * nn) * GT * (int)sizeof(S), ln.seg, Bv);
+              read_seg<S, T>(cur + (2 * nn + 1) * GT * (int)sizeof(S), ln.seg, Cv);
+              state_core<G, T>(Bv, Cv, a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du, sdelta,
+                               yv);
+            }
           }
-          if (has_next) st.commit(smem + ((gflat + 1) & 1) * C::kBuf, ln.tid);
+          wait_vmem();
+          __syncthreads();
+        };
+        for (int g = 0; g < ngrp; g += 2) {
+          group(ring0, ring1, g);
+          if (g + 1 < ngrp) group(ring1, ring0, g + 1);
+        }
+        if (c + 1 < nmain && (!cross || ngrp == 1)) {  // nothing was copied ahead: copy now and wait
+          if (!cross) bpl.copy(ring0, bc_rows(0), (c + 1) * GT);
+          if (ngrp == 1) dpl.copy(dtb, dt_rows, (c + 1) * GT);
+          wait_vmem();
           __syncthreads();
         }
-        if (ln.dvalid) store_outputs<T, VEC, true>(plane, rev, add, c * GT + ln.seg * T, L, yv);
+        if (ln.dvalid) {
+          if (last)
+            store_final<S, T, VEC, true>(plane, pcol, yout, c * GT + ln.seg * T, L, H, W, yv);
+          else
+            store_outputs<T, VEC, true>(plane, rev, add, c * GT + ln.seg * T, L, yv);
+        }
       }
+      c0 = nmain * GT;
+    } else {
+      // ---------------- rows not 16-byte aligned: every chunk staged through registers
+      for (; c0 + GT <= L; c0 += GT)
+        tail_chunk<S, G, T, NG, T, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+                                        plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
     }
 
     // ---------------- remainder chunks (fewer steps per lane)
-    int c0 = nmain * GT;
     while (L - c0 >= G * 8) {
-      tail_chunk<S, G, T, NG, 8, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, dtrow, xrow, Bbase, Cbase, plane, rev, col, add, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 8, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 8;
     }
     if (L - c0 >= G * 4) {
-      tail_chunk<S, G, T, NG, 4, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, dtrow, xrow, Bbase, Cbase, plane, rev, col, add, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 4, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 4;
     }
     if (L - c0 >= G * 2) {
-      tail_chunk<S, G, T, NG, 2, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, dtrow, xrow, Bbase, Cbase, plane, rev, col, add, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 2, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 2;
     }
     while (c0 < L) {
-      tail_chunk<S, G, T, NG, 1, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, dtrow, xrow, Bbase, Cbase, plane, rev, col, add, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 1, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G;
     }
     __syncthreads();  // this direction's plane writes are complete and visible to the block
-  }
-
-  // ---------------- y = row plane + transpose(column plane), 32x32 LDS tiles
-  float* tile = smem;  // [32][33]
-  S* y = static_cast<S*>(p.y);
-  const int tx = ln.tid & 31, ty = ln.tid >> 5;
-  for (int dd = 0; dd < CH; ++dd) {
-    const int dg = ln.d0 + dd;
-    if (dg >= p.D) break;
-    const int64_t off = ((int64_t)ln.b * p.D + dg) * L;
-    const float* pc = p.pcol + off;
-    const float* pr = p.prow + off;
-    for (int h0 = 0; h0 < H; h0 += 32) {
-      for (int w0 = 0; w0 < W; w0 += 32) {
-        for (int r = ty; r < 32; r += NTH / 32) {
-          const int w = w0 + r, h = h0 + tx;
-          if (w < W && h < H) tile[r * 33 + tx] = pc[(int64_t)w * H + h];
-        }
-        __syncthreads();
-        for (int r = ty; r < 32; r += NTH / 32) {
-          const int h = h0 + r, w = w0 + tx;
-          if (w < W && h < H) {
-            const int64_t pix = (int64_t)h * W + w;
-            Io<S>::st(y, off + pix, pr[pix] + tile[tx * 33 + r]);
-          }
-        }
-        __syncthreads();
-      }
-    }
   }
 }
 
@@ -596,7 +831,7 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
   p.N = (int)a.N;
   p.L = (int)(a.H * a.W);
   auto kern = ss2d_forward_kernel<S, G, Variant<G>::T, Variant<G>::NG, VEC>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)plan.blocks), dim3(kWaves * 64), plan.lds_bytes, a.stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)plan.blocks), dim3(kWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -615,10 +850,9 @@ hipError_t launch_s(const LaunchArgs& a, const Plan& plan, float* const planes[2
   }
 }
 
-template <int G>
+template <typename S, int G, bool VEC>
 size_t lds_bytes_for() {
-  constexpr int f = Cfg<G, Variant<G>::T, Variant<G>::NG>::kLds;
-  return sizeof(float) * (size_t)(f > 32 * 33 ? f : 32 * 33);
+  return (size_t)Layout<S, G, Variant<G>::T, Variant<G>::NG, VEC>::kBytes;
 }
 
 }  // namespace
@@ -633,7 +867,18 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   pl.waves = kWaves;
   pl.chans_per_block = kWaves * (64 / G);
   pl.blocks = B * ((D + pl.chans_per_block - 1) / pl.chans_per_block);
-  pl.lds_bytes = G == 16 ? lds_bytes_for<16>() : G == 32 ? lds_bytes_for<32>() : lds_bytes_for<64>();
+  const bool vec = L % 4 == 0;  // the ABI layer guarantees base alignment for this case
+  if (dtype == 0)
+    pl.lds_bytes = vec ? (G == 16 ? lds_bytes_for<float, 16, true>() : G == 32 ? lds_bytes_for<float, 32, true>()
+                                                                               : lds_bytes_for<float, 64, true>())
+                       : (G == 16 ? lds_bytes_for<float, 16, false>() : G == 32 ? lds_bytes_for<float, 32, false>()
+                                                                                 : lds_bytes_for<float, 64, false>());
+  else
+    pl.lds_bytes = vec ? (G == 16 ? lds_bytes_for<uint16_t, 16, true>() : G == 32 ? lds_bytes_for<uint16_t, 32, true>()
+                                                                                  : lds_bytes_for<uint16_t, 64, true>())
+                       : (G == 16 ? lds_bytes_for<uint16_t, 16, false>()
+                          : G == 32 ? lds_bytes_for<uint16_t, 32, false>()
+                                    : lds_bytes_for<uint16_t, 64, false>());
   pl.scratch_bytes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
   return pl;
 }
