@@ -25,6 +25,7 @@ struct LaunchArgs {
 // How a shape is mapped onto the machine.
 struct Plan {
   int lanes_per_seq;     // G: lanes that share one (b, k, d) sequence per chunk
+  int steps_per_lane;    // T: consecutive steps of one lane in a full chunk (16 or 8)
   int waves;             // waves per workgroup
   int chans_per_block;   // D channels one workgroup owns
   int64_t blocks;        // workgroups in the grid

@@ -623,7 +623,7 @@ __device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, f
 }
 
 template <typename S, int G, int T, int NG, bool VEC>
-__global__ __launch_bounds__(kWaves * 64, 3) void ss2d_forward_kernel(Params p) {
+__global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kernel(Params p) {
   using C = Cfg<G, T, NG>;
   using Y = Layout<S, G, T, NG, VEC>;
   constexpr int CH = C::kChans;
@@ -799,19 +799,16 @@ __global__ __launch_bounds__(kWaves * 64, 3) void ss2d_forward_kernel(Params p) 
   }
 }
 
-template <int G>
-struct Variant;
-// Steps per lane and states per staging group, chosen so one staging buffer holds
-// NG*2*G*T floats ~ 8 K (LDS ~ 40 KB per workgroup) and each thread prefetches
-// at most 4 float4 per group.
-template <>
-struct Variant<16> { static constexpr int T = 16, NG = 8; };
-template <>
-struct Variant<32> { static constexpr int T = 16, NG = 4; };
-template <>
-struct Variant<64> { static constexpr int T = 16, NG = 2; };
+// States per Bs/Cs staging group for G lanes x T steps: one group is 16 KB of
+// fp32 (8 KB of bf16) for T = 16, half that for T = 8, so the LDS of a
+// workgroup allows three (T = 16) or four (T = 8) workgroups per CU, matching
+// the register budget of each.
+template <int G, int T>
+constexpr int group_states() {
+  return T == 16 ? 2048 / (G * T) : 1024 / (G * T);
+}
 
-template <typename S, int G, bool VEC>
+template <typename S, int G, int T, bool VEC>
 hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const planes[2]) {
   Params p;
   p.x = a.x;
@@ -830,29 +827,40 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
   p.W = (int)a.W;
   p.N = (int)a.N;
   p.L = (int)(a.H * a.W);
-  auto kern = ss2d_forward_kernel<S, G, Variant<G>::T, Variant<G>::NG, VEC>;
+  auto kern = ss2d_forward_kernel<S, G, T, group_states<G, T>(), VEC>;
   hipLaunchKernelGGL(kern, dim3((unsigned)plan.blocks), dim3(kWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
-template <typename S, int G>
-hipError_t launch_g(const LaunchArgs& a, const Plan& plan, float* const planes[2]) {
-  if ((a.H * a.W) % 4 == 0) return launch_variant<S, G, true>(a, plan, planes);
-  return launch_variant<S, G, false>(a, plan, planes);
+template <typename S, int G, int T>
+hipError_t launch_gt(const LaunchArgs& a, const Plan& plan, float* const planes[2]) {
+  if ((a.H * a.W) % 4 == 0) return launch_variant<S, G, T, true>(a, plan, planes);
+  return launch_variant<S, G, T, false>(a, plan, planes);
 }
 
 template <typename S>
 hipError_t launch_s(const LaunchArgs& a, const Plan& plan, float* const planes[2]) {
+  if (plan.steps_per_lane == 8) {
+    if (plan.lanes_per_seq == 32) return launch_gt<S, 32, 8>(a, plan, planes);
+    return launch_gt<S, 64, 8>(a, plan, planes);
+  }
   switch (plan.lanes_per_seq) {
-    case 16: return launch_g<S, 16>(a, plan, planes);
-    case 32: return launch_g<S, 32>(a, plan, planes);
-    default: return launch_g<S, 64>(a, plan, planes);
+    case 16: return launch_gt<S, 16, 16>(a, plan, planes);
+    case 32: return launch_gt<S, 32, 16>(a, plan, planes);
+    default: return launch_gt<S, 64, 16>(a, plan, planes);
   }
 }
 
-template <typename S, int G, bool VEC>
-size_t lds_bytes_for() {
-  return (size_t)Layout<S, G, Variant<G>::T, Variant<G>::NG, VEC>::kBytes;
+template <typename S, int G, int T>
+size_t lds_bytes_for(bool vec) {
+  return vec ? (size_t)Layout<S, G, T, group_states<G, T>(), true>::kBytes
+             : (size_t)Layout<S, G, T, group_states<G, T>(), false>::kBytes;
+}
+
+template <typename S>
+size_t lds_bytes_s(int G, int T, bool vec) {
+  if (T == 8) return G == 32 ? lds_bytes_for<S, 32, 8>(vec) : lds_bytes_for<S, 64, 8>(vec);
+  return G == 16 ? lds_bytes_for<S, 16, 16>(vec) : G == 32 ? lds_bytes_for<S, 32, 16>(vec) : lds_bytes_for<S, 64, 16>(vec);
 }
 
 }  // namespace
@@ -863,22 +871,18 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   const int64_t L = H * W;
   int G = L < 512 ? 16 : 32;
   if (lanes_override == 16 || lanes_override == 32 || lanes_override == 64) G = lanes_override;
+  // Steps per lane: 16, unless the remainder after whole 16-step chunks would fill
+  // at least one 8-step chunk, which then runs at full speed instead of in the
+  // remainder path (8-step chunks exist for 32 and 64 lanes).
+  int T = 16;
+  if (G != 16 && L % (16 * G) >= 8 * G) T = 8;
   pl.lanes_per_seq = G;
+  pl.steps_per_lane = T;
   pl.waves = kWaves;
   pl.chans_per_block = kWaves * (64 / G);
   pl.blocks = B * ((D + pl.chans_per_block - 1) / pl.chans_per_block);
   const bool vec = L % 4 == 0;  // the ABI layer guarantees base alignment for this case
-  if (dtype == 0)
-    pl.lds_bytes = vec ? (G == 16 ? lds_bytes_for<float, 16, true>() : G == 32 ? lds_bytes_for<float, 32, true>()
-                                                                               : lds_bytes_for<float, 64, true>())
-                       : (G == 16 ? lds_bytes_for<float, 16, false>() : G == 32 ? lds_bytes_for<float, 32, false>()
-                                                                                 : lds_bytes_for<float, 64, false>());
-  else
-    pl.lds_bytes = vec ? (G == 16 ? lds_bytes_for<uint16_t, 16, true>() : G == 32 ? lds_bytes_for<uint16_t, 32, true>()
-                                                                                  : lds_bytes_for<uint16_t, 64, true>())
-                       : (G == 16 ? lds_bytes_for<uint16_t, 16, false>()
-                          : G == 32 ? lds_bytes_for<uint16_t, 32, false>()
-                                    : lds_bytes_for<uint16_t, 64, false>());
+  pl.lds_bytes = dtype == 0 ? lds_bytes_s<float>(G, T, vec) : lds_bytes_s<uint16_t>(G, T, vec);
   pl.scratch_bytes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
   return pl;
 }

@@ -146,6 +146,40 @@ def test_edge_shapes(B, D, H, W, N, dtype):
     check_scan_only(y, oracle.ss2d_inputs_f64(inp), dtype, f"edge {B}x{D}x{H}x{W} N={N}")
 
 
+# Every compiled (lanes per sequence, steps per lane) variant, forced through the
+# benchmarking knob: the automatic plan reaches only some of them on the shapes above.
+LANE_CASES = [
+    # lanes, (B, D, H, W, N, dtype), plan the shape gets
+    (16, (2, 5, 24, 32, 16, "f32")),   # 16 lanes x 16 steps, 3 chunks
+    (32, (2, 5, 24, 32, 16, "f32")),   # 32 x 8, 3 chunks
+    (64, (2, 5, 24, 32, 16, "f32")),   # 64 x 8, 1 chunk + remainder
+    (32, (1, 3, 40, 40, 16, "f32")),   # 32 x 16, 3 chunks + 64-step remainder
+    (64, (1, 3, 40, 40, 16, "f32")),   # 64 x 8, 3 chunks + remainder
+    (64, (1, 2, 64, 64, 16, "f32")),   # 64 x 16, 4 chunks
+    (64, (1, 3, 40, 40, 16, "bf16")),
+    (16, (1, 3, 24, 32, 16, "bf16")),
+]
+
+
+@pytest.mark.parametrize("lanes,shape", LANE_CASES)
+def test_lane_variants(lanes, shape):
+    B, D, H, W, N, dtype = shape
+    lib = _lib()
+    print(f"[case] lanes={lanes} {shape} plan: {lib.describe(B, D, H, W, N, 1 if dtype == 'bf16' else 0)}", flush=True)
+    inp = ss2d_inputs.tiny_random(B, D, H, W, N, seed=lanes + H, dtype=dtype)
+    lib.set_lanes_per_seq(lanes)
+    try:
+        print(f"[case] forced plan: {lib.describe(B, D, H, W, N, 1 if dtype == 'bf16' else 0)}", flush=True)
+        y = gpu_forward(inp, dtype)
+        ref = oracle.ss2d_inputs_f64(inp)
+        check(y, ref, dtype, f"lanes={lanes} {shape}")
+        inp["Ds"][:] = 0.0
+        y = gpu_forward(inp, dtype)
+        check_scan_only(y, oracle.ss2d_inputs_f64(inp), dtype, f"lanes={lanes} {shape}")
+    finally:
+        lib.set_lanes_per_seq(0)
+
+
 @pytest.mark.parametrize("bias", [-14.0, -6.0, 0.0, 3.0, 12.0, 25.0])
 def test_step_size_range(bias):
     """Tiny to large delta: softplus in both branches, decays from ~1 to ~0."""
