@@ -28,9 +28,12 @@ struct Plan {
   int steps_per_lane;    // T: consecutive steps of one lane in a full chunk (16 or 8)
   int waves;             // waves per workgroup
   int chans_per_block;   // D channels one workgroup owns
-  int64_t blocks;        // workgroups in the grid
-  size_t lds_bytes;      // dynamic LDS per workgroup
-  size_t scratch_bytes;  // fp32 merge planes in device memory (temporary)
+  int nseg;              // segments per sequence (1: whole sequences in one launch)
+  int seg_chunks;        // full chunks per segment
+  int64_t blocks;        // workgroups of one output launch
+  size_t lds_bytes;      // LDS per workgroup
+  size_t scratch_bytes;  // device temporary: fp32 merge planes, then the segment maps
+  size_t carry_offset;   // byte offset of the segment maps in the temporary
 };
 
 // lanes_override: 0 = automatic, else 16, 32 or 64 lanes per sequence.

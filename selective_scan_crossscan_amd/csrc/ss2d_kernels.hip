@@ -177,7 +177,20 @@ struct Params {
   void* y;
   float* prow;  // directions 0 and 2, row-major fp32: y itself (fp32 output) or a temporary (bf16)
   float* pcol;  // directions 1 and 3, column-major fp32 temporary
+  // Long sequences are cut into nseg segments of seg_chunks full chunks each (the
+  // last takes the rest).  carries[((b*4 + k)*D + d)*nseg + s][n] = {A, B}: the
+  // segment's affine map h -> A h + B, from a carry pass over segments 0..nseg-2.
+  float* carries;
+  int seg_chunks, nseg;
+  int kdir;  // the one direction of a segment output launch
   int B, D, H, W, N, L;
+};
+
+// What one launch does.
+enum Mode : int {
+  kFused = 0,     // whole sequences, all four directions, merge included
+  kCarry = 1,     // segment maps of every direction (no outputs)
+  kSegment = 2,   // one direction's outputs per segment, entering with the carried state
 };
 
 // Compile-time shape of one kernel variant: G lanes per sequence chunk, T steps
@@ -212,7 +225,7 @@ struct Layout {
   static constexpr int kRing0Bytes = kGroupBytes > kStagedBytes ? (kGroupBytes > kTileBytes ? kGroupBytes : kTileBytes)
                                                                 : (kStagedBytes > kTileBytes ? kStagedBytes : kTileBytes);
   static constexpr int kDtBytes = C::kChans * kGT * (int)sizeof(S);
-  static constexpr int kParFloats = 2 * C::kChans * kMaxN + 2 * C::kChans;
+  static constexpr int kParFloats = 3 * C::kChans * kMaxN + 2 * C::kChans;
   static constexpr int kBytes = kRing0Bytes + kGroupBytes + kDtBytes + 4 * kParFloats;
 };
 
@@ -452,6 +465,26 @@ __device__ __forceinline__ void state_core(const float (&Bv)[T], const float (&C
   if (seg == G - 1) *carry_slot = h;
 }
 
+// Carry pass: one state n of one chunk, without outputs.  The group's last lane
+// holds the chunk's map (A_chunk, B_chunk) after the inclusive scan and folds it
+// into the segment's map kept in LDS: carry = A_chunk carry + B_chunk and
+// aprod = A_chunk aprod.
+template <typename S, int G, int T>
+__device__ __forceinline__ void state_carry(const char* Brow, int seg, float A2n, float* carry_slot, float* aprod_slot,
+                                            const float (&delta)[T], const float (&du)[T], float sdelta) {
+  float Bv[T];
+  read_seg<S, T>(Brow, seg, Bv);
+  float Bl = du[0] * Bv[0];
+#pragma unroll
+  for (int i = 1; i < T; ++i) Bl = fmaf(__builtin_amdgcn_exp2f(delta[i] * A2n), Bl, du[i] * Bv[i]);
+  float Al = __builtin_amdgcn_exp2f(A2n * sdelta);
+  scan_inclusive<G>(Al, Bl);
+  if (seg == G - 1) {
+    *carry_slot = fmaf(Al, *carry_slot, Bl);
+    *aprod_slot *= Al;
+  }
+}
+
 // Writes (or adds) a lane's outputs of T consecutive steps into its plane.
 template <int T, bool VEC, bool FULL>
 __device__ __forceinline__ void store_outputs(float* plane, bool rev, bool add, int l0, int L, const float (&yv)[T]) {
@@ -622,7 +655,7 @@ __device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, f
   }
 }
 
-template <typename S, int G, int T, int NG, bool VEC>
+template <typename S, int G, int T, int NG, bool VEC, int MODE>
 __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kernel(Params p) {
   using C = Cfg<G, T, NG>;
   using Y = Layout<S, G, T, NG, VEC>;
@@ -639,9 +672,11 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   float* carry = a2s + CH * kMaxN;
   float* biass = carry + CH * kMaxN;
   float* dss = biass + CH;
+  float* aprod = dss + CH;
 
-  // Work id: consecutive ids (same batch, neighbouring channel blocks, which share
-  // Bs/Cs) stay on one XCD; workgroups are dealt round-robin over the 8 XCDs.
+  // Work id: consecutive ids (same batch and segment, neighbouring channel blocks,
+  // which share Bs/Cs) stay on one XCD; workgroups are dealt round-robin over the
+  // 8 XCDs.
   const int nb = gridDim.x;
   const int xcd = blockIdx.x & 7, bslot = blockIdx.x >> 3;
   const int per = nb >> 3, rem = nb & 7;
@@ -653,8 +688,11 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   ln.seg = lane % G;
   ln.dl = wave * (64 / G) + lane / G;
   const int nbd = (p.D + CH - 1) / CH;
-  ln.b = work / nbd;
-  ln.d0 = (work - ln.b * nbd) * CH;
+  const int nsw = MODE == kCarry ? p.nseg - 1 : p.nseg;  // segments handled by this launch
+  const int bs = work / nbd;                              // batch * nsw + segment
+  ln.b = bs / nsw;
+  const int sidx = bs - ln.b * nsw;
+  ln.d0 = (work - bs * nbd) * CH;
   ln.dvalid = ln.d0 + ln.dl < p.D;
   ln.dsafe = ln.dvalid ? ln.d0 + ln.dl : 0;
   const int L = p.L, N = p.N, H = p.H, W = p.W, D = p.D;
@@ -663,17 +701,33 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   const DmaPlan<S, G, T, 2 * NG, GB> bpl(ln.tid);  // one Bs/Cs group
   const DmaPlan<S, G, T, CH, GB> dpl(ln.tid);      // dt of one chunk
 
+  // Full chunks [cbeg, cend) of this workgroup's segment; the remainder steps
+  // after the last full chunk belong to the last segment.
+  const int nmain = L / GT;
+  const int cbeg = sidx * p.seg_chunks;
+  const bool last_seg = sidx == p.nseg - 1;
+  const int cend = last_seg ? nmain : cbeg + p.seg_chunks;
+
 #pragma unroll 1
-  for (int kk = 0; kk < 4; ++kk) {
-    const int k = (kk == 0) ? 1 : (kk == 1) ? 3 : (kk == 2) ? 0 : 2;  // column pair, then row pair
-    // per-direction parameters of the block's channels
+  for (int kk = 0; kk < (MODE == kSegment ? 1 : 4); ++kk) {
+    // column pair, then row pair: the last direction finishes the merge
+    const int k = MODE == kSegment ? p.kdir : (kk == 0) ? 1 : (kk == 1) ? 3 : (kk == 2) ? 0 : 2;
+    // per-direction parameters of the block's channels; the state entering the
+    // segment is the composition of the maps of the segments before it
     for (int i = ln.tid; i < CH * kMaxN; i += NTH) {
       const int dd = i / kMaxN, n = i - dd * kMaxN;
       const int dg = ln.d0 + dd;
-      float v = 0.f;
-      if (dg < D && n < N) v = -expf(p.A_log[(int64_t)(k * D + dg) * N + n]) * kLog2e;
+      float v = 0.f, h = 0.f;
+      if (dg < D && n < N) {
+        v = -expf(p.A_log[(int64_t)(k * D + dg) * N + n]) * kLog2e;
+        if (MODE == kSegment) {
+          const float* cr = p.carries + ((int64_t)(ln.b * 4 + k) * D + dg) * p.nseg * (2 * kMaxN);
+          for (int j = 0; j < sidx; ++j) h = fmaf(cr[j * 2 * kMaxN + 2 * n], h, cr[j * 2 * kMaxN + 2 * n + 1]);
+        }
+      }
       a2s[i] = v;
-      carry[i] = 0.f;
+      carry[i] = h;
+      aprod[i] = 1.f;
     }
     for (int i = ln.tid; i < CH; i += NTH) {
       const int dg = ln.d0 + i;
@@ -692,9 +746,8 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     const S* Cbase = static_cast<const S*>(p.Cs) + (int64_t)(ln.b * 4 + k) * N * L;
     const float bias = biass[ln.dl];
     const float dsk = dss[ln.dl];
-    const int nmain = L / GT;
     const int ngrp = (N + NG - 1) / NG;
-    int c0 = 0;
+    int c0 = cbeg * GT;
 
     if constexpr (VEC) {
       // ---------------- full chunks: Bs/Cs one group ahead and dt one chunk ahead, by DMA
@@ -709,16 +762,16 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
           return ((r & 1) ? Cbase : Bbase) + (int64_t)(n < N ? n : 0) * L;
         };
       };
-      if (nmain > 0) {
-        dpl.copy(dtb, dt_rows, 0);
-        bpl.copy(ring0, bc_rows(0), 0);
+      if (cend > cbeg) {
+        dpl.copy(dtb, dt_rows, cbeg * GT);
+        bpl.copy(ring0, bc_rows(0), cbeg * GT);
         wait_vmem();
         __syncthreads();
       }
       // Group g of every chunk lives in ring(g & 1); the next chunk's group 0 is
       // copied during this chunk's last group when that group is in ring1.
       const bool cross = (ngrp & 1) == 0;
-      for (int c = 0; c < nmain; ++c) {
+      for (int c = cbeg; c < cend; ++c) {
         float dtn[T], un[T];
         read_seg<S, T>(dtb + ln.dl * GT * (int)sizeof(S), ln.seg, dtn);
         load_x<S, T, VEC, true>(xrow, rev, col, c * GT + ln.seg * T, L, H, W, un);
@@ -731,19 +784,24 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
           // nxt was last read before the previous barrier
           if (more_states)
             bpl.copy(nxt, bc_rows(g + 1), c * GT);
-          else if (cross && c + 1 < nmain)
+          else if (cross && c + 1 < cend)
             bpl.copy(nxt, bc_rows(0), (c + 1) * GT);
-          if (g == 1 && c + 1 < nmain)  // every lane has read this chunk's dt (barrier after group 0)
+          if (g == 1 && c + 1 < cend)  // every lane has read this chunk's dt (barrier after group 0)
             dpl.copy(dtb, dt_rows, (c + 1) * GT);
 #pragma unroll 1
           for (int nn = 0; nn < NG; ++nn) {
             const int n = g * NG + nn;
             if (n < N) {
-              float Bv[T], Cv[T];
-              read_seg<S, T>(cur + (2 * nn) * GT * (int)sizeof(S), ln.seg, Bv);
-              read_seg<S, T>(cur + (2 * nn + 1) * GT * (int)sizeof(S), ln.seg, Cv);
-              state_core<G, T>(Bv, Cv, a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du, sdelta,
-                               yv);
+              if constexpr (MODE == kCarry) {
+                state_carry<S, G, T>(cur + (2 * nn) * GT * (int)sizeof(S), ln.seg, a2s[ln.dl * kMaxN + n],
+                                     carry + ln.dl * kMaxN + n, aprod + ln.dl * kMaxN + n, delta, du, sdelta);
+              } else {
+                float Bv[T], Cv[T];
+                read_seg<S, T>(cur + (2 * nn) * GT * (int)sizeof(S), ln.seg, Bv);
+                read_seg<S, T>(cur + (2 * nn + 1) * GT * (int)sizeof(S), ln.seg, Cv);
+                state_core<G, T>(Bv, Cv, a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du,
+                                 sdelta, yv);
+              }
             }
           }
           wait_vmem();
@@ -753,25 +811,45 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
           group(ring0, ring1, g);
           if (g + 1 < ngrp) group(ring1, ring0, g + 1);
         }
-        if (c + 1 < nmain && (!cross || ngrp == 1)) {  // nothing was copied ahead: copy now and wait
+        if (c + 1 < cend && (!cross || ngrp == 1)) {  // nothing was copied ahead: copy now and wait
           if (!cross) bpl.copy(ring0, bc_rows(0), (c + 1) * GT);
           if (ngrp == 1) dpl.copy(dtb, dt_rows, (c + 1) * GT);
           wait_vmem();
           __syncthreads();
         }
-        if (ln.dvalid) {
+        if (MODE != kCarry && ln.dvalid) {
           if (last)
             store_final<S, T, VEC, true>(plane, pcol, yout, c * GT + ln.seg * T, L, H, W, yv);
           else
             store_outputs<T, VEC, true>(plane, rev, add, c * GT + ln.seg * T, L, yv);
         }
       }
-      c0 = nmain * GT;
+      c0 = cend * GT;
     } else {
       // ---------------- rows not 16-byte aligned: every chunk staged through registers
       for (; c0 + GT <= L; c0 += GT)
         tail_chunk<S, G, T, NG, T, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
                                         plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
+    }
+
+    if constexpr (MODE == kCarry) {
+      // ---------------- the segment's map per (channel, state)
+      __syncthreads();
+      for (int i = ln.tid; i < CH * kMaxN; i += NTH) {
+        const int dd = i / kMaxN, n = i - dd * kMaxN;
+        const int dg = ln.d0 + dd;
+        if (dg < D && n < N) {
+          float* cr = p.carries + (((int64_t)(ln.b * 4 + k) * D + dg) * p.nseg + sidx) * (2 * kMaxN);
+          cr[2 * n] = aprod[i];
+          cr[2 * n + 1] = carry[i];
+        }
+      }
+      __syncthreads();
+      continue;
+    }
+    if (!last_seg) {
+      __syncthreads();  // this direction's plane writes are complete and visible to the block
+      continue;
     }
 
     // ---------------- remainder chunks (fewer steps per lane)
@@ -809,7 +887,7 @@ constexpr int group_states() {
 }
 
 template <typename S, int G, int T, bool VEC>
-hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const planes[2]) {
+hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
   Params p;
   p.x = a.x;
   p.dt = a.dt;
@@ -827,27 +905,53 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
   p.W = (int)a.W;
   p.N = (int)a.N;
   p.L = (int)(a.H * a.W);
-  auto kern = ss2d_forward_kernel<S, G, T, group_states<G, T>(), VEC>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)plan.blocks), dim3(kWaves * 64), 0, a.stream, p);
-  return hipGetLastError();
+  p.carries = carries;
+  p.seg_chunks = plan.seg_chunks;
+  p.nseg = plan.nseg;
+  p.kdir = 0;
+  constexpr int NG = group_states<G, T>();
+  const int64_t units = plan.blocks / plan.nseg;  // (batch, channel block) pairs
+  if (plan.nseg == 1) {
+    hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kFused>), dim3((unsigned)units), dim3(kWaves * 64), 0,
+                       a.stream, p);
+    return hipGetLastError();
+  }
+  if constexpr (VEC) {
+    // carry pass over every segment but the last, then one launch per direction in
+    // merge order (column pair, then row pair; each reads what the previous wrote)
+    hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kCarry>), dim3((unsigned)(units * (plan.nseg - 1))),
+                       dim3(kWaves * 64), 0, a.stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int order[4] = {1, 3, 0, 2};
+    for (int k : order) {
+      p.kdir = k;
+      hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kSegment>), dim3((unsigned)(units * plan.nseg)),
+                         dim3(kWaves * 64), 0, a.stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  return hipErrorInvalidValue;  // segments are planned only for rows aligned for the DMA copy
 }
 
 template <typename S, int G, int T>
-hipError_t launch_gt(const LaunchArgs& a, const Plan& plan, float* const planes[2]) {
-  if ((a.H * a.W) % 4 == 0) return launch_variant<S, G, T, true>(a, plan, planes);
-  return launch_variant<S, G, T, false>(a, plan, planes);
+hipError_t launch_gt(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
+  if ((a.H * a.W) % 4 == 0) return launch_variant<S, G, T, true>(a, plan, planes, carries);
+  return launch_variant<S, G, T, false>(a, plan, planes, carries);
 }
 
 template <typename S>
-hipError_t launch_s(const LaunchArgs& a, const Plan& plan, float* const planes[2]) {
+hipError_t launch_s(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
   if (plan.steps_per_lane == 8) {
-    if (plan.lanes_per_seq == 32) return launch_gt<S, 32, 8>(a, plan, planes);
-    return launch_gt<S, 64, 8>(a, plan, planes);
+    if (plan.lanes_per_seq == 32) return launch_gt<S, 32, 8>(a, plan, planes, carries);
+    return launch_gt<S, 64, 8>(a, plan, planes, carries);
   }
   switch (plan.lanes_per_seq) {
-    case 16: return launch_gt<S, 16, 16>(a, plan, planes);
-    case 32: return launch_gt<S, 32, 16>(a, plan, planes);
-    default: return launch_gt<S, 64, 16>(a, plan, planes);
+    case 16: return launch_gt<S, 16, 16>(a, plan, planes, carries);
+    case 32: return launch_gt<S, 32, 16>(a, plan, planes, carries);
+    default: return launch_gt<S, 64, 16>(a, plan, planes, carries);
   }
 }
 
@@ -880,22 +984,42 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   pl.steps_per_lane = T;
   pl.waves = kWaves;
   pl.chans_per_block = kWaves * (64 / G);
-  pl.blocks = B * ((D + pl.chans_per_block - 1) / pl.chans_per_block);
   const bool vec = L % 4 == 0;  // the ABI layer guarantees base alignment for this case
+  // Too few (batch, channel block) pairs to fill the machine and long sequences:
+  // cut each sequence into segments of at least four full chunks, aiming at about
+  // three workgroups per CU; a carry pass then supplies each segment's entering
+  // state.
+  const int64_t units = B * ((D + pl.chans_per_block - 1) / pl.chans_per_block);
+  const int64_t nmain = L / (G * T);
+  pl.nseg = 1;
+  pl.seg_chunks = (int)(nmain > 0 ? nmain : 1);
+  if (vec && units < 512 && nmain >= 8) {
+    int64_t nseg = (768 + units - 1) / units;
+    if (nseg > nmain / 4) nseg = nmain / 4;
+    if (nseg > 1) {
+      const int64_t per = (nmain + nseg - 1) / nseg;
+      pl.seg_chunks = (int)per;
+      pl.nseg = (int)((nmain + per - 1) / per);
+    }
+  }
+  pl.blocks = units * pl.nseg;
   pl.lds_bytes = dtype == 0 ? lds_bytes_s<float>(G, T, vec) : lds_bytes_s<uint16_t>(G, T, vec);
-  pl.scratch_bytes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
+  const size_t planes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
+  pl.carry_offset = planes;
+  pl.scratch_bytes = planes + (pl.nseg > 1 ? (size_t)(B * 4 * D) * pl.nseg * 2 * kMaxN * sizeof(float) : 0);
   return pl;
 }
 
 hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch) {
   const int64_t plane = a.B * a.D * a.H * a.W;
   // planes: row-major (directions 0, 2), column-major (directions 1, 3)
+  float* carries = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + plan.carry_offset);
   if (a.dtype == 0) {
     float* const planes[2] = {static_cast<float*>(a.y), scratch};
-    return launch_s<float>(a, plan, planes);
+    return launch_s<float>(a, plan, planes, carries);
   }
   float* const planes[2] = {scratch + plane, scratch};
-  return launch_s<uint16_t>(a, plan, planes);
+  return launch_s<uint16_t>(a, plan, planes, carries);
 }
 
 }  // namespace ss2d

@@ -132,6 +132,8 @@ EDGE = [
     (1, 3, 128, 128, 5, "bf16"),  # plane in a global fp32 temporary
     (2, 3, 5, 7, 16, "bf16"),
     (2, 9, 28, 28, 16, "bf16"),
+    (1, 11, 96, 100, 16, "f32"),  # long rows cut into segments, last one with a remainder
+    (2, 5, 80, 96, 16, "bf16"),   # segments, bf16
 ]
 
 
