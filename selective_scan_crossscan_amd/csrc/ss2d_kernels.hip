@@ -560,15 +560,19 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
   }
 }
 
-// Bs/Cs staging of one group: NG states x {B, C} x (G lanes x TT steps) for the
-// chunk at c0, states n0.. ; thread-private share in float4 registers.
-template <typename S, int G, int T, int NG, int TT, bool VEC, bool FULL>
+// Register staging of Bs/Cs for a remainder chunk: NG states x {B, C} x (G lanes
+// x TT steps) from step c0 and state n0 on, each thread holding its share in
+// float4 registers until it writes them to LDS.  One (state, array) takes
+// kArr = G * seg_stride(TT) floats there, lane segments padded against bank
+// conflicts.
+template <typename S, int G, int NG, int TT, bool VEC, bool FULL>
 struct Stager {
-  static constexpr int kNth = Cfg<G, T, NG>::kThreads;
+  static constexpr int kNth = kWaves * 64;
   static constexpr int kPer = G * TT / 4;        // float4 per (state, array)
   static constexpr int kF4 = NG * 2 * kPer;      // float4 per group
   static constexpr int kQ = (kF4 + kNth - 1) / kNth;
   static constexpr int kSS = seg_stride<TT>();
+  static constexpr int kArr = G * kSS;
   float4 r[kQ];
 
   __device__ __forceinline__ void fetch(const S* Bbase, const S* Cbase, int tid, int n0, int N, int c0, int L) {
@@ -592,7 +596,6 @@ struct Stager {
     }
   }
   __device__ __forceinline__ void commit(float* buf, int tid) const {
-    constexpr int kArr = Cfg<G, T, NG>::kArr;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int f = tid + q * kNth;
@@ -612,11 +615,13 @@ struct Lane {
   bool dvalid;
 };
 
-// A remainder chunk of G*TT steps (TT < T, possibly ragged), staged synchronously.
+// A remainder chunk of G*TT steps (TT <= T, possibly ragged), staged through
+// registers in groups of as many states as fit the LDS area at smem (kAreaBytes);
+// with few steps per lane that is all of them, so the chunk synchronises once.
 // Out of line, with plain arguments: it runs a few times per direction, and
 // inlining it would make the register allocator budget its arrays on top of the
 // main loop's.
-template <typename S, int G, int T, int NG, int TT, bool VEC>
+template <typename S, int G, int T, int NG0, int TT, bool VEC, int kAreaBytes>
 __device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, float* a2s, float* carry,
                                         const S* dtrow, const S* xrow, const S* Bbase, const S* Cbase, float* plane,
                                         const float* pcol, S* yout, bool rev, bool col, bool add, bool last, float bias,
@@ -626,7 +631,11 @@ __device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, f
   ln.seg = seg;
   ln.dl = dl;
   ln.dvalid = dvalid;
-  using C = Cfg<G, T, NG>;
+  constexpr int kStateBytes = 2 * G * seg_stride<TT>() * 4;
+  constexpr int kFit = kAreaBytes / kStateBytes;
+  constexpr int NG = kFit >= kMaxN ? kMaxN : (kFit >= NG0 ? kFit : NG0);
+  static_assert(NG * kStateBytes <= kAreaBytes, "staged group must fit its LDS area");
+  using St = Stager<S, G, NG, TT, VEC, false>;
   constexpr int SS = seg_stride<TT>();
   const int l0 = c0 + ln.seg * TT;
   float dtv[TT], uv[TT];
@@ -634,7 +643,7 @@ __device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, f
   float delta[TT], du[TT], yv[TT];
   const float sdelta = prepare_steps<TT>(dtv, uv, bias, dsk, ln.dvalid, L - l0, delta, du, yv);
   for (int n0 = 0; n0 < N; n0 += NG) {
-    Stager<S, G, T, NG, TT, VEC, false> st;
+    St st;
     st.fetch(Bbase, Cbase, ln.tid, n0, N, c0, L);
     st.commit(smem, ln.tid);
     __syncthreads();
@@ -642,7 +651,7 @@ __device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, f
     for (int nn = 0; nn < NG; ++nn) {
       const int n = n0 + nn;
       if (n < N)
-        state_step<G, TT>(smem + (nn * 2) * C::kArr + ln.seg * SS, smem + (nn * 2 + 1) * C::kArr + ln.seg * SS,
+        state_step<G, TT>(smem + (nn * 2) * St::kArr + ln.seg * SS, smem + (nn * 2 + 1) * St::kArr + ln.seg * SS,
                           a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du, sdelta, yv);
     }
     __syncthreads();
@@ -828,7 +837,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     } else {
       // ---------------- rows not 16-byte aligned: every chunk staged through registers
       for (; c0 + GT <= L; c0 += GT)
-        tail_chunk<S, G, T, NG, T, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+        tail_chunk<S, G, T, NG, T, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
                                         plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
     }
 
@@ -854,22 +863,22 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
 
     // ---------------- remainder chunks (fewer steps per lane)
     while (L - c0 >= G * 8) {
-      tail_chunk<S, G, T, NG, 8, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 8, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
                                       plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 8;
     }
     if (L - c0 >= G * 4) {
-      tail_chunk<S, G, T, NG, 4, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 4, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
                                       plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 4;
     }
     if (L - c0 >= G * 2) {
-      tail_chunk<S, G, T, NG, 2, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 2, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
                                       plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 2;
     }
     while (c0 < L) {
-      tail_chunk<S, G, T, NG, 1, VEC>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 1, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
                                       plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G;
     }
