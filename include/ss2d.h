@@ -34,7 +34,8 @@ typedef enum { SS2D_F32 = 0, SS2D_BF16 = 1 } ss2d_dtype;
 typedef enum {
   SS2D_OK = 0,
   SS2D_ERR_NULL = -1,           /* a required pointer is NULL                     */
-  SS2D_ERR_SHAPE = -2,          /* B, D, H or W < 1, or a size overflows int64    */
+  SS2D_ERR_SHAPE = -2,          /* B, D, H or W < 1, H*W > 2^25 - 1, or a size    */
+                                /* overflows int64                                */
   SS2D_ERR_UNSUPPORTED_N = -3,  /* N outside 1..16                                */
   SS2D_ERR_DTYPE = -4,          /* dtype is not an ss2d_dtype value               */
   SS2D_ERR_ALIAS = -5,          /* y overlaps one of the inputs                   */
@@ -66,9 +67,13 @@ typedef enum {
  * SS2D_OK the work has been enqueued asynchronously; execution faults surface at
  * the caller's next synchronisation.  Nothing is printed, thrown or aborted.
  * Each call takes a stream-ordered temporary of B*D*H*W fp32 values (2*B*D*H*W
- * for bf16) for the merge, allocated and freed on `stream` from the device's
- * default memory pool (whose release threshold the library raises so freed
- * blocks are reused).  NaN and Inf propagate.  Thread-safe.
+ * for bf16) for the merge -- plus 32 fp32 values per (batch, direction,
+ * channel, segment) when a long map is cut into segments (ss2d_describe shows
+ * the plan and the exact size) -- allocated and freed on `stream` from the
+ * device's default memory pool (whose release threshold the library raises so
+ * freed blocks are reused).  A call then runs one kernel, or five for segmented
+ * maps (a carry pass and one launch per direction), all on `stream`.  NaN and
+ * Inf propagate.  Thread-safe.
  */
 int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
                  const void* Bs, const void* Cs, const float* Ds, void* y,

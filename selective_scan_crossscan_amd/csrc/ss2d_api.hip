@@ -32,8 +32,10 @@ int check_shape(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype
   if (B < 1 || D < 1 || H < 1 || W < 1) return SS2D_ERR_SHAPE;
   int64_t L, t;
   // Every element count and byte count must fit comfortably: the kernels use
-  // 32-bit in-row offsets and 32-bit channel/batch indices.
-  if (!mul_ok(H, W, &L) || L > INT32_MAX / 4) return SS2D_ERR_SHAPE;
+  // 32-bit in-row offsets and 32-bit channel/batch indices, and address staged
+  // rows of up to 16 states or channels with 32-bit byte offsets (16 * L * 4 must
+  // stay below 2^31).
+  if (!mul_ok(H, W, &L) || L > INT32_MAX / 64) return SS2D_ERR_SHAPE;
   if (!mul_ok(B, 4, &t) || !mul_ok(t, D, &t) || !mul_ok(t, L, &t) || !mul_ok(t, 4, &t)) return SS2D_ERR_SHAPE;
   if (B > INT32_MAX / 4 || D > INT32_MAX / 4) return SS2D_ERR_SHAPE;
   if (N < 1 || N > 16) return SS2D_ERR_UNSUPPORTED_N;

@@ -207,7 +207,7 @@ struct Cfg {
 // LDS of a workgroup (bytes), for storage type S.  Separate arrays, so the
 // compiler can tell a DMA copy into one from reads of another and does not
 // make those reads wait for the copy.
-//   ring0, ring1  one Bs/Cs group each, copied in by DMA: [NG][B|C][G*T] of S;
+//   ring0, ring1  one Bs/Cs group each, copied in by DMA: [B|C][NG][G*T] of S;
 //                 ring0 also holds the register-staged group of a remainder
 //                 chunk and the tile of the final transpose
 //   dtb           dt of the next full chunk, copied in by DMA: [kChans][G*T] of S
@@ -254,13 +254,27 @@ struct Swz {
 // included) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// A row of a staged tensor: its buffer resource and the byte offset of the row
+// start in it.  Buffer resources keep the per-copy address arithmetic to a
+// 32-bit scalar offset (the lane part is one fixed register).
+struct RowRef {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off;
+};
+
+// Word 3 of a raw (unformatted, unswizzled) buffer resource on the gfx9 family.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
 // A copy of R rows of G*T elements into LDS, swizzled, split over the
 // workgroup: each lane moves GB bytes per copy instruction (16: fp32 rows
 // 16-byte aligned, else 4), a wave 64*GB bytes, which never straddle two rows.
 // The swizzle repeats every kPeriod = 16*SP slots, and a wave's copies all
-// start at the same offset inside that period, so a lane's element offset is a
-// per-lane constant plus a wave-uniform part: the address is a scalar row base
-// plus one 32-bit lane offset computed once.
+// start at the same offset inside that period, so a lane's byte offset is a
+// per-lane constant plus a wave-uniform part.
 template <typename S, int G, int T, int R, int GB>
 struct DmaPlan {
   using Z = Swz<S, T>;
@@ -274,7 +288,7 @@ struct DmaPlan {
   static_assert((kNth * GB) % kPeriod == 0 && kRowBytes % kPeriod == 0,
                 "a wave's copies must sit at one offset inside the swizzle period");
   int wave;
-  uint32_t lane_elem;
+  uint32_t lane_byte;
 
   __device__ __forceinline__ explicit DmaPlan(int tid) {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,27 +296,28 @@ struct DmaPlan {
     const int slot = rb >> 4;
     const int seg = slot / Z::kSP;
     const int q = (slot % Z::kSP) ^ Z::swz(seg);
-    lane_elem = seg * T + q * Z::kEps + (rb & 15) / (int)sizeof(S);
+    lane_byte = (seg * T + q * Z::kEps) * (int)sizeof(S) + (rb & 15);
   }
 
-  // Every thread of the workgroup calls it; row r starts at src(r) + c0.
+  // Every thread of the workgroup calls it; row(r) gives row r's RowRef, and the
+  // copy starts c0 elements into each row.
   template <typename RowFn>
-  __device__ __forceinline__ void copy(char* dst, RowFn src, int c0) const {
-    // Opaque copies of the plan: the addresses are cheap to form here, and
-    // hoisted out of the main loop they would hold registers through it.
-    int w = wave;
-    uint32_t le = lane_elem;
-    asm volatile("" : "+s"(w), "+v"(le));
+  __device__ __forceinline__ void copy(char* dst, RowFn row, int c0) const {
+    // Opaque copies of the plan: the offsets are cheap to form here, and hoisted
+    // out of the main loop they would hold registers through it.
+    uint32_t w = (uint32_t)wave;
+    uint32_t lb = lane_byte;
+    asm volatile("" : "+s"(w), "+v"(lb));
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
-      const int wbyte = (it * kNth + w * 64) * GB;  // first byte of this wave's copy
-      const int rowb = wbyte % kRowBytes;
-      const S* base = src(wbyte / kRowBytes) + c0 + (rowb - rowb % kPeriod) / (int)sizeof(S);
-      const S* g = base + le;
+      const uint32_t wbyte = ((uint32_t)it * kNth + w * 64u) * GB;  // first byte of this wave's copy
+      const uint32_t rowb = wbyte % (uint32_t)kRowBytes;
+      const RowRef rr = row((int)(wbyte / (uint32_t)kRowBytes));
+      const uint32_t soff = rr.off + (uint32_t)c0 * (uint32_t)sizeof(S) + (rowb - rowb % (uint32_t)kPeriod);
       if constexpr (GB == 16)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + wbyte), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr.r, (lds_void_t*)(dst + wbyte), 16, lb, soff, 0, 0);
       else
-        __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)(dst + wbyte), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr.r, (lds_void_t*)(dst + wbyte), 4, lb, soff, 0, 0);
     }
   }
 };
@@ -760,15 +775,19 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
 
     if constexpr (VEC) {
       // ---------------- full chunks: Bs/Cs one group ahead and dt one chunk ahead, by DMA
-      const int d0 = ln.d0;
-      auto dt_rows = [=](int r) {  // channel r of the block (a valid row stands in past D)
-        const int dg = d0 + r < D ? d0 + r : d0;
-        return dtdir + (int64_t)dg * L;
-      };
-      auto bc_rows = [=](int g) {  // row 2*nn + {0: B, 1: C} of state g*NG + nn (state 0 stands in past N)
+      // Staged rows: dt of the block's channels (a valid row stands in past D), and
+      // per Bs/Cs group the B rows of its NG states, then their C rows (state 0
+      // stands in past N).  Resources cover this (batch, direction) only.
+      const int nval = D - ln.d0 < CH ? D - ln.d0 : CH;
+      const uint32_t rowsz = (uint32_t)L * (uint32_t)sizeof(S);
+      const __amdgpu_buffer_rsrc_t rdt = make_rsrc(dtdir + (int64_t)ln.d0 * L, (uint32_t)nval * rowsz);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bbase, (uint32_t)N * rowsz);
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cbase, (uint32_t)N * rowsz);
+      auto dt_rows = [=](int r) { return RowRef{rdt, (uint32_t)(r < nval ? r : 0) * rowsz}; };
+      auto bc_rows = [=](int g) {
         return [=](int r) {
-          const int n = g * NG + (r >> 1);
-          return ((r & 1) ? Cbase : Bbase) + (int64_t)(n < N ? n : 0) * L;
+          const int n = g * NG + (r < NG ? r : r - NG);
+          return RowRef{r < NG ? rb : rc, (uint32_t)(n < N ? n : 0) * rowsz};
         };
       };
       if (cend > cbeg) {
@@ -802,12 +821,12 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
             const int n = g * NG + nn;
             if (n < N) {
               if constexpr (MODE == kCarry) {
-                state_carry<S, G, T>(cur + (2 * nn) * GT * (int)sizeof(S), ln.seg, a2s[ln.dl * kMaxN + n],
+                state_carry<S, G, T>(cur + nn * GT * (int)sizeof(S), ln.seg, a2s[ln.dl * kMaxN + n],
                                      carry + ln.dl * kMaxN + n, aprod + ln.dl * kMaxN + n, delta, du, sdelta);
               } else {
                 float Bv[T], Cv[T];
-                read_seg<S, T>(cur + (2 * nn) * GT * (int)sizeof(S), ln.seg, Bv);
-                read_seg<S, T>(cur + (2 * nn + 1) * GT * (int)sizeof(S), ln.seg, Cv);
+                read_seg<S, T>(cur + nn * GT * (int)sizeof(S), ln.seg, Bv);
+                read_seg<S, T>(cur + (NG + nn) * GT * (int)sizeof(S), ln.seg, Cv);
                 state_core<G, T>(Bv, Cv, a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du,
                                  sdelta, yv);
               }
