@@ -78,7 +78,8 @@ def test_null_pointer(which):
 
 
 @pytest.mark.parametrize("shape", [(0, 3, 4, 5), (2, 0, 4, 5), (2, 3, 0, 5), (2, 3, 4, 0), (-1, 3, 4, 5),
-                                   (1, 1, 1 << 31, 1 << 31), (1 << 40, 1 << 20, 8, 8)])
+                                   (1, 1, 1 << 31, 1 << 31), (1 << 40, 1 << 20, 8, 8),
+                                   (1, 1, 1 << 13, 1 << 12)])  # H*W = 2^25: past the 32-bit row offsets
 def test_bad_shape(shape):
     B, D, H, W = shape
     assert _call(B=B, D=D, H=H, W=W) == -2
