@@ -633,11 +633,10 @@ struct Lane {
 // A remainder chunk of G*TT steps (TT <= T, possibly ragged), staged through
 // registers in groups of as many states as fit the LDS area at smem (kAreaBytes);
 // with few steps per lane that is all of them, so the chunk synchronises once.
-// Out of line, with plain arguments: it runs a few times per direction, and
-// inlining it would make the register allocator budget its arrays on top of the
-// main loop's.
+// Inlined: as a call, the calling convention would make the main loop keep its
+// values in fewer, callee-saved registers, and the callee spill to scratch.
 template <typename S, int G, int T, int NG0, int TT, bool VEC, int kAreaBytes>
-__device__ __noinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, float* a2s, float* carry,
+__device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, float* a2s, float* carry,
                                         const S* dtrow, const S* xrow, const S* Bbase, const S* Cbase, float* plane,
                                         const float* pcol, S* yout, bool rev, bool col, bool add, bool last, float bias,
                                         float dsk, int c0, int L, int H, int W, int N) {
