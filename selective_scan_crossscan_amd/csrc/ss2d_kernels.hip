@@ -731,10 +731,9 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   const bool last_seg = sidx == p.nseg - 1;
   const int cend = last_seg ? nmain : cbeg + p.seg_chunks;
 
-#pragma unroll 1
-  for (int kk = 0; kk < (MODE == kSegment ? 1 : 4); ++kk) {
-    // column pair, then row pair: the last direction finishes the merge
-    const int k = MODE == kSegment ? p.kdir : (kk == 0) ? 1 : (kk == 1) ? 3 : (kk == 2) ? 0 : 2;
+  // One direction, specialised at compile time (walk order, merge mode).
+  auto direction = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
     // per-direction parameters of the block's channels; the state entering the
     // segment is the composition of the maps of the segments before it
     for (int i = ln.tid; i < CH * kMaxN; i += NTH) {
@@ -759,7 +758,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     }
     __syncthreads();
 
-    const bool rev = k >= 2, col = (k & 1) != 0, add = k == 3, last = k == 2;
+    constexpr bool rev = k >= 2, col = (k & 1) != 0, add = k == 3, last = k == 2;
     float* plane = (col ? p.pcol : p.prow) + plane_off;
     const float* pcol = p.pcol + plane_off;
     S* yout = static_cast<S*>(p.y) + plane_off;
@@ -798,14 +797,16 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       // Group g of every chunk lives in ring(g & 1); the next chunk's group 0 is
       // copied during this chunk's last group when that group is in ring1.
       const bool cross = (ngrp & 1) == 0;
+      float xn[T];  // x of the next chunk, loaded a whole chunk ahead
+      if (cbeg < cend) load_x<S, T, VEC, true>(xrow, rev, col, cbeg * GT + ln.seg * T, L, H, W, xn);
       for (int c = cbeg; c < cend; ++c) {
-        float dtn[T], un[T];
+        float dtn[T];
         read_seg<S, T>(dtb + ln.dl * GT * (int)sizeof(S), ln.seg, dtn);
-        load_x<S, T, VEC, true>(xrow, rev, col, c * GT + ln.seg * T, L, H, W, un);
         float delta[T], du[T], yv[T];
         // Lanes of a channel past D work on channel d0's data and store nothing; a
         // group of G lanes never mixes channels, so no masking is needed here.
-        const float sdelta = prepare_steps<T>(dtn, un, bias, dsk, true, T, delta, du, yv);
+        const float sdelta = prepare_steps<T>(dtn, xn, bias, dsk, true, T, delta, du, yv);
+        if (c + 1 < cend) load_x<S, T, VEC, true>(xrow, rev, col, (c + 1) * GT + ln.seg * T, L, H, W, xn);
         auto group = [&](const char* cur, char* nxt, int g) {
           const bool more_states = g + 1 < ngrp;
           // nxt was last read before the previous barrier
@@ -872,11 +873,11 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         }
       }
       __syncthreads();
-      continue;
+      return;
     }
     if (!last_seg) {
       __syncthreads();  // this direction's plane writes are complete and visible to the block
-      continue;
+      return;
     }
 
     // ---------------- remainder chunks (fewer steps per lane)
@@ -901,6 +902,21 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       c0 += G;
     }
     __syncthreads();  // this direction's plane writes are complete and visible to the block
+  };
+
+  if constexpr (MODE == kSegment) {
+    switch (p.kdir) {
+      case 0: direction(std::integral_constant<int, 0>{}); break;
+      case 1: direction(std::integral_constant<int, 1>{}); break;
+      case 2: direction(std::integral_constant<int, 2>{}); break;
+      default: direction(std::integral_constant<int, 3>{}); break;
+    }
+  } else {
+    // column pair, then row pair: the last direction finishes the merge
+    direction(std::integral_constant<int, 1>{});
+    direction(std::integral_constant<int, 3>{});
+    direction(std::integral_constant<int, 0>{});
+    direction(std::integral_constant<int, 2>{});
   }
 }
 
