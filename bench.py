@@ -39,9 +39,10 @@ TRANS_SLOTS = 4
 SLOTS_PER_UPDATE = 4 + TRANS_SLOTS
 PEAK_UPDATES_PER_S = CUS * CLOCK_HZ * VALU_LANES_PER_CLK / SLOTS_PER_UPDATE  # 9.83e12
 
-KERNEL_SOURCES = ["selective_scan_crossscan_amd/csrc/ss2d_kernels.hip",
-                  "selective_scan_crossscan_amd/csrc/ss2d_api.hip",
-                  "selective_scan_crossscan_amd/csrc/ss2d_internal.h"]
+KERNEL_SOURCES = sorted(
+    os.path.relpath(os.path.join(dp, f), ROOT)
+    for dp, _, fs in os.walk(os.path.join(ROOT, "selective_scan_crossscan_amd", "csrc"))
+    for f in fs if f.endswith((".hip", ".h")))
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 

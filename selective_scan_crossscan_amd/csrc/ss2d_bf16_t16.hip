@@ -1,0 +1,14 @@
+// Compiles the SS2D forward kernels for bf16 storage, 16 steps per lane.
+#include "ss2d_kernels.h"
+
+namespace ss2d {
+
+hipError_t launch_bf16_t16(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
+  switch (plan.lanes_per_seq) {
+    case 16: return launch_gt<uint16_t, 16, 16>(a, plan, planes, carries);
+    case 32: return launch_gt<uint16_t, 32, 16>(a, plan, planes, carries);
+    default: return launch_gt<uint16_t, 64, 16>(a, plan, planes, carries);
+  }
+}
+
+}  // namespace ss2d

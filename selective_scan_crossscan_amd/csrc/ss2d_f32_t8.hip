@@ -1,0 +1,11 @@
+// Compiles the SS2D forward kernels for fp32 storage, 8 steps per lane.
+#include "ss2d_kernels.h"
+
+namespace ss2d {
+
+hipError_t launch_f32_t8(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
+  if (plan.lanes_per_seq == 32) return launch_gt<float, 32, 8>(a, plan, planes, carries);
+  return launch_gt<float, 64, 8>(a, plan, planes, carries);
+}
+
+}  // namespace ss2d

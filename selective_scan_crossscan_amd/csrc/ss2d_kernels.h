@@ -1,4 +1,6 @@
-// SS2D forward kernels for gfx950 (CDNA4, wave64).
+// SS2D forward kernels for gfx950 (CDNA4, wave64): the kernel templates.
+// Included by the compilation units that instantiate them (one per storage
+// type and steps per lane, so they build in parallel) and by ss2d_plan.hip.
 //
 // What is computed (page [SS2D] "深入解析VMamba中的SS2D模块从理论到代码实现"):
 //   §3.1/§4  four scan sequences of the H x W map: row-major, column-major and
@@ -34,6 +36,8 @@
 //     both and writes y = (y0 + y2) + (y1 + y3), rounded once: the order of
 //     additions is fixed, so results are deterministic, with no atomics and no
 //     separate merge pass.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -300,9 +304,15 @@ struct DmaPlan {
   }
 
   // Every thread of the workgroup calls it; row(r) gives row r's RowRef, and the
-  // copy starts c0 elements into each row.
+  // copy starts c0 elements into each row.  Only the first lim elements of a row
+  // exist (lim < G*T for a partial last chunk): lanes past them copy the last
+  // existing granule instead, so nothing outside the tensor is read.
   template <typename RowFn>
-  __device__ __forceinline__ void copy(char* dst, RowFn row, int c0) const {
+  __device__ __forceinline__ void copy(char* dst, RowFn row, int c0, int lim = G * T) const {
+    if (lim < G * T) {
+      copy_partial(dst, row, c0, lim);
+      return;
+    }
     // Opaque copies of the plan: the offsets are cheap to form here, and hoisted
     // out of the main loop they would hold registers through it.
     uint32_t w = (uint32_t)wave;
@@ -318,6 +328,28 @@ struct DmaPlan {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rr.r, (lds_void_t*)(dst + wbyte), 16, lb, soff, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rr.r, (lds_void_t*)(dst + wbyte), 4, lb, soff, 0, 0);
+    }
+  }
+
+  // The partial-chunk form: the whole in-row offset goes into the lane offset,
+  // clamped to the last granule that exists (lim is a multiple of 4 elements, a
+  // granule is at most 4, so that granule lies wholly inside the row).
+  template <typename RowFn>
+  __device__ __forceinline__ void copy_partial(char* dst, RowFn row, int c0, int lim) const {
+    constexpr uint32_t kEg = GB / (int)sizeof(S);  // elements per granule
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const uint32_t wbyte = ((uint32_t)it * kNth + (uint32_t)wave * 64u) * GB;
+      const uint32_t rowb = wbyte % (uint32_t)kRowBytes;
+      const RowRef rr = row((int)(wbyte / (uint32_t)kRowBytes));
+      const uint32_t e = (rowb - rowb % (uint32_t)kPeriod) / (uint32_t)sizeof(S) + lane_byte / (uint32_t)sizeof(S);
+      const uint32_t ec = e < (uint32_t)lim ? e : (uint32_t)lim - kEg;
+      const uint32_t voff = ec * (uint32_t)sizeof(S);
+      const uint32_t soff = rr.off + (uint32_t)c0 * (uint32_t)sizeof(S);
+      if constexpr (GB == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr.r, (lds_void_t*)(dst + wbyte), 16, voff, soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr.r, (lds_void_t*)(dst + wbyte), 4, voff, soff, 0, 0);
     }
   }
 };
@@ -788,9 +820,15 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
           return RowRef{r < NG ? rb : rc, (uint32_t)(n < N ? n : 0) * rowsz};
         };
       };
-      if (cend > cbeg) {
-        dpl.copy(dtb, dt_rows, cbeg * GT);
-        bpl.copy(ring0, bc_rows(0), cbeg * GT);
+      // A sequence shorter than one chunk but at least half of one runs as a single
+      // partial chunk of this pipeline (its steps past L are identity maps)
+      // instead of remainder chunks.  Only 16-lane plans see such lengths (32
+      // lanes are planned from 512 steps on).
+      constexpr bool kPartial = G == 16;
+      const bool partial = kPartial && nmain == 0 && 2 * L >= GT;
+      if (cend > cbeg || partial) {
+        dpl.copy(dtb, dt_rows, cbeg * GT, partial ? L : GT);
+        bpl.copy(ring0, bc_rows(0), cbeg * GT, partial ? L : GT);
         wait_vmem();
         __syncthreads();
       }
@@ -798,23 +836,31 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       // copied during this chunk's last group when that group is in ring1.
       const bool cross = (ngrp & 1) == 0;
       float xn[T];  // x of the next chunk, loaded a whole chunk ahead
-      if (cbeg < cend) load_x<S, T, VEC, true>(xrow, rev, col, cbeg * GT + ln.seg * T, L, H, W, xn);
-      for (int c = cbeg; c < cend; ++c) {
+      if (partial)
+        load_x<S, T, VEC, false>(xrow, rev, col, ln.seg * T, L, H, W, xn);
+      else if (cbeg < cend)
+        load_x<S, T, VEC, true>(xrow, rev, col, cbeg * GT + ln.seg * T, L, H, W, xn);
+      // One chunk; PART: the partial last chunk (full chunks keep their checks
+      // out of the code).
+      auto chunk = [&](int c, auto part_c) {
+        constexpr bool PART = decltype(part_c)::value;
         float dtn[T];
         read_seg<S, T>(dtb + ln.dl * GT * (int)sizeof(S), ln.seg, dtn);
         float delta[T], du[T], yv[T];
         // Lanes of a channel past D work on channel d0's data and store nothing; a
         // group of G lanes never mixes channels, so no masking is needed here.
-        const float sdelta = prepare_steps<T>(dtn, xn, bias, dsk, true, T, delta, du, yv);
-        if (c + 1 < cend) load_x<S, T, VEC, true>(xrow, rev, col, (c + 1) * GT + ln.seg * T, L, H, W, xn);
+        // Steps past L (partial chunk) get delta = 0: the identity map.
+        const int nvalid = PART ? L - (c * GT + ln.seg * T) : T;
+        const float sdelta = prepare_steps<T>(dtn, xn, bias, dsk, true, nvalid, delta, du, yv);
+        if (!PART && c + 1 < cend) load_x<S, T, VEC, true>(xrow, rev, col, (c + 1) * GT + ln.seg * T, L, H, W, xn);
         auto group = [&](const char* cur, char* nxt, int g) {
           const bool more_states = g + 1 < ngrp;
           // nxt was last read before the previous barrier
           if (more_states)
-            bpl.copy(nxt, bc_rows(g + 1), c * GT);
-          else if (cross && c + 1 < cend)
+            bpl.copy(nxt, bc_rows(g + 1), c * GT, PART ? L : GT);
+          else if (!PART && cross && c + 1 < cend)
             bpl.copy(nxt, bc_rows(0), (c + 1) * GT);
-          if (g == 1 && c + 1 < cend)  // every lane has read this chunk's dt (barrier after group 0)
+          if (!PART && g == 1 && c + 1 < cend)  // every lane has read this chunk's dt (barrier after group 0)
             dpl.copy(dtb, dt_rows, (c + 1) * GT);
 #pragma unroll 1
           for (int nn = 0; nn < NG; ++nn) {
@@ -839,7 +885,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
           group(ring0, ring1, g);
           if (g + 1 < ngrp) group(ring1, ring0, g + 1);
         }
-        if (c + 1 < cend && (!cross || ngrp == 1)) {  // nothing was copied ahead: copy now and wait
+        if (!PART && c + 1 < cend && (!cross || ngrp == 1)) {  // nothing was copied ahead: copy now and wait
           if (!cross) bpl.copy(ring0, bc_rows(0), (c + 1) * GT);
           if (ngrp == 1) dpl.copy(dtb, dt_rows, (c + 1) * GT);
           wait_vmem();
@@ -847,12 +893,17 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         }
         if (MODE != kCarry && ln.dvalid) {
           if (last)
-            store_final<S, T, VEC, true>(plane, pcol, yout, c * GT + ln.seg * T, L, H, W, yv);
+            store_final<S, T, VEC, !PART>(plane, pcol, yout, c * GT + ln.seg * T, L, H, W, yv);
           else
-            store_outputs<T, VEC, true>(plane, rev, add, c * GT + ln.seg * T, L, yv);
+            store_outputs<T, VEC, !PART>(plane, rev, add, c * GT + ln.seg * T, L, yv);
         }
+      };
+      if constexpr (kPartial) {
+        if (partial) chunk(0, std::true_type{});
       }
-      c0 = cend * GT;
+      if (!partial)
+        for (int c = cbeg; c < cend; ++c) chunk(c, std::false_type{});
+      c0 = partial ? L : cend * GT;
     } else {
       // ---------------- rows not 16-byte aligned: every chunk staged through registers
       for (; c0 + GT <= L; c0 += GT)
@@ -985,19 +1036,6 @@ hipError_t launch_gt(const LaunchArgs& a, const Plan& plan, float* const planes[
   return launch_variant<S, G, T, false>(a, plan, planes, carries);
 }
 
-template <typename S>
-hipError_t launch_s(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
-  if (plan.steps_per_lane == 8) {
-    if (plan.lanes_per_seq == 32) return launch_gt<S, 32, 8>(a, plan, planes, carries);
-    return launch_gt<S, 64, 8>(a, plan, planes, carries);
-  }
-  switch (plan.lanes_per_seq) {
-    case 16: return launch_gt<S, 16, 16>(a, plan, planes, carries);
-    case 32: return launch_gt<S, 32, 16>(a, plan, planes, carries);
-    default: return launch_gt<S, 64, 16>(a, plan, planes, carries);
-  }
-}
-
 template <typename S, int G, int T>
 size_t lds_bytes_for(bool vec) {
   return vec ? (size_t)Layout<S, G, T, group_states<G, T>(), true>::kBytes
@@ -1012,57 +1050,11 @@ size_t lds_bytes_s(int G, int T, bool vec) {
 
 }  // namespace
 
-Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override) {
-  (void)N;
-  Plan pl;
-  const int64_t L = H * W;
-  int G = L < 512 ? 16 : 32;
-  if (lanes_override == 16 || lanes_override == 32 || lanes_override == 64) G = lanes_override;
-  // Steps per lane: 16, unless the remainder after whole 16-step chunks would fill
-  // at least one 8-step chunk, which then runs at full speed instead of in the
-  // remainder path (8-step chunks exist for 32 and 64 lanes).
-  int T = 16;
-  if (G != 16 && L % (16 * G) >= 8 * G) T = 8;
-  pl.lanes_per_seq = G;
-  pl.steps_per_lane = T;
-  pl.waves = kWaves;
-  pl.chans_per_block = kWaves * (64 / G);
-  const bool vec = L % 4 == 0;  // the ABI layer guarantees base alignment for this case
-  // Too few (batch, channel block) pairs to fill the machine and long sequences:
-  // cut each sequence into segments of at least four full chunks, aiming at about
-  // three workgroups per CU; a carry pass then supplies each segment's entering
-  // state.
-  const int64_t units = B * ((D + pl.chans_per_block - 1) / pl.chans_per_block);
-  const int64_t nmain = L / (G * T);
-  pl.nseg = 1;
-  pl.seg_chunks = (int)(nmain > 0 ? nmain : 1);
-  if (vec && units < 512 && nmain >= 8) {
-    int64_t nseg = (768 + units - 1) / units;
-    if (nseg > nmain / 4) nseg = nmain / 4;
-    if (nseg > 1) {
-      const int64_t per = (nmain + nseg - 1) / nseg;
-      pl.seg_chunks = (int)per;
-      pl.nseg = (int)((nmain + per - 1) / per);
-    }
-  }
-  pl.blocks = units * pl.nseg;
-  pl.lds_bytes = dtype == 0 ? lds_bytes_s<float>(G, T, vec) : lds_bytes_s<uint16_t>(G, T, vec);
-  const size_t planes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
-  pl.carry_offset = planes;
-  pl.scratch_bytes = planes + (pl.nseg > 1 ? (size_t)(B * 4 * D) * pl.nseg * 2 * kMaxN * sizeof(float) : 0);
-  return pl;
-}
-
-hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch) {
-  const int64_t plane = a.B * a.D * a.H * a.W;
-  // planes: row-major (directions 0, 2), column-major (directions 1, 3)
-  float* carries = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + plan.carry_offset);
-  if (a.dtype == 0) {
-    float* const planes[2] = {static_cast<float*>(a.y), scratch};
-    return launch_s<float>(a, plan, planes, carries);
-  }
-  float* const planes[2] = {scratch + plane, scratch};
-  return launch_s<uint16_t>(a, plan, planes, carries);
-}
+// Launchers of the compiled variants, one compilation unit each (steps per lane
+// T = 16 for 16/32/64 lanes, T = 8 for 32/64 lanes).
+hipError_t launch_f32_t16(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
+hipError_t launch_f32_t8(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
+hipError_t launch_bf16_t16(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
+hipError_t launch_bf16_t8(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
 
 }  // namespace ss2d

@@ -1,0 +1,61 @@
+// Launch planning and dispatch of the SS2D forward (the kernels are compiled in
+// the ss2d_{f32,bf16}_t{16,8}.hip units).
+#include "ss2d_kernels.h"
+
+namespace ss2d {
+
+Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override) {
+  (void)N;
+  Plan pl;
+  const int64_t L = H * W;
+  int G = L < 512 ? 16 : 32;
+  if (lanes_override == 16 || lanes_override == 32 || lanes_override == 64) G = lanes_override;
+  // Steps per lane: 16, unless the remainder after whole 16-step chunks would fill
+  // at least one 8-step chunk, which then runs at full speed instead of in the
+  // remainder path (8-step chunks exist for 32 and 64 lanes).
+  int T = 16;
+  if (G != 16 && L % (16 * G) >= 8 * G) T = 8;
+  pl.lanes_per_seq = G;
+  pl.steps_per_lane = T;
+  pl.waves = kWaves;
+  pl.chans_per_block = kWaves * (64 / G);
+  const bool vec = L % 4 == 0;  // the ABI layer guarantees base alignment for this case
+  // Too few (batch, channel block) pairs to fill the machine and long sequences:
+  // cut each sequence into segments of at least four full chunks, aiming at about
+  // three workgroups per CU; a carry pass then supplies each segment's entering
+  // state.
+  const int64_t units = B * ((D + pl.chans_per_block - 1) / pl.chans_per_block);
+  const int64_t nmain = L / (G * T);
+  pl.nseg = 1;
+  pl.seg_chunks = (int)(nmain > 0 ? nmain : 1);
+  if (vec && units < 512 && nmain >= 8) {
+    int64_t nseg = (768 + units - 1) / units;
+    if (nseg > nmain / 4) nseg = nmain / 4;
+    if (nseg > 1) {
+      const int64_t per = (nmain + nseg - 1) / nseg;
+      pl.seg_chunks = (int)per;
+      pl.nseg = (int)((nmain + per - 1) / per);
+    }
+  }
+  pl.blocks = units * pl.nseg;
+  pl.lds_bytes = dtype == 0 ? lds_bytes_s<float>(G, T, vec) : lds_bytes_s<uint16_t>(G, T, vec);
+  const size_t planes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
+  pl.carry_offset = planes;
+  pl.scratch_bytes = planes + (pl.nseg > 1 ? (size_t)(B * 4 * D) * pl.nseg * 2 * kMaxN * sizeof(float) : 0);
+  return pl;
+}
+
+hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch) {
+  const int64_t plane = a.B * a.D * a.H * a.W;
+  // planes: row-major (directions 0, 2), column-major (directions 1, 3)
+  float* carries = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + plan.carry_offset);
+  const bool t8 = plan.steps_per_lane == 8;
+  if (a.dtype == 0) {
+    float* const planes[2] = {static_cast<float*>(a.y), scratch};
+    return t8 ? launch_f32_t8(a, plan, planes, carries) : launch_f32_t16(a, plan, planes, carries);
+  }
+  float* const planes[2] = {scratch + plane, scratch};
+  return t8 ? launch_bf16_t8(a, plan, planes, carries) : launch_bf16_t16(a, plan, planes, carries);
+}
+
+}  // namespace ss2d

@@ -134,6 +134,8 @@ EDGE = [
     (2, 9, 28, 28, 16, "bf16"),
     (1, 11, 96, 100, 16, "f32"),  # long rows cut into segments, last one with a remainder
     (2, 5, 80, 96, 16, "bf16"),   # segments, bf16
+    (2, 7, 12, 16, 16, "f32"),    # one partial chunk (192 of 256 steps) in the DMA pipeline
+    (1, 5, 10, 20, 9, "bf16"),    # partial chunk, bf16, odd N
 ]
 
 
