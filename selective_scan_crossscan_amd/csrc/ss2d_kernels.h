@@ -492,6 +492,7 @@ template <int G, int T>
 __device__ __forceinline__ void state_core(const float (&Bv)[T], const float (&Cv)[T], float A2n, float* carry_slot,
                                            int seg, const float (&delta)[T], const float (&du)[T], float sdelta,
                                            float (&yv)[T]) {
+  const float cin = *carry_slot;  // read first: its LDS latency hides behind the fold
   float a[T], bb[T];
 #pragma unroll
   for (int i = 0; i < T; ++i) {
@@ -503,7 +504,7 @@ __device__ __forceinline__ void state_core(const float (&Bv)[T], const float (&C
   for (int i = 1; i < T; ++i) Bl = fmaf(a[i], Bl, bb[i]);
   float Al = __builtin_amdgcn_exp2f(A2n * sdelta);
   scan_inclusive<G>(Al, Bl);
-  float h = incoming_state<G>(Al, Bl, *carry_slot, seg);
+  float h = incoming_state<G>(Al, Bl, cin, seg);
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     h = fmaf(a[i], h, bb[i]);
