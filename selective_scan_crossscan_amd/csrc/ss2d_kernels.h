@@ -354,6 +354,77 @@ struct DmaPlan {
   }
 };
 
+// A copy of R rows of G*TT elements (a remainder chunk: TT < T) into LDS in
+// plain row-major order, row r at r * kRowBytes, segment s of a row at s * TT
+// elements.  Each wave-wide copy stays inside the rows of one tensor (row(r)
+// gives the same resource for all rows it covers: blocks of 16 rows are one
+// tensor), possibly spanning several short rows.  Steps past a row's end read
+// the next row or, past the tensor, the zeros a buffer load returns out of
+// range; the remainder step gives them delta = 0.
+template <typename S, int G, int TT, int R, int GB>
+struct PlainCopy {
+  static constexpr int kRowBytes = G * TT * (int)sizeof(S);
+  static constexpr int kWaveBytes = 64 * GB;
+  static constexpr int kCopies = R * kRowBytes / kWaveBytes;
+  static_assert((R * kRowBytes) % kWaveBytes == 0, "rows must fill whole wave-wide copies");
+  static_assert(kRowBytes % kWaveBytes == 0 || kWaveBytes % kRowBytes == 0, "row and copy sizes must nest");
+
+  template <typename RowFn>
+  __device__ __forceinline__ static void copy(char* dst, RowFn row, int c0, int tid) {
+    // Opaque, so the address arithmetic stays here instead of being hoisted out of
+    // the chunk loop into registers held through it.
+    uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t lb = (uint32_t)(tid & 63) * GB;
+    asm volatile("" : "+s"(wave), "+v"(lb), "+s"(c0));
+#pragma unroll
+    for (int j0 = 0; j0 < kCopies; j0 += kWaves) {
+      const int j = j0 + (int)wave;
+      if (j < kCopies) {
+        const uint32_t wbyte = (uint32_t)j * kWaveBytes;
+        const uint32_t byte = wbyte + lb;
+        const RowRef head = row((int)(wbyte / kRowBytes));  // resource of the copy
+        const RowRef mine = row((int)(byte / kRowBytes));   // this lane's row
+        const uint32_t voff = mine.off + (uint32_t)c0 * (uint32_t)sizeof(S) + byte % kRowBytes;
+        if constexpr (GB == 16)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(head.r, (lds_void_t*)(dst + wbyte), 16, voff, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(head.r, (lds_void_t*)(dst + wbyte), 4, voff, 0, 0, 0);
+      }
+    }
+  }
+};
+
+// The TT elements of segment `seg` of a plain row, as floats.
+template <typename S, int TT>
+__device__ __forceinline__ void read_plain(const char* row, int seg, float (&v)[TT]) {
+  const char* p = row + seg * TT * (int)sizeof(S);
+  if constexpr (sizeof(S) == 4) {
+    if constexpr (TT == 1) {
+      v[0] = *reinterpret_cast<const float*>(p);
+    } else if constexpr (TT == 2) {
+      const float2 q = *reinterpret_cast<const float2*>(p);
+      v[0] = q.x; v[1] = q.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < TT; i += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(p + i * 4);
+        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+      }
+    }
+  } else {
+    if constexpr (TT == 1) {
+      v[0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+    } else {
+#pragma unroll
+      for (int i = 0; i < TT; i += 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(p + i * 2);
+        v[i] = __uint_as_float(w << 16);
+        v[i + 1] = __uint_as_float(w & 0xffff0000u);
+      }
+    }
+  }
+}
+
 // The T elements of segment `seg` of a swizzled row, as floats.
 template <typename S, int T>
 __device__ __forceinline__ void read_seg(const char* row, int seg, float (&v)[T]) {
@@ -711,6 +782,35 @@ __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid
   }
 }
 
+// The first remainder chunk when it was prefetched during the last full chunk:
+// dt (one plain row per channel) at dts, Bs then Cs (kMaxN plain rows each) at
+// bcs, and x already in uv.  No global load waits here.
+template <typename S, int G, int TT, bool VEC>
+__device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, const char* bcs, const float (&uv)[TT],
+                                               const float* a2s, float* carry, float* plane, const float* pcol,
+                                               S* yout, bool rev, bool add, bool last, float bias, float dsk, int c0,
+                                               int L, int H, int W, int N) {
+  constexpr int RB = G * TT * (int)sizeof(S);
+  const int l0 = c0 + ln.seg * TT;
+  float dtv[TT];
+  read_plain<S, TT>(dts + ln.dl * RB, ln.seg, dtv);
+  float delta[TT], du[TT], yv[TT];
+  const float sdelta = prepare_steps<TT>(dtv, uv, bias, dsk, true, L - l0, delta, du, yv);
+#pragma unroll 1
+  for (int n = 0; n < N; ++n) {
+    float Bv[TT], Cv[TT];
+    read_plain<S, TT>(bcs + n * RB, ln.seg, Bv);
+    read_plain<S, TT>(bcs + (kMaxN + n) * RB, ln.seg, Cv);
+    state_core<G, TT>(Bv, Cv, a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du, sdelta, yv);
+  }
+  if (ln.dvalid) {
+    if (last)
+      store_final<S, TT, VEC, false>(plane, pcol, yout, l0, L, H, W, yv);
+    else
+      store_outputs<TT, VEC, false>(plane, rev, add, l0, L, yv);
+  }
+}
+
 template <typename S, int G, int T, int NG, bool VEC, int MODE>
 __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kernel(Params p) {
   using C = Cfg<G, T, NG>;
@@ -719,6 +819,10 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   constexpr int NTH = C::kThreads;
   constexpr int GT = G * T;
   constexpr int GB = (sizeof(S) == 4 && VEC) ? 16 : 4;  // bytes per lane of one DMA copy
+  // A remainder chunk of TT steps per lane is prefetched when the Bs/Cs rows of
+  // every state fit one ring.  Not for 16 lanes: that variant has no registers to
+  // spare, and serves sequences under 512 steps.
+  constexpr auto kTailFits = [](int tt) { return G >= 32 && kMaxN * tt <= NG * T; };
   __shared__ __align__(16) char ring0[Y::kRing0Bytes];
   __shared__ __align__(16) char ring1[Y::kGroupBytes];
   __shared__ __align__(16) char dtb[Y::kDtBytes];
@@ -827,6 +931,33 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       // lanes are planned from 512 steps on).
       constexpr bool kPartial = G == 16;
       const bool partial = kPartial && nmain == 0 && 2 * L >= GT;
+      // The first remainder chunk (T1 steps per lane) is prefetched during the last
+      // full chunk, where nothing else is: its dt into dtb, the Bs/Cs rows of every
+      // state into the ring the last group does not read, its x into xn.
+      const int Lt = L - cend * GT;
+      const int T1 = Lt >= 8 * G ? 8 : Lt >= 4 * G ? 4 : Lt >= 2 * G ? 2 : 1;
+      const bool tailpf = MODE != kCarry && last_seg && cend > cbeg && Lt > 0 && kTailFits(T1);
+      auto tail_bc_rows = [=](int r) {
+        const int n = r & (kMaxN - 1);
+        return RowRef{r < kMaxN ? rb : rc, (uint32_t)(n < N ? n : 0) * rowsz};
+      };
+      auto tail_copy = [&](char* bcdst, bool dt_part, auto tt) {
+        constexpr int TT = decltype(tt)::value;
+        if constexpr (kTailFits(TT)) {
+          if (dt_part)
+            PlainCopy<S, G, TT, CH, GB>::copy(dtb, dt_rows, cend * GT, ln.tid);
+          else
+            PlainCopy<S, G, TT, 2 * kMaxN, GB>::copy(bcdst, tail_bc_rows, cend * GT, ln.tid);
+        }
+      };
+      auto tail_copy_any = [&](char* bcdst, bool dt_part) {
+        switch (T1) {
+          case 8: tail_copy(bcdst, dt_part, std::integral_constant<int, 8>{}); break;
+          case 4: tail_copy(bcdst, dt_part, std::integral_constant<int, 4>{}); break;
+          case 2: tail_copy(bcdst, dt_part, std::integral_constant<int, 2>{}); break;
+          default: tail_copy(bcdst, dt_part, std::integral_constant<int, 1>{}); break;
+        }
+      };
       if (cend > cbeg || partial) {
         dpl.copy(dtb, dt_rows, cbeg * GT, partial ? L : GT);
         bpl.copy(ring0, bc_rows(0), cbeg * GT, partial ? L : GT);
@@ -841,6 +972,23 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         load_x<S, T, VEC, false>(xrow, rev, col, ln.seg * T, L, H, W, xn);
       else if (cbeg < cend)
         load_x<S, T, VEC, true>(xrow, rev, col, cbeg * GT + ln.seg * T, L, H, W, xn);
+      auto load_tail_x = [&](float (&xv)[T]) {  // x of the first remainder chunk, into xv[0, T1)
+        auto ld = [&](auto tt) {
+          constexpr int TT = decltype(tt)::value;
+          if constexpr (kTailFits(TT)) {
+            float v[TT];
+            load_x<S, TT, VEC, false>(xrow, rev, col, cend * GT + ln.seg * TT, L, H, W, v);
+#pragma unroll
+            for (int i = 0; i < TT; ++i) xv[i] = v[i];
+          }
+        };
+        switch (T1) {
+          case 8: ld(std::integral_constant<int, 8>{}); break;
+          case 4: ld(std::integral_constant<int, 4>{}); break;
+          case 2: ld(std::integral_constant<int, 2>{}); break;
+          default: ld(std::integral_constant<int, 1>{}); break;
+        }
+      };
       // One chunk; PART: the partial last chunk (full chunks keep their checks
       // out of the code).
       auto chunk = [&](int c, auto part_c) {
@@ -861,8 +1009,12 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
             bpl.copy(nxt, bc_rows(g + 1), c * GT, PART ? L : GT);
           else if (!PART && cross && c + 1 < cend)
             bpl.copy(nxt, bc_rows(0), (c + 1) * GT);
+          else if (!PART && tailpf && c + 1 == cend)
+            tail_copy_any(nxt, false);
           if (!PART && g == 1 && c + 1 < cend)  // every lane has read this chunk's dt (barrier after group 0)
             dpl.copy(dtb, dt_rows, (c + 1) * GT);
+          else if (!PART && g == 1 && tailpf)
+            tail_copy_any(dtb, true);
 #pragma unroll 1
           for (int nn = 0; nn < NG; ++nn) {
             const int n = g * NG + nn;
@@ -892,6 +1044,14 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
           wait_vmem();
           __syncthreads();
         }
+        if (!PART && tailpf && c + 1 == cend && ngrp == 1) {  // the remainder's dt was not copied yet
+          tail_copy_any(dtb, true);
+          wait_vmem();
+          __syncthreads();
+        }
+        // The remainder's x, loaded here rather than a chunk ahead: held through the
+        // state loops it would cost registers; here it overlaps this chunk's stores.
+        if (!PART && tailpf && c + 1 == cend) load_tail_x(xn);
         if (MODE != kCarry && ln.dvalid) {
           if (last)
             store_final<S, T, VEC, !PART>(plane, pcol, yout, c * GT + ln.seg * T, L, H, W, yv);
@@ -905,6 +1065,27 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       if (!partial)
         for (int c = cbeg; c < cend; ++c) chunk(c, std::false_type{});
       c0 = partial ? L : cend * GT;
+      if (tailpf) {
+        char* bcs = (ngrp & 1) ? ring1 : ring0;  // the ring the last group did not read
+        auto run = [&](auto tt) {
+          constexpr int TT = decltype(tt)::value;
+          if constexpr (kTailFits(TT)) {
+            float uv[TT];
+#pragma unroll
+            for (int i = 0; i < TT; ++i) uv[i] = xn[i];
+            tail_chunk_lds<S, G, TT, VEC>(ln, dtb, bcs, uv, a2s, carry, plane, pcol, yout, rev, add, last, bias, dsk,
+                                          c0, L, H, W, N);
+          }
+        };
+        switch (T1) {
+          case 8: run(std::integral_constant<int, 8>{}); break;
+          case 4: run(std::integral_constant<int, 4>{}); break;
+          case 2: run(std::integral_constant<int, 2>{}); break;
+          default: run(std::integral_constant<int, 1>{}); break;
+        }
+        c0 = Lt < G * T1 ? L : c0 + G * T1;
+        __syncthreads();  // the rings and dtb are free again
+      }
     } else {
       // ---------------- rows not 16-byte aligned: every chunk staged through registers
       for (; c0 + GT <= L; c0 += GT)

@@ -136,6 +136,12 @@ EDGE = [
     (2, 5, 80, 96, 16, "bf16"),   # segments, bf16
     (2, 7, 12, 16, 16, "f32"),    # one partial chunk (192 of 256 steps) in the DMA pipeline
     (1, 5, 10, 20, 9, "bf16"),    # partial chunk, bf16, odd N
+    # remainders prefetched during the last full chunk (32 lanes)
+    (1, 3, 32, 37, 16, "f32"),    # 160-step remainder: 128 prefetched (4 steps per lane), 32 after
+    (1, 2, 4, 281, 16, "f32"),    # 100-step remainder: 64 prefetched, then a ragged one
+    (1, 11, 40, 40, 7, "f32"),    # 64-step prefetched remainder, odd N, D past the channel block
+    (1, 5, 72, 72, 16, "f32"),    # two segments, the last with a prefetched remainder
+    (1, 4, 72, 72, 9, "bf16"),    # the same in bf16, odd N
 ]
 
 
