@@ -496,6 +496,38 @@ __device__ __forceinline__ void load_x(const S* xrow, bool rev, bool col, int l0
   }
 }
 
+// x of T consecutive steps of a column walk from l0 (all inside the sequence),
+// for H >= T: a lane's steps then change column at most once.  Step i of a
+// forward walk is at pixel p0 + i*W until h0 + i reaches H, and one column on
+// (1 - H*W further) from there; a reversed walk goes -W per step and one column
+// back (H*W - 1 further) once h0 - i drops below 0.  Each load is a buffer load
+// whose scalar offset is the step's multiple of W and whose lane offset is one of
+// two per lane: a select per step instead of index arithmetic.
+// rx: buffer over H*W biasing elements then the block's rows of x (every offset
+// stays non-negative and inside it); xlane: this lane's channel row (elements).
+template <typename S, int T>
+__device__ __forceinline__ void load_x_col(__amdgpu_buffer_rsrc_t rx, uint32_t xlane, bool rev, int l0, int L, int H,
+                                           int W, float (&uv)[T]) {
+  constexpr uint32_t sz = sizeof(S);
+  const int s0 = rev ? L - 1 - l0 : l0;
+  const int w0 = s0 / H, h0 = s0 - w0 * H;
+  const uint32_t HW = (uint32_t)(H * W), Wb = (uint32_t)W * sz;
+  // byte offset of step 0 (forward) or of step T-1's row (reversed), before the change
+  uint32_t a = (xlane + HW + (uint32_t)(h0 * W + w0)) * sz;
+  if (rev) a -= (uint32_t)(T - 1) * Wb;  // >= 0: H >= T
+  const uint32_t b = rev ? a + (HW - 1) * sz : a - (HW - 1) * sz;  // after the change
+  const int k = rev ? h0 + 1 : H - h0;                              // first step after the change
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const uint32_t off = i < k ? a : b;
+    const int so = (int)((uint32_t)(rev ? T - 1 - i : i) * Wb);
+    if constexpr (sizeof(S) == 4)
+      uv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, so, 0));
+    else
+      uv[i] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rx, off, so, 0));
+  }
+}
+
 template <typename S, int T, bool VEC, bool FULL>
 __device__ __forceinline__ void load_inputs(const S* dtrow, const S* xrow, bool rev, bool col, int l0, int L, int H,
                                             int W, float (&dtv)[T], float (&uv)[T]) {
@@ -968,10 +1000,26 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       // copied during this chunk's last group when that group is in ring1.
       const bool cross = (ngrp & 1) == 0;
       float xn[T];  // x of the next chunk, loaded a whole chunk ahead
+      // x of a full chunk's T steps from l0: column walks with H >= T by the
+      // select-per-step gather, everything else by load_x
+      const int nxr = D - ln.d0 < CH ? D - ln.d0 : CH;  // valid channel rows of the block
+      const __amdgpu_buffer_rsrc_t rx =
+          make_rsrc(static_cast<const S*>(p.x) + ((int64_t)ln.b * D + ln.d0) * L - (int64_t)H * W,
+                    (uint32_t)((int64_t)H * W + (int64_t)nxr * L) * (uint32_t)sizeof(S));
+      const uint32_t xlane = (uint32_t)(ln.dvalid ? ln.dl : 0) * (uint32_t)L;
+      auto load_full_x = [&](int l0) {
+        if constexpr (col) {
+          if (H >= T) {
+            load_x_col<S, T>(rx, xlane, rev, l0, L, H, W, xn);
+            return;
+          }
+        }
+        load_x<S, T, VEC, true>(xrow, rev, col, l0, L, H, W, xn);
+      };
       if (partial)
         load_x<S, T, VEC, false>(xrow, rev, col, ln.seg * T, L, H, W, xn);
       else if (cbeg < cend)
-        load_x<S, T, VEC, true>(xrow, rev, col, cbeg * GT + ln.seg * T, L, H, W, xn);
+        load_full_x(cbeg * GT + ln.seg * T);
       auto load_tail_x = [&](float (&xv)[T]) {  // x of the first remainder chunk, into xv[0, T1)
         auto ld = [&](auto tt) {
           constexpr int TT = decltype(tt)::value;
@@ -1001,7 +1049,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         // Steps past L (partial chunk) get delta = 0: the identity map.
         const int nvalid = PART ? L - (c * GT + ln.seg * T) : T;
         const float sdelta = prepare_steps<T>(dtn, xn, bias, dsk, true, nvalid, delta, du, yv);
-        if (!PART && c + 1 < cend) load_x<S, T, VEC, true>(xrow, rev, col, (c + 1) * GT + ln.seg * T, L, H, W, xn);
+        if (!PART && c + 1 < cend) load_full_x((c + 1) * GT + ln.seg * T);
         auto group = [&](const char* cur, char* nxt, int g) {
           const bool more_states = g + 1 < ngrp;
           // nxt was last read before the previous barrier
@@ -1015,9 +1063,12 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
             dpl.copy(dtb, dt_rows, (c + 1) * GT);
           else if (!PART && g == 1 && tailpf)
             tail_copy_any(dtb, true);
-#pragma unroll 1
+          // Unrolled, so the LDS offsets of each state are immediates; the barrier keeps
+          // the states apart (interleaved, their registers would not fit).
+#pragma unroll
           for (int nn = 0; nn < NG; ++nn) {
             const int n = g * NG + nn;
+            __builtin_amdgcn_sched_barrier(0);
             if (n < N) {
               if constexpr (MODE == kCarry) {
                 state_carry<S, G, T>(cur + nn * GT * (int)sizeof(S), ln.seg, a2s[ln.dl * kMaxN + n],

@@ -142,6 +142,9 @@ EDGE = [
     (1, 11, 40, 40, 7, "f32"),    # 64-step prefetched remainder, odd N, D past the channel block
     (1, 5, 72, 72, 16, "f32"),    # two segments, the last with a prefetched remainder
     (1, 4, 72, 72, 9, "bf16"),    # the same in bf16, odd N
+    # column walks whose lane steps cross more than one column (H < steps per lane)
+    (1, 3, 8, 64, 16, "f32"),     # H = 8 < 16, full chunks
+    (1, 3, 12, 48, 16, "bf16"),   # H = 12 < 16, full chunks + prefetched remainder
 ]
 
 
