@@ -176,6 +176,7 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
   a.N = N;
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
+  a.device = di.device;
 
   float* scratch = nullptr;
   {

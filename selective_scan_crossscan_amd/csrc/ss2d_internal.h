@@ -20,6 +20,7 @@ struct LaunchArgs {
   int64_t B, D, H, W, N;
   int dtype;  // 0 = fp32, 1 = bf16
   hipStream_t stream;
+  int device;  // current device of the calling thread
 };
 
 // How a shape is mapped onto the machine.

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "ss2d_internal.h"
@@ -169,6 +171,16 @@ __device__ __forceinline__ float incoming_state(float A, float B, float carry, i
   return seg == 0 ? carry : h;
 }
 
+// Wave priority 0..3 (the instruction takes an immediate).
+__device__ __forceinline__ void set_priority(int level) {
+  switch (level) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 // ------------------------------------------------------------------ kernel state
 struct Params {
   const void* x;
@@ -187,6 +199,9 @@ struct Params {
   float* carries;
   int seg_chunks, nseg;
   int kdir;  // the one direction of a segment output launch
+  // Wave priority rotation (0: off): the launch fits one round of prio_levels
+  // resident workgroups on each of prio_ncu CUs.
+  int prio_ncu, prio_levels;
   int B, D, H, W, N, L;
 };
 
@@ -873,6 +888,18 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   const int xcd = blockIdx.x & 7, bslot = blockIdx.x >> 3;
   const int per = nb >> 3, rem = nb & 7;
   const int work = (xcd < rem) ? xcd * (per + 1) + bslot : rem * (per + 1) + (xcd - rem) * per + bslot;
+  // The hardware serves co-resident waves oldest first, so in a launch that fits
+  // one round the workgroups of a CU finish one after another, in dispatch order,
+  // and the last runs its end alone (on stage-1 shapes 360, 450 and 540 us).  A
+  // CU receives one workgroup per round of prio_ncu dispatches; rotating the
+  // priority every chunk by (that rank + chunks done) gives each the lead in turn.
+  int prio_tick = p.prio_ncu > 0 ? (int)(blockIdx.x / (unsigned)p.prio_ncu) % p.prio_levels : 0;
+  auto rotate_priority = [&]() {
+    if (p.prio_ncu > 0) {
+      set_priority(prio_tick);
+      prio_tick = prio_tick + 1 == p.prio_levels ? 0 : prio_tick + 1;
+    }
+  };
 
   Lane ln;
   ln.tid = threadIdx.x;
@@ -1041,6 +1068,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       // out of the code).
       auto chunk = [&](int c, auto part_c) {
         constexpr bool PART = decltype(part_c)::value;
+        rotate_priority();
         float dtn[T];
         read_seg<S, T>(dtb + ln.dl * GT * (int)sizeof(S), ln.seg, dtn);
         float delta[T], du[T], yv[T];
@@ -1213,6 +1241,40 @@ constexpr int group_states() {
   return T == 16 ? 2048 / (G * T) : 1024 / (G * T);
 }
 
+// Compute units of a device (0 if unknown), queried once per device.
+inline int cu_count(int device) {
+  static std::atomic<int> cache[64];
+  if (device < 0 || device >= 64) return 0;
+  int v = cache[device].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || v <= 0) return 0;
+    cache[device].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Workgroups of `kernel` resident per CU (0 if unknown), queried once per kernel
+// and device.
+inline int resident_blocks(const void* kernel, int device) {
+  struct Entry {
+    const void* kernel;
+    int device, blocks;
+  };
+  static std::mutex m;
+  static Entry seen[64];
+  static int nseen = 0;
+  std::lock_guard<std::mutex> lk(m);
+  for (int i = 0; i < nseen; ++i)
+    if (seen[i].kernel == kernel && seen[i].device == device) return seen[i].blocks;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kWaves * 64, 0) != hipSuccess) {
+    n = 0;
+    (void)hipGetLastError();  // the query's own error; nothing was launched
+  }
+  if (nseen < 64) seen[nseen++] = Entry{kernel, device, n};
+  return n;
+}
+
 template <typename S, int G, int T, bool VEC>
 hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
   Params p;
@@ -1238,7 +1300,20 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
   p.kdir = 0;
   constexpr int NG = group_states<G, T>();
   const int64_t units = plan.blocks / plan.nseg;  // (batch, channel block) pairs
+  // priority rotation for launches of at most one round (see the kernel)
+  auto rotation = [&](const void* kernel, int64_t grid) {
+    p.prio_ncu = 0;
+    p.prio_levels = 1;
+    const int ncu = cu_count(a.device);
+    const int per = resident_blocks(kernel, a.device);
+    if (ncu > 0 && per >= 2 && per <= 4 && grid <= (int64_t)ncu * per) {
+      p.prio_ncu = ncu;
+      p.prio_levels = per;
+    }
+  };
   if (plan.nseg == 1) {
+    const void* kf = reinterpret_cast<const void*>(&ss2d_forward_kernel<S, G, T, NG, VEC, kFused>);
+    rotation(kf, units);
     hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kFused>), dim3((unsigned)units), dim3(kWaves * 64), 0,
                        a.stream, p);
     return hipGetLastError();
@@ -1246,11 +1321,13 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
   if constexpr (VEC) {
     // carry pass over every segment but the last, then one launch per direction in
     // merge order (column pair, then row pair; each reads what the previous wrote)
+    rotation(reinterpret_cast<const void*>(&ss2d_forward_kernel<S, G, T, NG, VEC, kCarry>), units * (plan.nseg - 1));
     hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kCarry>), dim3((unsigned)(units * (plan.nseg - 1))),
                        dim3(kWaves * 64), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int order[4] = {1, 3, 0, 2};
+    rotation(reinterpret_cast<const void*>(&ss2d_forward_kernel<S, G, T, NG, VEC, kSegment>), units * plan.nseg);
     for (int k : order) {
       p.kdir = k;
       hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kSegment>), dim3((unsigned)(units * plan.nseg)),
