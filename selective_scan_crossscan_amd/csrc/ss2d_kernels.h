@@ -129,44 +129,61 @@ __device__ __forceinline__ float softplus_f32(float v) {
   return fmaxf(v, 0.0f) + l;
 }
 
-// One level of the inclusive prefix combine of affine maps h -> A h + B.  The
-// DPP source lane is earlier in the sequence.  Fused forms:
-//   B += dpp(B) * A   (v_fmac_f32_dpp),   A = dpp(A) * A   (v_mul_f32_dpp).
-// Lanes whose source is out of range (or whose row is masked off) are not
-// written, which is the identity map.  s_nop 1 gives the two wait states a DPP
-// read needs after a VALU write of its source.
-#define SS2D_SCAN_LEVEL(DPP)                                                     \
-  asm volatile("s_nop 1\n\t"                                                     \
-               "v_fmac_f32_dpp %1, %1, %0 " DPP " bank_mask:0xf\n\t"             \
-               "v_mul_f32_dpp %0, %0, %0 " DPP " bank_mask:0xf"                  \
-               : "+v"(A), "+v"(B))
+// The inclusive prefix combine of affine maps h -> A h + B inside groups of G
+// lanes (G = 16, 32 or 64): one level per power of two, each a fused
+//   B += dpp(B) * A   (v_fmac_f32_dpp),   A = dpp(A) * A   (v_mul_f32_dpp),
+// whose DPP source lane is earlier in the sequence.  Lanes whose source is out of
+// range (or whose row is masked off) are not written: the identity map.
+// All levels are one asm block, so the compiler adds no wait states of its own
+// between them.  A DPP read needs two wait states after a VALU write of its
+// source: s_nop 1 before the first level (A and B were just computed); after that
+// one s_nop 0 per level suffices, since each fmac reads the B written two
+// instructions earlier and each mul the A written two instructions earlier.
+#define SS2D_SCAN_STEP(DPP) \
+  "v_fmac_f32_dpp %1, %1, %0 " DPP " bank_mask:0xf\n\tv_mul_f32_dpp %0, %0, %0 " DPP " bank_mask:0xf\n\t"
+#define SS2D_SCAN_NEXT(DPP) "s_nop 0\n\t" SS2D_SCAN_STEP(DPP)
 
-// Inclusive scan inside groups of G lanes (G = 16, 32 or 64).
 template <int G>
 __device__ __forceinline__ void scan_inclusive(float& A, float& B) {
-  SS2D_SCAN_LEVEL("row_shr:1 row_mask:0xf");
-  SS2D_SCAN_LEVEL("row_shr:2 row_mask:0xf");
-  SS2D_SCAN_LEVEL("row_shr:4 row_mask:0xf");
-  SS2D_SCAN_LEVEL("row_shr:8 row_mask:0xf");
-  if constexpr (G >= 32) SS2D_SCAN_LEVEL("row_bcast:15 row_mask:0xa");
-  if constexpr (G >= 64) SS2D_SCAN_LEVEL("row_bcast:31 row_mask:0xc");
+  if constexpr (G == 16) {
+    asm volatile("s_nop 1\n\t" SS2D_SCAN_STEP("row_shr:1 row_mask:0xf") SS2D_SCAN_NEXT("row_shr:2 row_mask:0xf")
+                     SS2D_SCAN_NEXT("row_shr:4 row_mask:0xf") SS2D_SCAN_NEXT("row_shr:8 row_mask:0xf")
+                 : "+v"(A), "+v"(B));
+  } else if constexpr (G == 32) {
+    asm volatile("s_nop 1\n\t" SS2D_SCAN_STEP("row_shr:1 row_mask:0xf") SS2D_SCAN_NEXT("row_shr:2 row_mask:0xf")
+                     SS2D_SCAN_NEXT("row_shr:4 row_mask:0xf") SS2D_SCAN_NEXT("row_shr:8 row_mask:0xf")
+                         SS2D_SCAN_NEXT("row_bcast:15 row_mask:0xa")
+                 : "+v"(A), "+v"(B));
+  } else {
+    static_assert(G == 64, "lanes per sequence must be 16, 32 or 64");
+    asm volatile("s_nop 1\n\t" SS2D_SCAN_STEP("row_shr:1 row_mask:0xf") SS2D_SCAN_NEXT("row_shr:2 row_mask:0xf")
+                     SS2D_SCAN_NEXT("row_shr:4 row_mask:0xf") SS2D_SCAN_NEXT("row_shr:8 row_mask:0xf")
+                         SS2D_SCAN_NEXT("row_bcast:15 row_mask:0xa") SS2D_SCAN_NEXT("row_bcast:31 row_mask:0xc")
+                 : "+v"(A), "+v"(B));
+  }
 }
 
 // State entering this lane's steps: the previous lane's inclusive map applied
 // to the group's carried state, h = A_prev * carry + B_prev; the group's first
-// lane takes the carry itself.
+// lane takes the carry itself.  One asm block: the add reads B (last written by
+// the scan, well before) through DPP and the product through its plain operand.
 template <int G>
 __device__ __forceinline__ float incoming_state(float A, float B, float carry, int seg) {
-  float t = carry;
-  float h;
+  float h = carry;
   if constexpr (G == 16) {
-    asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf" : "+v"(t) : "v"(A));
-    h = t;
-    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf" : "+v"(h) : "v"(B));
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %0, %2, %0 row_shr:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(h)
+        : "v"(A), "v"(B));
   } else {
-    asm volatile("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 wave_shr:1 row_mask:0xf bank_mask:0xf" : "+v"(t) : "v"(A));
-    h = t;
-    asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %0 wave_shr:1 row_mask:0xf bank_mask:0xf" : "+v"(h) : "v"(B));
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %1, %0 wave_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %0, %2, %0 wave_shr:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(h)
+        : "v"(A), "v"(B));
   }
   return seg == 0 ? carry : h;
 }
@@ -869,7 +886,12 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   // A remainder chunk of TT steps per lane is prefetched when the Bs/Cs rows of
   // every state fit one ring.  Not for 16 lanes: that variant has no registers to
   // spare, and serves sequences under 512 steps.
-  constexpr auto kTailFits = [](int tt) { return G >= 32 && kMaxN * tt <= NG * T; };
+  // The plain copies also need whole wave-wide copies for the dt and Bs/Cs rows.
+  constexpr auto kTailFits = [](int tt) {
+    const int row = G * tt * (int)sizeof(S), wave_bytes = 64 * GB;
+    return G >= 32 && kMaxN * tt <= NG * T && (C::kChans * row) % wave_bytes == 0 &&
+           (kMaxN * row) % wave_bytes == 0 && (row % wave_bytes == 0 || wave_bytes % row == 0);
+  };
   __shared__ __align__(16) char ring0[Y::kRing0Bytes];
   __shared__ __align__(16) char ring1[Y::kGroupBytes];
   __shared__ __align__(16) char dtb[Y::kDtBytes];
