@@ -323,6 +323,14 @@ struct DmaPlan {
   static_assert(kRowBytes % (64 * GB) == 0, "a wave's copy must stay inside one row");
   static_assert((kNth * GB) % kPeriod == 0 && kRowBytes % kPeriod == 0,
                 "a wave's copies must sit at one offset inside the swizzle period");
+  // Copies are dealt to waves in contiguous runs (a wave's rows then come from one
+  // tensor, so its copies share the resource and step the offset) when a wave
+  // copy spans whole swizzle periods; otherwise interleaved, every wave at one
+  // offset inside the period.
+  static constexpr bool kContig = (64 * GB) % kPeriod == 0;
+  static __device__ __forceinline__ uint32_t copy_byte(uint32_t w, int it) {
+    return kContig ? (w * (uint32_t)kIters + (uint32_t)it) * 64u * GB : ((uint32_t)it * kNth + w * 64u) * GB;
+  }
   int wave;
   uint32_t lane_byte;
 
@@ -352,7 +360,7 @@ struct DmaPlan {
     asm volatile("" : "+s"(w), "+v"(lb));
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
-      const uint32_t wbyte = ((uint32_t)it * kNth + w * 64u) * GB;  // first byte of this wave's copy
+      const uint32_t wbyte = copy_byte(w, it);  // first byte of this wave's copy
       const uint32_t rowb = wbyte % (uint32_t)kRowBytes;
       const RowRef rr = row((int)(wbyte / (uint32_t)kRowBytes));
       const uint32_t soff = rr.off + (uint32_t)c0 * (uint32_t)sizeof(S) + (rowb - rowb % (uint32_t)kPeriod);
@@ -371,7 +379,7 @@ struct DmaPlan {
     constexpr uint32_t kEg = GB / (int)sizeof(S);  // elements per granule
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
-      const uint32_t wbyte = ((uint32_t)it * kNth + (uint32_t)wave * 64u) * GB;
+      const uint32_t wbyte = copy_byte((uint32_t)wave, it);
       const uint32_t rowb = wbyte % (uint32_t)kRowBytes;
       const RowRef rr = row((int)(wbyte / (uint32_t)kRowBytes));
       const uint32_t e = (rowb - rowb % (uint32_t)kPeriod) / (uint32_t)sizeof(S) + lane_byte / (uint32_t)sizeof(S);
