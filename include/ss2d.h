@@ -67,13 +67,15 @@ typedef enum {
  * SS2D_OK the work has been enqueued asynchronously; execution faults surface at
  * the caller's next synchronisation.  Nothing is printed, thrown or aborted.
  * Each call takes a stream-ordered temporary of B*D*H*W fp32 values (2*B*D*H*W
- * for bf16) for the merge -- plus 32 fp32 values per (batch, direction,
- * channel, segment) when a long map is cut into segments (ss2d_describe shows
- * the plan and the exact size) -- allocated and freed on `stream` from the
- * device's default memory pool (whose release threshold the library raises so
- * freed blocks are reused).  A call then runs one kernel, or five for segmented
- * maps (a carry pass and one launch per direction), all on `stream`.  NaN and
- * Inf propagate.  Thread-safe.
+ * for bf16) for the merge.  When a long map is cut into segments it also holds
+ * 32 fp32 values per (batch, direction, channel, segment), a copy of x with H
+ * and W swapped, and an fp32 B*D*H*W transposed merge plane (ss2d_describe shows
+ * the plan and the exact size).  The temporary is allocated and freed on
+ * `stream` from the device's default memory pool (whose release threshold the
+ * library raises so freed blocks are reused).  A call then runs one kernel, or
+ * seven for segmented maps (a transpose of x, a carry pass, one launch per
+ * direction and a transpose of the merge plane before the last), all on
+ * `stream`.  NaN and Inf propagate.  Thread-safe.
  */
 int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
                  const void* Bs, const void* Cs, const float* Ds, void* y,

@@ -3,9 +3,9 @@
 
 namespace ss2d {
 
-hipError_t launch_bf16_t8(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
-  if (plan.lanes_per_seq == 32) return launch_gt<uint16_t, 32, 8>(a, plan, planes, carries);
-  return launch_gt<uint16_t, 64, 8>(a, plan, planes, carries);
+hipError_t launch_bf16_t8(const LaunchArgs& a, const Plan& plan, const Scratch& s) {
+  if (plan.lanes_per_seq == 32) return launch_gt<uint16_t, 32, 8>(a, plan, s);
+  return launch_gt<uint16_t, 64, 8>(a, plan, s);
 }
 
 }  // namespace ss2d

@@ -33,8 +33,20 @@ struct Plan {
   int seg_chunks;        // full chunks per segment
   int64_t blocks;        // workgroups of one output launch
   size_t lds_bytes;      // LDS per workgroup
-  size_t scratch_bytes;  // device temporary: fp32 merge planes, then the segment maps
+  size_t scratch_bytes;  // device temporary: fp32 merge planes, segment maps, transposed copies
   size_t carry_offset;   // byte offset of the segment maps in the temporary
+  bool transpose;        // column walks read a transposed copy of x, the merge a transposed column plane
+  size_t xt_offset;      // byte offsets of those copies in the temporary (transpose only)
+  size_t pct_offset;
+};
+
+// Device buffers of one forward, carved from the temporary.
+struct Scratch {
+  float* prow;     // row-major merge plane (directions 0, 2): y itself for fp32 output
+  float* pcol;     // column-major merge plane (directions 1, 3)
+  float* carries;  // segment maps
+  void* xT;        // x with H and W swapped, or null
+  float* pcolT;    // the column plane in row-major order, or null
 };
 
 // lanes_override: 0 = automatic, else 16, 32 or 64 lanes per sequence.

@@ -214,6 +214,10 @@ struct Params {
   // last takes the rest).  carries[((b*4 + k)*D + d)*nseg + s][n] = {A, B}: the
   // segment's affine map h -> A h + B, from a carry pass over segments 0..nseg-2.
   float* carries;
+  // Transposed copies (null: not used): x as [W][H] per plane, read by the column
+  // walks as contiguous rows; the column plane as [H][W], read by direction 2.
+  const void* xT;
+  const float* pcolT;
   int seg_chunks, nseg;
   int kdir;  // the one direction of a segment output launch
   // Wave priority rotation (0: off): the launch fits one round of prio_levels
@@ -709,9 +713,10 @@ __device__ __forceinline__ void store_outputs(float* plane, bool rev, bool add, 
 // visits pixel L-1-l0-i.  The row plane holds direction 0 (it is y itself for
 // fp32 output: each element is read, then written, by the same lane), the
 // column plane directions 1 + 3, so y = (y0 + y2) + (y1 + y3).
+// pct: the column plane transposed to row-major order, or null (then gathered).
 template <typename S, int T, bool VEC, bool FULL>
-__device__ __forceinline__ void store_final(const float* prow, const float* pcol, S* y, int l0, int L, int H, int W,
-                                            const float (&yv)[T]) {
+__device__ __forceinline__ void store_final(const float* prow, const float* pcol, const float* pct, S* y, int l0,
+                                            int L, int H, int W, const float (&yv)[T]) {
   if constexpr (VEC && FULL && (T % 4 == 0)) {
     const int s_lo = L - l0 - T;  // pixels s_lo .. s_lo+T-1; pixel s_lo+j holds yv[T-1-j]
     float v[T];
@@ -723,15 +728,26 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
       v[j + 2] = o.z + yv[T - 3 - j];
       v[j + 3] = o.w + yv[T - 4 - j];
     }
-    int h = s_lo / W;
-    int w = s_lo - h * W;
+    if (pct != nullptr) {
 #pragma unroll
-    for (int j = 0; j < T; ++j) {
-      v[j] += pcol[w * H + h];
-      ++w;
-      const bool wrap = w == W;
-      w = wrap ? 0 : w;
-      h += wrap ? 1 : 0;
+      for (int j = 0; j < T; j += 4) {
+        const float4 o = *reinterpret_cast<const float4*>(pct + s_lo + j);
+        v[j] += o.x;
+        v[j + 1] += o.y;
+        v[j + 2] += o.z;
+        v[j + 3] += o.w;
+      }
+    } else {
+      int h = s_lo / W;
+      int w = s_lo - h * W;
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        v[j] += pcol[w * H + h];
+        ++w;
+        const bool wrap = w == W;
+        w = wrap ? 0 : w;
+        h += wrap ? 1 : 0;
+      }
     }
 #pragma unroll
     for (int j = 0; j < T; j += 4) Io<S>::st4(y, s_lo + j, make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]));
@@ -741,7 +757,7 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
     int w = pix - h * W;
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      if (FULL || l0 + i < L) Io<S>::st(y, pix, (prow[pix] + yv[i]) + pcol[w * H + h]);
+      if (FULL || l0 + i < L) Io<S>::st(y, pix, (prow[pix] + yv[i]) + (pct != nullptr ? pct[pix] : pcol[w * H + h]));
       --pix;
       --w;
       const bool wrap = w < 0;
@@ -814,7 +830,8 @@ struct Lane {
 template <typename S, int G, int T, int NG0, int TT, bool VEC, int kAreaBytes>
 __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, float* a2s, float* carry,
                                         const S* dtrow, const S* xrow, const S* Bbase, const S* Cbase, float* plane,
-                                        const float* pcol, S* yout, bool rev, bool col, bool add, bool last, float bias,
+                                        const float* pcol, const float* pct, S* yout, bool rev, bool col, bool add,
+                                        bool last, float bias,
                                         float dsk, int c0, int L, int H, int W, int N) {
   Lane ln;
   ln.tid = tid;
@@ -848,7 +865,7 @@ __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid
   }
   if (ln.dvalid) {
     if (last)
-      store_final<S, TT, VEC, false>(plane, pcol, yout, l0, L, H, W, yv);
+      store_final<S, TT, VEC, false>(plane, pcol, pct, yout, l0, L, H, W, yv);
     else
       store_outputs<TT, VEC, false>(plane, rev, add, l0, L, yv);
   }
@@ -860,7 +877,8 @@ __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid
 template <typename S, int G, int TT, bool VEC>
 __device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, const char* bcs, const float (&uv)[TT],
                                                const float* a2s, float* carry, float* plane, const float* pcol,
-                                               S* yout, bool rev, bool add, bool last, float bias, float dsk, int c0,
+                                               const float* pct, S* yout, bool rev, bool add, bool last, float bias,
+                                               float dsk, int c0,
                                                int L, int H, int W, int N) {
   constexpr int RB = G * TT * (int)sizeof(S);
   const int l0 = c0 + ln.seg * TT;
@@ -877,7 +895,7 @@ __device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, 
   }
   if (ln.dvalid) {
     if (last)
-      store_final<S, TT, VEC, false>(plane, pcol, yout, l0, L, H, W, yv);
+      store_final<S, TT, VEC, false>(plane, pcol, pct, yout, l0, L, H, W, yv);
     else
       store_outputs<TT, VEC, false>(plane, rev, add, l0, L, yv);
   }
@@ -990,6 +1008,12 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     S* yout = static_cast<S*>(p.y) + plane_off;
     const S* dtdir = static_cast<const S*>(p.dt) + (int64_t)(ln.b * 4 + k) * D * L;
     const S* dtrow = dtdir + (int64_t)ln.dsafe * L;
+    // column walks over the transposed copy of x read contiguous rows; direction 2
+    // reads a transposed column plane when there is one
+    const bool xt = col && p.xT != nullptr;
+    const S* xsrc = xt ? static_cast<const S*>(p.xT) + plane_off : xrow;
+    const bool xcol = col && !xt;
+    const float* pct = p.pcolT != nullptr ? p.pcolT + plane_off : nullptr;
     const S* Bbase = static_cast<const S*>(p.Bs) + (int64_t)(ln.b * 4 + k) * N * L;
     const S* Cbase = static_cast<const S*>(p.Cs) + (int64_t)(ln.b * 4 + k) * N * L;
     const float bias = biass[ln.dl];
@@ -1066,15 +1090,15 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       const uint32_t xlane = (uint32_t)(ln.dvalid ? ln.dl : 0) * (uint32_t)L;
       auto load_full_x = [&](int l0) {
         if constexpr (col) {
-          if (H >= T) {
+          if (!xt && H >= T) {
             load_x_col<S, T>(rx, xlane, rev, l0, L, H, W, xn);
             return;
           }
         }
-        load_x<S, T, VEC, true>(xrow, rev, col, l0, L, H, W, xn);
+        load_x<S, T, VEC, true>(xsrc, rev, xcol, l0, L, H, W, xn);
       };
       if (partial)
-        load_x<S, T, VEC, false>(xrow, rev, col, ln.seg * T, L, H, W, xn);
+        load_x<S, T, VEC, false>(xsrc, rev, xcol, ln.seg * T, L, H, W, xn);
       else if (cbeg < cend)
         load_full_x(cbeg * GT + ln.seg * T);
       auto load_tail_x = [&](float (&xv)[T]) {  // x of the first remainder chunk, into xv[0, T1)
@@ -1082,7 +1106,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
           constexpr int TT = decltype(tt)::value;
           if constexpr (kTailFits(TT)) {
             float v[TT];
-            load_x<S, TT, VEC, false>(xrow, rev, col, cend * GT + ln.seg * TT, L, H, W, v);
+            load_x<S, TT, VEC, false>(xsrc, rev, xcol, cend * GT + ln.seg * TT, L, H, W, v);
 #pragma unroll
             for (int i = 0; i < TT; ++i) xv[i] = v[i];
           }
@@ -1163,7 +1187,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         if (!PART && tailpf && c + 1 == cend) load_tail_x(xn);
         if (MODE != kCarry && ln.dvalid) {
           if (last)
-            store_final<S, T, VEC, !PART>(plane, pcol, yout, c * GT + ln.seg * T, L, H, W, yv);
+            store_final<S, T, VEC, !PART>(plane, pcol, pct, yout, c * GT + ln.seg * T, L, H, W, yv);
           else
             store_outputs<T, VEC, !PART>(plane, rev, add, c * GT + ln.seg * T, L, yv);
         }
@@ -1182,8 +1206,8 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
             float uv[TT];
 #pragma unroll
             for (int i = 0; i < TT; ++i) uv[i] = xn[i];
-            tail_chunk_lds<S, G, TT, VEC>(ln, dtb, bcs, uv, a2s, carry, plane, pcol, yout, rev, add, last, bias, dsk,
-                                          c0, L, H, W, N);
+            tail_chunk_lds<S, G, TT, VEC>(ln, dtb, bcs, uv, a2s, carry, plane, pcol, pct, yout, rev, add, last, bias,
+                                          dsk, c0, L, H, W, N);
           }
         };
         switch (T1) {
@@ -1198,8 +1222,8 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     } else {
       // ---------------- rows not 16-byte aligned: every chunk staged through registers
       for (; c0 + GT <= L; c0 += GT)
-        tail_chunk<S, G, T, NG, T, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
-                                        plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
+        tail_chunk<S, G, T, NG, T, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+                                        plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
     }
 
     if constexpr (MODE == kCarry) {
@@ -1224,23 +1248,23 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
 
     // ---------------- remainder chunks (fewer steps per lane)
     while (L - c0 >= G * 8) {
-      tail_chunk<S, G, T, NG, 8, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
-                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 8, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 8;
     }
     if (L - c0 >= G * 4) {
-      tail_chunk<S, G, T, NG, 4, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
-                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 4, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 4;
     }
     if (L - c0 >= G * 2) {
-      tail_chunk<S, G, T, NG, 2, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
-                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 2, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 2;
     }
     while (c0 < L) {
-      tail_chunk<S, G, T, NG, 1, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xrow, Bbase, Cbase,
-                                      plane, pcol, yout, rev, col, add, last, bias, dsk, c0, L, H, W, N);
+      tail_chunk<S, G, T, NG, 1, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G;
     }
     __syncthreads();  // this direction's plane writes are complete and visible to the block
@@ -1269,6 +1293,44 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
 template <int G, int T>
 constexpr int group_states() {
   return T == 16 ? 2048 / (G * T) : 1024 / (G * T);
+}
+
+// Plane transpose: out[p][c][r] = in[p][r][c] for `planes` planes of R x C, in
+// 64 x 64 tiles through LDS (coalesced reads along c, writes along r).
+template <typename S>
+__global__ __launch_bounds__(256) void transpose_planes(const S* __restrict__ in, S* __restrict__ out, int R, int C,
+                                                        int tiles_r, int tiles_c) {
+  __shared__ float tile[64][65];
+  const int t = blockIdx.x;
+  const int tc = t % tiles_c;
+  const int rest = t / tiles_c;
+  const int tr = rest % tiles_r;
+  const int64_t plane = rest / tiles_r;
+  const S* src = in + plane * R * C;
+  S* dst = out + plane * R * C;
+  const int r0 = tr * 64, c0 = tc * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll 4
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) tile[i][tx] = Io<S>::ld(src, (int64_t)r * C + c);
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) Io<S>::st(dst, (int64_t)c * R + r, tile[tx][i]);
+  }
+}
+
+template <typename S>
+hipError_t launch_transpose(const S* in, S* out, int planes, int R, int C, hipStream_t stream) {
+  const int tiles_r = (R + 63) / 64, tiles_c = (C + 63) / 64;
+  const int64_t blocks = (int64_t)planes * tiles_r * tiles_c;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((transpose_planes<S>), dim3((unsigned)blocks), dim3(256), 0, stream, in, out, R, C, tiles_r,
+                     tiles_c);
+  return hipGetLastError();
 }
 
 // Compute units of a device (0 if unknown), queried once per device.
@@ -1306,7 +1368,7 @@ inline int resident_blocks(const void* kernel, int device) {
 }
 
 template <typename S, int G, int T, bool VEC>
-hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
+hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, const Scratch& s) {
   Params p;
   p.x = a.x;
   p.dt = a.dt;
@@ -1316,15 +1378,17 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
   p.Cs = a.Cs;
   p.Ds = a.Ds;
   p.y = a.y;
-  p.prow = planes[0];
-  p.pcol = planes[1];
+  p.prow = s.prow;
+  p.pcol = s.pcol;
+  p.xT = s.xT;
+  p.pcolT = nullptr;
   p.B = (int)a.B;
   p.D = (int)a.D;
   p.H = (int)a.H;
   p.W = (int)a.W;
   p.N = (int)a.N;
   p.L = (int)(a.H * a.W);
-  p.carries = carries;
+  p.carries = s.carries;
   p.seg_chunks = plan.seg_chunks;
   p.nseg = plan.nseg;
   p.kdir = 0;
@@ -1350,7 +1414,14 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
   }
   if constexpr (VEC) {
     // carry pass over every segment but the last, then one launch per direction in
-    // merge order (column pair, then row pair; each reads what the previous wrote)
+    // merge order (column pair, then row pair; each reads what the previous wrote);
+    // with transposed copies: x before everything, the column plane before
+    // direction 2
+    const int planes = (int)(a.B * a.D);
+    if (s.xT) {
+      hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(s.xT), planes, p.H, p.W, a.stream);
+      if (e != hipSuccess) return e;
+    }
     rotation(reinterpret_cast<const void*>(&ss2d_forward_kernel<S, G, T, NG, VEC, kCarry>), units * (plan.nseg - 1));
     hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kCarry>), dim3((unsigned)(units * (plan.nseg - 1))),
                        dim3(kWaves * 64), 0, a.stream, p);
@@ -1360,6 +1431,12 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
     rotation(reinterpret_cast<const void*>(&ss2d_forward_kernel<S, G, T, NG, VEC, kSegment>), units * plan.nseg);
     for (int k : order) {
       p.kdir = k;
+      if (k == 2 && s.pcolT) {
+        // the column plane is complete after direction 3; as pixels [W][H] -> [H][W]
+        e = launch_transpose<float>(s.pcol, s.pcolT, planes, p.W, p.H, a.stream);
+        if (e != hipSuccess) return e;
+        p.pcolT = s.pcolT;
+      }
       hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kSegment>), dim3((unsigned)(units * plan.nseg)),
                          dim3(kWaves * 64), 0, a.stream, p);
       e = hipGetLastError();
@@ -1371,9 +1448,9 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, float* const pl
 }
 
 template <typename S, int G, int T>
-hipError_t launch_gt(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries) {
-  if ((a.H * a.W) % 4 == 0) return launch_variant<S, G, T, true>(a, plan, planes, carries);
-  return launch_variant<S, G, T, false>(a, plan, planes, carries);
+hipError_t launch_gt(const LaunchArgs& a, const Plan& plan, const Scratch& s) {
+  if ((a.H * a.W) % 4 == 0) return launch_variant<S, G, T, true>(a, plan, s);
+  return launch_variant<S, G, T, false>(a, plan, s);
 }
 
 template <typename S, int G, int T>
@@ -1392,9 +1469,9 @@ size_t lds_bytes_s(int G, int T, bool vec) {
 
 // Launchers of the compiled variants, one compilation unit each (steps per lane
 // T = 16 for 16/32/64 lanes, T = 8 for 32/64 lanes).
-hipError_t launch_f32_t16(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
-hipError_t launch_f32_t8(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
-hipError_t launch_bf16_t16(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
-hipError_t launch_bf16_t8(const LaunchArgs& a, const Plan& plan, float* const planes[2], float* carries);
+hipError_t launch_f32_t16(const LaunchArgs& a, const Plan& plan, const Scratch& s);
+hipError_t launch_f32_t8(const LaunchArgs& a, const Plan& plan, const Scratch& s);
+hipError_t launch_bf16_t16(const LaunchArgs& a, const Plan& plan, const Scratch& s);
+hipError_t launch_bf16_t8(const LaunchArgs& a, const Plan& plan, const Scratch& s);
 
 }  // namespace ss2d

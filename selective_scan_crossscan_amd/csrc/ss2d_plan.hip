@@ -42,20 +42,33 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   const size_t planes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
   pl.carry_offset = planes;
   pl.scratch_bytes = planes + (pl.nseg > 1 ? (size_t)(B * 4 * D) * pl.nseg * 2 * kMaxN * sizeof(float) : 0);
+  // Segmented plans are for large maps, where a column walk or the merge's column
+  // plane read at stride H or W use one cache line per element and the working set
+  // outgrows L2: they transpose x once, and the column plane before direction 2.
+  pl.transpose = pl.nseg > 1;
+  pl.xt_offset = pl.pct_offset = 0;
+  if (pl.transpose) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    pl.xt_offset = up(pl.scratch_bytes);
+    pl.pct_offset = up(pl.xt_offset + (size_t)(B * D * L) * (dtype == 0 ? 4 : 2));
+    pl.scratch_bytes = pl.pct_offset + (size_t)(B * D * L) * sizeof(float);
+  }
   return pl;
 }
 
 hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch) {
   const int64_t plane = a.B * a.D * a.H * a.W;
+  char* base = reinterpret_cast<char*>(scratch);
+  Scratch s;
   // planes: row-major (directions 0, 2), column-major (directions 1, 3)
-  float* carries = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + plan.carry_offset);
+  s.prow = a.dtype == 0 ? static_cast<float*>(a.y) : scratch + plane;
+  s.pcol = scratch;
+  s.carries = reinterpret_cast<float*>(base + plan.carry_offset);
+  s.xT = plan.transpose ? static_cast<void*>(base + plan.xt_offset) : nullptr;
+  s.pcolT = plan.transpose ? reinterpret_cast<float*>(base + plan.pct_offset) : nullptr;
   const bool t8 = plan.steps_per_lane == 8;
-  if (a.dtype == 0) {
-    float* const planes[2] = {static_cast<float*>(a.y), scratch};
-    return t8 ? launch_f32_t8(a, plan, planes, carries) : launch_f32_t16(a, plan, planes, carries);
-  }
-  float* const planes[2] = {scratch + plane, scratch};
-  return t8 ? launch_bf16_t8(a, plan, planes, carries) : launch_bf16_t16(a, plan, planes, carries);
+  if (a.dtype == 0) return t8 ? launch_f32_t8(a, plan, s) : launch_f32_t16(a, plan, s);
+  return t8 ? launch_bf16_t8(a, plan, s) : launch_bf16_t16(a, plan, s);
 }
 
 }  // namespace ss2d

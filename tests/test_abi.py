@@ -48,6 +48,22 @@ def test_describe_plans_the_workloads():
     assert f"scratch_bytes={2 * 64 * 384 * 784 * 4}" in s
     s = ss2d.describe(32, 768, 14, 14, 16, ss2d.SS2D_F32)
     assert "lanes_per_seq=16" in s and "chans_per_block=16" in s
+    assert "transpose=0" in s
+
+
+def test_describe_segmented_plan_includes_transposed_copies():
+    """256x256 maps are cut into segments; their temporary adds the segment maps,
+    a transposed x (storage type) and a transposed fp32 merge plane, 256-byte aligned."""
+    B, D, L = 2, 192, 256 * 256
+    s = ss2d.describe(B, D, 256, 256, 16, ss2d.SS2D_F32)
+    fields = dict(kv.split("=") for kv in s.split())
+    nseg = int(fields["segments"])
+    assert nseg > 1 and fields["transpose"] == "1"
+    up = lambda v: (v + 255) // 256 * 256
+    base = B * D * L * 4 + B * 4 * D * nseg * 2 * 16 * 4
+    xt = up(base)
+    pct = up(xt + B * D * L * 4)
+    assert int(fields["scratch_bytes"]) == pct + B * D * L * 4
 
 
 def test_lanes_override_knob():
