@@ -501,20 +501,24 @@ __device__ __forceinline__ int walk_index(bool rev, int l, int L) { return rev ?
 template <typename S, int T, bool VEC, bool FULL>
 __device__ __forceinline__ void load_x(const S* xrow, bool rev, bool col, int l0, int L, int H, int W,
                                        float (&uv)[T]) {
-  constexpr bool V4 = VEC && FULL && (T % 4 == 0);
+  // With VEC, L and l0 are multiples of 4 (T % 4 == 0), so each group of 4 steps
+  // lies wholly inside or wholly outside the sequence: one guard per group.
+  constexpr bool V4 = VEC && (T % 4 == 0);
   if (!col) {
     if constexpr (V4) {
       if (!rev) {
 #pragma unroll
         for (int i = 0; i < T; i += 4) {
-          const float4 q = Io<S>::ld4(xrow, l0 + i);
+          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (FULL || l0 + i < L) q = Io<S>::ld4(xrow, l0 + i);
           uv[i] = q.x; uv[i + 1] = q.y; uv[i + 2] = q.z; uv[i + 3] = q.w;
         }
       } else {
         const int s_lo = L - l0 - T;  // walk indices s_lo .. s_lo+T-1; step i is at s_lo+T-1-i
 #pragma unroll
         for (int i = 0; i < T; i += 4) {
-          const float4 q = Io<S>::ld4(xrow, s_lo + i);
+          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (FULL || s_lo + i >= 0) q = Io<S>::ld4(xrow, s_lo + i);
           uv[T - 1 - i] = q.x; uv[T - 2 - i] = q.y; uv[T - 3 - i] = q.z; uv[T - 4 - i] = q.w;
         }
       }
@@ -575,10 +579,11 @@ __device__ __forceinline__ void load_x_col(__amdgpu_buffer_rsrc_t rx, uint32_t x
 template <typename S, int T, bool VEC, bool FULL>
 __device__ __forceinline__ void load_inputs(const S* dtrow, const S* xrow, bool rev, bool col, int l0, int L, int H,
                                             int W, float (&dtv)[T], float (&uv)[T]) {
-  if constexpr (VEC && FULL && (T % 4 == 0)) {
+  if constexpr (VEC && (T % 4 == 0)) {  // groups of 4 wholly inside or outside (see load_x)
 #pragma unroll
     for (int i = 0; i < T; i += 4) {
-      const float4 q = Io<S>::ld4(dtrow, l0 + i);
+      float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (FULL || l0 + i < L) q = Io<S>::ld4(dtrow, l0 + i);
       dtv[i] = q.x; dtv[i + 1] = q.y; dtv[i + 2] = q.z; dtv[i + 3] = q.w;
     }
   } else {
@@ -683,10 +688,11 @@ __device__ __forceinline__ void state_carry(const char* Brow, int seg, float A2n
 // Writes (or adds) a lane's outputs of T consecutive steps into its plane.
 template <int T, bool VEC, bool FULL>
 __device__ __forceinline__ void store_outputs(float* plane, bool rev, bool add, int l0, int L, const float (&yv)[T]) {
-  if constexpr (VEC && FULL && (T % 4 == 0)) {
+  if constexpr (VEC && (T % 4 == 0)) {  // groups of 4 wholly inside or outside (see load_x)
     const int s_lo = rev ? L - l0 - T : l0;
 #pragma unroll
     for (int i = 0; i < T; i += 4) {
+      if (!FULL && (s_lo + i < 0 || s_lo + i >= L)) continue;
       float4* q = reinterpret_cast<float4*>(plane + s_lo + i);
       float4 v = rev ? make_float4(yv[T - 1 - i], yv[T - 2 - i], yv[T - 3 - i], yv[T - 4 - i])
                      : make_float4(yv[i], yv[i + 1], yv[i + 2], yv[i + 3]);
@@ -717,12 +723,15 @@ __device__ __forceinline__ void store_outputs(float* plane, bool rev, bool add, 
 template <typename S, int T, bool VEC, bool FULL>
 __device__ __forceinline__ void store_final(const float* prow, const float* pcol, const float* pct, S* y, int l0,
                                             int L, int H, int W, const float (&yv)[T]) {
-  if constexpr (VEC && FULL && (T % 4 == 0)) {
-    const int s_lo = L - l0 - T;  // pixels s_lo .. s_lo+T-1; pixel s_lo+j holds yv[T-1-j]
+  if constexpr (VEC && (T % 4 == 0)) {
+    // pixels s_lo .. s_lo+T-1; pixel s_lo+j holds yv[T-1-j].  A partial chunk's
+    // pixels below 0 come in whole groups of 4 (see load_x) and are skipped.
+    const int s_lo = L - l0 - T;
     float v[T];
 #pragma unroll
     for (int j = 0; j < T; j += 4) {
-      const float4 o = *reinterpret_cast<const float4*>(prow + s_lo + j);
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (FULL || s_lo + j >= 0) o = *reinterpret_cast<const float4*>(prow + s_lo + j);
       v[j] = o.x + yv[T - 1 - j];
       v[j + 1] = o.y + yv[T - 2 - j];
       v[j + 2] = o.z + yv[T - 3 - j];
@@ -731,6 +740,7 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
     if (pct != nullptr) {
 #pragma unroll
       for (int j = 0; j < T; j += 4) {
+        if (!FULL && s_lo + j < 0) continue;
         const float4 o = *reinterpret_cast<const float4*>(pct + s_lo + j);
         v[j] += o.x;
         v[j + 1] += o.y;
@@ -738,10 +748,12 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
         v[j + 3] += o.w;
       }
     } else {
-      int h = s_lo / W;
-      int w = s_lo - h * W;
+      const int s0 = FULL ? s_lo : max(s_lo, 0);
+      int h = s0 / W;
+      int w = s0 - h * W;
 #pragma unroll
       for (int j = 0; j < T; ++j) {
+        if (!FULL && s_lo + j < 0) continue;
         v[j] += pcol[w * H + h];
         ++w;
         const bool wrap = w == W;
@@ -750,7 +762,8 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
       }
     }
 #pragma unroll
-    for (int j = 0; j < T; j += 4) Io<S>::st4(y, s_lo + j, make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]));
+    for (int j = 0; j < T; j += 4)
+      if (FULL || s_lo + j >= 0) Io<S>::st4(y, s_lo + j, make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]));
   } else {
     int pix = L - 1 - (FULL ? l0 : min(l0, L - 1));
     int h = pix / W;
