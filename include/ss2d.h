@@ -108,6 +108,35 @@ int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dty
  */
 int ss2d_set_lanes_per_seq(int lanes);
 
+/*
+ * ss2d_measure_peaks -- measure, on the current device, the rates the forward is
+ * judged against (its roofline), one probe kernel per rate, each timed with HIP
+ * events as the best of three runs on `stream`:
+ *   exp_per_s         v_exp_f32 results per second (8 independent chains per lane)
+ *   fma_per_s         plain fp32 FMA results per second
+ *   update_mix_per_s  state-update-shaped work per second: one exp2 and four fp32
+ *                     VALU operations per update, as the scan's inner loop needs
+ *   hbm_read_Bps      streaming read bandwidth over hbm_bytes
+ *   hbm_copy_Bps      device copy of hbm_bytes/2, bytes read plus bytes written
+ *   lds_read_Bps      16-byte LDS reads, all CUs
+ *   compute_units     CUs of the device
+ * The probes allocate hbm_bytes (1 MiB .. 64 GiB, multiple of 32) plus a small
+ * sink from the device's default memory pool on `stream` and free them; the call
+ * returns after synchronising `stream`.  Codes: SS2D_ERR_NULL (out), SS2D_ERR_SHAPE
+ * (hbm_bytes), SS2D_ERR_NO_DEVICE, SS2D_ERR_HIP.  For benchmarking only; not
+ * needed by ss2d_forward.
+ */
+typedef struct {
+  double exp_per_s;
+  double fma_per_s;
+  double update_mix_per_s;
+  double hbm_read_Bps;
+  double hbm_copy_Bps;
+  double lds_read_Bps;
+  int compute_units;
+} ss2d_peaks;
+int ss2d_measure_peaks(ss2d_peaks* out, int64_t hbm_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

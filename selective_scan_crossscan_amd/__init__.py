@@ -33,6 +33,14 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+class Peaks(ctypes.Structure):
+    """ss2d_peaks: rates measured on the device by ss2d_measure_peaks."""
+    _fields_ = [("exp_per_s", ctypes.c_double), ("fma_per_s", ctypes.c_double),
+                ("update_mix_per_s", ctypes.c_double), ("hbm_read_Bps", ctypes.c_double),
+                ("hbm_copy_Bps", ctypes.c_double), ("lds_read_Bps", ctypes.c_double),
+                ("compute_units", ctypes.c_int)]
+
+
 def lib():
     """The loaded libss2d.so (ctypes), with argument types declared."""
     global _lib
@@ -55,6 +63,8 @@ def lib():
             L.ss2d_describe.restype = ctypes.c_int
             L.ss2d_set_lanes_per_seq.argtypes = [ctypes.c_int]
             L.ss2d_set_lanes_per_seq.restype = ctypes.c_int
+            L.ss2d_measure_peaks.argtypes = [ctypes.POINTER(Peaks), i64, vp]
+            L.ss2d_measure_peaks.restype = ctypes.c_int
             _lib = L
     return _lib
 
@@ -85,6 +95,15 @@ def set_lanes_per_seq(lanes: int) -> None:
 def ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, stream) -> int:
     """Raw C-ABI call with integer device addresses; returns the status code."""
     return lib().ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype), stream)
+
+
+def measure_peaks(hbm_bytes: int = 1 << 30, stream: int = 0) -> dict:
+    """Roofline probes on the current device (ss2d_measure_peaks); rates per second."""
+    p = Peaks()
+    rc = lib().ss2d_measure_peaks(ctypes.byref(p), int(hbm_bytes), stream)
+    if rc != 0:
+        _raise(rc)
+    return {name: getattr(p, name) for name, _ in Peaks._fields_}
 
 
 def _raise(rc: int):

@@ -100,6 +100,28 @@ int ss2d_set_lanes_per_seq(int lanes) {
 
 const char* ss2d_last_hip_error(void) { return g_last_hip_error; }
 
+int ss2d_measure_peaks(ss2d_peaks* out, int64_t hbm_bytes, void* stream) {
+  if (!out) return SS2D_ERR_NULL;
+  if (hbm_bytes < (1 << 20) || hbm_bytes > ((int64_t)64 << 30) || hbm_bytes % 32 != 0) return SS2D_ERR_SHAPE;
+  DeviceInfo di;
+  const int rc = device_info(&di);
+  if (rc != SS2D_OK) return rc;
+  ss2d::PeakRates r{};
+  const hipError_t e = ss2d::measure_peaks(&r, hbm_bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  out->exp_per_s = r.exp_per_s;
+  out->fma_per_s = r.fma_per_s;
+  out->update_mix_per_s = r.update_mix_per_s;
+  out->hbm_read_Bps = r.hbm_read_Bps;
+  out->hbm_copy_Bps = r.hbm_copy_Bps;
+  out->lds_read_Bps = r.lds_read_Bps;
+  out->compute_units = r.compute_units;
+  return SS2D_OK;
+}
+
 const char* ss2d_status_string(int status) {
   switch (status) {
     case SS2D_OK: return "ok";

@@ -49,6 +49,15 @@ struct Scratch {
   float* pcolT;    // the column plane in row-major order, or null
 };
 
+// Rates measured on the device (see ss2d_measure_peaks in ss2d.h).
+struct PeakRates {
+  double exp_per_s, fma_per_s, update_mix_per_s, hbm_read_Bps, hbm_copy_Bps, lds_read_Bps;
+  int compute_units;
+};
+
+// Runs the roofline probes on the current device, on `stream` (synchronises it).
+hipError_t measure_peaks(PeakRates* out, int64_t hbm_bytes, hipStream_t stream);
+
 // lanes_override: 0 = automatic, else 16, 32 or 64 lanes per sequence.
 Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override);
 

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["ss2d_forward", "ss2d_status_string", "ss2d_last_hip_error", "ss2d_version",
-                            "ss2d_describe", "ss2d_set_lanes_per_seq"])
+                            "ss2d_describe", "ss2d_set_lanes_per_seq", "ss2d_measure_peaks"])
     lib = ctypes.CDLL(ss2d.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -137,5 +137,14 @@ def _no_device_here():
 
 
 @pytest.mark.skipif(not _no_device_here(), reason="only meaningful where no GPU is present")
+def test_measure_peaks_validates_before_touching_a_device():
+    L = ss2d.lib()
+    p = ss2d.Peaks()
+    assert L.ss2d_measure_peaks(None, 1 << 20, None) == -1
+    for bad in (0, 1000, (1 << 20) + 4, (65 << 30)):
+        assert L.ss2d_measure_peaks(ctypes.byref(p), bad, None) == -2, bad
+    assert L.ss2d_measure_peaks(ctypes.byref(p), 1 << 20, None) == -7  # no GPU in this container
+
+
 def test_valid_call_without_device_reports_no_device():
     assert _call() == -7
