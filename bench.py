@@ -91,9 +91,11 @@ PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats -f csv -d {d} -o stats -- "
              "python bench.py --config {c} --steps 20 --warmup 5 --no-cpu-baseline > {d}/stats_bench.json",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d} -o fetch -- "
-             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mib 512",
+             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks "
+             "--copy-probe-mib 512",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d} -o write -- "
-             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mib 512",
+             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks "
+             "--copy-probe-mib 512",
 }
 COPY_PROBE_MIB = 512
 
