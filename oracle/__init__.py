@@ -3,7 +3,7 @@
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The HIP library never calls it and shares no code with it.
 
-Three independent formulations live here:
+Three independent formulations of the scan, and the projections, live here:
   * `ss2d_f64`      -- plain C loops in double precision (ss2d_oracle.c),
                         OpenMP across (b, d) planes only.  The reference result.
   * `ops_numpy`     -- the page's tensor-op formulation (stack / transpose / flip
@@ -12,6 +12,10 @@ Three independent formulations live here:
   * `brute`         -- an O(L^2) unrolled sum with no recurrence at all, for tiny
                         maps, walking the map in the orders the direction table
                         describes.
+  * `projection`    -- the per-direction input projections of §3.2 (x_proj,
+                        the split into dts/Bs/Cs, the rank-R dt map) in numpy
+                        float64, and the forward from the feature map and
+                        the projection weights built on them.
 Pages: [SS2D] "深入解析VMamba中的SS2D模块从理论到代码实现" §3.1-§4.
 """
 from __future__ import annotations

@@ -120,6 +120,41 @@ def generate(shape: Shape, seed: int = 0, a_log: str = "s4d", dt_min: float = 1e
     return dict(x=x, dt=dt, A_log=np.ascontiguousarray(A_log), dt_bias=dt_bias, Bs=Bs, Cs=Cs, Ds=Ds)
 
 
+def default_rank(D: int) -> int:
+    """dt rank of a block with D inner channels: ceil(d_model / 16) with
+    d_model = D / 2 (expansion ratio 2), the page's "auto" sizing ([SS2D] §1)."""
+    return max(1, math.ceil(D / 32))
+
+
+def generate_projected(shape: Shape, seed: int = 0, R: int | None = None, dt_min: float = 1e-3,
+                       dt_max: float = 1e-1) -> dict:
+    """Inputs of the SS2D forward from the feature map and projection weights.
+
+    Returns float32 arrays keyed x (B,D,H,W), x_proj_weight (4, R+2N, D),
+    dt_projs_weight (4, D, R), A_log (4D, N), dt_bias (4D,), Ds (4D,).
+    Recipe (seed s, PCG64, draws in this order): x ~ N(0, 1); x_proj_weight
+    ~ U(-1/sqrt(D), 1/sqrt(D)) (a linear layer's default initialisation);
+    dt_projs_weight ~ U(-R^-1/2, R^-1/2) (the page's "random" dt init with
+    dt_scale 1, [SS2D] §2.1); dt_bias by the inverse-softplus recipe of
+    `generate`; A_log[c, n] = ln(n + 1); Ds = 1.  For bf16 shapes x is
+    rounded to bfloat16; the weights stay float32."""
+    B, D, H, W, N = shape.B, shape.D, shape.H, shape.W, shape.N
+    R = default_rank(D) if R is None else R
+    rng = np.random.default_rng(seed)
+    x = _f32(rng.standard_normal((B, D, H, W)))
+    wx = _f32(rng.uniform(-1.0, 1.0, size=(4, R + 2 * N, D)) / math.sqrt(D))
+    wdt = _f32(rng.uniform(-1.0, 1.0, size=(4, D, R)) / math.sqrt(R))
+    U = rng.random(4 * D)
+    dt0 = np.exp(U * (math.log(dt_max) - math.log(dt_min)) + math.log(dt_min))
+    dt_bias = _f32(dt0 + np.log(-np.expm1(-dt0)))
+    A_log = _f32(np.broadcast_to(np.log(np.arange(1, N + 1, dtype=np.float64)), (4 * D, N)))
+    Ds = np.ones(4 * D, dtype=np.float32)
+    if shape.dtype == "bf16":
+        x = round_to_bf16(x)
+    return dict(x=x, x_proj_weight=wx, dt_projs_weight=wdt, A_log=np.ascontiguousarray(A_log), dt_bias=dt_bias,
+                Ds=Ds)
+
+
 def tiny_random(B: int, D: int, H: int, W: int, N: int, seed: int, dtype: str = "f32",
                 a_log: str = "random") -> dict:
     """Small inputs of arbitrary shape (non-square maps, ragged lengths) for tests."""
