@@ -82,6 +82,54 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
                  int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
                  int dtype, void* stream);
 
+/*
+ * ss2d_project -- enqueue the per-direction input projections of SS2D on `stream`:
+ * from the feature map and the projection weights, the dt, Bs and Cs that
+ * ss2d_forward consumes.  Page [SS2D] "深入解析VMamba中的SS2D模块从理论到代码实现"
+ * §3.2 (the parameter projection before the selective scan: x_proj over the four
+ * scan sequences, the split into dts / Bs / Cs, and the dt_projs map); the rank
+ * R is sized ceil(d_model / 16) there (§1), any R >= 1 is accepted here.
+ *
+ * Every pointer is DEVICE memory owned by the caller, dense, row-major.  With
+ * C = R + 2N and u the D channels of the pixel direction k visits at step l:
+ *   x                [B, D, H, W]   dtype  channel-first feature map.
+ *   x_proj_weight    [4, C, D]      fp32   row c of direction k: the c-th
+ *                                          projection (rows 0..R-1 feed dt,
+ *                                          R..R+N-1 are Bs, R+N..C-1 are Cs).
+ *   dt_projs_weight  [4, D, R]      fp32
+ *   dt               [B, 4, D, L]   dtype  out: sum_r dt_projs_weight[k,d,r] *
+ *                                          (x_proj_weight[k,r,:] . u); no bias.
+ *   Bs, Cs           [B, 4, N, L]   dtype  out: x_proj_weight[k,R+n,:] . u and
+ *                                          x_proj_weight[k,R+N+n,:] . u.
+ * All three outputs are in scan order, the layout ss2d_forward reads, and are
+ * fully overwritten; they must not overlap each other or any input
+ * (SS2D_ERR_ALIAS).  Products and sums are fp32 on the matrix cores; bf16
+ * outputs are rounded once, to nearest even.  2*(R + 2N) may be at most 128
+ * (SS2D_ERR_SHAPE otherwise, as for R < 1); N is 1..16 as for ss2d_forward.
+ * Takes a stream-ordered temporary of one copy of x (with H and W swapped) and
+ * runs two kernels on `stream`.  Validation, error reporting and thread safety
+ * as for ss2d_forward; the weights need 4-byte alignment (SS2D_ERR_ALIGN).
+ */
+int ss2d_project(const void* x, const float* x_proj_weight, const float* dt_projs_weight,
+                 void* dt, void* Bs, void* Cs,
+                 int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
+                 int dtype, void* stream);
+
+/*
+ * ss2d_forward_from_x -- enqueue the SS2D forward from the feature map and the
+ * projection weights: ss2d_project, then ss2d_forward on its outputs, with the
+ * intermediate dt, Bs and Cs (in `dtype`) kept in a stream-ordered temporary.
+ * Page [SS2D] §3.2 steps in order: projections, selective scan (A = -exp(A_log),
+ * delta bias dt_bias, softplus), then §3.3 the merge.  Arguments as for the two
+ * calls; y must not overlap any input.  The temporary holds x transposed, dt,
+ * Bs, Cs and what ss2d_forward needs; the scan's column walks read the
+ * transposed copy of x.  Three kernels (more for segmented maps) on `stream`.
+ */
+int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* dt_projs_weight,
+                        const float* A_log, const float* dt_bias, const float* Ds, void* y,
+                        int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
+                        int dtype, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ss2d_status_string(int status);
 

@@ -11,7 +11,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["forward", "ss2d_forward", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
+__all__ = ["forward", "ss2d_forward", "project", "ss2d_project", "forward_from_x", "ss2d_forward_from_x",
+           "measure_peaks", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
            "SS2D_F32", "SS2D_BF16", "SS2DError"]
 
 SS2D_F32 = 0
@@ -25,7 +26,7 @@ _lib = None
 
 class SS2DError(RuntimeError):
     def __init__(self, code: int, message: str):
-        super().__init__(f"ss2d_forward failed ({code}): {message}")
+        super().__init__(f"libss2d call failed ({code}): {message}")
         self.code = code
 
 
@@ -63,6 +64,10 @@ def lib():
             L.ss2d_describe.restype = ctypes.c_int
             L.ss2d_set_lanes_per_seq.argtypes = [ctypes.c_int]
             L.ss2d_set_lanes_per_seq.restype = ctypes.c_int
+            L.ss2d_project.argtypes = [vp] * 6 + [i64] * 6 + [ctypes.c_int, vp]
+            L.ss2d_project.restype = ctypes.c_int
+            L.ss2d_forward_from_x.argtypes = [vp] * 7 + [i64] * 6 + [ctypes.c_int, vp]
+            L.ss2d_forward_from_x.restype = ctypes.c_int
             L.ss2d_measure_peaks.argtypes = [ctypes.POINTER(Peaks), i64, vp]
             L.ss2d_measure_peaks.restype = ctypes.c_int
             _lib = L
@@ -95,6 +100,112 @@ def set_lanes_per_seq(lanes: int) -> None:
 def ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, stream) -> int:
     """Raw C-ABI call with integer device addresses; returns the status code."""
     return lib().ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype), stream)
+
+
+def ss2d_project(x, x_proj_weight, dt_projs_weight, dt, Bs, Cs, B, D, H, W, N, R, dtype, stream) -> int:
+    """Raw C-ABI call with integer device addresses; returns the status code."""
+    return lib().ss2d_project(x, x_proj_weight, dt_projs_weight, dt, Bs, Cs, B, D, H, W, N, R, int(dtype), stream)
+
+
+def ss2d_forward_from_x(x, x_proj_weight, dt_projs_weight, A_log, dt_bias, Ds, y, B, D, H, W, N, R, dtype,
+                        stream) -> int:
+    """Raw C-ABI call with integer device addresses; returns the status code."""
+    return lib().ss2d_forward_from_x(x, x_proj_weight, dt_projs_weight, A_log, dt_bias, Ds, y, B, D, H, W, N, R,
+                                     int(dtype), stream)
+
+
+def _check_tensors(x, io, params):
+    import torch
+
+    for t in io + params:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU fallback)")
+        if t.device != x.device:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    for t in io:
+        if t.dtype != x.dtype:
+            raise TypeError("feature map and outputs must share one dtype")
+    for t in params:
+        if t.dtype != torch.float32:
+            raise TypeError("weights and per-channel parameters must be float32")
+
+
+def _dtype_code(x) -> int:
+    import torch
+
+    if x.dtype == torch.float32:
+        return SS2D_F32
+    if x.dtype == torch.bfloat16:
+        return SS2D_BF16
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def _projection_shapes(x, x_proj_weight, dt_projs_weight, N):
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    B, D, H, W = x.shape
+    if dt_projs_weight.dim() != 3 or dt_projs_weight.shape[0] != 4 or dt_projs_weight.shape[1] != D:
+        raise ValueError("dt_projs_weight must be (4, D, R)")
+    R = dt_projs_weight.shape[2]
+    if tuple(x_proj_weight.shape) != (4, R + 2 * N, D):
+        raise ValueError("x_proj_weight must be (4, R + 2N, D)")
+    return B, D, H, W, R
+
+
+def project(x, x_proj_weight, dt_projs_weight, N: int, stream=None):
+    """Per-direction input projections on torch tensors (ss2d_project).
+
+    x (B,D,H,W) float32 or bfloat16; x_proj_weight (4, R+2N, D), dt_projs_weight (4, D, R) float32.
+    Returns (dt (B,4,D,L), Bs (B,4,N,L), Cs (B,4,N,L)) in x's dtype, scan order.
+    """
+    import torch
+
+    code = _dtype_code(x)
+    B, D, H, W, R = _projection_shapes(x, x_proj_weight, dt_projs_weight, N)
+    L = H * W
+    dt = torch.empty((B, 4, D, L), dtype=x.dtype, device=x.device)
+    Bs = torch.empty((B, 4, N, L), dtype=x.dtype, device=x.device)
+    Cs = torch.empty((B, 4, N, L), dtype=x.dtype, device=x.device)
+    _check_tensors(x, (x, dt, Bs, Cs), (x_proj_weight, dt_projs_weight))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        rc = ss2d_project(x.data_ptr(), x_proj_weight.data_ptr(), dt_projs_weight.data_ptr(), dt.data_ptr(),
+                          Bs.data_ptr(), Cs.data_ptr(), B, D, H, W, N, R, code, stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return dt, Bs, Cs
+
+
+def forward_from_x(x, x_proj_weight, dt_projs_weight, A_log, dt_bias, Ds, out=None, stream=None):
+    """SS2D forward from the feature map and the projection weights (ss2d_forward_from_x).
+
+    x (B,D,H,W) float32 or bfloat16; x_proj_weight (4, R+2N, D), dt_projs_weight (4, D, R),
+    A_log (4D,N), dt_bias (4D,), Ds (4D,) float32.  Returns y (B,D,H,W) in x's dtype.
+    """
+    import torch
+
+    code = _dtype_code(x)
+    N = A_log.shape[-1]
+    B, D, H, W, R = _projection_shapes(x, x_proj_weight, dt_projs_weight, N)
+    if tuple(A_log.shape) != (4 * D, N) or tuple(dt_bias.shape) != (4 * D,) or tuple(Ds.shape) != (4 * D,):
+        raise ValueError("A_log must be (4D,N); dt_bias and Ds (4D,)")
+    if out is None:
+        out = torch.empty((B, D, H, W), dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != (B, D, H, W) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B,D,H,W) tensor of x's dtype")
+    _check_tensors(x, (x, out), (x_proj_weight, dt_projs_weight, A_log, dt_bias, Ds))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        rc = ss2d_forward_from_x(x.data_ptr(), x_proj_weight.data_ptr(), dt_projs_weight.data_ptr(),
+                                 A_log.data_ptr(), dt_bias.data_ptr(), Ds.data_ptr(), out.data_ptr(),
+                                 B, D, H, W, N, R, code, stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
 
 
 def measure_peaks(hbm_bytes: int = 1 << 30, stream: int = 0) -> dict:

@@ -218,4 +218,146 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
   return SS2D_OK;
 }
 
+namespace {
+
+// Checks shared by the two projection entry points: R, the weights' sizes, and
+// element alignment of the weights.
+int check_projection(int64_t D, int64_t N, int64_t R, const float* wx, const float* wdt) {
+  if (R < 1 || R > INT32_MAX / 4 || 2 * (R + 2 * N) > ss2d::project_max_rows()) return SS2D_ERR_SHAPE;
+  if (((uintptr_t)wx & 3) || ((uintptr_t)wdt & 3)) return SS2D_ERR_ALIGN;
+  (void)D;
+  return SS2D_OK;
+}
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+constexpr bool kScanReadsXT = true;
+
+}  // namespace
+
+int ss2d_project(const void* x, const float* x_proj_weight, const float* dt_projs_weight, void* dt, void* Bs,
+                 void* Cs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R, int dtype,
+                 void* stream) {
+  if (!x || !x_proj_weight || !dt_projs_weight || !dt || !Bs || !Cs) return SS2D_ERR_NULL;
+  int rc = check_shape(B, D, H, W, N, dtype);
+  if (rc != SS2D_OK) return rc;
+  rc = check_projection(D, N, R, x_proj_weight, dt_projs_weight);
+  if (rc != SS2D_OK) return rc;
+  const int64_t L = H * W;
+  const int64_t s = dtype == SS2D_BF16 ? 2 : 4;
+  const int64_t xbytes = B * D * L * s, dtbytes = B * 4 * D * L * s, bcbytes = B * 4 * N * L * s;
+  const int64_t wxbytes = 4 * (R + 2 * N) * D * 4, wdtbytes = 4 * D * R * 4;
+  const void* outs[3] = {dt, Bs, Cs};
+  const int64_t osz[3] = {dtbytes, bcbytes, bcbytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], osz[i], x, xbytes) || overlaps(outs[i], osz[i], x_proj_weight, wxbytes) ||
+        overlaps(outs[i], osz[i], dt_projs_weight, wdtbytes))
+      return SS2D_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SS2D_ERR_ALIAS;
+  }
+  const uintptr_t m = (uintptr_t)(s - 1);
+  if (((uintptr_t)x & m) || ((uintptr_t)dt & m) || ((uintptr_t)Bs & m) || ((uintptr_t)Cs & m)) return SS2D_ERR_ALIGN;
+
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc != SS2D_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* xT = nullptr;
+  hipError_t e = hipMallocAsync(&xT, (size_t)xbytes, st);
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  e = ss2d::launch_transpose_x(x, xT, B * D, H, W, dtype, st);
+  if (e == hipSuccess) {
+    ss2d::ProjectArgs pa{x, xT, x_proj_weight, dt_projs_weight, dt, Bs, Cs, B, D, H, W, N, R, dtype, st};
+    e = ss2d::launch_project(pa);
+  }
+  hipError_t e2 = hipFreeAsync(xT, st);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  return SS2D_OK;
+}
+
+int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* dt_projs_weight,
+                        const float* A_log, const float* dt_bias, const float* Ds, void* y, int64_t B, int64_t D,
+                        int64_t H, int64_t W, int64_t N, int64_t R, int dtype, void* stream) {
+  if (!x || !x_proj_weight || !dt_projs_weight || !A_log || !dt_bias || !Ds || !y) return SS2D_ERR_NULL;
+  int rc = check_shape(B, D, H, W, N, dtype);
+  if (rc != SS2D_OK) return rc;
+  rc = check_projection(D, N, R, x_proj_weight, dt_projs_weight);
+  if (rc != SS2D_OK) return rc;
+  const int64_t L = H * W;
+  const int64_t s = dtype == SS2D_BF16 ? 2 : 4;
+  const int64_t xbytes = B * D * L * s, dtbytes = B * 4 * D * L * s, bcbytes = B * 4 * N * L * s;
+  const int64_t wxbytes = 4 * (R + 2 * N) * D * 4, wdtbytes = 4 * D * R * 4;
+  const int64_t pbytes = 4 * D * N * 4, vbytes = 4 * D * 4;
+  if (overlaps(y, xbytes, x, xbytes) || overlaps(y, xbytes, x_proj_weight, wxbytes) ||
+      overlaps(y, xbytes, dt_projs_weight, wdtbytes) || overlaps(y, xbytes, A_log, pbytes) ||
+      overlaps(y, xbytes, dt_bias, vbytes) || overlaps(y, xbytes, Ds, vbytes))
+    return SS2D_ERR_ALIAS;
+  const uintptr_t m = (uintptr_t)(s - 1);
+  if (((uintptr_t)x & m) || ((uintptr_t)y & m) || ((uintptr_t)A_log & 3) || ((uintptr_t)dt_bias & 3) ||
+      ((uintptr_t)Ds & 3))
+    return SS2D_ERR_ALIGN;
+  const uintptr_t vm = (uintptr_t)(4 * s - 1);
+  if (L % 4 == 0 && (((uintptr_t)x & vm) || ((uintptr_t)y & vm))) return SS2D_ERR_ALIGN;
+
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc != SS2D_OK) return rc;
+  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
+  // one temporary: x transposed, dt, Bs, Cs, then what the scan itself needs
+  const size_t o_dt = up256((size_t)xbytes), o_b = o_dt + up256((size_t)dtbytes);
+  const size_t o_c = o_b + up256((size_t)bcbytes), o_scan = o_c + up256((size_t)bcbytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* tmp = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&tmp), o_scan + plan.scratch_bytes, st);
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  void* xT = tmp;
+  void *dt = tmp + o_dt, *Bs = tmp + o_b, *Cs = tmp + o_c;
+  e = ss2d::launch_transpose_x(x, xT, B * D, H, W, dtype, st);
+  if (e == hipSuccess) {
+    ss2d::ProjectArgs pa{x, xT, x_proj_weight, dt_projs_weight, dt, Bs, Cs, B, D, H, W, N, R, dtype, st};
+    e = ss2d::launch_project(pa);
+  }
+  if (e == hipSuccess) {
+    ss2d::LaunchArgs a;
+    a.x = x;
+    a.dt = dt;
+    a.A_log = A_log;
+    a.dt_bias = dt_bias;
+    a.Bs = Bs;
+    a.Cs = Cs;
+    a.Ds = Ds;
+    a.y = y;
+    a.B = B;
+    a.D = D;
+    a.H = H;
+    a.W = W;
+    a.N = N;
+    a.dtype = dtype;
+    a.stream = st;
+    a.device = di.device;
+    // the scan's column walks read the transposed copy too (segmented plans
+    // would otherwise make their own)
+    e = ss2d::launch_forward(a, plan, reinterpret_cast<float*>(tmp + o_scan),
+                             (kScanReadsXT || plan.nseg > 1) ? xT : nullptr);
+  }
+  hipError_t e2 = hipFreeAsync(tmp, st);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  return SS2D_OK;
+}
+
 }  // extern "C"

@@ -47,6 +47,7 @@ struct Scratch {
   float* carries;  // segment maps
   void* xT;        // x with H and W swapped, or null
   float* pcolT;    // the column plane in row-major order, or null
+  bool xT_given;   // xT already holds the transpose (made by the caller)
 };
 
 // Rates measured on the device (see ss2d_measure_peaks in ss2d.h).
@@ -61,8 +62,30 @@ hipError_t measure_peaks(PeakRates* out, int64_t hbm_bytes, hipStream_t stream);
 // lanes_override: 0 = automatic, else 16, 32 or 64 lanes per sequence.
 Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override);
 
-// Enqueue the forward.  `scratch` holds plan.scratch_bytes.  Returns hipSuccess
-// or the first HIP error.
-hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch);
+// Enqueue the forward.  `scratch` holds plan.scratch_bytes.  `xT`, when not null,
+// already holds x with H and W swapped (B*D planes of W x H): column walks then
+// read it instead of gathering.  Returns hipSuccess or the first HIP error.
+hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch, const void* xT = nullptr);
+
+// The per-direction input projections (x_proj, split, rank-R dt map), written in
+// scan order.  xT must already hold x with H and W swapped.
+struct ProjectArgs {
+  const void* x;
+  const void* xT;
+  const float* wx;   // (4, R + 2N, D)
+  const float* wdt;  // (4, D, R)
+  void* dt;          // (B, 4, D, L)
+  void* Bs;          // (B, 4, N, L)
+  void* Cs;          // (B, 4, N, L)
+  int64_t B, D, H, W, N, R;
+  int dtype;
+  hipStream_t stream;
+};
+hipError_t launch_project(const ProjectArgs& a);
+// Largest 2 * (R + 2N) the projection kernel takes.
+int project_max_rows();
+// x (B*D planes of H x W) -> xT (planes of W x H).
+hipError_t launch_transpose_x(const void* x, void* xT, int64_t planes, int64_t H, int64_t W, int dtype,
+                              hipStream_t stream);
 
 }  // namespace ss2d

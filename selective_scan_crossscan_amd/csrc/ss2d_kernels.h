@@ -1431,7 +1431,7 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, const Scratch& 
     // with transposed copies: x before everything, the column plane before
     // direction 2
     const int planes = (int)(a.B * a.D);
-    if (s.xT) {
+    if (s.xT && !s.xT_given) {
       hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(s.xT), planes, p.H, p.W, a.stream);
       if (e != hipSuccess) return e;
     }

@@ -56,7 +56,7 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   return pl;
 }
 
-hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch) {
+hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch, const void* xT) {
   const int64_t plane = a.B * a.D * a.H * a.W;
   char* base = reinterpret_cast<char*>(scratch);
   Scratch s;
@@ -64,7 +64,8 @@ hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch)
   s.prow = a.dtype == 0 ? static_cast<float*>(a.y) : scratch + plane;
   s.pcol = scratch;
   s.carries = reinterpret_cast<float*>(base + plan.carry_offset);
-  s.xT = plan.transpose ? static_cast<void*>(base + plan.xt_offset) : nullptr;
+  s.xT = xT ? const_cast<void*>(xT) : plan.transpose ? static_cast<void*>(base + plan.xt_offset) : nullptr;
+  s.xT_given = xT != nullptr;
   s.pcolT = plan.transpose ? reinterpret_cast<float*>(base + plan.pct_offset) : nullptr;
   const bool t8 = plan.steps_per_lane == 8;
   if (a.dtype == 0) return t8 ? launch_f32_t8(a, plan, s) : launch_f32_t16(a, plan, s);

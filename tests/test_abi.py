@@ -25,7 +25,8 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["ss2d_forward", "ss2d_status_string", "ss2d_last_hip_error", "ss2d_version",
-                            "ss2d_describe", "ss2d_set_lanes_per_seq", "ss2d_measure_peaks"])
+                            "ss2d_describe", "ss2d_set_lanes_per_seq", "ss2d_measure_peaks", "ss2d_project",
+                            "ss2d_forward_from_x"])
     lib = ctypes.CDLL(ss2d.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -148,3 +149,58 @@ def test_measure_peaks_validates_before_touching_a_device():
 
 def test_valid_call_without_device_reports_no_device():
     assert _call() == -7
+
+
+# the projection entry points: same fake addresses, weights in their own slots
+WX, WDT = BASE + 8 * (1 << 34), BASE + 9 * (1 << 34)
+
+
+def _proj(x=X, wx=WX, wdt=WDT, dt=DT, bs=BS, cs=CS, B=2, D=3, H=4, W=5, N=16, R=2, dtype=0):
+    return ss2d.ss2d_project(x, wx, wdt, dt, bs, cs, B, D, H, W, N, R, dtype, None)
+
+
+def _fromx(x=X, wx=WX, wdt=WDT, al=AL, bi=BI, ds=DS, y=Y, B=2, D=3, H=4, W=5, N=16, R=2, dtype=0):
+    return ss2d.ss2d_forward_from_x(x, wx, wdt, al, bi, ds, y, B, D, H, W, N, R, dtype, None)
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_project_null_pointer(which):
+    args = [X, WX, WDT, DT, BS, CS]
+    args[which] = None
+    assert _proj(*args) == -1
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_forward_from_x_null_pointer(which):
+    args = [X, WX, WDT, AL, BI, DS, Y]
+    args[which] = None
+    assert _fromx(*args) == -1
+
+
+@pytest.mark.parametrize("call", [_proj, _fromx])
+def test_projection_rank_and_row_limits(call):
+    assert call(R=0) == -2
+    assert call(R=-3) == -2
+    assert call(N=16, R=33) == -2     # 2 * (33 + 32) = 130 rows > 128
+    assert call(N=1, R=63) == -2      # 2 * (63 + 2) = 130
+    assert call(N=17) == -3
+    assert call(dtype=3) == -4
+    assert call(B=0) == -2
+
+
+def test_projection_aliasing_and_alignment():
+    assert _proj(dt=X) == -5
+    assert _proj(bs=CS) == -5          # two outputs on one buffer
+    assert _proj(cs=WX + 64) == -5     # an output over a weight
+    assert _proj(wx=WX + 2) == -6
+    assert _proj(x=X + 1, dtype=1) == -6
+    assert _fromx(y=X) == -5
+    assert _fromx(y=WDT) == -5
+    assert _fromx(wdt=WDT + 1) == -6
+    assert _fromx(x=X + 4, H=4, W=4) == -6   # fp32, L % 4 == 0: 16-byte bases
+
+
+def test_projection_valid_calls_without_device_report_no_device():
+    assert _proj() == -7
+    assert _proj(N=16, R=32) == -7     # exactly 128 rows is allowed
+    assert _fromx() == -7
