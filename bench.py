@@ -38,6 +38,7 @@ TRANS_SLOTS = 4
 # Minimal work of one state update: exp2(delta*A) plus 4 VALU (delta*A, du*B, h fma, y fma).
 SLOTS_PER_UPDATE = 4 + TRANS_SLOTS
 PEAK_UPDATES_PER_S = CUS * CLOCK_HZ * VALU_LANES_PER_CLK / SLOTS_PER_UPDATE  # 9.83e12
+FP32_MFMA_PEAK = 157.3e12  # dense fp32 matrix FLOP/s
 
 KERNEL_SOURCES = sorted(
     os.path.relpath(os.path.join(dp, f), ROOT)
@@ -193,6 +194,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = VMamba-T stage-1")
+    ap.add_argument("--path", choices=["scan", "from_x"], default="scan",
+                    help="scan: the forward from x, dt, Bs, Cs (the headline); from_x: the forward from x and the "
+                         "projection weights (projections on the matrix cores, then the scan)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity")
     ap.add_argument("--lanes", type=int, default=0, help="force lanes per sequence chunk (16/32/64; 0 = auto)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -224,7 +228,8 @@ def main() -> int:
         ss2d.set_lanes_per_seq(args.lanes)
     shape = ss2d_inputs.CONFIGS[args.config]
     print(f"[bench] workload {shape}", file=sys.stderr, flush=True)
-    inp = ss2d_inputs.generate(shape, seed=0)
+    from_x = args.path == "from_x"
+    inp = ss2d_inputs.generate_projected(shape, seed=0) if from_x else ss2d_inputs.generate(shape, seed=0)
     tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
     d = {}
     for k, v in inp.items():
@@ -235,8 +240,14 @@ def main() -> int:
     y = torch.empty((shape.B, shape.D, shape.H, shape.W), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        ss2d.forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], out=y, stream=stream)
+    if from_x:
+        def step():
+            ss2d.forward_from_x(d["x"], d["x_proj_weight"], d["dt_projs_weight"], d["A_log"], d["dt_bias"],
+                                d["Ds"], out=y, stream=stream)
+    else:
+        def step():
+            ss2d.forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], out=y,
+                         stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -272,6 +283,43 @@ def main() -> int:
         flushed = {"steps": args.flush_steps, "median_us": float(np.median(per_us)), "min_us": float(min(per_us)),
                    "flush": "1 GiB fill before each step"}
 
+    proj = None
+    if from_x:
+        # the projections alone (transpose of x + the MFMA projection kernel), into preallocated outputs
+        R = d["dt_projs_weight"].shape[2]
+        C = R + 2 * shape.N
+        pdt = torch.empty((shape.B, 4, shape.D, shape.L), dtype=tdt, device=dev)
+        pB = torch.empty((shape.B, 4, shape.N, shape.L), dtype=tdt, device=dev)
+        pC = torch.empty_like(pB)
+        code = 1 if shape.dtype == "bf16" else 0
+
+        def proj_step():
+            rc = ss2d.ss2d_project(d["x"].data_ptr(), d["x_proj_weight"].data_ptr(), d["dt_projs_weight"].data_ptr(),
+                                   pdt.data_ptr(), pB.data_ptr(), pC.data_ptr(), shape.B, shape.D, shape.H,
+                                   shape.W, shape.N, R, code, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ss2d_project failed: {rc}")
+
+        for _ in range(args.warmup):
+            proj_step()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        p0.record(stream)
+        for _ in range(args.steps):
+            proj_step()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        proj_s = p0.elapsed_time(p1) * 1e-3 / args.steps
+        s_el = shape.elem_bytes
+        flops = 2.0 * shape.B * 4 * shape.L * (C * shape.D + shape.D * R)
+        nbytes = s_el * shape.B * shape.L * (shape.D + 4 * (shape.D + 2 * shape.N)) + 4 * 4 * (C * shape.D + shape.D * R)
+        proj = {"us": proj_s * 1e6, "kernels": "transpose of x + MFMA projection", "R": R,
+                "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                "achieved_TFLOPs": flops / proj_s / 1e12, "frac_fp32_mfma_peak": flops / proj_s / FP32_MFMA_PEAK,
+                "achieved_GBps": nbytes / proj_s / 1e9, "frac_hbm_peak": nbytes / proj_s / 1e9 / HBM_PEAK_GBPS,
+                "bound": "hbm" if nbytes / (HBM_PEAK_GBPS * 1e9) > flops / FP32_MFMA_PEAK else "mfma"}
+        del pdt, pB, pC
+
     peaks = None
     if not args.no_peaks:
         peaks = ss2d.measure_peaks(1 << 30, stream.cuda_stream)
@@ -305,7 +353,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic (seeded numpy PCG64, VMamba-shaped value recipe)",
-        "config": {"workload": shape.name, "B": shape.B, "D": shape.D, "H": shape.H, "W": shape.W,
+        "config": {"workload": shape.name + ("_from_x" if from_x else ""), "path": args.path, "B": shape.B, "D": shape.D, "H": shape.H, "W": shape.W,
                    "N": shape.N, "K": 4, "L": shape.L, "io_dtype": shape.dtype,
                    "plan": ss2d.describe(shape.B, shape.D, shape.H, shape.W, shape.N,
                                          1 if shape.dtype == "bf16" else 0)},
@@ -321,6 +369,9 @@ def main() -> int:
                 "frac_of_peak": hbm_gbps / HBM_PEAK_GBPS, "peak_GBps": HBM_PEAK_GBPS},
         "kernel_us": kernel_s * 1e6,
     }
+    if proj is not None:
+        result["projection"] = proj
+        result["roofline"]["unit"] += "; from_x: the whole path (transpose, projection, scan) per step"
     if flushed is not None:
         flushed["frac_of_roofline_peak"] = updates / (flushed["median_us"] * 1e-6) / PEAK_UPDATES_PER_S
         result["flushed"] = flushed
@@ -342,7 +393,11 @@ def main() -> int:
         x64 = {k: np.ascontiguousarray(v, dtype=np.float64) for k, v in inp.items()}
         threads = oracle.threads()
         t0 = time.perf_counter()
-        ref = oracle.ss2d_f64(**x64)
+        if from_x:
+            from oracle import projection
+            ref = projection.ss2d_from_x_f64(**x64)
+        else:
+            ref = oracle.ss2d_f64(**x64)
         cpu_s = time.perf_counter() - t0
         got = y.double().cpu().numpy()
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
@@ -352,8 +407,9 @@ def main() -> int:
             "unit": "state-updates/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole workload ({shape.B}x{shape.D} planes, {updates:.3e} updates), fp64 C "
-                      f"loops, OpenMP over (b,d) planes; {cpu_s:.2f} s on {cpu_model()}",
+            "sample": f"the whole workload ({shape.B}x{shape.D} planes, {updates:.3e} updates), "
+                      + ("numpy float64 projections (einsum), then " if from_x else "")
+                      + f"fp64 C loops, OpenMP over (b,d) planes; {cpu_s:.2f} s on {cpu_model()}",
         }
         result["parity"] = {"rel_l2": rel, "max_abs": max_abs, "max_abs_y": float(np.max(np.abs(ref))),
                             "vs": "fp64 oracle, whole output"}

@@ -145,8 +145,9 @@ int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dty
   const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
   snprintf(buf, (size_t)len,
            "kernel=chunked_dpp_scan lanes_per_seq=%d steps_per_lane=%d waves=%d chans_per_block=%d "
-           "segments=%d transpose=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu",
-           pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.transpose ? 1 : 0,
+           "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu",
+           pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.xtrans ? 1 : 0,
+           pl.transpose ? 1 : 0,
            (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes);
   return SS2D_OK;
 }
@@ -230,8 +231,6 @@ int check_projection(int64_t D, int64_t N, int64_t R, const float* wx, const flo
 }
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-constexpr bool kScanReadsXT = true;
 
 }  // namespace
 
@@ -346,10 +345,8 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
     a.dtype = dtype;
     a.stream = st;
     a.device = di.device;
-    // the scan's column walks read the transposed copy too (segmented plans
-    // would otherwise make their own)
-    e = ss2d::launch_forward(a, plan, reinterpret_cast<float*>(tmp + o_scan),
-                             (kScanReadsXT || plan.nseg > 1) ? xT : nullptr);
+    // the scan's column walks read the transposed copy made for the projections
+    e = ss2d::launch_forward(a, plan, reinterpret_cast<float*>(tmp + o_scan), xT);
   }
   hipError_t e2 = hipFreeAsync(tmp, st);
   if (e == hipSuccess) e = e2;

@@ -35,8 +35,9 @@ struct Plan {
   size_t lds_bytes;      // LDS per workgroup
   size_t scratch_bytes;  // device temporary: fp32 merge planes, segment maps, transposed copies
   size_t carry_offset;   // byte offset of the segment maps in the temporary
-  bool transpose;        // column walks read a transposed copy of x, the merge a transposed column plane
-  size_t xt_offset;      // byte offsets of those copies in the temporary (transpose only)
+  bool xtrans;           // x is transposed first; column walks read the copy
+  bool transpose;        // the column merge plane is transposed before the last direction (segmented plans)
+  size_t xt_offset;      // byte offsets of those copies in the temporary
   size_t pct_offset;
 };
 

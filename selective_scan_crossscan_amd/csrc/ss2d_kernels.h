@@ -1336,8 +1336,58 @@ __global__ __launch_bounds__(256) void transpose_planes(const S* __restrict__ in
   }
 }
 
+// Whole planes of at most kSmallPlane LDS slots (R rows of C + 1) through LDS: workgroup w
+// transposes planes w, w + gridDim.x, ...  One element per thread and step, so
+// global reads and writes are 256 contiguous bytes per wave (fp32) and the LDS
+// rows, padded to C + 1, are read down a column without bank conflicts.
+constexpr int kSmallPlane = 12288;  // 48 KB
+
+template <typename S>
+__global__ __launch_bounds__(256) void transpose_small(const S* __restrict__ in, S* __restrict__ out, int planes,
+                                                       int R, int C) {
+  extern __shared__ float tile_s[];  // R rows of C + 1
+  const int n = R * C, ld = C + 1;
+  const int tid = threadIdx.x;
+  // (row, column) of element tid of the plane, and of output element tid, and the
+  // steps of both for 256 elements
+  const int r0 = tid / C, c0 = tid - r0 * C, dq = 256 / C, dr = 256 - dq * C;
+  const int oc0 = tid / R, or0 = tid - oc0 * R, oq = 256 / R, orr = 256 - oq * R;
+  for (int64_t pl = blockIdx.x; pl < planes; pl += gridDim.x) {
+    const S* src = in + pl * n;
+    S* dst = out + pl * n;
+    int r = r0, c = c0;
+    for (int i = tid; i < n; i += 256) {
+      tile_s[r * ld + c] = Io<S>::ld(src, i);
+      r += dq;
+      c += dr;
+      if (c >= C) {
+        c -= C;
+        ++r;
+      }
+    }
+    __syncthreads();
+    int oc = oc0, orow = or0;
+    for (int o = tid; o < n; o += 256) {  // output element o = oc * R + orow is input (orow, oc)
+      Io<S>::st(dst, o, tile_s[orow * ld + oc]);
+      oc += oq;
+      orow += orr;
+      if (orow >= R) {
+        orow -= R;
+        ++oc;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename S>
 hipError_t launch_transpose(const S* in, S* out, int planes, int R, int C, hipStream_t stream) {
+  if ((int64_t)R * (C + 1) <= kSmallPlane) {
+    const size_t lds = (size_t)R * (C + 1) * sizeof(float);
+    const int grid = planes < 2048 ? planes : 2048;
+    hipLaunchKernelGGL((transpose_small<S>), dim3((unsigned)grid), dim3(256), lds, stream, in, out, planes, R, C);
+    return hipGetLastError();
+  }
   const int tiles_r = (R + 63) / 64, tiles_c = (C + 63) / 64;
   const int64_t blocks = (int64_t)planes * tiles_r * tiles_c;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -1419,6 +1469,11 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, const Scratch& 
     }
   };
   if (plan.nseg == 1) {
+    if (s.xT && !s.xT_given) {
+      hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(s.xT), (int)(a.B * a.D), p.H,
+                                         p.W, a.stream);
+      if (e != hipSuccess) return e;
+    }
     const void* kf = reinterpret_cast<const void*>(&ss2d_forward_kernel<S, G, T, NG, VEC, kFused>);
     rotation(kf, units);
     hipLaunchKernelGGL((ss2d_forward_kernel<S, G, T, NG, VEC, kFused>), dim3((unsigned)units), dim3(kWaves * 64), 0,

@@ -4,6 +4,10 @@
 
 namespace ss2d {
 
+// Maps from this many pixels on transpose x first (below it the transpose costs
+// more than the gathers it saves: measured on 14x14 and 28x28 maps).
+constexpr int64_t kTransposeXFrom = 2048;
+
 Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override) {
   (void)N;
   Plan pl;
@@ -42,15 +46,21 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   const size_t planes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
   pl.carry_offset = planes;
   pl.scratch_bytes = planes + (pl.nseg > 1 ? (size_t)(B * 4 * D) * pl.nseg * 2 * kMaxN * sizeof(float) : 0);
-  // Segmented plans are for large maps, where a column walk or the merge's column
-  // plane read at stride H or W use one cache line per element and the working set
-  // outgrows L2: they transpose x once, and the column plane before direction 2.
+  // A column walk reading x in place touches one cache line per step and lane;
+  // those gathers load the same L1 path the Bs/Cs copies use.  So on large maps
+  // x is transposed once first and the column walks read the copy.  Segmented
+  // plans (large maps, whose working set outgrows L2) also transpose the column
+  // merge plane before direction 2.
+  pl.xtrans = vec && (pl.nseg > 1 || L >= kTransposeXFrom);
   pl.transpose = pl.nseg > 1;
   pl.xt_offset = pl.pct_offset = 0;
-  if (pl.transpose) {
-    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  if (pl.xtrans) {
     pl.xt_offset = up(pl.scratch_bytes);
-    pl.pct_offset = up(pl.xt_offset + (size_t)(B * D * L) * (dtype == 0 ? 4 : 2));
+    pl.scratch_bytes = pl.xt_offset + (size_t)(B * D * L) * (dtype == 0 ? 4 : 2);
+  }
+  if (pl.transpose) {
+    pl.pct_offset = up(pl.scratch_bytes);
     pl.scratch_bytes = pl.pct_offset + (size_t)(B * D * L) * sizeof(float);
   }
   return pl;
@@ -64,7 +74,7 @@ hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch,
   s.prow = a.dtype == 0 ? static_cast<float*>(a.y) : scratch + plane;
   s.pcol = scratch;
   s.carries = reinterpret_cast<float*>(base + plan.carry_offset);
-  s.xT = xT ? const_cast<void*>(xT) : plan.transpose ? static_cast<void*>(base + plan.xt_offset) : nullptr;
+  s.xT = xT ? const_cast<void*>(xT) : plan.xtrans ? static_cast<void*>(base + plan.xt_offset) : nullptr;
   s.xT_given = xT != nullptr;
   s.pcolT = plan.transpose ? reinterpret_cast<float*>(base + plan.pct_offset) : nullptr;
   const bool t8 = plan.steps_per_lane == 8;

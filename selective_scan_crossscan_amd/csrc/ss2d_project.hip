@@ -12,19 +12,21 @@
 //
 // How it runs.  Directions 0 and 2 visit the pixels in row-major order, 2 in
 // reverse; directions 1 and 3 in column-major order, 3 in reverse.  So one
-// workgroup (one wave) takes 64 consecutive positions of one orientation (row-
-// major from x, column-major from x transposed) and produces the rows of both
-// directions of that orientation: direction 0 (or 1) at those positions, and
-// direction 2 (or 3) at the mirrored positions L-1-l.
+// workgroup takes 64 consecutive positions of one orientation (row-major from x,
+// column-major from x transposed) and produces the rows of both directions of
+// that orientation: direction 0 (or 1) at those positions, and direction 2 (or
+// 3) at the mirrored positions L-1-l.
 //   * The projection is a (2C x D) by (D x 64) product in fp32 on
-//     v_mfma_f32_16x16x4_f32: 2C rows in 16-row tiles, the 64 positions as four
-//     16-column tiles whose column j holds position 4j + t of tile t, so each
-//     lane loads four consecutive positions with one vector load and holds four
-//     consecutive outputs per row for one vector store.  Sixteen channels are
-//     consumed per step: lane group g (lanes 16g..16g+15) feeds channels
-//     4g..4g+3 over four MFMAs, which is one vector load of the weights too.
+//     v_mfma_f32_16x16x4_f32: 2C rows in 16-row tiles dealt to the four waves,
+//     the 64 positions as four 16-column tiles whose column j holds position
+//     4j + t of tile t, so each lane loads four consecutive positions with one
+//     vector load and holds four consecutive outputs per row for one vector
+//     store.  Sixteen channels are consumed per step: lane group g (lanes
+//     16g..16g+15) feeds channels 4g..4g+3 over four MFMAs, which is one vector
+//     load of the weights too.
 //   * The R rows of the rank-R dt input go to LDS; dt = W_dt (D x R) times
-//     them is a second MFMA product with R in steps of four.
+//     them is a second MFMA product with R in steps of four, its 16-channel
+//     blocks dealt to the four waves.
 //   * Every store is a 16-byte (fp32) or 8-byte (bf16) write of four
 //     consecutive scan positions; a wave writes 256 contiguous bytes (fp32) of
 //     each of four rows.
@@ -35,6 +37,7 @@ namespace {
 
 constexpr int kStrip = 64;   // positions per workgroup
 constexpr int kMaxTiles = 8;  // 16-row tiles of the stacked projection rows: 2C <= 128
+constexpr int kMaxRSteps = 16;  // steps of four over R in the dt map (R <= 64 follows from 2C <= 128)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -47,6 +50,7 @@ struct ProjParams {
   void* Bs;          // (B, 4, N, L)
   void* Cs;          // (B, 4, N, L)
   int D, L, N, R, C, strips;
+  int tiles;  // 16-row tiles of the 2C stacked rows
 };
 
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
@@ -55,6 +59,27 @@ __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ float comp(const float4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// An MFMA operand: four values at i..i+3 of a row of length n, and whether they
+// are real (else they count as zero).  VEC: n and i are multiples of 4 and the
+// row is aligned, so the four are all there or all missing; the load then
+// always happens, at a clamped address, with no branch, and the mask is applied
+// where the operand is used: a branch or a select right after each load would
+// make the compiler wait for every load in turn.
+struct Operand {
+  float4 v;
+  bool ok;
+  __device__ __forceinline__ float4 get() const { return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+
+template <typename S, bool VEC>
+__device__ __forceinline__ Operand ld4_operand(const S* row, int i, int n, bool row_ok) {
+  if (VEC) {
+    const bool ok = row_ok && i < n;
+    return Operand{Io<S>::ld4(row, ok ? i : 0), ok};
+  }
+  return Operand{row_ok ? ld4_guarded<S>(row, i, n, false) : make_float4(0.f, 0.f, 0.f, 0.f), true};
 }
 
 // Four consecutive scan positions pos..pos+3 of a row of length L, written in
@@ -75,127 +100,148 @@ __device__ __forceinline__ void put4(S* row, int pos, int L, bool mirror, float4
     if (pos + i < L) Io<S>::st(row, mirror ? L - 1 - (pos + i) : pos + i, comp(v, i));
 }
 
-// MT: 16-row tiles covering the 2C stacked rows.  VEC: L and D are multiples of
-// 4 and the bases are aligned for the vector forms.
-template <typename S, int MT, bool VEC>
-__global__ __launch_bounds__(64) void project_kernel(ProjParams p) {
+// One workgroup of four waves per 64 positions.  The 16-row tiles of the 2C
+// stacked rows are dealt to the waves (wave w takes tiles w and w + 4: MTW is
+// how many a wave may hold); the dt blocks (direction, 16 channels) likewise.
+// VEC: L and D are multiples of 4 and the bases are aligned for the vector forms.
+template <typename S, int MTW, bool VEC>
+__global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
   extern __shared__ __align__(16) float dts[];  // [2][R][kStrip]
-  const int D = p.D, L = p.L, N = p.N, R = p.R, C = p.C;
+  const int D = p.D, L = p.L, N = p.N, R = p.R, C = p.C, MT = p.tiles;
   const int strip = blockIdx.x % p.strips;
   const int rest = blockIdx.x / p.strips;
   const int o = rest & 1;  // orientation: 0 row-major (directions 0, 2), 1 column-major (1, 3)
   const int b = rest >> 1;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, g = lane >> 4;
   const int pos = strip * kStrip + 4 * col;  // this lane's four positions
   const S* src = static_cast<const S*>(o ? p.xT : p.x) + (int64_t)b * D * L;
 
   // A operand rows: stacked row m = mt*16 + col is row c of direction o + 2*kk
-  const float* arow[MT];
-  bool aval[MT];
+  const float* arow[MTW];
+  bool aval[MTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + col;
+  for (int i = 0; i < MTW; ++i) {
+    const int m = (wave + 4 * i) * 16 + col;
     const int kk = m >= C ? 1 : 0;
-    aval[mt] = m < 2 * C;
-    arow[mt] = p.wx + (aval[mt] ? ((int64_t)(o + 2 * kk) * C + (m - kk * C)) * D : 0);
+    aval[i] = m < 2 * C;
+    arow[i] = p.wx + (aval[i] ? ((int64_t)(o + 2 * kk) * C + (m - kk * C)) * D : 0);
   }
+  const bool any = wave < MT;  // this wave holds at least one tile
 
-  f32x4 acc[MT][4];
+  f32x4 acc[MTW][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int d0 = 0; d0 < D; d0 += 16) {
-    const int dg = d0 + 4 * g;  // channels dg..dg+3 of this lane group
-    float4 bv[4];
+  if (any) {
+    // operands of 16 channels: x rows dg..dg+3 at this lane's positions, and the
+    // weights of this lane's rows at channels dg..dg+3 (dg = d0 + 4g); the next
+    // step's are loaded before this step's products
+    Operand bv[4], av[MTW];
+    auto load_step = [&](int d0) {
+      const int dg = d0 + 4 * g;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = dg + j;
-      bv[j] = d < D ? ld4_guarded<S>(src + (int64_t)d * L, pos, L, VEC) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < 4; ++j) {
+        const int d = dg + j;
+        bv[j] = ld4_operand<S, VEC>(src + (int64_t)(d < D ? d : 0) * L, pos, L, d < D);
+      }
+#pragma unroll
+      for (int i = 0; i < MTW; ++i) av[i] = ld4_operand<float, VEC>(arow[i], dg, D, aval[i]);
+    };
+    load_step(0);
+    for (int d0 = 0; d0 < D; d0 += 16) {
+      float4 bc[4], ac[MTW];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bc[j] = bv[j].get();
+#pragma unroll
+      for (int i = 0; i < MTW; ++i) ac[i] = av[i].get();
+      if (d0 + 16 < D) load_step(d0 + 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[i][t] = mfma_16x16x4(comp(ac[i], j), comp(bc[j], t), acc[i][t]);
     }
-    float4 av[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      av[mt] = aval[mt] ? ld4_guarded<float>(arow[mt], dg, D, VEC) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_16x16x4(comp(av[mt], j), comp(bv[j], t), acc[mt][t]);
-  }
 
-  // lane (g, col) holds stacked rows mt*16 + 4g + i at positions pos..pos+3
-  const int64_t bk0 = (int64_t)b * 4 + o;
+    // lane (g, col) holds stacked rows mt*16 + 4g + r at positions pos..pos+3
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+    for (int i = 0; i < MTW; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + 4 * g + i;
-      if (m >= 2 * C) continue;
-      const int kk = m >= C ? 1 : 0;
-      const int c = m - kk * C;
-      const float4 v = make_float4(acc[mt][0][i], acc[mt][1][i], acc[mt][2][i], acc[mt][3][i]);
-      if (c < R) {
-        *reinterpret_cast<float4*>(dts + (kk * R + c) * kStrip + 4 * col) = v;
-      } else {
-        const int64_t bk = bk0 + 2 * kk;
-        S* row = c < R + N ? static_cast<S*>(p.Bs) + (bk * N + (c - R)) * L
-                           : static_cast<S*>(p.Cs) + (bk * N + (c - R - N)) * L;
-        put4<S, VEC>(row, pos, L, kk == 1, v);
+      for (int r = 0; r < 4; ++r) {
+        const int m = (wave + 4 * i) * 16 + 4 * g + r;
+        if (m >= 2 * C) continue;
+        const int kk = m >= C ? 1 : 0;
+        const int c = m - kk * C;
+        const float4 v = make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
+        if (c < R) {
+          *reinterpret_cast<float4*>(dts + (kk * R + c) * kStrip + 4 * col) = v;
+        } else {
+          const int64_t bk = (int64_t)b * 4 + o + 2 * kk;
+          S* row = c < R + N ? static_cast<S*>(p.Bs) + (bk * N + (c - R)) * L
+                             : static_cast<S*>(p.Cs) + (bk * N + (c - R - N)) * L;
+          put4<S, VEC>(row, pos, L, kk == 1, v);
+        }
       }
     }
   }
   __syncthreads();
 
-  // dt = W_dt (D x R) times the R rows, per direction, 16 channels at a time
-  for (int kk = 0; kk < 2; ++kk) {
-    const int k = o + 2 * kk;
-    const float* wk = p.wdt + (int64_t)k * D * R;
-    S* dtk = static_cast<S*>(p.dt) + (bk0 + 2 * kk) * D * L;
-    for (int dm = 0; dm < D; dm += 16) {
-      f32x4 c4[4];
+  // dt = W_dt (D x R) times the R rows, per direction, 16 channels at a time.
+  // Block jb of the 2 * nd (direction, 16 channels) blocks goes to wave jb % 4;
+  // per lane it needs W_dt[k, 16m + col, 4q + g] for the R steps q, and the
+  // wave's next block's are loaded before this block's products.
+  const int nd = (D + 15) / 16, nrq = (R + 3) / 4, nblk = 2 * nd;
+  float an[kMaxRSteps] = {};
+  auto load_a = [&](int jb) {
+    const int kk = jb >= nd ? 1 : 0;
+    const int da = (jb - kk * nd) * 16 + col;
+    const float* wrow = p.wdt + ((int64_t)(o + 2 * kk) * D + (da < D ? da : 0)) * R;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) c4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int da = dm + col;
-      for (int r0 = 0; r0 < R; r0 += 4) {
-        const int r = r0 + g;
-        const float a = (r < R && da < D) ? wk[(int64_t)da * R + r] : 0.f;
-        const float4 q = r < R ? *reinterpret_cast<const float4*>(dts + (kk * R + r) * kStrip + 4 * col)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < kMaxRSteps; ++q) {
+      const int r = 4 * q + g;
+      if (q < nrq) an[q] = (r < R && da < D) ? wrow[r] : 0.f;
+    }
+  };
+  if (wave < nblk) load_a(wave);
+  for (int jb = wave; jb < nblk; jb += 4) {
+    const int kk = jb >= nd ? 1 : 0;
+    const int dm = (jb - kk * nd) * 16;
+    float ac[kMaxRSteps];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) c4[t] = mfma_16x16x4(a, comp(q, t), c4[t]);
-      }
+    for (int q = 0; q < kMaxRSteps; ++q) ac[q] = an[q];
+    if (jb + 4 < nblk) load_a(jb + 4);
+    f32x4 c4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = dm + 4 * g + i;
-        if (d < D) put4<S, VEC>(dtk + (int64_t)d * L, pos, L, kk == 1, make_float4(c4[0][i], c4[1][i], c4[2][i], c4[3][i]));
-      }
+    for (int t = 0; t < 4; ++t) c4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < kMaxRSteps; ++q) {
+      if (q >= nrq) continue;
+      const int r = 4 * q + g;
+      const float4 v = r < R ? *reinterpret_cast<const float4*>(dts + (kk * R + r) * kStrip + 4 * col)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) c4[t] = mfma_16x16x4(ac[q], comp(v, t), c4[t]);
+    }
+    S* dtk = static_cast<S*>(p.dt) + ((int64_t)b * 4 + o + 2 * kk) * D * L;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = dm + 4 * g + i;
+      if (d < D)
+        put4<S, VEC>(dtk + (int64_t)d * L, pos, L, kk == 1, make_float4(c4[0][i], c4[1][i], c4[2][i], c4[3][i]));
     }
   }
 }
 
 template <typename S, bool VEC>
-hipError_t launch_tiles(const ProjParams& p, int tiles, unsigned blocks, size_t lds, hipStream_t stream) {
-  switch (tiles) {
-#define SS2D_PROJ_CASE(T_)                                                                               \
-  case T_:                                                                                               \
-    hipLaunchKernelGGL((project_kernel<S, T_, VEC>), dim3(blocks), dim3(64), lds, stream, p);            \
-    return hipGetLastError();
-    SS2D_PROJ_CASE(1)
-    SS2D_PROJ_CASE(2)
-    SS2D_PROJ_CASE(3)
-    SS2D_PROJ_CASE(4)
-    SS2D_PROJ_CASE(5)
-    SS2D_PROJ_CASE(6)
-    SS2D_PROJ_CASE(7)
-    SS2D_PROJ_CASE(8)
-#undef SS2D_PROJ_CASE
-    default:
-      return hipErrorInvalidValue;
-  }
+hipError_t launch_tiles(const ProjParams& p, unsigned blocks, size_t lds, hipStream_t stream) {
+  if (p.tiles <= 4)
+    hipLaunchKernelGGL((project_kernel<S, 1, VEC>), dim3(blocks), dim3(256), lds, stream, p);
+  else
+    hipLaunchKernelGGL((project_kernel<S, 2, VEC>), dim3(blocks), dim3(256), lds, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -226,8 +272,8 @@ hipError_t launch_project(const ProjectArgs& a) {
   p.R = (int)a.R;
   p.C = (int)(a.R + 2 * a.N);
   p.strips = (p.L + kStrip - 1) / kStrip;
-  const int tiles = (2 * p.C + 15) / 16;
-  if (tiles > kMaxTiles) return hipErrorInvalidValue;
+  p.tiles = (2 * p.C + 15) / 16;
+  if (p.tiles > kMaxTiles) return hipErrorInvalidValue;
   const int64_t blocks = a.B * 2 * p.strips;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const size_t lds = (size_t)2 * p.R * kStrip * sizeof(float);
@@ -236,10 +282,10 @@ hipError_t launch_project(const ProjectArgs& a) {
                    !((uintptr_t)a.dt & am) && !((uintptr_t)a.Bs & am) && !((uintptr_t)a.Cs & am) &&
                    !((uintptr_t)a.wx & 15);
   if (a.dtype == 0)
-    return vec ? launch_tiles<float, true>(p, tiles, (unsigned)blocks, lds, a.stream)
-               : launch_tiles<float, false>(p, tiles, (unsigned)blocks, lds, a.stream);
-  return vec ? launch_tiles<uint16_t, true>(p, tiles, (unsigned)blocks, lds, a.stream)
-             : launch_tiles<uint16_t, false>(p, tiles, (unsigned)blocks, lds, a.stream);
+    return vec ? launch_tiles<float, true>(p, (unsigned)blocks, lds, a.stream)
+               : launch_tiles<float, false>(p, (unsigned)blocks, lds, a.stream);
+  return vec ? launch_tiles<uint16_t, true>(p, (unsigned)blocks, lds, a.stream)
+             : launch_tiles<uint16_t, false>(p, (unsigned)blocks, lds, a.stream);
 }
 
 }  // namespace ss2d

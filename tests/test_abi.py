@@ -44,12 +44,16 @@ def test_version_and_strings():
 def test_describe_plans_the_workloads():
     s = ss2d.describe(32, 192, 56, 56, 16, ss2d.SS2D_F32)
     assert "lanes_per_seq=32" in s and "chans_per_block=8" in s and "blocks=768" in s
-    assert f"scratch_bytes={32 * 192 * 3136 * 4}" in s
+    # the fp32 column plane, then x transposed
+    assert f"scratch_bytes={2 * 32 * 192 * 3136 * 4}" in s and "x_transposed=1 plane_transposed=0" in s
+    # small maps gather x in place
     s = ss2d.describe(64, 384, 28, 28, 16, ss2d.SS2D_BF16)
-    assert f"scratch_bytes={2 * 64 * 384 * 784 * 4}" in s
+    assert f"scratch_bytes={2 * 64 * 384 * 784 * 4}" in s and "x_transposed=0" in s
     s = ss2d.describe(32, 768, 14, 14, 16, ss2d.SS2D_F32)
     assert "lanes_per_seq=16" in s and "chans_per_block=16" in s
-    assert "transpose=0" in s
+    assert "segments=1 x_transposed=0 plane_transposed=0" in s
+    # rows that are not 16-byte aligned keep x in place
+    assert "x_transposed=0" in ss2d.describe(2, 16, 5, 7, 16, ss2d.SS2D_F32)
 
 
 def test_describe_segmented_plan_includes_transposed_copies():
@@ -59,7 +63,7 @@ def test_describe_segmented_plan_includes_transposed_copies():
     s = ss2d.describe(B, D, 256, 256, 16, ss2d.SS2D_F32)
     fields = dict(kv.split("=") for kv in s.split())
     nseg = int(fields["segments"])
-    assert nseg > 1 and fields["transpose"] == "1"
+    assert nseg > 1 and fields["x_transposed"] == "1" and fields["plane_transposed"] == "1"
     up = lambda v: (v + 255) // 256 * 256
     base = B * D * L * 4 + B * 4 * D * nseg * 2 * 16 * 4
     xt = up(base)

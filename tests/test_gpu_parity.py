@@ -145,6 +145,11 @@ EDGE = [
     # column walks whose lane steps cross more than one column (H < steps per lane)
     (1, 3, 8, 64, 16, "f32"),     # H = 8 < 16, full chunks
     (1, 3, 12, 48, 16, "bf16"),   # H = 12 < 16, full chunks + prefetched remainder
+    # one launch after a transpose of x: column walks read the transposed copy
+    (2, 24, 40, 64, 16, "f32"),   # 2560 steps, whole chunks
+    (1, 8, 64, 33, 16, "bf16"),   # 2112 steps: a 64-step prefetched remainder
+    (3, 9, 45, 48, 7, "f32"),     # D past the channel block, odd N, ragged remainder
+    (1, 4, 8, 264, 16, "f32"),    # H = 8: a lane's steps span columns of the copy
 ]
 
 
