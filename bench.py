@@ -46,6 +46,8 @@ KERNEL_SOURCES = sorted(
     for f in fs if f.endswith((".hip", ".h")))
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
+# Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
+STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel"}
 
 
 def traffic_file(workload: str) -> str:
@@ -134,6 +136,7 @@ def summarize_profile(folder: str, cfg: int) -> int:
              "Command (from the repository root):", "", "```", cmds["stats"], "```", "",
              "| kernel | calls | average µs | min µs | max µs | share |", "|---|---|---|---|---|---|"]
     kern_avg = None
+    launches, step_ns = 0, 0.0
     for r in stats:
         name = r["Name"]
         if len(name) > 90:
@@ -141,11 +144,17 @@ def summarize_profile(folder: str, cfg: int) -> int:
         avg = float(r["AverageNs"]) / 1e3
         if KERNEL_PREFIX in r["Name"]:
             kern_avg = avg
+            launches = int(r["Calls"])
+        if any(f"::{k}<" in r["Name"] for k in STEP_KERNELS):
+            step_ns += float(r["TotalDurationNs"])
         lines.append(f"| `{name}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    per_step = step_ns / 1e3 / launches if launches else float("nan")
     lines += ["", f"bench.py's own HIP-event average over the timed steps of this run: "
-                  f"{bench['kernel_us']:.1f} µs per launch (roofline frac {bench['roofline']['frac']:.3f}).",
-              f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs.", "",
+                  f"{bench['kernel_us']:.1f} µs per step (roofline frac {bench['roofline']['frac']:.3f}).",
+              f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs for the scan kernel; "
+              f"{per_step:.1f} µs per step with the other kernels of a forward "
+              f"({', '.join(sorted(STEP_KERNELS))}).", "",
               "Bench line of this run:", "", "```json", bench_line, "```", ""]
     with open(os.path.join(PROFILES, f"ss2d_forward_kernel_{shape.name}_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines))
@@ -184,7 +193,8 @@ def summarize_profile(folder: str, cfg: int) -> int:
               "```json", json.dumps(rec, indent=1), "```", ""]
     with open(traffic_file(shape.name), "w") as f:
         f.write("\n".join(lines))
-    print(f"wrote profiles for {shape.name}: kernel avg {kern_avg:.1f} us, traffic {(fetch_b + write_b) / 1e6:.1f} MB")
+    print(f"wrote profiles for {shape.name}: scan kernel avg {kern_avg:.1f} us, step {per_step:.1f} us, "
+          f"traffic {(fetch_b + write_b) / 1e6:.1f} MB")
     return 0
 
 
@@ -332,6 +342,12 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
+    plan = dict(kv.split("=") for kv in ss2d.describe(shape.B, shape.D, shape.H, shape.W, shape.N,
+                                                       1 if shape.dtype == "bf16" else 0).split())
+    nseg = int(plan["segments"])
+    launches = int(plan["x_transposed"]) + (1 if nseg == 1 else 5 + int(plan["plane_transposed"]))
+    if from_x:
+        launches += 1 + (1 - int(plan["x_transposed"]))  # the projection, and its own transpose of x
     ms_per_step = wall * 1e3 / args.steps
     kernel_s = ev_ms * 1e-3 / args.steps  # one kernel launch per step, same stream
     updates = shape.updates
@@ -364,6 +380,9 @@ def main() -> int:
             "unit": "Gupdates/s (1 exp2 + 4 fp32 VALU per update = 8 of 128 issue slots/clk/CU)",
             "frac": achieved / PEAK_UPDATES_PER_S,
             "traffic": traffic,
+            "timed": f"HIP events around each step on the launch stream: {launches} launch(es) "
+                     "(the scan kernel, after a transpose of x on maps of 2048+ pixels; traffic is the scan "
+                     "kernel's own)",
         },
         "hbm": {"algorithmic_bytes": shape.algorithmic_bytes, "achieved_GBps": hbm_gbps,
                 "frac_of_peak": hbm_gbps / HBM_PEAK_GBPS, "peak_GBps": HBM_PEAK_GBPS},

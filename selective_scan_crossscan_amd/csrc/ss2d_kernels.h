@@ -1355,18 +1355,29 @@ __global__ __launch_bounds__(256) void transpose_small(const S* __restrict__ in,
   for (int64_t pl = blockIdx.x; pl < planes; pl += gridDim.x) {
     const S* src = in + pl * n;
     S* dst = out + pl * n;
+    // eight loads in flight per thread before any is written to LDS
     int r = r0, c = c0;
-    for (int i = tid; i < n; i += 256) {
-      tile_s[r * ld + c] = Io<S>::ld(src, i);
-      r += dq;
-      c += dr;
-      if (c >= C) {
-        c -= C;
-        ++r;
+    for (int i0 = tid; i0 < n; i0 += 8 * 256) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256;
+        v[u] = i < n ? Io<S>::ld(src, i) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u * 256 < n) tile_s[r * ld + c] = v[u];
+        r += dq;
+        c += dr;
+        if (c >= C) {
+          c -= C;
+          ++r;
+        }
       }
     }
     __syncthreads();
     int oc = oc0, orow = or0;
+#pragma unroll 4
     for (int o = tid; o < n; o += 256) {  // output element o = oc * R + orow is input (orow, oc)
       Io<S>::st(dst, o, tile_s[orow * ld + oc]);
       oc += oq;
