@@ -50,8 +50,8 @@ KERNEL_PREFIX = "ss2d_forward_kernel"
 STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel"}
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"ss2d_forward_kernel_{workload}_hbm_traffic.md")
+def traffic_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.md")
 
 
 def kernel_source_hash() -> str:
@@ -92,12 +92,12 @@ def cpu_model() -> str:
 # Each runs from the repository root; {d} is the output folder and {c} the workload index.
 PROFILE_COMMANDS = {
     "stats": "rocprofv3 --kernel-trace --stats -f csv -d {d} -o stats -- "
-             "python bench.py --config {c} --steps 20 --warmup 5 --no-cpu-baseline > {d}/stats_bench.json",
+             "python bench.py --config {c}{x} --steps 20 --warmup 5 --no-cpu-baseline > {d}/stats_bench.json",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d} -o fetch -- "
-             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks "
+             "python bench.py --config {c}{x} --steps 3 --warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks "
              "--copy-probe-mib 512",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d} -o write -- "
-             "python bench.py --config {c} --steps 3 --warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks "
+             "python bench.py --config {c}{x} --steps 3 --warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks "
              "--copy-probe-mib 512",
 }
 COPY_PROBE_MIB = 512
@@ -117,12 +117,17 @@ def _counter_rows(folder: str, prefix: str):
         return list(csv.DictReader(f))
 
 
-def summarize_profile(folder: str, cfg: int) -> int:
-    """Write the rocprofv3 summaries of one workload into profiles/ (text only)."""
+def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
+    """Write the rocprofv3 summaries of one workload into profiles/ (text only).
+    path "scan": the scan kernel of the forward; "from_x": the projection kernel of
+    the forward from x and the projection weights."""
     import csv
     shape = ss2d_inputs.CONFIGS[cfg]
     os.makedirs(PROFILES, exist_ok=True)
-    cmds = {k: v.format(d=folder, c=cfg) for k, v in PROFILE_COMMANDS.items()}
+    from_x = path == "from_x"
+    kernel = "project_kernel" if from_x else KERNEL_PREFIX
+    workload = shape.name + ("_from_x" if from_x else "")
+    cmds = {k: v.format(d=folder, c=cfg, x=" --path from_x" if from_x else "") for k, v in PROFILE_COMMANDS.items()}
 
     # Kernel-trace statistics, next to the bench line printed by the same run.
     with open(_find(folder, "stats_kernel_stats.csv")) as f:
@@ -130,52 +135,64 @@ def summarize_profile(folder: str, cfg: int) -> int:
     with open(os.path.join(folder, "stats_bench.json")) as f:
         bench_line = [ln for ln in f.read().splitlines() if ln.startswith("{")][-1]
     bench = json.loads(bench_line)
-    lines = [f"# ss2d_forward_kernel — {shape.name} — rocprofv3 kernel trace", "",
-             f"Workload: {shape}.  Updates per launch: {shape.updates:.4e}; "
-             f"algorithmic bytes per launch: {shape.algorithmic_bytes:.4e}.", "",
+    if from_x:
+        alg_bytes, alg_flops = projection_work(shape)
+        work = (f"Projection per launch: {alg_flops:.4e} FLOP (fp32 MFMA), algorithmic bytes {alg_bytes:.4e} "
+                "(x read once; dt, Bs, Cs written once; weights).")
+    else:
+        alg_bytes = shape.algorithmic_bytes
+        work = f"Updates per launch: {shape.updates:.4e}; algorithmic bytes per launch: {alg_bytes:.4e}."
+    lines = [f"# {kernel} — {workload} — rocprofv3 kernel trace", "", f"Workload: {shape}.  {work}", "",
              "Command (from the repository root):", "", "```", cmds["stats"], "```", "",
              "| kernel | calls | average µs | min µs | max µs | share |", "|---|---|---|---|---|---|"]
     kern_avg = None
-    launches, step_ns = 0, 0.0
+    per_step = 0.0  # fused plans launch each of a forward's kernels once per step
     for r in stats:
         name = r["Name"]
         if len(name) > 90:
             name = name[:87] + "..."
         avg = float(r["AverageNs"]) / 1e3
-        if KERNEL_PREFIX in r["Name"]:
+        if f"::{kernel}<" in r["Name"]:
             kern_avg = avg
-            launches = int(r["Calls"])
         if any(f"::{k}<" in r["Name"] for k in STEP_KERNELS):
-            step_ns += float(r["TotalDurationNs"])
+            per_step += avg
         lines.append(f"| `{name}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-    per_step = step_ns / 1e3 / launches if launches else float("nan")
     lines += ["", f"bench.py's own HIP-event average over the timed steps of this run: "
                   f"{bench['kernel_us']:.1f} µs per step (roofline frac {bench['roofline']['frac']:.3f}).",
-              f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs for the scan kernel; "
-              f"{per_step:.1f} µs per step with the other kernels of a forward "
-              f"({', '.join(sorted(STEP_KERNELS))}).", "",
-              "Bench line of this run:", "", "```json", bench_line, "```", ""]
-    with open(os.path.join(PROFILES, f"ss2d_forward_kernel_{shape.name}_kernel_stats.md"), "w") as f:
+              f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs for {kernel}; "
+              f"{per_step:.1f} µs per step as the sum of the averages of the kernels a forward launches once "
+              f"each ({', '.join(sorted(STEP_KERNELS))}, where present).", ""]
+    if from_x:
+        pj = bench["projection"]
+        lines += [f"The projection alone, timed by bench.py with HIP events (transpose of x + {kernel}): "
+                  f"{pj['us']:.1f} µs; {kernel} by rocprofv3: {kern_avg:.1f} µs, i.e. "
+                  f"{alg_flops / (kern_avg * 1e-6) / 1e12:.1f} TFLOP/s "
+                  f"({alg_flops / (kern_avg * 1e-6) / FP32_MFMA_PEAK:.3f} of the fp32 MFMA peak) and "
+                  f"{alg_bytes / (kern_avg * 1e-6) / 1e9:.0f} GB/s of algorithmic bytes "
+                  f"({alg_bytes / (kern_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s).", ""]
+    lines += ["Bench line of this run:", "", "```json", bench_line, "```", ""]
+    with open(os.path.join(PROFILES, f"{kernel}_{workload}_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines))
 
-    # HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), calibrated on a plain device copy.
+    # HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), calibrated on a plain device copy
+    # (the runtime's copy kernel; the largest of its dispatches is the probe).
     per = {}
     for counter, prefix in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = [r for r in _counter_rows(folder, prefix) if r["Counter_Name"] == counter]
-        kern = [float(r["Counter_Value"]) for r in rows if KERNEL_PREFIX in r["Kernel_Name"]]
-        other = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if KERNEL_PREFIX not in r["Kernel_Name"]]
-        probe_kib, probe_name = max(other)
+        kern = [float(r["Counter_Value"]) for r in rows if f"::{kernel}<" in r["Kernel_Name"]]
+        copies = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        probe_kib, probe_name = max(copies)
         expected_kib = COPY_PROBE_MIB * 1024.0
         per[counter] = {"kernel_kib_per_dispatch": sum(kern) / len(kern), "dispatches": len(kern),
                         "copy_probe_kib": probe_kib, "copy_probe_kernel": probe_name,
                         "copy_expected_kib": expected_kib, "scale": expected_kib / probe_kib}
     fetch_b = per["FETCH_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["FETCH_SIZE"]["scale"]
     write_b = per["WRITE_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["WRITE_SIZE"]["scale"]
-    rec = {"workload": shape.name, "kernel_source_hash": kernel_source_hash(),
+    rec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(),
            "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
-           "algorithmic_bytes": shape.algorithmic_bytes, "counters": per}
-    lines = [f"# ss2d_forward_kernel — {shape.name} — HBM traffic (rocprofv3 counters)", "",
+           "algorithmic_bytes": alg_bytes, "counters": per}
+    lines = [f"# {kernel} — {workload} — HBM traffic (rocprofv3 counters)", "",
              "Two counter runs, one counter each, from the repository root:", "", "```", cmds["fetch"],
              cmds["write"], "```", "",
              f"Each run also performs one {COPY_PROBE_MIB} MiB device-to-device copy; the scale factor is the "
@@ -187,15 +204,26 @@ def summarize_profile(folder: str, cfg: int) -> int:
         lines.append(f"| {counter} | {c['kernel_kib_per_dispatch']:.0f} | {c['copy_probe_kib']:.0f} | "
                      f"{c['copy_expected_kib']:.0f} | {c['scale']:.4f} | {b / 1e6:.1f} MB |")
     lines += ["", f"HBM traffic per launch: {(fetch_b + write_b) / 1e6:.1f} MB against "
-                  f"{shape.algorithmic_bytes / 1e6:.1f} MB algorithmic "
-                  f"(ratio {(fetch_b + write_b) / shape.algorithmic_bytes:.2f}).", "",
+                  f"{alg_bytes / 1e6:.1f} MB algorithmic "
+                  f"(ratio {(fetch_b + write_b) / alg_bytes:.2f}).", "",
               "Record read by bench.py (valid only while the kernel sources hash to the value below):", "",
               "```json", json.dumps(rec, indent=1), "```", ""]
-    with open(traffic_file(shape.name), "w") as f:
+    with open(traffic_file(workload, kernel), "w") as f:
         f.write("\n".join(lines))
-    print(f"wrote profiles for {shape.name}: scan kernel avg {kern_avg:.1f} us, step {per_step:.1f} us, "
+    print(f"wrote profiles for {workload}: {kernel} avg {kern_avg:.1f} us, step {per_step:.1f} us, "
           f"traffic {(fetch_b + write_b) / 1e6:.1f} MB")
     return 0
+
+
+def projection_work(shape, R=None):
+    """Algorithmic bytes and FLOP of the projections of one forward: x read once, dt, Bs, Cs
+    written once (storage type), fp32 weights; 2 FLOP per multiply-add of x_proj and the dt map."""
+    R = ss2d_inputs.default_rank(shape.D) if R is None else R
+    C = R + 2 * shape.N
+    flops = 2.0 * shape.B * 4 * shape.L * (C * shape.D + shape.D * R)
+    nbytes = (shape.elem_bytes * shape.B * shape.L * (shape.D + 4 * (shape.D + 2 * shape.N))
+              + 4 * 4 * (C * shape.D + shape.D * R))
+    return nbytes, flops
 
 
 def main() -> int:
@@ -218,7 +246,7 @@ def main() -> int:
                     help="turn the rocprofv3 output of PROFILE_COMMANDS in DIR into the summaries under profiles/")
     args = ap.parse_args()
     if args.summarize_profile:
-        return summarize_profile(args.summarize_profile, args.config)
+        return summarize_profile(args.summarize_profile, args.config, args.path)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -320,9 +348,7 @@ def main() -> int:
         p1.record(stream)
         torch.cuda.synchronize()
         proj_s = p0.elapsed_time(p1) * 1e-3 / args.steps
-        s_el = shape.elem_bytes
-        flops = 2.0 * shape.B * 4 * shape.L * (C * shape.D + shape.D * R)
-        nbytes = s_el * shape.B * shape.L * (shape.D + 4 * (shape.D + 2 * shape.N)) + 4 * 4 * (C * shape.D + shape.D * R)
+        nbytes, flops = projection_work(shape, R)
         proj = {"us": proj_s * 1e6, "kernels": "transpose of x + MFMA projection", "R": R,
                 "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                 "achieved_TFLOPs": flops / proj_s / 1e12, "frac_fp32_mfma_peak": flops / proj_s / FP32_MFMA_PEAK,
