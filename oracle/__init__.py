@@ -16,6 +16,9 @@ Three independent formulations of the scan, and the projections, live here:
                         the split into dts/Bs/Cs, the rank-R dt map) in numpy
                         float64, and the forward from the feature map and
                         the projection weights built on them.
+  * `epilogue`      -- the channel-last transpose after the merge and a
+                        LayerNorm over the channels of each pixel, in numpy
+                        float64.
 Pages: [SS2D] "深入解析VMamba中的SS2D模块从理论到代码实现" §3.1-§4.
 """
 from __future__ import annotations
