@@ -242,6 +242,8 @@ def main() -> int:
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="extra steps timed one by one with a 1 GiB fill between them (0 = skip)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device roofline probes")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="also time the channel-last LayerNorm epilogue on the forward's output")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="turn the rocprofv3 output of PROFILE_COMMANDS in DIR into the summaries under profiles/")
     args = ap.parse_args()
@@ -356,6 +358,27 @@ def main() -> int:
                 "bound": "hbm" if nbytes / (HBM_PEAK_GBPS * 1e9) > flops / FP32_MFMA_PEAK else "mfma"}
         del pdt, pB, pC
 
+    epi = None
+    if args.epilogue:
+        gamma = torch.linspace(0.5, 1.5, shape.D, device=dev)
+        beta = torch.linspace(-0.1, 0.1, shape.D, device=dev)
+        eout = torch.empty((shape.B, shape.H, shape.W, shape.D), dtype=tdt, device=dev)
+        for _ in range(args.warmup):
+            ss2d.channel_last(y, gamma, beta, out=eout, stream=stream)
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        q0.record(stream)
+        for _ in range(args.steps):
+            ss2d.channel_last(y, gamma, beta, out=eout, stream=stream)
+        q1.record(stream)
+        torch.cuda.synchronize()
+        epi_s = q0.elapsed_time(q1) * 1e-3 / args.steps
+        ebytes = 2 * shape.elem_bytes * shape.B * shape.D * shape.L + 8 * shape.D
+        epi = {"us": epi_s * 1e6, "kernel": "channel_last_kernel (LayerNorm over D, channel-last out)",
+               "algorithmic_bytes": ebytes, "achieved_GBps": ebytes / epi_s / 1e9,
+               "frac_hbm_peak": ebytes / epi_s / 1e9 / HBM_PEAK_GBPS, "bound": "hbm"}
+        del eout
+
     peaks = None
     if not args.no_peaks:
         peaks = ss2d.measure_peaks(1 << 30, stream.cuda_stream)
@@ -414,6 +437,8 @@ def main() -> int:
                 "frac_of_peak": hbm_gbps / HBM_PEAK_GBPS, "peak_GBps": HBM_PEAK_GBPS},
         "kernel_us": kernel_s * 1e6,
     }
+    if epi is not None:
+        result["epilogue"] = epi
     if proj is not None:
         result["projection"] = proj
         result["roofline"]["unit"] += "; from_x: the whole path (transpose, projection, scan) per step"

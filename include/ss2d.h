@@ -130,6 +130,27 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
                         int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R,
                         int dtype, void* stream);
 
+/*
+ * ss2d_channel_last -- enqueue the step after the merge on `stream`: y in
+ * channel-first layout to channel-last, optionally normalised over its channels.
+ * Page [SS2D] "深入解析VMamba中的SS2D模块从理论到代码实现" §3.3 (the merged y is
+ * transposed to (B, H, W, D)); [VSSD] §5.3 (fusing the LayerNorm that follows).
+ *   y      [B, D, H, W]   dtype  device memory, read only.
+ *   gamma  [D]            fp32   per-channel scale, or NULL for 1.
+ *   beta   [D]            fp32   per-channel shift, or NULL for 0.
+ *   out    [B, H, W, D]   dtype  fully overwritten; must not overlap y, gamma or
+ *                                beta (SS2D_ERR_ALIAS).
+ * normalize = 0: out[b,h,w,d] = y[b,d,h,w] (gamma, beta and eps unused).
+ * normalize = 1: with m and v the mean and the biased variance of the D values
+ *   y[b,:,h,w], out[b,h,w,d] = (y[b,d,h,w] - m) / sqrt(v + eps) * gamma[d] + beta[d],
+ *   statistics in fp32; bf16 output is rounded once.  eps must be >= 0 and finite.
+ * D may be at most 4096 and normalize must be 0 or 1 (SS2D_ERR_SHAPE otherwise;
+ * a bad eps is SS2D_ERR_SHAPE too).  One kernel on `stream`, no temporary.
+ * Validation, error reporting and thread safety as for ss2d_forward.
+ */
+int ss2d_channel_last(const void* y, const float* gamma, const float* beta, float eps, int normalize,
+                      void* out, int64_t B, int64_t D, int64_t H, int64_t W, int dtype, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ss2d_status_string(int status);
 

@@ -12,7 +12,7 @@ import os
 import threading
 
 __all__ = ["forward", "ss2d_forward", "project", "ss2d_project", "forward_from_x", "ss2d_forward_from_x",
-           "measure_peaks", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
+           "channel_last", "ss2d_channel_last", "measure_peaks", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
            "SS2D_F32", "SS2D_BF16", "SS2DError"]
 
 SS2D_F32 = 0
@@ -68,6 +68,9 @@ def lib():
             L.ss2d_project.restype = ctypes.c_int
             L.ss2d_forward_from_x.argtypes = [vp] * 7 + [i64] * 6 + [ctypes.c_int, vp]
             L.ss2d_forward_from_x.restype = ctypes.c_int
+            L.ss2d_channel_last.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_int, vp] + [i64] * 4 + [
+                ctypes.c_int, vp]
+            L.ss2d_channel_last.restype = ctypes.c_int
             L.ss2d_measure_peaks.argtypes = [ctypes.POINTER(Peaks), i64, vp]
             L.ss2d_measure_peaks.restype = ctypes.c_int
             _lib = L
@@ -203,6 +206,41 @@ def forward_from_x(x, x_proj_weight, dt_projs_weight, A_log, dt_bias, Ds, out=No
         rc = ss2d_forward_from_x(x.data_ptr(), x_proj_weight.data_ptr(), dt_projs_weight.data_ptr(),
                                  A_log.data_ptr(), dt_bias.data_ptr(), Ds.data_ptr(), out.data_ptr(),
                                  B, D, H, W, N, R, code, stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+def ss2d_channel_last(y, gamma, beta, eps, normalize, out, B, D, H, W, dtype, stream) -> int:
+    """Raw C-ABI call with integer device addresses; returns the status code."""
+    return lib().ss2d_channel_last(y, gamma, beta, float(eps), int(normalize), out, B, D, H, W, int(dtype), stream)
+
+
+def channel_last(y, gamma=None, beta=None, eps: float = 1e-5, normalize: bool = True, out=None, stream=None):
+    """y (B,D,H,W) -> (B,H,W,D), LayerNorm over D per pixel when `normalize` (ss2d_channel_last).
+
+    gamma, beta: (D,) float32 or None (scale 1, shift 0).  Returns the channel-last tensor in y's dtype.
+    """
+    import torch
+
+    code = _dtype_code(y)
+    if y.dim() != 4:
+        raise ValueError("y must be (B, D, H, W)")
+    B, D, H, W = y.shape
+    for v in (gamma, beta):
+        if v is not None and tuple(v.shape) != (D,):
+            raise ValueError("gamma and beta must be (D,)")
+    if out is None:
+        out = torch.empty((B, H, W, D), dtype=y.dtype, device=y.device)
+    elif tuple(out.shape) != (B, H, W, D) or out.dtype != y.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (B,H,W,D) tensor of y's dtype")
+    _check_tensors(y, (y, out), tuple(v for v in (gamma, beta) if v is not None))
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device)
+    with torch.cuda.device(y.device):
+        rc = ss2d_channel_last(y.data_ptr(), gamma.data_ptr() if gamma is not None else None,
+                               beta.data_ptr() if beta is not None else None, eps, 1 if normalize else 0,
+                               out.data_ptr(), B, D, H, W, code, stream.cuda_stream)
     if rc != 0:
         _raise(rc)
     return out

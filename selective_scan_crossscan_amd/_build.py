@@ -14,7 +14,8 @@ LIB = os.path.join(PKG, "libss2d.so")
 # The kernel templates (ss2d_kernels.h) are instantiated in one unit per storage
 # type and steps per lane, compiled in parallel.
 SOURCES = ["ss2d_api.hip", "ss2d_plan.hip", "ss2d_f32_t16.hip", "ss2d_f32_t8.hip", "ss2d_bf16_t16.hip",
-           "ss2d_bf16_t8.hip", "ss2d_peaks.hip", "ss2d_project.hip"]
+           "ss2d_bf16_t8.hip", "ss2d_peaks.hip", "ss2d_project.hip",
+           "ss2d_epilogue.hip"]
 
 # -packed-fp32-ops: no packed FP32 instructions are generated (plain VALU only).
 HIPCC_FLAGS = [

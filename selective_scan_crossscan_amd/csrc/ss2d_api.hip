@@ -357,4 +357,32 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
   return SS2D_OK;
 }
 
+int ss2d_channel_last(const void* y, const float* gamma, const float* beta, float eps, int normalize, void* out,
+                      int64_t B, int64_t D, int64_t H, int64_t W, int dtype, void* stream) {
+  if (!y || !out) return SS2D_ERR_NULL;
+  int rc = check_shape(B, D, H, W, 1, dtype);
+  if (rc != SS2D_OK) return rc;
+  if (D > ss2d::epilogue_max_channels()) return SS2D_ERR_SHAPE;
+  if (normalize != 0 && normalize != 1) return SS2D_ERR_SHAPE;
+  if (normalize && !(eps >= 0.f && eps <= 1e30f)) return SS2D_ERR_SHAPE;  // also rejects NaN
+  const int64_t s = dtype == SS2D_BF16 ? 2 : 4;
+  const int64_t ybytes = B * D * H * W * s, vbytes = D * 4;
+  if (overlaps(out, ybytes, y, ybytes) || (gamma && overlaps(out, ybytes, gamma, vbytes)) ||
+      (beta && overlaps(out, ybytes, beta, vbytes)))
+    return SS2D_ERR_ALIAS;
+  const uintptr_t m = (uintptr_t)(s - 1);
+  if (((uintptr_t)y & m) || ((uintptr_t)out & m) || ((uintptr_t)gamma & 3) || ((uintptr_t)beta & 3))
+    return SS2D_ERR_ALIGN;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc != SS2D_OK) return rc;
+  ss2d::EpilogueArgs a{y, gamma, beta, out, eps, normalize != 0, B, D, H, W, dtype, static_cast<hipStream_t>(stream)};
+  hipError_t e = ss2d::launch_channel_last(a);
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  return SS2D_OK;
+}
+
 }  // extern "C"

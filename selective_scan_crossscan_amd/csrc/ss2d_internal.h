@@ -85,6 +85,22 @@ struct ProjectArgs {
 hipError_t launch_project(const ProjectArgs& a);
 // Largest 2 * (R + 2N) the projection kernel takes.
 int project_max_rows();
+// y (B, D, H, W) -> out (B, H, W, D), optionally normalised over D per pixel.
+struct EpilogueArgs {
+  const void* y;
+  const float* gamma;  // (D) or null (scale 1)
+  const float* beta;   // (D) or null (shift 0)
+  void* out;
+  float eps;
+  bool normalize;
+  int64_t B, D, H, W;
+  int dtype;
+  hipStream_t stream;
+};
+hipError_t launch_channel_last(const EpilogueArgs& a);
+// Largest D the epilogue takes.
+int epilogue_max_channels();
+
 // x (B*D planes of H x W) -> xT (planes of W x H).
 hipError_t launch_transpose_x(const void* x, void* xT, int64_t planes, int64_t H, int64_t W, int dtype,
                               hipStream_t stream);

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["ss2d_forward", "ss2d_status_string", "ss2d_last_hip_error", "ss2d_version",
                             "ss2d_describe", "ss2d_set_lanes_per_seq", "ss2d_measure_peaks", "ss2d_project",
-                            "ss2d_forward_from_x"])
+                            "ss2d_forward_from_x", "ss2d_channel_last"])
     lib = ctypes.CDLL(ss2d.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -208,3 +208,35 @@ def test_projection_valid_calls_without_device_report_no_device():
     assert _proj() == -7
     assert _proj(N=16, R=32) == -7     # exactly 128 rows is allowed
     assert _fromx() == -7
+
+
+# the channel-last epilogue
+GM, BT, OUT = BASE + 10 * (1 << 34), BASE + 11 * (1 << 34), BASE + 12 * (1 << 34)
+
+
+def _epi(y=X, g=GM, b=BT, eps=1e-5, norm=1, out=OUT, B=2, D=3, H=4, W=5, dtype=0):
+    return ss2d.ss2d_channel_last(y, g, b, eps, norm, out, B, D, H, W, dtype, None)
+
+
+def test_channel_last_validation():
+    assert _epi(y=None) == -1
+    assert _epi(out=None) == -1
+    assert _epi(D=4097) == -2
+    assert _epi(norm=2) == -2
+    assert _epi(eps=-1.0) == -2
+    assert _epi(eps=float("nan")) == -2
+    assert _epi(eps=float("inf")) == -2
+    assert _epi(dtype=5) == -4
+    assert _epi(H=0) == -2
+    assert _epi(out=X + 8) == -5
+    assert _epi(out=GM) == -5
+    assert _epi(y=X + 1, dtype=1) == -6
+    assert _epi(g=GM + 2) == -6
+    assert _epi(out=OUT + 4, D=8) == -7             # element alignment is enough (then: no device)
+
+
+def test_channel_last_valid_calls_without_device_report_no_device():
+    assert _epi() == -7
+    assert _epi(g=None, b=None) == -7               # scale and shift are optional
+    assert _epi(norm=0, eps=-1.0) == -7             # eps is unused without the normalisation
+    assert _epi(D=4096) == -7
