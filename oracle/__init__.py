@@ -19,6 +19,8 @@ Three independent formulations of the scan, and the projections, live here:
   * `epilogue`      -- the channel-last transpose after the merge and a
                         LayerNorm over the channels of each pixel, in numpy
                         float64.
+  * `backward`      -- the forward's gradients by the chain rule (state
+                        adjoints walked from the end), in numpy float64.
 Pages: [SS2D] "深入解析VMamba中的SS2D模块从理论到代码实现" §3.1-§4.
 """
 from __future__ import annotations
