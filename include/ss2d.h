@@ -151,6 +151,36 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
 int ss2d_channel_last(const void* y, const float* gamma, const float* beta, float eps, int normalize,
                       void* out, int64_t B, int64_t D, int64_t H, int64_t W, int dtype, void* stream);
 
+/*
+ * ss2d_backward -- enqueue the gradients of the forward on `stream`: given dy,
+ * the gradient of a loss with respect to y, write the gradients with respect to
+ * every input of ss2d_forward.  Page [SS2D] "深入解析VMamba中的SS2D模块从理论到
+ * 代码实现" §3.1-§3.3 define the forward; the gradients follow by the chain rule,
+ * with the state adjoint q_l = Cs[n,l] dy_l + exp(delta_{l+1} A) q_{l+1} walked
+ * from the end of each sequence (dy_l: dy at the pixel the direction visits).
+ *   inputs  x, dt, A_log, dt_bias, Bs, Cs, Ds  as for ss2d_forward (fp32);
+ *           dy      [B, D, H, W]   fp32
+ *   outputs dx      [B, D, H, W]   fp32
+ *           ddt     [B, 4, D, L]   fp32
+ *           dA_log  [4*D, N]       fp32   summed over the batch
+ *           ddt_bias[4*D]          fp32   summed over the batch and steps
+ *           dBs, dCs[B, 4, N, L]   fp32   summed over the D channels
+ *           dDs     [4*D]          fp32   summed over the batch and steps
+ * Every output is fully overwritten (no accumulation into existing values) and
+ * must not overlap an input or another output (SS2D_ERR_ALIAS).  dtype must be
+ * SS2D_F32 (SS2D_ERR_DTYPE otherwise); N is 1..16.  All sums run in a fixed
+ * order, so results are deterministic.  Takes a stream-ordered temporary of
+ * about 2*B*4*D*L + 2*B*4*ceil(D/16)*N*L + B*4*D*N*ceil(L/16) fp32 values (state
+ * checkpoints every 16 steps, du, per-channel-block partials of dBs and dCs) and
+ * runs four kernels on `stream`.  Validation, error reporting and thread safety
+ * as for ss2d_forward; pointers need 4-byte alignment (SS2D_ERR_ALIGN).
+ */
+int ss2d_backward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
+                  const void* Bs, const void* Cs, const float* Ds, const void* dy,
+                  void* dx, void* ddt, float* dA_log, float* ddt_bias, void* dBs, void* dCs,
+                  float* dDs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                  int dtype, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ss2d_status_string(int status);
 

@@ -12,7 +12,7 @@ import os
 import threading
 
 __all__ = ["forward", "ss2d_forward", "project", "ss2d_project", "forward_from_x", "ss2d_forward_from_x",
-           "channel_last", "ss2d_channel_last", "measure_peaks", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
+           "channel_last", "ss2d_channel_last", "backward", "ss2d_backward", "measure_peaks", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
            "SS2D_F32", "SS2D_BF16", "SS2DError"]
 
 SS2D_F32 = 0
@@ -71,6 +71,8 @@ def lib():
             L.ss2d_channel_last.argtypes = [vp, vp, vp, ctypes.c_float, ctypes.c_int, vp] + [i64] * 4 + [
                 ctypes.c_int, vp]
             L.ss2d_channel_last.restype = ctypes.c_int
+            L.ss2d_backward.argtypes = [vp] * 15 + [i64] * 5 + [ctypes.c_int, vp]
+            L.ss2d_backward.restype = ctypes.c_int
             L.ss2d_measure_peaks.argtypes = [ctypes.POINTER(Peaks), i64, vp]
             L.ss2d_measure_peaks.restype = ctypes.c_int
             _lib = L
@@ -241,6 +243,39 @@ def channel_last(y, gamma=None, beta=None, eps: float = 1e-5, normalize: bool = 
         rc = ss2d_channel_last(y.data_ptr(), gamma.data_ptr() if gamma is not None else None,
                                beta.data_ptr() if beta is not None else None, eps, 1 if normalize else 0,
                                out.data_ptr(), B, D, H, W, code, stream.cuda_stream)
+    if rc != 0:
+        _raise(rc)
+    return out
+
+
+def ss2d_backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs, B, D, H, W, N,
+                  dtype, stream) -> int:
+    """Raw C-ABI call with integer device addresses; returns the status code."""
+    return lib().ss2d_backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs,
+                               B, D, H, W, N, int(dtype), stream)
+
+
+def backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream=None) -> dict:
+    """Gradients of the forward given dy (ss2d_backward), float32 tensors on one ROCm device.
+
+    Returns dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs (shapes of the matching inputs)."""
+    import torch
+
+    if x.dtype != torch.float32:
+        raise TypeError("the backward takes float32 tensors")
+    B, D, H, W = x.shape
+    N = A_log.shape[-1]
+    ins = (x, dt, A_log, dt_bias, Bs, Cs, Ds, dy)
+    if tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("dy must have x's shape")
+    out = {name: torch.empty_like(t) for name, t in
+           (("dx", x), ("ddt", dt), ("dA_log", A_log), ("ddt_bias", dt_bias), ("dBs", Bs), ("dCs", Cs), ("dDs", Ds))}
+    _check_tensors(x, (), ins + tuple(out.values()))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        rc = ss2d_backward(*(t.data_ptr() for t in ins), *(t.data_ptr() for t in out.values()), B, D, H, W, N,
+                           SS2D_F32, stream.cuda_stream)
     if rc != 0:
         _raise(rc)
     return out

@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libss2d.so")
 # type and steps per lane, compiled in parallel.
 SOURCES = ["ss2d_api.hip", "ss2d_plan.hip", "ss2d_f32_t16.hip", "ss2d_f32_t8.hip", "ss2d_bf16_t16.hip",
            "ss2d_bf16_t8.hip", "ss2d_peaks.hip", "ss2d_project.hip",
-           "ss2d_epilogue.hip"]
+           "ss2d_epilogue.hip", "ss2d_backward.hip"]
 
 # -packed-fp32-ops: no packed FP32 instructions are generated (plain VALU only).
 HIPCC_FLAGS = [

@@ -385,4 +385,55 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
   return SS2D_OK;
 }
 
+int ss2d_backward(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                  const void* Cs, const float* Ds, const void* dy, void* dx, void* ddt, float* dA_log,
+                  float* ddt_bias, void* dBs, void* dCs, float* dDs, int64_t B, int64_t D, int64_t H, int64_t W,
+                  int64_t N, int dtype, void* stream) {
+  if (!x || !dt || !A_log || !dt_bias || !Bs || !Cs || !Ds || !dy || !dx || !ddt || !dA_log || !ddt_bias || !dBs ||
+      !dCs || !dDs)
+    return SS2D_ERR_NULL;
+  int rc = check_shape(B, D, H, W, N, dtype);
+  if (rc != SS2D_OK) return rc;
+  if (dtype != SS2D_F32) return SS2D_ERR_DTYPE;  // the gradients are fp32 only
+  const int64_t L = H * W;
+  const int64_t xb = B * D * L * 4, dtb = B * 4 * D * L * 4, bcb = B * 4 * N * L * 4, pb = 4 * D * N * 4,
+                vb = 4 * D * 4;
+  const void* ins[8] = {x, dt, A_log, dt_bias, Bs, Cs, Ds, dy};
+  const int64_t isz[8] = {xb, dtb, pb, vb, bcb, bcb, vb, xb};
+  const void* outs[7] = {dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs};
+  const int64_t osz[7] = {xb, dtb, pb, vb, bcb, bcb, vb};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return SS2D_ERR_ALIAS;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SS2D_ERR_ALIAS;
+  }
+  for (int j = 0; j < 8; ++j)
+    if ((uintptr_t)ins[j] & 3) return SS2D_ERR_ALIGN;
+  for (int i = 0; i < 7; ++i)
+    if ((uintptr_t)outs[i] & 3) return SS2D_ERR_ALIGN;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc != SS2D_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* tmp = nullptr;
+  hipError_t e = hipMallocAsync(&tmp, ss2d::backward_scratch_bytes(B, D, H, W, N), st);
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  ss2d::BackwardArgs a{static_cast<const float*>(x), static_cast<const float*>(dt), A_log, dt_bias,
+                       static_cast<const float*>(Bs), static_cast<const float*>(Cs), Ds,
+                       static_cast<const float*>(dy), static_cast<float*>(dx), static_cast<float*>(ddt), dA_log,
+                       ddt_bias, static_cast<float*>(dBs), static_cast<float*>(dCs), dDs, B, D, H, W, N, st};
+  e = ss2d::launch_backward(a, tmp);
+  hipError_t e2 = hipFreeAsync(tmp, st);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  return SS2D_OK;
+}
+
 }  // extern "C"

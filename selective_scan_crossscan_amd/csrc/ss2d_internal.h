@@ -101,6 +101,29 @@ hipError_t launch_channel_last(const EpilogueArgs& a);
 // Largest D the epilogue takes.
 int epilogue_max_channels();
 
+// Gradients of the forward (fp32): every output fully written.
+struct BackwardArgs {
+  const float* x;
+  const float* dt;
+  const float* A_log;
+  const float* dt_bias;
+  const float* Bs;
+  const float* Cs;
+  const float* Ds;
+  const float* dy;
+  float* dx;
+  float* ddt;
+  float* dA_log;
+  float* ddt_bias;
+  float* dBs;
+  float* dCs;
+  float* dDs;
+  int64_t B, D, H, W, N;
+  hipStream_t stream;
+};
+size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N);
+hipError_t launch_backward(const BackwardArgs& a, void* scratch);
+
 // x (B*D planes of H x W) -> xT (planes of W x H).
 hipError_t launch_transpose_x(const void* x, void* xT, int64_t planes, int64_t H, int64_t W, int dtype,
                               hipStream_t stream);

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert names == sorted(["ss2d_forward", "ss2d_status_string", "ss2d_last_hip_error", "ss2d_version",
                             "ss2d_describe", "ss2d_set_lanes_per_seq", "ss2d_measure_peaks", "ss2d_project",
-                            "ss2d_forward_from_x", "ss2d_channel_last"])
+                            "ss2d_forward_from_x", "ss2d_channel_last", "ss2d_backward"])
     lib = ctypes.CDLL(ss2d.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -240,3 +240,32 @@ def test_channel_last_valid_calls_without_device_report_no_device():
     assert _epi(g=None, b=None) == -7               # scale and shift are optional
     assert _epi(norm=0, eps=-1.0) == -7             # eps is unused without the normalisation
     assert _epi(D=4096) == -7
+
+
+# the backward
+GRAD = [BASE + (13 + i) * (1 << 34) for i in range(8)]  # dy, then the seven outputs
+
+
+def _bwd(ptrs=None, B=2, D=3, H=4, W=5, N=16, dtype=0):
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD if ptrs is None else ptrs
+    return ss2d.ss2d_backward(*p, B, D, H, W, N, dtype, None)
+
+
+def test_backward_validation():
+    for i in range(15):
+        p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+        p[i] = None
+        assert _bwd(p) == -1, i
+    assert _bwd(dtype=1) == -4            # fp32 only
+    assert _bwd(N=17) == -3
+    assert _bwd(W=0) == -2
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+    p[8] = X                              # dx on top of x
+    assert _bwd(p) == -5
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+    p[13] = p[12]                         # dCs on top of dBs
+    assert _bwd(p) == -5
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+    p[10] = GRAD[3] + 2                   # dA_log misaligned
+    assert _bwd(p) == -6
+    assert _bwd() == -7                   # valid, no device here
