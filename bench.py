@@ -232,9 +232,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = VMamba-T stage-1")
-    ap.add_argument("--path", choices=["scan", "from_x"], default="scan",
+    ap.add_argument("--path", choices=["scan", "from_x", "backward"], default="scan",
                     help="scan: the forward from x, dt, Bs, Cs (the headline); from_x: the forward from x and the "
-                         "projection weights (projections on the matrix cores, then the scan)")
+                         "projection weights (projections on the matrix cores, then the scan); backward: the "
+                         "gradients of the forward given dy (fp32 workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity")
     ap.add_argument("--lanes", type=int, default=0, help="force lanes per sequence chunk (16/32/64; 0 = auto)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -269,6 +270,10 @@ def main() -> int:
     shape = ss2d_inputs.CONFIGS[args.config]
     print(f"[bench] workload {shape}", file=sys.stderr, flush=True)
     from_x = args.path == "from_x"
+    bwd = args.path == "backward"
+    if bwd and shape.dtype != "f32":
+        print("bench.py: the backward takes fp32 workloads only", file=sys.stderr)
+        return 2
     inp = ss2d_inputs.generate_projected(shape, seed=0) if from_x else ss2d_inputs.generate(shape, seed=0)
     tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
     d = {}
@@ -280,7 +285,15 @@ def main() -> int:
     y = torch.empty((shape.B, shape.D, shape.H, shape.W), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    if from_x:
+    if bwd:
+        dy = torch.from_numpy(np.random.default_rng(1).standard_normal((shape.B, shape.D, shape.H, shape.W))
+                              .astype(np.float32)).to(dev)
+        grads = {}
+
+        def step():
+            grads.update(ss2d.backward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], dy,
+                                       stream=stream))
+    elif from_x:
         def step():
             ss2d.forward_from_x(d["x"], d["x_proj_weight"], d["dt_projs_weight"], d["A_log"], d["dt_bias"],
                                 d["Ds"], out=y, stream=stream)
@@ -395,6 +408,8 @@ def main() -> int:
                                                        1 if shape.dtype == "bf16" else 0).split())
     nseg = int(plan["segments"])
     launches = int(plan["x_transposed"]) + (1 if nseg == 1 else 5 + int(plan["plane_transposed"]))
+    if bwd:
+        launches = 4  # the reverse scan, the dBs/dCs sum, the dx merge, the parameter sums
     if from_x:
         launches += 1 + (1 - int(plan["x_transposed"]))  # the projection, and its own transpose of x
     ms_per_step = wall * 1e3 / args.steps
@@ -418,7 +433,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic (seeded numpy PCG64, VMamba-shaped value recipe)",
-        "config": {"workload": shape.name + ("_from_x" if from_x else ""), "path": args.path, "B": shape.B, "D": shape.D, "H": shape.H, "W": shape.W,
+        "config": {"workload": shape.name + ("_from_x" if from_x else "_backward" if bwd else ""), "path": args.path, "B": shape.B, "D": shape.D, "H": shape.H, "W": shape.W,
                    "N": shape.N, "K": 4, "L": shape.L, "io_dtype": shape.dtype,
                    "plan": ss2d.describe(shape.B, shape.D, shape.H, shape.W, shape.N,
                                          1 if shape.dtype == "bf16" else 0)},
@@ -437,6 +452,9 @@ def main() -> int:
                 "frac_of_peak": hbm_gbps / HBM_PEAK_GBPS, "peak_GBps": HBM_PEAK_GBPS},
         "kernel_us": kernel_s * 1e6,
     }
+    if bwd:
+        result["roofline"]["unit"] += ("; backward: each (b,k,d,n,l) counted once, though the backward recomputes "
+                                       "the forward twice and adds the adjoint walk")
     if epi is not None:
         result["epilogue"] = epi
     if proj is not None:
@@ -463,26 +481,37 @@ def main() -> int:
         x64 = {k: np.ascontiguousarray(v, dtype=np.float64) for k, v in inp.items()}
         threads = oracle.threads()
         t0 = time.perf_counter()
-        if from_x:
+        if bwd:
+            # a bounded sample: the float64 backward oracle on the first batch element
+            from oracle import backward as obwd
+            x1 = {k: (v[:1] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in x64.items()}
+            refs = obwd.ss2d_backward_f64(**x1, dy=dy[:1].double().cpu().numpy())
+            cpu_s = (time.perf_counter() - t0) * shape.B
+            ref = refs["dx"]
+        elif from_x:
             from oracle import projection
             ref = projection.ss2d_from_x_f64(**x64)
+            cpu_s = time.perf_counter() - t0
         else:
             ref = oracle.ss2d_f64(**x64)
-        cpu_s = time.perf_counter() - t0
-        got = y.double().cpu().numpy()
+            cpu_s = time.perf_counter() - t0
+        got = (grads["dx"][:1] if bwd else y).double().cpu().numpy()
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         max_abs = float(np.max(np.abs(got - ref)))
         result["cpu_baseline"] = {
             "value": updates / cpu_s,
             "unit": "state-updates/s",
-            "cores": threads,
+            "cores": 1 if bwd else threads,
             "kind": "oracle",
-            "sample": f"the whole workload ({shape.B}x{shape.D} planes, {updates:.3e} updates), "
-                      + ("numpy float64 projections (einsum), then " if from_x else "")
-                      + f"fp64 C loops, OpenMP over (b,d) planes; {cpu_s:.2f} s on {cpu_model()}",
+            "sample": (f"the float64 numpy backward oracle on 1 of {shape.B} batch elements, scaled by {shape.B}; "
+                       f"{cpu_s / shape.B:.2f} s for the sample on {cpu_model()}") if bwd else
+                      (f"the whole workload ({shape.B}x{shape.D} planes, {updates:.3e} updates), "
+                       + ("numpy float64 projections (einsum), then " if from_x else "")
+                       + f"fp64 C loops, OpenMP over (b,d) planes; {cpu_s:.2f} s on {cpu_model()}"),
         }
         result["parity"] = {"rel_l2": rel, "max_abs": max_abs, "max_abs_y": float(np.max(np.abs(ref))),
-                            "vs": "fp64 oracle, whole output"}
+                            "vs": "fp64 backward oracle, dx of batch element 0" if bwd else
+                            "fp64 oracle, whole output"}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -20,8 +20,10 @@
 //   * Pass 1 walks the sequence forwards and stores the state entering every
 //     16-step segment.  Pass 2 walks the segments backwards: it recomputes the
 //     segment's states from its checkpoint into registers, then walks the steps
-//     backwards with the state adjoint.  A segment's operands are loaded before
-//     its arithmetic.
+//     backwards with the state adjoint.
+//   * A segment's operands (x, dy, dt per channel; Bs, Cs per state) are loaded
+//     once per workgroup, one value per thread, a segment ahead, and staged in
+//     LDS; the sums over states run once per segment for all its steps.
 //   * dBs/dCs partials are summed over the workgroup's 16 channels through LDS
 //     once per segment and written per channel block; a second kernel sums the
 //     blocks in a fixed order, so results are deterministic (no atomics).
@@ -64,136 +66,144 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// Pixel visited at step l of direction k, tracked as (row, column) of the walk:
-// start() for a step, next() for the step after it.
-struct Walk {
-  int k, L, H, W, r, cix;  // for column walks: r = row h, cix = column w of the current pixel
-  int l;
-  __device__ void start(int l0) {
-    l = l0;
-    const int m = k >= 2 ? L - 1 - l0 : l0;
-    if (k & 1) {
-      cix = m / H;
-      r = m - cix * H;
-    }
-  }
-  __device__ int pixel() const {
-    if ((k & 1) == 0) return k >= 2 ? L - 1 - l : l;
-    return r * W + cix;
-  }
-  __device__ void next() {
-    ++l;
-    if (k & 1) {
-      if (k == 1) {
-        if (++r == H) {
-          r = 0;
-          ++cix;
-        }
-      } else {
-        if (--r < 0) {
-          r = H - 1;
-          --cix;
-        }
-      }
-    }
-  }
-};
+// Operands of one 16-step segment, staged in LDS once per workgroup: per channel
+// (x and dy at the visited pixels, delta = softplus(dt + dt_bias) and its
+// derivative sigmoid(dt + dt_bias)) and per state (Bs, Cs).  delta and the
+// sigmoid are computed once per (channel, step) by the staging thread.
+enum { kOpX, kOpG, kOpDel, kOpSig, kOpB, kOpC, kOps };
 
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   __shared__ float red[2][kSeg][256];
+  __shared__ float op[2][kOps][kSeg][16];  // double-buffered, [step][channel or state]
   const int tid = threadIdx.x, n = tid & 15, ch = tid >> 4;
   const int blk = blockIdx.x % p.nblk;
   const int bk = blockIdx.x / p.nblk;  // b * 4 + k
   const int k = bk & 3, b = bk >> 2;
-  const int D = p.D, L = p.L, N = p.N;
+  const int D = p.D, L = p.L, N = p.N, H = p.H, W = p.W;
   const int d = blk * kBwdChans + ch;
   const bool dval = d < D, val = dval && n < N;
   const int ds = dval ? d : 0, ns = n < N ? n : 0;
   const int c = k * D + ds;
   const float A = val ? -expf(p.A_log[(int64_t)c * N + ns]) : 0.f;
   const float Al2 = A * kLog2e;
-  const float bias = p.dt_bias[c], Dsk = p.Ds[c];
-  const float* xr = p.x + ((int64_t)b * D + ds) * L;
-  const float* gr = p.dy + ((int64_t)b * D + ds) * L;
-  const float* dtr = p.dt + ((int64_t)bk * D + ds) * L;
-  const float* Br = p.Bs + ((int64_t)bk * N + ns) * L;
-  const float* Cr = p.Cs + ((int64_t)bk * N + ns) * L;
+  const float Dsk = p.Ds[c];
   auto hck = [&](int s) -> float& { return p.hck[(((int64_t)bk * p.nseg + s) * D + ds) * N + ns]; };
-  Walk wk{k, L, p.H, p.W, 0, 0, 0};
+
+  // this thread's share of the staging: step i = tid & 15 of the segment, for
+  // channel (tid >> 4) of the per-channel operands and state (tid >> 4) of the
+  // per-state ones
+  const int si = tid & 15, sr = tid >> 4;
+  const int sd = blk * kBwdChans + sr;
+  const bool sdv = sd < D, snv = sr < N;
+  const int sdc = sdv ? sd : 0, snc = snv ? sr : 0;
+  const float sbias = p.dt_bias[k * D + sdc];
+  const float* sx = p.x + ((int64_t)b * D + sdc) * L;
+  const float* sg = p.dy + ((int64_t)b * D + sdc) * L;
+  const float* sdt = p.dt + ((int64_t)bk * D + sdc) * L;
+  const float* sB = p.Bs + ((int64_t)bk * N + snc) * L;
+  const float* sC = p.Cs + ((int64_t)bk * N + snc) * L;
+  auto pixel = [&](int l) {  // pixel visited at step l of direction k
+    const int m = k >= 2 ? L - 1 - l : l;
+    if ((k & 1) == 0) return m;
+    const int w = m / H;
+    return (m - w * H) * W + w;
+  };
+  float stage[kOps];
+  auto load_stage = [&](int s, bool with_g) {
+    const int l = s * kSeg + si;
+    const bool in = l < L;
+    const int px = in ? pixel(l) : 0, lc = in ? l : 0;
+    stage[kOpX] = sx[px];
+    stage[kOpG] = with_g ? sg[px] : 0.f;
+    stage[kOpDel] = sdt[lc] + sbias;  // dt + dt_bias until stored
+    stage[kOpB] = sB[lc];
+    stage[kOpC] = with_g ? sC[lc] : 0.f;
+  };
+  auto store_stage = [&](int buf) {
+    const float pre = stage[kOpDel];
+    stage[kOpDel] = softplus_f32(pre);
+    stage[kOpSig] = 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e));
+#pragma unroll
+    for (int j = 0; j < kOps; ++j) op[buf][j][si][sr] = stage[j];
+  };
 
   // pass 1: states entering every segment
   float h = 0.f;
+  load_stage(0, false);
+  store_stage(0);
+  __syncthreads();
   for (int s = 0; s < p.nseg; ++s) {
+    const int buf = s & 1;
     if (val) hck(s) = h;
-    const int l0 = s * kSeg;
-    const int cnt = L - l0 < kSeg ? L - l0 : kSeg;
-    float uu[kSeg], pre[kSeg], bb[kSeg];
-    wk.start(l0);
-#pragma unroll
-    for (int i = 0; i < kSeg; ++i) {
-      const bool in = i < cnt;
-      uu[i] = xr[in ? wk.pixel() : 0];
-      pre[i] = dtr[in ? l0 + i : 0] + bias;
-      bb[i] = Br[in ? l0 + i : 0];
-      wk.next();
-    }
+    if (s + 1 < p.nseg) load_stage(s + 1, false);
+    const int cnt = L - s * kSeg < kSeg ? L - s * kSeg : kSeg;
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) {
       if (i < cnt) {
-        const float del = softplus_f32(pre[i]);
-        h = fmaf(__builtin_amdgcn_exp2f(del * Al2), h, del * bb[i] * uu[i]);
+        const float del = op[buf][kOpDel][i][ch];
+        h = fmaf(__builtin_amdgcn_exp2f(del * Al2), h, del * op[buf][kOpB][i][n] * op[buf][kOpX][i][ch]);
       }
     }
+    if (s + 1 < p.nseg) store_stage(buf ^ 1);
+    __syncthreads();
   }
 
   // pass 2: segments from the last, steps from the last
   float q = 0.f, a_next = 0.f, dA = 0.f, dbias = 0.f, dD = 0.f;
   const int64_t row = ((int64_t)bk * D + ds) * L;  // (b, k, d) row of ddt and du
+  int buf = 0;
+  load_stage(p.nseg - 1, true);
+  store_stage(buf);
+  __syncthreads();
   for (int s = p.nseg - 1; s >= 0; --s) {
     const int l0 = s * kSeg;
     const int cnt = L - l0 < kSeg ? L - l0 : kSeg;
     const float h_in = val ? hck(s) : 0.f;
-    float uu[kSeg], gg[kSeg], pre[kSeg], bb[kSeg], cc[kSeg];
-    wk.start(l0);
-#pragma unroll
-    for (int i = 0; i < kSeg; ++i) {
-      const bool in = i < cnt;
-      const int px = in ? wk.pixel() : 0;
-      uu[i] = xr[px];
-      gg[i] = gr[px];
-      pre[i] = dtr[in ? l0 + i : 0] + bias;
-      bb[i] = Br[in ? l0 + i : 0];
-      cc[i] = Cr[in ? l0 + i : 0];
-      wk.next();
-    }
+    if (s > 0) load_stage(s - 1, true);
     float hs[kSeg], del[kSeg], aa[kSeg];
     float hv = h_in;
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) {
-      del[i] = softplus_f32(pre[i]);
+      del[i] = op[buf][kOpDel][i][ch];
       aa[i] = __builtin_amdgcn_exp2f(del[i] * Al2);
-      hv = fmaf(aa[i], hv, del[i] * bb[i] * uu[i]);
+      hv = fmaf(aa[i], hv, del[i] * op[buf][kOpB][i][n] * op[buf][kOpX][i][ch]);
       hs[i] = hv;
     }
+    float dup[kSeg], ddp[kSeg];
 #pragma unroll
     for (int i = kSeg - 1; i >= 0; --i) {
+      dup[i] = 0.f;
+      ddp[i] = 0.f;
       if (i < cnt) {
+        const float g = op[buf][kOpG][i][ch], u = op[buf][kOpX][i][ch];
+        const float Bv = op[buf][kOpB][i][n], Cv = op[buf][kOpC][i][n];
         const float hp = i > 0 ? hs[i - 1] : h_in;
-        q = fmaf(a_next, q, cc[i] * gg[i]);
+        q = fmaf(a_next, q, Cv * g);
         const float qd = q * del[i];
         dA = fmaf(qd * aa[i], hp, dA);
         a_next = aa[i];
-        red[0][i][tid] = val ? hs[i] * gg[i] : 0.f;
-        red[1][i][tid] = val ? qd * uu[i] : 0.f;
-        const float du = row_sum16(val ? qd * bb[i] : 0.f);
-        const float ddl = row_sum16(val ? q * fmaf(A * aa[i], hp, bb[i] * uu[i]) : 0.f);
-        if (n == 0 && dval) {
-          const float sig = 1.f / (1.f + __builtin_amdgcn_exp2f(-pre[i] * kLog2e));
-          const float ddt = ddl * sig;
+        red[0][i][tid] = val ? hs[i] * g : 0.f;
+        red[1][i][tid] = val ? qd * u : 0.f;
+        dup[i] = val ? qd * Bv : 0.f;
+        ddp[i] = val ? q * fmaf(A * aa[i], hp, Bv * u) : 0.f;
+      }
+    }
+    // sums over the 16 states of each channel, all steps of the segment at once
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      dup[i] = row_sum16(dup[i]);
+      ddp[i] = row_sum16(ddp[i]);
+    }
+    if (n == 0 && dval) {
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) {
+        if (i < cnt) {
+          const float g = op[buf][kOpG][i][ch], u = op[buf][kOpX][i][ch];
+          const float ddt = ddp[i] * op[buf][kOpSig][i][ch];
           p.ddt[row + l0 + i] = ddt;
-          p.du[row + l0 + i] = fmaf(Dsk, gg[i], du);
+          p.du[row + l0 + i] = fmaf(Dsk, g, dup[i]);
           dbias += ddt;
-          dD = fmaf(gg[i], uu[i], dD);
+          dD = fmaf(g, u, dD);
         }
       }
     }
@@ -210,6 +220,8 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
         dst[(((int64_t)bk * p.nblk + blk) * N + nn) * L + l0 + i] = sum;
       }
     }
+    if (s > 0) store_stage(buf ^ 1);
+    buf ^= 1;
     __syncthreads();
   }
   if (val) p.dAp[((int64_t)b * 4 * D + c) * N + ns] = dA;
