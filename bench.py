@@ -47,7 +47,8 @@ KERNEL_SOURCES = sorted(
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
-STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel"}
+STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel", "bwd_scan_kernel",
+                "bwd_reduce_bc", "bwd_merge", "bwd_params"}
 
 
 def traffic_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
@@ -103,6 +104,11 @@ PROFILE_COMMANDS = {
 COPY_PROBE_MIB = 512
 
 
+def _is_kernel(name: str, kernel: str) -> bool:
+    """Whether a rocprofv3 kernel name is `kernel` (a template instance or a plain function)."""
+    return f"::{kernel}<" in name or f"::{kernel}(" in name
+
+
 def _find(folder: str, suffix: str) -> str:
     import glob
     hits = sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True))
@@ -124,10 +130,11 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
     import csv
     shape = ss2d_inputs.CONFIGS[cfg]
     os.makedirs(PROFILES, exist_ok=True)
-    from_x = path == "from_x"
-    kernel = "project_kernel" if from_x else KERNEL_PREFIX
-    workload = shape.name + ("_from_x" if from_x else "")
-    cmds = {k: v.format(d=folder, c=cfg, x=" --path from_x" if from_x else "") for k, v in PROFILE_COMMANDS.items()}
+    from_x, bwd = path == "from_x", path == "backward"
+    kernel = "project_kernel" if from_x else "bwd_scan_kernel" if bwd else KERNEL_PREFIX
+    workload = shape.name + ("_from_x" if from_x else "_backward" if bwd else "")
+    cmds = {k: v.format(d=folder, c=cfg, x=f" --path {path}" if path != "scan" else "")
+            for k, v in PROFILE_COMMANDS.items()}
 
     # Kernel-trace statistics, next to the bench line printed by the same run.
     with open(_find(folder, "stats_kernel_stats.csv")) as f:
@@ -139,6 +146,10 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
         alg_bytes, alg_flops = projection_work(shape)
         work = (f"Projection per launch: {alg_flops:.4e} FLOP (fp32 MFMA), algorithmic bytes {alg_bytes:.4e} "
                 "(x read once; dt, Bs, Cs written once; weights).")
+    elif bwd:
+        alg_bytes = 4 * shape.B * shape.L * (11 * shape.D + 16 * shape.N)
+        work = (f"Backward per launch: {shape.updates:.4e} (b,k,d,n,l) terms; algorithmic bytes {alg_bytes:.4e} "
+                "(x, dy, dt, Bs, Cs read once; dx, ddt, dBs, dCs written once).")
     else:
         alg_bytes = shape.algorithmic_bytes
         work = f"Updates per launch: {shape.updates:.4e}; algorithmic bytes per launch: {alg_bytes:.4e}."
@@ -152,9 +163,9 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
         if len(name) > 90:
             name = name[:87] + "..."
         avg = float(r["AverageNs"]) / 1e3
-        if f"::{kernel}<" in r["Name"]:
+        if _is_kernel(r["Name"], kernel):
             kern_avg = avg
-        if any(f"::{k}<" in r["Name"] for k in STEP_KERNELS):
+        if any(_is_kernel(r["Name"], k) for k in STEP_KERNELS):
             per_step += avg
         lines.append(f"| `{name}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
@@ -180,7 +191,7 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
     per = {}
     for counter, prefix in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = [r for r in _counter_rows(folder, prefix) if r["Counter_Name"] == counter]
-        kern = [float(r["Counter_Value"]) for r in rows if f"::{kernel}<" in r["Kernel_Name"]]
+        kern = [float(r["Counter_Value"]) for r in rows if _is_kernel(r["Kernel_Name"], kernel)]
         copies = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         probe_kib, probe_name = max(copies)
         expected_kib = COPY_PROBE_MIB * 1024.0
@@ -409,7 +420,7 @@ def main() -> int:
     nseg = int(plan["segments"])
     launches = int(plan["x_transposed"]) + (1 if nseg == 1 else 5 + int(plan["plane_transposed"]))
     if bwd:
-        launches = 4  # the reverse scan, the dBs/dCs sum, the dx merge, the parameter sums
+        launches = 6  # two transposes, the reverse scan, the dBs/dCs sum, the dx merge, the parameter sums
     if from_x:
         launches += 1 + (1 - int(plan["x_transposed"]))  # the projection, and its own transpose of x
     ms_per_step = wall * 1e3 / args.steps

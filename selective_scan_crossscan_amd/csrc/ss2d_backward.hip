@@ -27,6 +27,8 @@
 //   * dBs/dCs partials are summed over the workgroup's 16 channels through LDS
 //     once per segment and written per channel block; a second kernel sums the
 //     blocks in a fixed order, so results are deterministic (no atomics).
+//   * Column walks read transposed copies of x and dy (made first), so every
+//     operand load is contiguous along the steps.
 //   * du goes to a temporary; a gather kernel merges it into dx, and a small
 //     kernel sums the per-batch parameter gradients.
 #include "ss2d_kernels.h"
@@ -46,6 +48,8 @@ struct BwdParams {
   const float* Cs;
   const float* Ds;
   const float* dy;
+  const float* xT;   // x and dy with H and W swapped: column walks read them in order
+  const float* dyT;
   float* ddt;  // (B, 4, D, L) out
   float* du;   // (B, 4, D, L) temporary
   float* hck;  // (B*4, nseg, D, N) temporary: state entering each segment
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   const int blk = blockIdx.x % p.nblk;
   const int bk = blockIdx.x / p.nblk;  // b * 4 + k
   const int k = bk & 3, b = bk >> 2;
-  const int D = p.D, L = p.L, N = p.N, H = p.H, W = p.W;
+  const int D = p.D, L = p.L, N = p.N;
   const int d = blk * kBwdChans + ch;
   const bool dval = d < D, val = dval && n < N;
   const int ds = dval ? d : 0, ns = n < N ? n : 0;
@@ -97,16 +101,14 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
   const bool sdv = sd < D, snv = sr < N;
   const int sdc = sdv ? sd : 0, snc = snv ? sr : 0;
   const float sbias = p.dt_bias[k * D + sdc];
-  const float* sx = p.x + ((int64_t)b * D + sdc) * L;
-  const float* sg = p.dy + ((int64_t)b * D + sdc) * L;
+  // column walks read the transposed copies, where step l of direction 1 is element l
+  const float* sx = ((k & 1) ? p.xT : p.x) + ((int64_t)b * D + sdc) * L;
+  const float* sg = ((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + sdc) * L;
   const float* sdt = p.dt + ((int64_t)bk * D + sdc) * L;
   const float* sB = p.Bs + ((int64_t)bk * N + snc) * L;
   const float* sC = p.Cs + ((int64_t)bk * N + snc) * L;
-  auto pixel = [&](int l) {  // pixel visited at step l of direction k
-    const int m = k >= 2 ? L - 1 - l : l;
-    if ((k & 1) == 0) return m;
-    const int w = m / H;
-    return (m - w * H) * W + w;
+  auto pixel = [&](int l) {  // element of sx / sg visited at step l of direction k
+    return k >= 2 ? L - 1 - l : l;
   };
   float stage[kOps];
   auto load_stage = [&](int s, bool with_g) {
@@ -296,7 +298,7 @@ size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_
   const int64_t L = H * W, nseg = (L + kSeg - 1) / kSeg, nblk = (D + kBwdChans - 1) / kBwdChans;
   auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
   return up(B * 4 * D * L) + up(B * 4 * nseg * D * N) + 2 * up(B * 4 * nblk * N * L) + up(B * 4 * D * N) +
-         2 * up(B * 4 * D);
+         2 * up(B * 4 * D) + 2 * up(B * D * L);
 }
 
 hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
@@ -326,6 +328,12 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.dbp = reinterpret_cast<float*>(base);
   base += up(a.B * 4 * a.D);
   p.dDp = reinterpret_cast<float*>(base);
+  base += up(a.B * 4 * a.D);
+  float* xT = reinterpret_cast<float*>(base);
+  base += up(a.B * a.D * L);
+  float* dyT = reinterpret_cast<float*>(base);
+  p.xT = xT;
+  p.dyT = dyT;
   p.D = (int)a.D;
   p.H = (int)a.H;
   p.W = (int)a.W;
@@ -335,9 +343,11 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.nblk = (int)nblk;
   const int64_t blocks = a.B * 4 * nblk;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_transpose<float>(a.x, xT, (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
   if (e != hipSuccess) return e;
+  if ((e = launch_transpose<float>(a.dy, dyT, (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_bc, dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, a.dBs, a.dCs, a.B * 4,
                      (int)nblk, (int)a.N, (int)L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
