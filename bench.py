@@ -40,10 +40,15 @@ SLOTS_PER_UPDATE = 4 + TRANS_SLOTS
 PEAK_UPDATES_PER_S = CUS * CLOCK_HZ * VALU_LANES_PER_CLK / SLOTS_PER_UPDATE  # 9.83e12
 FP32_MFMA_PEAK = 157.3e12  # dense fp32 matrix FLOP/s
 
-KERNEL_SOURCES = sorted(
-    os.path.relpath(os.path.join(dp, f), ROOT)
-    for dp, _, fs in os.walk(os.path.join(ROOT, "selective_scan_crossscan_amd", "csrc"))
-    for f in fs if f.endswith((".hip", ".h")))
+_CSRC = os.path.join("selective_scan_crossscan_amd", "csrc")
+# The sources that define each profiled kernel and its launch (a counter record is
+# valid while these are unchanged).
+KERNEL_SOURCES = {
+    "ss2d_forward_kernel": ["ss2d_kernels.h", "ss2d_plan.hip", "ss2d_f32_t16.hip", "ss2d_f32_t8.hip",
+                            "ss2d_bf16_t16.hip", "ss2d_bf16_t8.hip"],
+    "project_kernel": ["ss2d_kernels.h", "ss2d_project.hip"],
+    "bwd_scan_kernel": ["ss2d_kernels.h", "ss2d_backward.hip"],
+}
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
@@ -55,10 +60,10 @@ def traffic_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
     return os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.md")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "ss2d_forward_kernel") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, _CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -200,7 +205,8 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
                         "copy_expected_kib": expected_kib, "scale": expected_kib / probe_kib}
     fetch_b = per["FETCH_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["FETCH_SIZE"]["scale"]
     write_b = per["WRITE_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["WRITE_SIZE"]["scale"]
-    rec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(),
+    rec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
+           "kernel_sources": KERNEL_SOURCES[kernel],
            "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
            "algorithmic_bytes": alg_bytes, "counters": per}
     lines = [f"# {kernel} — {workload} — HBM traffic (rocprofv3 counters)", "",
