@@ -48,12 +48,13 @@ KERNEL_SOURCES = {
                             "ss2d_bf16_t16.hip", "ss2d_bf16_t8.hip"],
     "project_kernel": ["ss2d_kernels.h", "ss2d_project.hip"],
     "bwd_scan_kernel": ["ss2d_kernels.h", "ss2d_backward.hip"],
+    "channel_last_kernel": ["ss2d_kernels.h", "ss2d_epilogue.hip"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
 STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel", "bwd_scan_kernel",
-                "bwd_reduce_bc", "bwd_merge", "bwd_params"}
+                "bwd_reduce_bc", "bwd_merge", "bwd_params", "channel_last_kernel"}
 
 
 def traffic_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
@@ -135,11 +136,12 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
     import csv
     shape = ss2d_inputs.CONFIGS[cfg]
     os.makedirs(PROFILES, exist_ok=True)
-    from_x, bwd = path == "from_x", path == "backward"
-    kernel = "project_kernel" if from_x else "bwd_scan_kernel" if bwd else KERNEL_PREFIX
-    workload = shape.name + ("_from_x" if from_x else "_backward" if bwd else "")
-    cmds = {k: v.format(d=folder, c=cfg, x=f" --path {path}" if path != "scan" else "")
-            for k, v in PROFILE_COMMANDS.items()}
+    from_x, bwd, epi = path == "from_x", path == "backward", path == "epilogue"
+    kernel = ("project_kernel" if from_x else "bwd_scan_kernel" if bwd else "channel_last_kernel" if epi
+              else KERNEL_PREFIX)
+    workload = shape.name + ("" if path == "scan" else "_" + path)
+    extra = " --epilogue" if epi else f" --path {path}" if path != "scan" else ""
+    cmds = {k: v.format(d=folder, c=cfg, x=extra) for k, v in PROFILE_COMMANDS.items()}
 
     # Kernel-trace statistics, next to the bench line printed by the same run.
     with open(_find(folder, "stats_kernel_stats.csv")) as f:
@@ -151,6 +153,10 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
         alg_bytes, alg_flops = projection_work(shape)
         work = (f"Projection per launch: {alg_flops:.4e} FLOP (fp32 MFMA), algorithmic bytes {alg_bytes:.4e} "
                 "(x read once; dt, Bs, Cs written once; weights).")
+    elif epi:
+        alg_bytes = 2 * shape.elem_bytes * shape.B * shape.D * shape.L + 8 * shape.D
+        work = (f"Epilogue per launch: algorithmic bytes {alg_bytes:.4e} (y read once, the channel-last output "
+                "written once, gamma and beta).")
     elif bwd:
         alg_bytes = 4 * shape.B * shape.L * (11 * shape.D + 16 * shape.N)
         work = (f"Backward per launch: {shape.updates:.4e} (b,k,d,n,l) terms; algorithmic bytes {alg_bytes:.4e} "
@@ -179,6 +185,11 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
               f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs for {kernel}; "
               f"{per_step:.1f} µs per step as the sum of the averages of the kernels a forward launches once "
               f"each ({', '.join(sorted(STEP_KERNELS))}, where present).", ""]
+    if epi:
+        ej = bench["epilogue"]
+        lines += [f"The epilogue timed by bench.py with HIP events: {ej['us']:.1f} µs; {kernel} by rocprofv3: "
+                  f"{kern_avg:.1f} µs, i.e. {alg_bytes / (kern_avg * 1e-6) / 1e9:.0f} GB/s of algorithmic bytes "
+                  f"({alg_bytes / (kern_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s).", ""]
     if from_x:
         pj = bench["projection"]
         lines += [f"The projection alone, timed by bench.py with HIP events (transpose of x + {kernel}): "
@@ -262,11 +273,13 @@ def main() -> int:
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device roofline probes")
     ap.add_argument("--epilogue", action="store_true",
                     help="also time the channel-last LayerNorm epilogue on the forward's output")
+    ap.add_argument("--summarize-kind", choices=["scan", "from_x", "backward", "epilogue"], default=None,
+                    help="which kernel --summarize-profile summarises (default: --path)")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="turn the rocprofv3 output of PROFILE_COMMANDS in DIR into the summaries under profiles/")
     args = ap.parse_args()
     if args.summarize_profile:
-        return summarize_profile(args.summarize_profile, args.config, args.path)
+        return summarize_profile(args.summarize_profile, args.config, args.summarize_kind or args.path)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
