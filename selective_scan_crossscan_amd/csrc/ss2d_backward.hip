@@ -115,11 +115,13 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
     const int l = s * kSeg + si;
     const bool in = l < L;
     const int px = in ? pixel(l) : 0, lc = in ? l : 0;
-    stage[kOpX] = sx[px];
-    stage[kOpG] = with_g ? sg[px] : 0.f;
+    // channels past D stage x = dy = 0 and states past N stage Bs = Cs = 0, so
+    // their lanes compute zero states, adjoints and partials with no masks
+    stage[kOpX] = sdv ? sx[px] : 0.f;
+    stage[kOpG] = with_g && sdv ? sg[px] : 0.f;
     stage[kOpDel] = sdt[lc] + sbias;  // dt + dt_bias until stored
-    stage[kOpB] = sB[lc];
-    stage[kOpC] = with_g ? sC[lc] : 0.f;
+    stage[kOpB] = snv ? sB[lc] : 0.f;
+    stage[kOpC] = with_g && snv ? sC[lc] : 0.f;
   };
   auto store_stage = [&](int buf) {
     const float pre = stage[kOpDel];
@@ -184,10 +186,10 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
         const float qd = q * del[i];
         dA = fmaf(qd * aa[i], hp, dA);
         a_next = aa[i];
-        red[0][i][tid] = val ? hs[i] * g : 0.f;
-        red[1][i][tid] = val ? qd * u : 0.f;
-        dup[i] = val ? qd * Bv : 0.f;
-        ddp[i] = val ? q * fmaf(A * aa[i], hp, Bv * u) : 0.f;
+        red[0][i][tid] = hs[i] * g;
+        red[1][i][tid] = qd * u;
+        dup[i] = qd * Bv;
+        ddp[i] = q * fmaf(A * aa[i], hp, Bv * u);
       }
     }
     // sums over the 16 states of each channel, all steps of the segment at once
