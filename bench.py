@@ -47,13 +47,13 @@ KERNEL_SOURCES = {
     "ss2d_forward_kernel": ["ss2d_kernels.h", "ss2d_plan.hip", "ss2d_f32_t16.hip", "ss2d_f32_t8.hip",
                             "ss2d_bf16_t16.hip", "ss2d_bf16_t8.hip"],
     "project_kernel": ["ss2d_kernels.h", "ss2d_project.hip"],
-    "bwd_scan_kernel": ["ss2d_kernels.h", "ss2d_backward.hip"],
+    "bwd_chunk_kernel": ["ss2d_kernels.h", "ss2d_backward.hip"],
     "channel_last_kernel": ["ss2d_kernels.h", "ss2d_epilogue.hip"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
-STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel", "bwd_scan_kernel",
+STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel", "bwd_chunk_kernel",
                 "bwd_reduce_bc", "bwd_merge", "bwd_params", "channel_last_kernel"}
 
 
@@ -137,7 +137,7 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
     shape = ss2d_inputs.CONFIGS[cfg]
     os.makedirs(PROFILES, exist_ok=True)
     from_x, bwd, epi = path == "from_x", path == "backward", path == "epilogue"
-    kernel = ("project_kernel" if from_x else "bwd_scan_kernel" if bwd else "channel_last_kernel" if epi
+    kernel = ("project_kernel" if from_x else "bwd_chunk_kernel" if bwd else "channel_last_kernel" if epi
               else KERNEL_PREFIX)
     workload = shape.name + ("" if path == "scan" else "_" + path)
     extra = " --epilogue" if epi else f" --path {path}" if path != "scan" else ""

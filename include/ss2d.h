@@ -170,9 +170,9 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
  * must not overlap an input or another output (SS2D_ERR_ALIAS).  dtype must be
  * SS2D_F32 (SS2D_ERR_DTYPE otherwise); N is 1..16.  All sums run in a fixed
  * order, so results are deterministic.  Takes a stream-ordered temporary of
- * about B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*N*L + B*4*D*N*ceil(L/16) fp32 values
- * (du, transposed copies of x and dy, per-channel-block partials of dBs and dCs,
- * state checkpoints every 16 steps) and runs six kernels on `stream`.  Validation, error reporting and thread safety
+ * about B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*N*L + 16*B*4*D*N*ceil(L/128) fp32
+ * values (du, transposed copies of x and dy, per-channel-block partials of dBs
+ * and dCs, the state entering every 8 steps) and runs six kernels on `stream`.  Validation, error reporting and thread safety
  * as for ss2d_forward; pointers need 4-byte alignment (SS2D_ERR_ALIGN).
  */
 int ss2d_backward(const void* x, const void* dt, const float* A_log, const float* dt_bias,

@@ -12,20 +12,22 @@
 //   dA_log = A * sum_{b,l} q_l delta_l a_l h_{l-1},  ddt_bias = sum_{b,l} ddt_l,
 //   dDs = sum_{b,l} g_l u_l,  dx = the merge of du.
 //
-// How it runs (a first, plain design: one lane per (batch, direction, channel,
-// state) walking the whole sequence).
-//   * A workgroup is 16 channels x 16 states of one (batch, direction): a DPP row
-//     of 16 lanes holds the states of one channel, so the sums over states are
-//     four row rotations.
-//   * Pass 1 walks the sequence forwards and stores the state entering every
-//     16-step segment.  Pass 2 walks the segments backwards: it recomputes the
-//     segment's states from its checkpoint into registers, then walks the steps
-//     backwards with the state adjoint.
-//   * A segment's operands (x, dy, dt per channel; Bs, Cs per state) are loaded
-//     once per workgroup, one value per thread, a segment ahead, and staged in
-//     LDS; the sums over states run once per segment for all its steps.
-//   * dBs/dCs partials are summed over the workgroup's 16 channels through LDS
-//     once per segment and written per channel block; a second kernel sums the
+// How it runs (the forward's decomposition, run twice).
+//   * A workgroup is 16 channels of one (batch, direction); a DPP row of 16 lanes
+//     owns one channel, lane s the 8 consecutive steps 8s.. of each 128-step
+//     chunk, and every lane loops over the states.
+//   * Pass A walks the chunks forwards: per state each lane folds its steps into
+//     one affine map h -> P h + Q, an inclusive prefix scan of the row's maps
+//     (DPP row_shr) gives every lane its entering state, which is stored; lane
+//     15 carries the chunk's last state to the next chunk.
+//   * Pass B walks the chunks backwards: per state each lane recomputes its
+//     states from the stored one, folds the adjoint q_l = a_{l+1} q_{l+1} +
+//     Cs_l g_l over its steps from the right, a suffix scan (DPP row_shl) gives
+//     every lane the adjoint entering from its right, and the lane walks its
+//     steps backwards accumulating du and ddelta over the states in registers.
+//     Lane 0 carries q and a of the chunk's first step to the chunk before.
+//   * dBs/dCs partials are summed over the workgroup's 16 channels through LDS per
+//     state and chunk and written per channel block; a second kernel sums the
 //     blocks in a fixed order, so results are deterministic (no atomics).
 //   * Column walks read transposed copies of x and dy (made first), so every
 //     operand load is contiguous along the steps.
@@ -36,7 +38,6 @@
 namespace ss2d {
 namespace {
 
-constexpr int kSeg = 16;      // steps per checkpointed segment
 constexpr int kBwdChans = 16;  // channels per workgroup
 
 struct BwdParams {
@@ -52,7 +53,7 @@ struct BwdParams {
   const float* dyT;
   float* ddt;  // (B, 4, D, L) out
   float* du;   // (B, 4, D, L) temporary
-  float* hck;  // (B*4, nseg, D, N) temporary: state entering each segment
+  float* hck;  // (B*4, nseg, D, N, 16) temporary: state entering each lane's steps of each chunk
   float* dBp;  // (B*4, nblk, N, L) temporary
   float* dCp;
   float* dAp;  // (B, 4D, N) temporary
@@ -70,168 +71,220 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// Operands of one 16-step segment, staged in LDS once per workgroup: per channel
-// (x and dy at the visited pixels, delta = softplus(dt + dt_bias) and its
-// derivative sigmoid(dt + dt_bias)) and per state (Bs, Cs).  delta and the
-// sigmoid are computed once per (channel, step) by the staging thread.
-enum { kOpX, kOpG, kOpDel, kOpSig, kOpB, kOpC, kOps };
+// ---------------------------------------------------------------- chunked form
+// The same gradients with the forward's decomposition: a DPP row of 16 lanes owns
+// one channel, lane s the kCT consecutive steps s*kCT.. of each 128-step chunk,
+// and every lane loops over the states.  The recurrence crosses the lanes as an
+// inclusive prefix scan of affine maps h -> P h + Q (pass A, chunks left to
+// right), its adjoint q_l = a_{l+1} q_{l+1} + Cs_l g_l as a suffix scan of the
+// same maps (pass B, chunks right to left), so the sums over states are plain
+// register accumulations and each step costs a few operations per state.
+constexpr int kCT = 8;                // steps per lane in a chunk
+constexpr int kChunk = 16 * kCT;      // steps per chunk
+constexpr int kPad = kChunk + 16;     // LDS row: one pad slot per lane's run, so a row's lanes hit distinct banks
 
-__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdParams p) {
-  __shared__ float red[2][kSeg][256];
-  __shared__ float op[2][kOps][kSeg][16];  // double-buffered, [step][channel or state]
-  const int tid = threadIdx.x, n = tid & 15, ch = tid >> 4;
+template <int CTRL>
+__device__ __forceinline__ float dppf(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Value of lane j (0..15) of this lane's row.
+__device__ __forceinline__ float row_lane(float v, int j) {
+  const int lane = threadIdx.x & 63;
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & ~15) + j) << 2, __float_as_int(v)));
+}
+
+// Inclusive scans over a row of maps x -> P x + Q.  Prefix: lane i composes lanes
+// 0..i, the lower lanes applied first.  Suffix: lane i composes lanes i..15, the
+// higher lanes applied first (the adjoint runs from the end).  A lane past the
+// row edge contributes the identity (1, 0).
+template <int SHIFT_BASE>
+__device__ __forceinline__ void scan_maps(float& P, float& Q) {
+#pragma unroll
+  for (int lv = 0; lv < 4; ++lv) {
+    float Pk, Qk;
+    switch (lv) {
+      case 0: Pk = dppf<SHIFT_BASE + 1>(1.f, P); Qk = dppf<SHIFT_BASE + 1>(0.f, Q); break;
+      case 1: Pk = dppf<SHIFT_BASE + 2>(1.f, P); Qk = dppf<SHIFT_BASE + 2>(0.f, Q); break;
+      case 2: Pk = dppf<SHIFT_BASE + 4>(1.f, P); Qk = dppf<SHIFT_BASE + 4>(0.f, Q); break;
+      default: Pk = dppf<SHIFT_BASE + 8>(1.f, P); Qk = dppf<SHIFT_BASE + 8>(0.f, Q); break;
+    }
+    Q = fmaf(P, Qk, Q);
+    P = P * Pk;
+  }
+}
+constexpr int kRowShr = 0x110;  // row_shr:n = 0x110 + n (from lane i - n)
+constexpr int kRowShl = 0x100;  // row_shl:n = 0x100 + n (from lane i + n)
+
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
+  __shared__ float sB[16][kPad];
+  __shared__ float sC[16][kPad];
+  __shared__ float red[2][16][kPad];
+  __shared__ float carry_q[16][16], carry_a[16][16], dA_s[16][16], a2s[16][16];
+  const int tid = threadIdx.x, s = tid & 15, ch = tid >> 4;
   const int blk = blockIdx.x % p.nblk;
   const int bk = blockIdx.x / p.nblk;  // b * 4 + k
   const int k = bk & 3, b = bk >> 2;
-  const int D = p.D, L = p.L, N = p.N;
+  const int D = p.D, L = p.L, N = p.N, nch = p.nseg;
   const int d = blk * kBwdChans + ch;
-  const bool dval = d < D, val = dval && n < N;
-  const int ds = dval ? d : 0, ns = n < N ? n : 0;
-  const int c = k * D + ds;
-  const float A = val ? -expf(p.A_log[(int64_t)c * N + ns]) : 0.f;
-  const float Al2 = A * kLog2e;
-  const float Dsk = p.Ds[c];
-  auto hck = [&](int s) -> float& { return p.hck[(((int64_t)bk * p.nseg + s) * D + ds) * N + ns]; };
+  const bool dval = d < D;
+  const int ds = dval ? d : 0;
+  const int c_idx = k * D + ds;
+  a2s[ch][s] = (dval && s < N) ? -expf(p.A_log[(int64_t)c_idx * N + s]) * kLog2e : 0.f;
+  carry_q[ch][s] = 0.f;
+  carry_a[ch][s] = 1.f;
+  dA_s[ch][s] = 0.f;
+  const float bias = p.dt_bias[c_idx], Dsk = p.Ds[c_idx];
+  const float* xs = ((k & 1) ? p.xT : p.x) + ((int64_t)b * D + ds) * L;
+  const float* gs = ((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + ds) * L;
+  const float* dtr = p.dt + ((int64_t)bk * D + ds) * L;
+  const float* Bb = p.Bs + (int64_t)bk * N * L;
+  const float* Cb = p.Cs + (int64_t)bk * N * L;
+  const int64_t row = ((int64_t)bk * D + ds) * L;
+  auto hck = [&](int c, int n) -> float& {
+    return p.hck[((((int64_t)bk * nch + c) * D + ds) * N + n) * 16 + s];
+  };
+  const int j0 = s * kCT, jp0 = j0 + s;  // first step of this lane in the chunk, and its padded LDS slot
 
-  // this thread's share of the staging: step i = tid & 15 of the segment, for
-  // channel (tid >> 4) of the per-channel operands and state (tid >> 4) of the
-  // per-state ones
-  const int si = tid & 15, sr = tid >> 4;
-  const int sd = blk * kBwdChans + sr;
-  const bool sdv = sd < D, snv = sr < N;
-  const int sdc = sdv ? sd : 0, snc = snv ? sr : 0;
-  const float sbias = p.dt_bias[k * D + sdc];
-  // column walks read the transposed copies, where step l of direction 1 is element l
-  const float* sx = ((k & 1) ? p.xT : p.x) + ((int64_t)b * D + sdc) * L;
-  const float* sg = ((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + sdc) * L;
-  const float* sdt = p.dt + ((int64_t)bk * D + sdc) * L;
-  const float* sB = p.Bs + ((int64_t)bk * N + snc) * L;
-  const float* sC = p.Cs + ((int64_t)bk * N + snc) * L;
-  auto pixel = [&](int l) {  // element of sx / sg visited at step l of direction k
-    return k >= 2 ? L - 1 - l : l;
-  };
-  float stage[kOps];
-  auto load_stage = [&](int s, bool with_g) {
-    const int l = s * kSeg + si;
-    const bool in = l < L;
-    const int px = in ? pixel(l) : 0, lc = in ? l : 0;
-    // channels past D stage x = dy = 0 and states past N stage Bs = Cs = 0, so
-    // their lanes compute zero states, adjoints and partials with no masks
-    stage[kOpX] = sdv ? sx[px] : 0.f;
-    stage[kOpG] = with_g && sdv ? sg[px] : 0.f;
-    stage[kOpDel] = sdt[lc] + sbias;  // dt + dt_bias until stored
-    stage[kOpB] = snv ? sB[lc] : 0.f;
-    stage[kOpC] = with_g && snv ? sC[lc] : 0.f;
-  };
-  auto store_stage = [&](int buf) {
-    const float pre = stage[kOpDel];
-    stage[kOpDel] = softplus_f32(pre);
-    stage[kOpSig] = 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e));
+  float del[kCT], uu[kCT], gg[kCT], sig[kCT];
+  auto load_lane = [&](int c, bool with_g) {
 #pragma unroll
-    for (int j = 0; j < kOps; ++j) op[buf][j][si][sr] = stage[j];
-  };
-
-  // pass 1: states entering every segment
-  float h = 0.f;
-  load_stage(0, false);
-  store_stage(0);
-  __syncthreads();
-  for (int s = 0; s < p.nseg; ++s) {
-    const int buf = s & 1;
-    if (val) hck(s) = h;
-    if (s + 1 < p.nseg) load_stage(s + 1, false);
-    const int cnt = L - s * kSeg < kSeg ? L - s * kSeg : kSeg;
-#pragma unroll
-    for (int i = 0; i < kSeg; ++i) {
-      if (i < cnt) {
-        const float del = op[buf][kOpDel][i][ch];
-        h = fmaf(__builtin_amdgcn_exp2f(del * Al2), h, del * op[buf][kOpB][i][n] * op[buf][kOpX][i][ch]);
-      }
+    for (int i = 0; i < kCT; ++i) {
+      const int l = c * kChunk + j0 + i;
+      const bool in = dval && l < L;
+      const int li = in ? l : 0, xi = in ? (k >= 2 ? L - 1 - l : l) : 0;
+      const float pre = dtr[li] + bias;
+      del[i] = in ? softplus_f32(pre) : 0.f;
+      sig[i] = in ? 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;
+      uu[i] = in ? xs[xi] : 0.f;
+      gg[i] = in && with_g ? gs[xi] : 0.f;
     }
-    if (s + 1 < p.nseg) store_stage(buf ^ 1);
+  };
+  auto stage = [&](int c, bool with_c) {
+    for (int e = tid; e < 16 * kChunk; e += 256) {
+      const int n = e / kChunk, j = e - n * kChunk;
+      const int l = c * kChunk + j;
+      const bool in = n < N && l < L;
+      const int64_t off = in ? (int64_t)n * L + l : 0;
+      const int jp = j + j / kCT;
+      sB[n][jp] = in ? Bb[off] : 0.f;
+      if (with_c) sC[n][jp] = in ? Cb[off] : 0.f;
+    }
+  };
+  __syncthreads();
+
+  // pass A: the state entering each lane's steps of every chunk
+  for (int c = 0; c < nch; ++c) {
+    stage(c, false);
+    load_lane(c, false);
+    __syncthreads();
+    float sdel = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) sdel += del[i];
+    for (int n = 0; n < N; ++n) {
+      const float A2 = a2s[ch][n];
+      float P = __builtin_amdgcn_exp2f(A2 * sdel), Q = 0.f;
+#pragma unroll
+      for (int i = 0; i < kCT; ++i)
+        Q = fmaf(__builtin_amdgcn_exp2f(del[i] * A2), Q, del[i] * uu[i] * sB[n][jp0 + i]);
+      scan_maps<kRowShr>(P, Q);
+      const float Pe = dppf<kRowShr + 1>(1.f, P), Qe = dppf<kRowShr + 1>(0.f, Q);
+      const float hc = carry_q[ch][n];
+      if (dval) hck(c, n) = fmaf(Pe, hc, Qe);
+      const float hout = fmaf(P, hc, Q);  // lane 15: the state leaving the chunk
+      if (s == 15) carry_q[ch][n] = hout;
+    }
     __syncthreads();
   }
 
-  // pass 2: segments from the last, steps from the last
-  float q = 0.f, a_next = 0.f, dA = 0.f, dbias = 0.f, dD = 0.f;
-  const int64_t row = ((int64_t)bk * D + ds) * L;  // (b, k, d) row of ddt and du
-  int buf = 0;
-  load_stage(p.nseg - 1, true);
-  store_stage(buf);
+  // pass B: chunks from the last; the adjoint enters each lane from the right
+  carry_q[ch][s] = 0.f;
   __syncthreads();
-  for (int s = p.nseg - 1; s >= 0; --s) {
-    const int l0 = s * kSeg;
-    const int cnt = L - l0 < kSeg ? L - l0 : kSeg;
-    const float h_in = val ? hck(s) : 0.f;
-    if (s > 0) load_stage(s - 1, true);
-    float hs[kSeg], del[kSeg], aa[kSeg];
-    float hv = h_in;
+  float dbias = 0.f, dD = 0.f;
+  for (int c = nch - 1; c >= 0; --c) {
+    stage(c, true);
+    load_lane(c, true);
+    __syncthreads();
+    float du[kCT], dd[kCT];
 #pragma unroll
-    for (int i = 0; i < kSeg; ++i) {
-      del[i] = op[buf][kOpDel][i][ch];
-      aa[i] = __builtin_amdgcn_exp2f(del[i] * Al2);
-      hv = fmaf(aa[i], hv, del[i] * op[buf][kOpB][i][n] * op[buf][kOpX][i][ch]);
-      hs[i] = hv;
-    }
-    float dup[kSeg], ddp[kSeg];
+    for (int i = 0; i < kCT; ++i) du[i] = dd[i] = 0.f;
+    for (int n = 0; n < N; ++n) {
+      const float A2 = a2s[ch][n], A = A2 * kLn2;
+      float a[kCT], h[kCT];
+      const float h_in = dval ? hck(c, n) : 0.f;
+      float hv = h_in;
 #pragma unroll
-    for (int i = kSeg - 1; i >= 0; --i) {
-      dup[i] = 0.f;
-      ddp[i] = 0.f;
-      if (i < cnt) {
-        const float g = op[buf][kOpG][i][ch], u = op[buf][kOpX][i][ch];
-        const float Bv = op[buf][kOpB][i][n], Cv = op[buf][kOpC][i][n];
-        const float hp = i > 0 ? hs[i - 1] : h_in;
-        q = fmaf(a_next, q, Cv * g);
-        const float qd = q * del[i];
-        dA = fmaf(qd * aa[i], hp, dA);
-        a_next = aa[i];
-        red[0][i][tid] = hs[i] * g;
-        red[1][i][tid] = qd * u;
-        dup[i] = qd * Bv;
-        ddp[i] = q * fmaf(A * aa[i], hp, Bv * u);
+      for (int i = 0; i < kCT; ++i) {
+        a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
+        hv = fmaf(a[i], hv, del[i] * uu[i] * sB[n][jp0 + i]);
+        h[i] = hv;
       }
-    }
-    // sums over the 16 states of each channel, all steps of the segment at once
+      const float acar = carry_a[ch][n], qcar = carry_q[ch][n];
+      const float a_right = dppf<kRowShl + 1>(acar, a[0]);  // decay of the step after this lane's last
+      float P = 1.f, Q = 0.f;
 #pragma unroll
-    for (int i = 0; i < kSeg; ++i) {
-      dup[i] = row_sum16(dup[i]);
-      ddp[i] = row_sum16(ddp[i]);
-    }
-    if (n == 0 && dval) {
+      for (int i = kCT - 1; i >= 0; --i) {
+        const float an = i == kCT - 1 ? a_right : a[i + 1];
+        Q = fmaf(an, Q, sC[n][jp0 + i] * gg[i]);
+        P *= an;
+      }
+      scan_maps<kRowShl>(P, Q);
+      const float Pe = dppf<kRowShl + 1>(1.f, P), Qe = dppf<kRowShl + 1>(0.f, Q);
+      float q = fmaf(Pe, qcar, Qe);  // adjoint at the step after this lane's last
+      float dA = 0.f;
 #pragma unroll
-      for (int i = 0; i < kSeg; ++i) {
-        if (i < cnt) {
-          const float g = op[buf][kOpG][i][ch], u = op[buf][kOpX][i][ch];
-          const float ddt = ddp[i] * op[buf][kOpSig][i][ch];
-          p.ddt[row + l0 + i] = ddt;
-          p.du[row + l0 + i] = fmaf(Dsk, g, dup[i]);
-          dbias += ddt;
-          dD = fmaf(g, u, dD);
+      for (int i = kCT - 1; i >= 0; --i) {
+        const float an = i == kCT - 1 ? a_right : a[i + 1];
+        const float Bv = sB[n][jp0 + i];
+        q = fmaf(an, q, sC[n][jp0 + i] * gg[i]);
+        const float hp = i > 0 ? h[i - 1] : h_in;
+        const float qd = q * del[i];
+        du[i] = fmaf(qd, Bv, du[i]);
+        dd[i] = fmaf(q, fmaf(A * a[i], hp, Bv * uu[i]), dd[i]);
+        dA = fmaf(qd * a[i], hp, dA);
+        red[0][ch][jp0 + i] = h[i] * gg[i];
+        red[1][ch][jp0 + i] = qd * uu[i];
+      }
+      const float q0 = row_lane(q, 0), a0 = row_lane(a[0], 0);
+      dA = row_sum16(dA);
+      if (s == 0) {
+        carry_q[ch][n] = q0;
+        carry_a[ch][n] = a0;
+        dA_s[ch][n] += dA;
+      }
+      __syncthreads();
+      for (int o = tid; o < 2 * kChunk; o += 256) {
+        const int which = o / kChunk, j = o - which * kChunk;
+        const int l = c * kChunk + j;
+        if (l < L) {
+          const int jp = j + j / kCT;
+          float sum = 0.f;
+#pragma unroll
+          for (int c2 = 0; c2 < 16; ++c2) sum += red[which][c2][jp];
+          float* dst = which == 0 ? p.dCp : p.dBp;
+          dst[(((int64_t)bk * p.nblk + blk) * N + n) * L + l] = sum;
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
-    // dCs (0) and dBs (1) partials of the segment, summed over the 16 channels
-    for (int o = tid; o < 2 * kSeg * 16; o += 256) {
-      const int which = o / (kSeg * 16), rem = o - which * (kSeg * 16);
-      const int i = rem >> 4, nn = rem & 15;
-      if (i < cnt && nn < N) {
-        float sum = 0.f;
 #pragma unroll
-        for (int c2 = 0; c2 < kBwdChans; ++c2) sum += red[which][i][c2 * 16 + nn];
-        float* dst = which == 0 ? p.dCp : p.dBp;
-        dst[(((int64_t)bk * p.nblk + blk) * N + nn) * L + l0 + i] = sum;
+    for (int i = 0; i < kCT; ++i) {
+      const int l = c * kChunk + j0 + i;
+      if (dval && l < L) {
+        const float ddt = dd[i] * sig[i];
+        p.ddt[row + l] = ddt;
+        p.du[row + l] = fmaf(Dsk, gg[i], du[i]);
+        dbias += ddt;
+        dD = fmaf(gg[i], uu[i], dD);
       }
     }
-    if (s > 0) store_stage(buf ^ 1);
-    buf ^= 1;
-    __syncthreads();
   }
-  if (val) p.dAp[((int64_t)b * 4 * D + c) * N + ns] = dA;
-  if (n == 0 && dval) {
-    p.dbp[(int64_t)b * 4 * D + c] = dbias;
-    p.dDp[(int64_t)b * 4 * D + c] = dD;
+  dbias = row_sum16(dbias);
+  dD = row_sum16(dD);
+  if (dval && s < N) p.dAp[((int64_t)b * 4 * D + c_idx) * N + s] = dA_s[ch][s];
+  if (dval && s == 0) {
+    p.dbp[(int64_t)b * 4 * D + c_idx] = dbias;
+    p.dDp[(int64_t)b * 4 * D + c_idx] = dD;
   }
 }
 
@@ -297,14 +350,14 @@ __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_lo
 }  // namespace
 
 size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
-  const int64_t L = H * W, nseg = (L + kSeg - 1) / kSeg, nblk = (D + kBwdChans - 1) / kBwdChans;
+  const int64_t L = H * W, nch = (L + kChunk - 1) / kChunk, nblk = (D + kBwdChans - 1) / kBwdChans;
   auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
-  return up(B * 4 * D * L) + up(B * 4 * nseg * D * N) + 2 * up(B * 4 * nblk * N * L) + up(B * 4 * D * N) +
+  return up(B * 4 * D * L) + up(B * 4 * nch * D * N * 16) + 2 * up(B * 4 * nblk * N * L) + up(B * 4 * D * N) +
          2 * up(B * 4 * D) + 2 * up(B * D * L);
 }
 
 hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
-  const int64_t L = a.H * a.W, nseg = (L + kSeg - 1) / kSeg, nblk = (a.D + kBwdChans - 1) / kBwdChans;
+  const int64_t L = a.H * a.W, nseg = (L + kChunk - 1) / kChunk, nblk = (a.D + kBwdChans - 1) / kBwdChans;
   auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
   char* base = static_cast<char*>(scratch);
   BwdParams p;
@@ -320,7 +373,7 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.du = reinterpret_cast<float*>(base);
   base += up(a.B * 4 * a.D * L);
   p.hck = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * nseg * a.D * a.N);
+  base += up(a.B * 4 * nseg * a.D * a.N * 16);
   p.dBp = reinterpret_cast<float*>(base);
   base += up(a.B * 4 * nblk * a.N * L);
   p.dCp = reinterpret_cast<float*>(base);
@@ -348,7 +401,7 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   hipError_t e = launch_transpose<float>(a.x, xT, (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
   if (e != hipSuccess) return e;
   if ((e = launch_transpose<float>(a.dy, dyT, (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream, p);
+  hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_bc, dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, a.dBs, a.dCs, a.B * 4,
                      (int)nblk, (int)a.N, (int)L);
