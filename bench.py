@@ -169,6 +169,7 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
              "| kernel | calls | average µs | min µs | max µs | share |", "|---|---|---|---|---|---|"]
     kern_avg = None
     per_step = 0.0  # fused plans launch each of a forward's kernels once per step
+    present = []
     for r in stats:
         name = r["Name"]
         if len(name) > 90:
@@ -176,15 +177,17 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
         avg = float(r["AverageNs"]) / 1e3
         if _is_kernel(r["Name"], kernel):
             kern_avg = avg
-        if any(_is_kernel(r["Name"], k) for k in STEP_KERNELS):
-            per_step += avg
+        for k in STEP_KERNELS:
+            if _is_kernel(r["Name"], k):
+                per_step += avg
+                present.append(k)
         lines.append(f"| `{name}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
     lines += ["", f"bench.py's own HIP-event average over the timed steps of this run: "
                   f"{bench['kernel_us']:.1f} µs per step (roofline frac {bench['roofline']['frac']:.3f}).",
               f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs for {kernel}; "
-              f"{per_step:.1f} µs per step as the sum of the averages of the kernels a forward launches once "
-              f"each ({', '.join(sorted(STEP_KERNELS))}, where present).", ""]
+              f"{per_step:.1f} µs per step as the sum of the average durations of the step's kernels, one launch each "
+              f"({', '.join(sorted(present))}).", ""]
     if epi:
         ej = bench["epilogue"]
         lines += [f"The epilogue timed by bench.py with HIP events: {ej['us']:.1f} µs; {kernel} by rocprofv3: "
