@@ -304,9 +304,6 @@ def main() -> int:
     print(f"[bench] workload {shape}", file=sys.stderr, flush=True)
     from_x = args.path == "from_x"
     bwd = args.path == "backward"
-    if bwd and shape.dtype != "f32":
-        print("bench.py: the backward takes fp32 workloads only", file=sys.stderr)
-        return 2
     inp = ss2d_inputs.generate_projected(shape, seed=0) if from_x else ss2d_inputs.generate(shape, seed=0)
     tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
     d = {}
@@ -320,7 +317,7 @@ def main() -> int:
 
     if bwd:
         dy = torch.from_numpy(np.random.default_rng(1).standard_normal((shape.B, shape.D, shape.H, shape.W))
-                              .astype(np.float32)).to(dev)
+                              .astype(np.float32)).to(tdt).to(dev)
         grads = {}
 
         def step():

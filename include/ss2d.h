@@ -158,22 +158,24 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
  * 代码实现" §3.1-§3.3 define the forward; the gradients follow by the chain rule,
  * with the state adjoint q_l = Cs[n,l] dy_l + exp(delta_{l+1} A) q_{l+1} walked
  * from the end of each sequence (dy_l: dy at the pixel the direction visits).
- *   inputs  x, dt, A_log, dt_bias, Bs, Cs, Ds  as for ss2d_forward (fp32);
- *           dy      [B, D, H, W]   fp32
- *   outputs dx      [B, D, H, W]   fp32
- *           ddt     [B, 4, D, L]   fp32
+ *   inputs  x, dt, A_log, dt_bias, Bs, Cs, Ds  as for ss2d_forward;
+ *           dy      [B, D, H, W]   dtype
+ *   outputs dx      [B, D, H, W]   dtype
+ *           ddt     [B, 4, D, L]   dtype
  *           dA_log  [4*D, N]       fp32   summed over the batch
  *           ddt_bias[4*D]          fp32   summed over the batch and steps
- *           dBs, dCs[B, 4, N, L]   fp32   summed over the D channels
+ *           dBs, dCs[B, 4, N, L]   dtype  summed over the D channels
  *           dDs     [4*D]          fp32   summed over the batch and steps
  * Every output is fully overwritten (no accumulation into existing values) and
- * must not overlap an input or another output (SS2D_ERR_ALIAS).  dtype must be
- * SS2D_F32 (SS2D_ERR_DTYPE otherwise); N is 1..16.  All sums run in a fixed
+ * must not overlap an input or another output (SS2D_ERR_ALIAS).  All arithmetic
+ * is fp32; bf16 outputs are rounded once.  N is 1..16.  All sums run in a fixed
  * order, so results are deterministic.  Takes a stream-ordered temporary of
  * about B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*N*L + 16*B*4*D*N*ceil(L/128) fp32
  * values (du, transposed copies of x and dy, per-channel-block partials of dBs
- * and dCs, the state entering every 8 steps) and runs six kernels on `stream`.  Validation, error reporting and thread safety
- * as for ss2d_forward; pointers need 4-byte alignment (SS2D_ERR_ALIGN).
+ * and dCs, the state entering every 8 steps) and runs six kernels on `stream`.
+ * Validation, error reporting and thread safety as for ss2d_forward; pointers
+ * need element alignment: the storage type for the dtype tensors, 4 bytes for
+ * the fp32 ones (SS2D_ERR_ALIGN).
  */
 int ss2d_backward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
                   const void* Bs, const void* Cs, const float* Ds, const void* dy,

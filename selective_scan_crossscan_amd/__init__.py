@@ -256,13 +256,16 @@ def ss2d_backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bi
 
 
 def backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream=None) -> dict:
-    """Gradients of the forward given dy (ss2d_backward), float32 tensors on one ROCm device.
+    """Gradients of the forward given dy (ss2d_backward), tensors on one ROCm device.
 
-    Returns dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs (shapes of the matching inputs)."""
+    x, dt, Bs, Cs, dy: float32 or bfloat16, all the same; A_log, dt_bias, Ds: float32.
+    Returns dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs (shapes and dtypes of the matching inputs)."""
     import torch
 
-    if x.dtype != torch.float32:
-        raise TypeError("the backward takes float32 tensors")
+    code = _dtype_code(x)
+    for t in (dt, Bs, Cs, dy):
+        if t.dtype != x.dtype:
+            raise TypeError("x, dt, Bs, Cs and dy must share one dtype")
     B, D, H, W = x.shape
     N = A_log.shape[-1]
     ins = (x, dt, A_log, dt_bias, Bs, Cs, Ds, dy)
@@ -270,12 +273,13 @@ def backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream=None) -> dict:
         raise ValueError("dy must have x's shape")
     out = {name: torch.empty_like(t) for name, t in
            (("dx", x), ("ddt", dt), ("dA_log", A_log), ("ddt_bias", dt_bias), ("dBs", Bs), ("dCs", Cs), ("dDs", Ds))}
-    _check_tensors(x, (), ins + tuple(out.values()))
+    io = (x, dt, Bs, Cs, dy, out["dx"], out["ddt"], out["dBs"], out["dCs"])
+    _check_tensors(x, io, (A_log, dt_bias, Ds, out["dA_log"], out["ddt_bias"], out["dDs"]))
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
         rc = ss2d_backward(*(t.data_ptr() for t in ins), *(t.data_ptr() for t in out.values()), B, D, H, W, N,
-                           SS2D_F32, stream.cuda_stream)
+                           code, stream.cuda_stream)
     if rc != 0:
         _raise(rc)
     return out

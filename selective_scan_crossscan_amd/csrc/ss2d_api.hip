@@ -394,9 +394,9 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
     return SS2D_ERR_NULL;
   int rc = check_shape(B, D, H, W, N, dtype);
   if (rc != SS2D_OK) return rc;
-  if (dtype != SS2D_F32) return SS2D_ERR_DTYPE;  // the gradients are fp32 only
   const int64_t L = H * W;
-  const int64_t xb = B * D * L * 4, dtb = B * 4 * D * L * 4, bcb = B * 4 * N * L * 4, pb = 4 * D * N * 4,
+  const int64_t sz = dtype == SS2D_BF16 ? 2 : 4;
+  const int64_t xb = B * D * L * sz, dtb = B * 4 * D * L * sz, bcb = B * 4 * N * L * sz, pb = 4 * D * N * 4,
                 vb = 4 * D * 4;
   const void* ins[8] = {x, dt, A_log, dt_bias, Bs, Cs, Ds, dy};
   const int64_t isz[8] = {xb, dtb, pb, vb, bcb, bcb, vb, xb};
@@ -408,10 +408,13 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
     for (int j = i + 1; j < 7; ++j)
       if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SS2D_ERR_ALIAS;
   }
+  // storage-type tensors need element alignment, the fp32 per-channel ones 4 bytes
+  const bool io_in[8] = {true, true, false, false, true, true, false, true};
+  const bool io_out[7] = {true, true, false, false, true, true, false};
   for (int j = 0; j < 8; ++j)
-    if ((uintptr_t)ins[j] & 3) return SS2D_ERR_ALIGN;
+    if ((uintptr_t)ins[j] & (uintptr_t)(io_in[j] ? sz - 1 : 3)) return SS2D_ERR_ALIGN;
   for (int i = 0; i < 7; ++i)
-    if ((uintptr_t)outs[i] & 3) return SS2D_ERR_ALIGN;
+    if ((uintptr_t)outs[i] & (uintptr_t)(io_out[i] ? sz - 1 : 3)) return SS2D_ERR_ALIGN;
   DeviceInfo di;
   rc = device_info(&di);
   if (rc != SS2D_OK) return rc;
@@ -422,10 +425,8 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
     remember(e);
     return SS2D_ERR_HIP;
   }
-  ss2d::BackwardArgs a{static_cast<const float*>(x), static_cast<const float*>(dt), A_log, dt_bias,
-                       static_cast<const float*>(Bs), static_cast<const float*>(Cs), Ds,
-                       static_cast<const float*>(dy), static_cast<float*>(dx), static_cast<float*>(ddt), dA_log,
-                       ddt_bias, static_cast<float*>(dBs), static_cast<float*>(dCs), dDs, B, D, H, W, N, st};
+  ss2d::BackwardArgs a{x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs,
+                       B, D, H, W, N, dtype, st};
   e = ss2d::launch_backward(a, tmp);
   hipError_t e2 = hipFreeAsync(tmp, st);
   if (e == hipSuccess) e = e2;

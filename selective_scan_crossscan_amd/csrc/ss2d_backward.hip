@@ -41,17 +41,17 @@ namespace {
 constexpr int kBwdChans = 16;  // channels per workgroup
 
 struct BwdParams {
-  const float* x;
-  const float* dt;
+  const void* x;  // x, dt, Bs, Cs, dy, xT, dyT and ddt in the storage type
+  const void* dt;
   const float* A_log;
   const float* dt_bias;
-  const float* Bs;
-  const float* Cs;
+  const void* Bs;
+  const void* Cs;
   const float* Ds;
-  const float* dy;
-  const float* xT;   // x and dy with H and W swapped: column walks read them in order
-  const float* dyT;
-  float* ddt;  // (B, 4, D, L) out
+  const void* dy;
+  const void* xT;   // x and dy with H and W swapped: column walks read them in order
+  const void* dyT;
+  void* ddt;   // (B, 4, D, L) out
   float* du;   // (B, 4, D, L) temporary
   float* hck;  // (B*4, nseg, D, N, 16) temporary: state entering each lane's steps of each chunk
   float* dBp;  // (B*4, nblk, N, L) temporary
@@ -116,6 +116,7 @@ __device__ __forceinline__ void scan_maps(float& P, float& Q) {
 constexpr int kRowShr = 0x110;  // row_shr:n = 0x110 + n (from lane i - n)
 constexpr int kRowShl = 0x100;  // row_shl:n = 0x100 + n (from lane i + n)
 
+template <typename S>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   __shared__ float sB[16][kPad];
   __shared__ float sC[16][kPad];
@@ -135,11 +136,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   carry_a[ch][s] = 1.f;
   dA_s[ch][s] = 0.f;
   const float bias = p.dt_bias[c_idx], Dsk = p.Ds[c_idx];
-  const float* xs = ((k & 1) ? p.xT : p.x) + ((int64_t)b * D + ds) * L;
-  const float* gs = ((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + ds) * L;
-  const float* dtr = p.dt + ((int64_t)bk * D + ds) * L;
-  const float* Bb = p.Bs + (int64_t)bk * N * L;
-  const float* Cb = p.Cs + (int64_t)bk * N * L;
+  const S* xs = static_cast<const S*>((k & 1) ? p.xT : p.x) + ((int64_t)b * D + ds) * L;
+  const S* gs = static_cast<const S*>((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + ds) * L;
+  const S* dtr = static_cast<const S*>(p.dt) + ((int64_t)bk * D + ds) * L;
+  const S* Bb = static_cast<const S*>(p.Bs) + (int64_t)bk * N * L;
+  const S* Cb = static_cast<const S*>(p.Cs) + (int64_t)bk * N * L;
   const int64_t row = ((int64_t)bk * D + ds) * L;
   auto hck = [&](int c, int n) -> float& {
     return p.hck[((((int64_t)bk * nch + c) * D + ds) * N + n) * 16 + s];
@@ -153,11 +154,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
       const int l = c * kChunk + j0 + i;
       const bool in = dval && l < L;
       const int li = in ? l : 0, xi = in ? (k >= 2 ? L - 1 - l : l) : 0;
-      const float pre = dtr[li] + bias;
+      const float pre = Io<S>::ld(dtr, li) + bias;
       del[i] = in ? softplus_f32(pre) : 0.f;
       sig[i] = in ? 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;
-      uu[i] = in ? xs[xi] : 0.f;
-      gg[i] = in && with_g ? gs[xi] : 0.f;
+      uu[i] = in ? Io<S>::ld(xs, xi) : 0.f;
+      gg[i] = in && with_g ? Io<S>::ld(gs, xi) : 0.f;
     }
   };
   auto stage = [&](int c, bool with_c) {
@@ -167,8 +168,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
       const bool in = n < N && l < L;
       const int64_t off = in ? (int64_t)n * L + l : 0;
       const int jp = j + j / kCT;
-      sB[n][jp] = in ? Bb[off] : 0.f;
-      if (with_c) sC[n][jp] = in ? Cb[off] : 0.f;
+      sB[n][jp] = in ? Io<S>::ld(Bb, off) : 0.f;
+      if (with_c) sC[n][jp] = in ? Io<S>::ld(Cb, off) : 0.f;
     }
   };
   __syncthreads();
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
       const int l = c * kChunk + j0 + i;
       if (dval && l < L) {
         const float ddt = dd[i] * sig[i];
-        p.ddt[row + l] = ddt;
+        Io<S>::st(static_cast<S*>(p.ddt), row + l, ddt);
         p.du[row + l] = fmaf(Dsk, gg[i], du[i]);
         dbias += ddt;
         dD = fmaf(gg[i], uu[i], dD);
@@ -289,8 +290,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
 }
 
 // dBs / dCs: the channel blocks' partials summed in block order.
+template <typename S>
 __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ dBp, const float* __restrict__ dCp,
-                                                    float* __restrict__ dBs, float* __restrict__ dCs, int64_t BK,
+                                                    S* __restrict__ dBs, S* __restrict__ dCs, int64_t BK,
                                                     int nblk, int N, int L) {
   const int64_t total = BK * N * L;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
@@ -301,13 +303,14 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ d
       sb += dBp[src];
       sc += dCp[src];
     }
-    dBs[e] = sb;
-    dCs[e] = sc;
+    Io<S>::st(dBs, e, sb);
+    Io<S>::st(dCs, e, sc);
   }
 }
 
 // dx[b, d, p] = du of directions 0, 1, 2, 3 at the steps that visit p, added in that order.
-__global__ __launch_bounds__(256) void bwd_merge(const float* __restrict__ du, float* __restrict__ dx, int64_t BD,
+template <typename S>
+__global__ __launch_bounds__(256) void bwd_merge(const float* __restrict__ du, S* __restrict__ dx, int64_t BD,
                                                 int D, int H, int W) {
   const int L = H * W;
   const int64_t total = BD * L;
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256) void bwd_merge(const float* __restrict__ du, f
     const float* r1 = du + ((b * 4 + 1) * D + d) * L;
     const float* r2 = du + ((b * 4 + 2) * D + d) * L;
     const float* r3 = du + ((b * 4 + 3) * D + d) * L;
-    dx[e] = ((r0[px] + r1[lc]) + r2[L - 1 - px]) + r3[L - 1 - lc];
+    Io<S>::st(dx, e, ((r0[px] + r1[lc]) + r2[L - 1 - px]) + r3[L - 1 - lc]);
   }
 }
 
@@ -347,13 +350,33 @@ __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_lo
   }
 }
 
+// The kernels that read or write the storage type: transposes of x and dy, the
+// chunked scan, the dBs/dCs sums and the dx merge.
+template <typename S>
+hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t blocks, int64_t nblk, int64_t L) {
+  hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(const_cast<void*>(p.xT)),
+                                     (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
+  if (e != hipSuccess) return e;
+  e = launch_transpose<S>(static_cast<const S*>(a.dy), static_cast<S*>(const_cast<void*>(p.dyT)), (int)(a.B * a.D),
+                          (int)a.H, (int)a.W, a.stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chunk_kernel<S>), dim3((unsigned)blocks), dim3(256), 0, a.stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, static_cast<S*>(a.dBs),
+                     static_cast<S*>(a.dCs), a.B * 4, (int)nblk, (int)a.N, (int)L);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_merge<S>), dim3(4096), dim3(256), 0, a.stream, p.du, static_cast<S*>(a.dx), a.B * a.D,
+                     (int)a.D, (int)a.H, (int)a.W);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
   const int64_t L = H * W, nch = (L + kChunk - 1) / kChunk, nblk = (D + kBwdChans - 1) / kBwdChans;
   auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
   return up(B * 4 * D * L) + up(B * 4 * nch * D * N * 16) + 2 * up(B * 4 * nblk * N * L) + up(B * 4 * D * N) +
-         2 * up(B * 4 * D) + 2 * up(B * D * L);
+         2 * up(B * 4 * D) + 2 * up(B * D * L);  // the transposed copies are sized for fp32 (bf16 uses half)
 }
 
 hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
@@ -384,9 +407,9 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   base += up(a.B * 4 * a.D);
   p.dDp = reinterpret_cast<float*>(base);
   base += up(a.B * 4 * a.D);
-  float* xT = reinterpret_cast<float*>(base);
+  void* xT = base;
   base += up(a.B * a.D * L);
-  float* dyT = reinterpret_cast<float*>(base);
+  void* dyT = base;
   p.xT = xT;
   p.dyT = dyT;
   p.D = (int)a.D;
@@ -398,17 +421,8 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.nblk = (int)nblk;
   const int64_t blocks = a.B * 4 * nblk;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipError_t e = launch_transpose<float>(a.x, xT, (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
+  hipError_t e = a.dtype == 0 ? launch_io<float>(a, p, blocks, nblk, L) : launch_io<uint16_t>(a, p, blocks, nblk, L);
   if (e != hipSuccess) return e;
-  if ((e = launch_transpose<float>(a.dy, dyT, (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_reduce_bc, dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, a.dBs, a.dCs, a.B * 4,
-                     (int)nblk, (int)a.N, (int)L);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_merge, dim3(4096), dim3(256), 0, a.stream, p.du, a.dx, a.B * a.D, (int)a.D, (int)a.H,
-                     (int)a.W);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int C4 = (int)(4 * a.D);
   hipLaunchKernelGGL(bwd_params, dim3((unsigned)((C4 * a.N + 255) / 256)), dim3(256), 0, a.stream, a.A_log, p.dAp,
                      p.dbp, p.dDp, a.dA_log, a.ddt_bias, a.dDs, (int)a.B, C4, (int)a.N);

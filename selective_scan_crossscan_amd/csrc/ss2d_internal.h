@@ -101,24 +101,26 @@ hipError_t launch_channel_last(const EpilogueArgs& a);
 // Largest D the epilogue takes.
 int epilogue_max_channels();
 
-// Gradients of the forward (fp32): every output fully written.
+// Gradients of the forward: every output fully written.  x, dt, Bs, Cs, dy, dx,
+// ddt, dBs, dCs in the storage type; the per-channel tensors fp32.
 struct BackwardArgs {
-  const float* x;
-  const float* dt;
+  const void* x;
+  const void* dt;
   const float* A_log;
   const float* dt_bias;
-  const float* Bs;
-  const float* Cs;
+  const void* Bs;
+  const void* Cs;
   const float* Ds;
-  const float* dy;
-  float* dx;
-  float* ddt;
+  const void* dy;
+  void* dx;
+  void* ddt;
   float* dA_log;
   float* ddt_bias;
-  float* dBs;
-  float* dCs;
+  void* dBs;
+  void* dCs;
   float* dDs;
   int64_t B, D, H, W, N;
+  int dtype;
   hipStream_t stream;
 };
 size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N);

@@ -256,7 +256,11 @@ def test_backward_validation():
         p = [X, DT, AL, BI, BS, CS, DS] + GRAD
         p[i] = None
         assert _bwd(p) == -1, i
-    assert _bwd(dtype=1) == -4            # fp32 only
+    assert _bwd(dtype=2) == -4
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+    p[0] = X + 1                          # bf16 tensors need 2-byte alignment
+    assert _bwd(p, dtype=1) == -6
+    assert _bwd(dtype=1) == -7            # bf16 is accepted (then: no device)
     assert _bwd(N=17) == -3
     assert _bwd(W=0) == -2
     p = [X, DT, AL, BI, BS, CS, DS] + GRAD
