@@ -54,7 +54,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
 STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel", "bwd_chunk_kernel",
-                "bwd_reduce_bc", "bwd_merge", "bwd_params", "channel_last_kernel"}
+                "bwd_seg_carry", "bwd_reduce_bc", "bwd_merge", "bwd_params", "channel_last_kernel"}
 
 
 def traffic_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
@@ -69,17 +69,18 @@ def kernel_source_hash(kernel: str = "ss2d_forward_kernel") -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters,
-    scaled by the copy-kernel calibration; None when absent or the kernel changed since."""
+def measured_traffic(workload: str, kernel: str = KERNEL_PREFIX):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, scaled by the copy-kernel calibration; None when absent or the kernel
+    changed since."""
     try:
-        with open(traffic_file(workload)) as f:
+        with open(traffic_file(workload, kernel)) as f:
             text = f.read()
         m = re.search(r"```json\n(.*?)\n```", text, re.S)
         rec = json.loads(m.group(1)) if m else {}
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+    if rec.get("kernel_source_hash") != kernel_source_hash(kernel) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -167,6 +168,8 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
     lines = [f"# {kernel} — {workload} — rocprofv3 kernel trace", "", f"Workload: {shape}.  {work}", "",
              "Command (from the repository root):", "", "```", cmds["stats"], "```", "",
              "| kernel | calls | average µs | min µs | max µs | share |", "|---|---|---|---|---|---|"]
+    # Each template instance of the kernel runs once per step (a segmented backward
+    # runs two: its two passes), so its time per step is the sum of their averages.
     kern_avg = None
     per_step = 0.0  # fused plans launch each of a forward's kernels once per step
     present = []
@@ -176,7 +179,7 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
             name = name[:87] + "..."
         avg = float(r["AverageNs"]) / 1e3
         if _is_kernel(r["Name"], kernel):
-            kern_avg = avg
+            kern_avg = (kern_avg or 0.0) + avg
         for k in STEP_KERNELS:
             if _is_kernel(r["Name"], k):
                 per_step += avg
@@ -210,11 +213,15 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
     per = {}
     for counter, prefix in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = [r for r in _counter_rows(folder, prefix) if r["Counter_Name"] == counter]
-        kern = [float(r["Counter_Value"]) for r in rows if _is_kernel(r["Kernel_Name"], kernel)]
+        inst = {}  # template instance -> its dispatches' values
+        for r in rows:
+            if _is_kernel(r["Kernel_Name"], kernel):
+                inst.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         copies = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         probe_kib, probe_name = max(copies)
         expected_kib = COPY_PROBE_MIB * 1024.0
-        per[counter] = {"kernel_kib_per_dispatch": sum(kern) / len(kern), "dispatches": len(kern),
+        per[counter] = {"kernel_kib_per_dispatch": sum(sum(v) / len(v) for v in inst.values()),
+                        "dispatches": sum(len(v) for v in inst.values()), "instances": len(inst),
                         "copy_probe_kib": probe_kib, "copy_probe_kernel": probe_name,
                         "copy_expected_kib": expected_kib, "scale": expected_kib / probe_kib}
     fetch_b = per["FETCH_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["FETCH_SIZE"]["scale"]
@@ -227,7 +234,9 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
              "Two counter runs, one counter each, from the repository root:", "", "```", cmds["fetch"],
              cmds["write"], "```", "",
              f"Each run also performs one {COPY_PROBE_MIB} MiB device-to-device copy; the scale factor is the "
-             "copy's known size divided by what the same counter reads for it.", "",
+             "copy's known size divided by what the same counter reads for it.  Where the kernel has several "
+             "template instances in a step (the two passes of a segmented backward), the per-dispatch figure "
+             "is the sum of the instances' averages.", "",
              "| counter | kernel KiB / dispatch | copy probe KiB | copy expected KiB | scale | kernel bytes |",
              "|---|---|---|---|---|---|"]
     for counter, b in (("FETCH_SIZE", fetch_b), ("WRITE_SIZE", write_b)):
@@ -439,7 +448,9 @@ def main() -> int:
     nseg = int(plan["segments"])
     launches = int(plan["x_transposed"]) + (1 if nseg == 1 else 5 + int(plan["plane_transposed"]))
     if bwd:
-        launches = 6  # two transposes, the reverse scan, the dBs/dCs sum, the dx merge, the parameter sums
+        # two transposes, the chunked scan (or, on a segmented map, its two passes
+        # and the segment carry), the dBs/dCs sum, the dx merge, the parameter sums
+        launches = 6 if int(plan["backward_segments"]) == 1 else 8
     if from_x:
         launches += 1 + (1 - int(plan["x_transposed"]))  # the projection, and its own transpose of x
     ms_per_step = wall * 1e3 / args.steps
@@ -448,7 +459,10 @@ def main() -> int:
     value = updates * args.steps / wall
     achieved = updates / kernel_s
     hbm_gbps = shape.algorithmic_bytes / kernel_s / 1e9
-    traffic = measured_traffic(shape.name)
+    # the counters of the step's dominant kernel: the scan (forward, from_x) or the
+    # chunked backward kernel
+    traffic = (measured_traffic(shape.name + "_backward", "bwd_chunk_kernel") if bwd
+               else measured_traffic(shape.name))
 
     result = {
         "metric": "SS2D state-updates/s (B·4·D·L·N) and achieved HBM GB/s % of peak",
@@ -474,9 +488,11 @@ def main() -> int:
             "unit": "Gupdates/s (1 exp2 + 4 fp32 VALU per update = 8 of 128 issue slots/clk/CU)",
             "frac": achieved / PEAK_UPDATES_PER_S,
             "traffic": traffic,
-            "timed": f"HIP events around each step on the launch stream: {launches} launch(es) "
+            "timed": f"HIP events around each step on the launch stream: {launches} launch(es) " + (
+                     "(transposes of x and dy, the chunked backward kernel, the dBs/dCs sum, the dx merge, the "
+                     "parameter sums; traffic is the chunked kernel's own)" if bwd else
                      "(the scan kernel, after a transpose of x on maps of 2048+ pixels; traffic is the scan "
-                     "kernel's own)",
+                     "kernel's own)"),
         },
         "hbm": {"algorithmic_bytes": shape.algorithmic_bytes, "achieved_GBps": hbm_gbps,
                 "frac_of_peak": hbm_gbps / HBM_PEAK_GBPS, "peak_GBps": HBM_PEAK_GBPS},

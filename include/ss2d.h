@@ -173,6 +173,9 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
  * about B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*N*L + 16*B*4*D*N*ceil(L/128) fp32
  * values (du, transposed copies of x and dy, per-channel-block partials of dBs
  * and dCs, the state entering every 8 steps) and runs six kernels on `stream`.
+ * When B*4*ceil(D/16) is small, each sequence is cut into S segments of at least
+ * 512 steps (S from ss2d_describe): two more kernels, and about
+ * 16*B*4*D*ceil(L/128) + 3*B*4*S*D*N more temporary values.
  * Validation, error reporting and thread safety as for ss2d_forward; pointers
  * need element alignment: the storage type for the dtype tensors, 4 bytes for
  * the fp32 ones (SS2D_ERR_ALIGN).
@@ -195,8 +198,9 @@ int ss2d_version(void);
 /*
  * ss2d_describe -- write a one-line, NUL-terminated description of how
  * ss2d_forward would run this shape (kernel variant, lanes per sequence,
- * channels per workgroup, grid size, LDS and temporary sizes) into
- * buf[0..len).  Host only; no device work.  Returns SS2D_OK or a validation code.
+ * channels per workgroup, grid size, LDS and temporary sizes), followed by the
+ * number of segments ss2d_backward cuts each sequence into, into buf[0..len).
+ * Host only; no device work.  Returns SS2D_OK or a validation code.
  */
 int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
                   char* buf, int64_t len);

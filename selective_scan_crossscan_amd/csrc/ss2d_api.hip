@@ -145,10 +145,12 @@ int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dty
   const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
   snprintf(buf, (size_t)len,
            "kernel=chunked_dpp_scan lanes_per_seq=%d steps_per_lane=%d waves=%d chans_per_block=%d "
-           "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu",
+           "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu "
+           "backward_segments=%lld",
            pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.xtrans ? 1 : 0,
            pl.transpose ? 1 : 0,
-           (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes);
+           (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes,
+           (long long)ss2d::backward_segments(B, D, H, W, N));
   return SS2D_OK;
 }
 

@@ -33,6 +33,16 @@
 //     operand load is contiguous along the steps.
 //   * du goes to a temporary; a gather kernel merges it into dx, and a small
 //     kernel sums the per-batch parameter gradients.
+//   * Maps too long for one workgroup per channel block to fill the chip are cut
+//     into segments of consecutive chunks, one workgroup each, in three launches:
+//     pass A from a zero state, which also folds the segment's whole forward map
+//     h -> P h + F and adjoint map r -> P r + R (r: the adjoint entering from the
+//     right times the decay of the step it enters at); a small kernel chains the
+//     segments in order to their true entering state and adjoint; pass B, which
+//     corrects each stored state by the entering state times the decay since the
+//     segment's start.
+#include <algorithm>
+
 #include "ss2d_kernels.h"
 
 namespace ss2d {
@@ -56,10 +66,15 @@ struct BwdParams {
   float* hck;  // (B*4, nseg, D, N, 16) temporary: state entering each lane's steps of each chunk
   float* dBp;  // (B*4, nblk, N, L) temporary
   float* dCp;
-  float* dAp;  // (B, 4D, N) temporary
-  float* dbp;  // (B, 4D) temporary
+  float* dAp;  // (B, nsp, 4D, N) temporary
+  float* dbp;  // (B, nsp, 4D) temporary
   float* dDp;
+  float* cdl;   // (B*4, nseg, D, 16): delta summed from the segment's start to each lane's first step (nsp > 1)
+  float* segP;  // (B*4, nsp, D, N): the segment's decay, forward offset, adjoint offset; the carry kernel
+  float* segF;  //   turns F into the state entering the segment and R into the adjoint entering it
+  float* segR;
   int D, H, W, L, N, nseg, nblk;
+  int nsp, cps;  // segments, chunks per segment
 };
 
 // Sum over the 16 lanes of a DPP row (four rotations).
@@ -116,25 +131,38 @@ __device__ __forceinline__ void scan_maps(float& P, float& Q) {
 constexpr int kRowShr = 0x110;  // row_shr:n = 0x110 + n (from lane i - n)
 constexpr int kRowShl = 0x100;  // row_shl:n = 0x100 + n (from lane i + n)
 
-template <typename S>
+// MODE kWhole: one workgroup walks every chunk, pass A then pass B.  kSegMaps: pass
+// A over one segment from a zero state, with the segment's maps as records.
+// kSegGrads: pass B over one segment, from the chained records.
+enum BwdMode { kWhole = 0, kSegMaps = 1, kSegGrads = 2 };
+
+template <typename S, int MODE>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   __shared__ float sB[16][kPad];
   __shared__ float sC[16][kPad];
   __shared__ float red[2][16][kPad];
   __shared__ float carry_q[16][16], carry_a[16][16], dA_s[16][16], a2s[16][16];
+  __shared__ float adj_p[16][16], adj_q[16][16];  // kSegMaps: the adjoint map of the chunks walked so far
   const int tid = threadIdx.x, s = tid & 15, ch = tid >> 4;
-  const int blk = blockIdx.x % p.nblk;
-  const int bk = blockIdx.x / p.nblk;  // b * 4 + k
+  const int sg = blockIdx.x % p.nsp;
+  const int grp = blockIdx.x / p.nsp;
+  const int blk = grp % p.nblk;
+  const int bk = grp / p.nblk;  // b * 4 + k
   const int k = bk & 3, b = bk >> 2;
   const int D = p.D, L = p.L, N = p.N, nch = p.nseg;
+  const int c0 = sg * p.cps, c1 = min(nch, c0 + p.cps);
   const int d = blk * kBwdChans + ch;
   const bool dval = d < D;
   const int ds = dval ? d : 0;
   const int c_idx = k * D + ds;
-  a2s[ch][s] = (dval && s < N) ? -expf(p.A_log[(int64_t)c_idx * N + s]) * kLog2e : 0.f;
-  carry_q[ch][s] = 0.f;
+  const int64_t rec = (((int64_t)bk * p.nsp + sg) * D + ds) * N + s;  // this lane's segment record (state s)
+  const bool rval = dval && s < N;
+  a2s[ch][s] = rval ? -expf(p.A_log[(int64_t)c_idx * N + s]) * kLog2e : 0.f;
+  carry_q[ch][s] = MODE == kSegGrads && rval ? p.segR[rec] : 0.f;
   carry_a[ch][s] = 1.f;
   dA_s[ch][s] = 0.f;
+  adj_p[ch][s] = 1.f;
+  adj_q[ch][s] = MODE == kSegGrads && rval ? p.segF[rec] : 0.f;  // kSegGrads: the state entering the segment
   const float bias = p.dt_bias[c_idx], Dsk = p.Ds[c_idx];
   const S* xs = static_cast<const S*>((k & 1) ? p.xT : p.x) + ((int64_t)b * D + ds) * L;
   const S* gs = static_cast<const S*>((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + ds) * L;
@@ -145,6 +173,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   auto hck = [&](int c, int n) -> float& {
     return p.hck[((((int64_t)bk * nch + c) * D + ds) * N + n) * 16 + s];
   };
+  auto cdl = [&](int c) -> float& { return p.cdl[(((int64_t)bk * nch + c) * D + ds) * 16 + s]; };
   const int j0 = s * kCT, jp0 = j0 + s;  // first step of this lane in the chunk, and its padded LDS slot
 
   float del[kCT], uu[kCT], gg[kCT], sig[kCT];
@@ -174,45 +203,85 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   };
   __syncthreads();
 
-  // pass A: the state entering each lane's steps of every chunk
-  for (int c = 0; c < nch; ++c) {
-    stage(c, false);
-    load_lane(c, false);
-    __syncthreads();
-    float sdel = 0.f;
+  if (MODE != kSegGrads) {
+    // pass A: the state entering each lane's steps of every chunk
+    constexpr bool seg = MODE == kSegMaps;
+    float cum = 0.f;  // kSegMaps: delta summed over the segment's chunks before this one
+    for (int c = c0; c < c1; ++c) {
+      stage(c, seg);
+      load_lane(c, seg);
+      __syncthreads();
+      float sdel = 0.f;
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) sdel += del[i];
-    for (int n = 0; n < N; ++n) {
-      const float A2 = a2s[ch][n];
-      float P = __builtin_amdgcn_exp2f(A2 * sdel), Q = 0.f;
+      for (int i = 0; i < kCT; ++i) sdel += del[i];
+      if (seg) {
+        float incl = sdel;  // inclusive prefix over the row
+        incl += dppf<kRowShr + 1>(0.f, incl);
+        incl += dppf<kRowShr + 2>(0.f, incl);
+        incl += dppf<kRowShr + 4>(0.f, incl);
+        incl += dppf<kRowShr + 8>(0.f, incl);
+        if (dval) cdl(c) = cum + (incl - sdel);
+        cum += row_lane(incl, 15);
+      }
+      for (int n = 0; n < N; ++n) {
+        const float A2 = a2s[ch][n];
+        const float Pl = __builtin_amdgcn_exp2f(A2 * sdel);
+        float P = Pl, Q = 0.f, a[kCT];
 #pragma unroll
-      for (int i = 0; i < kCT; ++i)
-        Q = fmaf(__builtin_amdgcn_exp2f(del[i] * A2), Q, del[i] * uu[i] * sB[n][jp0 + i]);
-      scan_maps<kRowShr>(P, Q);
-      const float Pe = dppf<kRowShr + 1>(1.f, P), Qe = dppf<kRowShr + 1>(0.f, Q);
-      const float hc = carry_q[ch][n];
-      if (dval) hck(c, n) = fmaf(Pe, hc, Qe);
-      const float hout = fmaf(P, hc, Q);  // lane 15: the state leaving the chunk
-      if (s == 15) carry_q[ch][n] = hout;
+        for (int i = 0; i < kCT; ++i) {
+          a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
+          Q = fmaf(a[i], Q, del[i] * uu[i] * sB[n][jp0 + i]);
+        }
+        if (seg) {
+          // the lane's adjoint map r -> Pl r + R (r enters after its last step),
+          // composed over the row: lane 0 holds the chunk's
+          float Pb = Pl, R = 0.f;
+#pragma unroll
+          for (int i = kCT - 1; i >= 0; --i) R = a[i] * fmaf(sC[n][jp0 + i], gg[i], R);
+          scan_maps<kRowShl>(Pb, R);
+          if (s == 0) {  // the chunks so far, then this one: (P1, Q1) o (Pb, R)
+            const float P1 = adj_p[ch][n];
+            adj_q[ch][n] = fmaf(P1, R, adj_q[ch][n]);
+            adj_p[ch][n] = P1 * Pb;
+          }
+        }
+        scan_maps<kRowShr>(P, Q);
+        const float Pe = dppf<kRowShr + 1>(1.f, P), Qe = dppf<kRowShr + 1>(0.f, Q);
+        const float hc = carry_q[ch][n];
+        if (dval) hck(c, n) = fmaf(Pe, hc, Qe);
+        const float hout = fmaf(P, hc, Q);  // lane 15: the state leaving the chunk
+        if (s == 15) carry_q[ch][n] = hout;
+      }
+      __syncthreads();
     }
+    if (seg) {
+      if (rval) {
+        p.segP[rec] = adj_p[ch][s];
+        p.segF[rec] = carry_q[ch][s];
+        p.segR[rec] = adj_q[ch][s];
+      }
+      return;
+    }
+    // pass B: chunks from the last; the adjoint enters each lane from the right
+    carry_q[ch][s] = 0.f;
     __syncthreads();
   }
 
-  // pass B: chunks from the last; the adjoint enters each lane from the right
-  carry_q[ch][s] = 0.f;
-  __syncthreads();
   float dbias = 0.f, dD = 0.f;
-  for (int c = nch - 1; c >= 0; --c) {
+  for (int c = c1 - 1; c >= c0; --c) {
     stage(c, true);
     load_lane(c, true);
     __syncthreads();
     float du[kCT], dd[kCT];
 #pragma unroll
     for (int i = 0; i < kCT; ++i) du[i] = dd[i] = 0.f;
+    const float cum = MODE == kSegGrads && dval ? cdl(c) : 0.f;
     for (int n = 0; n < N; ++n) {
       const float A2 = a2s[ch][n], A = A2 * kLn2;
       float a[kCT], h[kCT];
-      const float h_in = dval ? hck(c, n) : 0.f;
+      float h_in = dval ? hck(c, n) : 0.f;
+      // a segment's stored states start from zero: add the entering state's decayed part
+      if (MODE == kSegGrads) h_in = fmaf(__builtin_amdgcn_exp2f(A2 * cum), adj_q[ch][n], h_in);
       float hv = h_in;
 #pragma unroll
       for (int i = 0; i < kCT; ++i) {
@@ -282,10 +351,35 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   }
   dbias = row_sum16(dbias);
   dD = row_sum16(dD);
-  if (dval && s < N) p.dAp[((int64_t)b * 4 * D + c_idx) * N + s] = dA_s[ch][s];
+  const int64_t pc = ((int64_t)b * p.nsp + sg) * 4 * D + c_idx;  // this channel's per-(batch, segment) slot
+  if (rval) p.dAp[pc * N + s] = dA_s[ch][s];
   if (dval && s == 0) {
-    p.dbp[(int64_t)b * 4 * D + c_idx] = dbias;
-    p.dDp[(int64_t)b * 4 * D + c_idx] = dD;
+    p.dbp[pc] = dbias;
+    p.dDp[pc] = dD;
+  }
+}
+
+// The segments of each (batch, direction, channel, state) chained in order:
+// F becomes the state entering the segment, R the adjoint entering it from the right.
+__global__ __launch_bounds__(256) void bwd_seg_carry(const float* __restrict__ segP, float* __restrict__ segF,
+                                                    float* __restrict__ segR, int64_t cols, int64_t DN, int nsp) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (bk, d, n)
+  if (e >= cols) return;
+  const int64_t bk = e / DN;
+  const int64_t base = bk * nsp * DN + (e - bk * DN);
+  float h = 0.f;
+  for (int sg = 0; sg < nsp; ++sg) {
+    const int64_t i = base + sg * DN;
+    const float f = segF[i];
+    segF[i] = h;
+    h = fmaf(segP[i], h, f);
+  }
+  float r = 0.f;
+  for (int sg = nsp - 1; sg >= 0; --sg) {
+    const int64_t i = base + sg * DN;
+    const float q = segR[i];
+    segR[i] = r;
+    r = fmaf(segP[i], r, q);
   }
 }
 
@@ -351,38 +445,96 @@ __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_lo
 }
 
 // The kernels that read or write the storage type: transposes of x and dy, the
-// chunked scan, the dBs/dCs sums and the dx merge.
+// chunked scan (one launch, or three for a segmented map), the dBs/dCs sums and
+// the dx merge.
 template <typename S>
-hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t blocks, int64_t nblk, int64_t L) {
+hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L) {
   hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(const_cast<void*>(p.xT)),
                                      (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
   if (e != hipSuccess) return e;
   e = launch_transpose<S>(static_cast<const S*>(a.dy), static_cast<S*>(const_cast<void*>(p.dyT)), (int)(a.B * a.D),
                           (int)a.H, (int)a.W, a.stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chunk_kernel<S>), dim3((unsigned)blocks), dim3(256), 0, a.stream, p);
+  const unsigned blocks = (unsigned)(a.B * 4 * p.nblk * p.nsp);
+  if (p.nsp == 1) {
+    hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole>), dim3(blocks), dim3(256), 0, a.stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegMaps>), dim3(blocks), dim3(256), 0, a.stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t cols = a.B * 4 * a.D * a.N;
+    hipLaunchKernelGGL(bwd_seg_carry, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, a.stream, p.segP, p.segF,
+                       p.segR, cols, a.D * a.N, p.nsp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegGrads>), dim3(blocks), dim3(256), 0, a.stream, p);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, static_cast<S*>(a.dBs),
-                     static_cast<S*>(a.dCs), a.B * 4, (int)nblk, (int)a.N, (int)L);
+                     static_cast<S*>(a.dCs), a.B * 4, p.nblk, (int)a.N, (int)L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_merge<S>), dim3(4096), dim3(256), 0, a.stream, p.du, static_cast<S*>(a.dx), a.B * a.D,
                      (int)a.D, (int)a.H, (int)a.W);
   return hipGetLastError();
 }
 
+// Segments: a map whose channel blocks alone give fewer workgroups than about
+// six per compute unit is cut into segments of at least kMinSegChunks chunks.
+constexpr int64_t kBwdTargetBlocks = 1536;
+constexpr int64_t kMinSegChunks = 4;
+
+struct BwdLayout {
+  int64_t L, nch, nblk, nsp, cps;
+  size_t du, hck, dBp, dCp, dAp, dbp, dDp, cdl, segP, segF, segR, xT, dyT, total;  // byte offsets
+};
+
+BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
+  BwdLayout o;
+  o.L = H * W;
+  o.nch = (o.L + kChunk - 1) / kChunk;
+  o.nblk = (D + kBwdChans - 1) / kBwdChans;
+  const int64_t base = B * 4 * o.nblk;
+  int64_t nsp = 1;
+  if (base < kBwdTargetBlocks) nsp = std::min((kBwdTargetBlocks + base - 1) / base, o.nch / kMinSegChunks);
+  if (nsp < 2) nsp = 1;
+  o.cps = (o.nch + nsp - 1) / nsp;
+  o.nsp = (o.nch + o.cps - 1) / o.cps;  // no empty segment
+  auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
+  size_t off = 0;
+  auto take = [&](size_t& at, int64_t floats) {
+    at = off;
+    off += up(floats);
+  };
+  take(o.du, B * 4 * D * o.L);
+  take(o.hck, B * 4 * o.nch * D * N * 16);
+  take(o.dBp, B * 4 * o.nblk * N * o.L);
+  take(o.dCp, B * 4 * o.nblk * N * o.L);
+  take(o.dAp, B * o.nsp * 4 * D * N);
+  take(o.dbp, B * o.nsp * 4 * D);
+  take(o.dDp, B * o.nsp * 4 * D);
+  const bool seg = o.nsp > 1;
+  take(o.cdl, seg ? B * 4 * o.nch * D * 16 : 0);
+  take(o.segP, seg ? B * 4 * o.nsp * D * N : 0);
+  take(o.segF, seg ? B * 4 * o.nsp * D * N : 0);
+  take(o.segR, seg ? B * 4 * o.nsp * D * N : 0);
+  take(o.xT, B * D * o.L);  // the transposed copies are sized for fp32 (bf16 uses half)
+  take(o.dyT, B * D * o.L);
+  o.total = off;
+  return o;
+}
+
 }  // namespace
 
 size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
-  const int64_t L = H * W, nch = (L + kChunk - 1) / kChunk, nblk = (D + kBwdChans - 1) / kBwdChans;
-  auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
-  return up(B * 4 * D * L) + up(B * 4 * nch * D * N * 16) + 2 * up(B * 4 * nblk * N * L) + up(B * 4 * D * N) +
-         2 * up(B * 4 * D) + 2 * up(B * D * L);  // the transposed copies are sized for fp32 (bf16 uses half)
+  return bwd_layout(B, D, H, W, N).total;
+}
+
+int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
+  return bwd_layout(B, D, H, W, N).nsp;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
-  const int64_t L = a.H * a.W, nseg = (L + kChunk - 1) / kChunk, nblk = (a.D + kBwdChans - 1) / kBwdChans;
-  auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
+  const BwdLayout o = bwd_layout(a.B, a.D, a.H, a.W, a.N);
   char* base = static_cast<char*>(scratch);
+  auto f = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   BwdParams p;
   p.x = a.x;
   p.dt = a.dt;
@@ -393,39 +545,34 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.Ds = a.Ds;
   p.dy = a.dy;
   p.ddt = a.ddt;
-  p.du = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * a.D * L);
-  p.hck = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * nseg * a.D * a.N * 16);
-  p.dBp = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * nblk * a.N * L);
-  p.dCp = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * nblk * a.N * L);
-  p.dAp = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * a.D * a.N);
-  p.dbp = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * a.D);
-  p.dDp = reinterpret_cast<float*>(base);
-  base += up(a.B * 4 * a.D);
-  void* xT = base;
-  base += up(a.B * a.D * L);
-  void* dyT = base;
-  p.xT = xT;
-  p.dyT = dyT;
+  p.du = f(o.du);
+  p.hck = f(o.hck);
+  p.dBp = f(o.dBp);
+  p.dCp = f(o.dCp);
+  p.dAp = f(o.dAp);
+  p.dbp = f(o.dbp);
+  p.dDp = f(o.dDp);
+  p.cdl = f(o.cdl);
+  p.segP = f(o.segP);
+  p.segF = f(o.segF);
+  p.segR = f(o.segR);
+  p.xT = base + o.xT;
+  p.dyT = base + o.dyT;
   p.D = (int)a.D;
   p.H = (int)a.H;
   p.W = (int)a.W;
-  p.L = (int)L;
+  p.L = (int)o.L;
   p.N = (int)a.N;
-  p.nseg = (int)nseg;
-  p.nblk = (int)nblk;
-  const int64_t blocks = a.B * 4 * nblk;
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipError_t e = a.dtype == 0 ? launch_io<float>(a, p, blocks, nblk, L) : launch_io<uint16_t>(a, p, blocks, nblk, L);
+  p.nseg = (int)o.nch;
+  p.nblk = (int)o.nblk;
+  p.nsp = (int)o.nsp;
+  p.cps = (int)o.cps;
+  if (a.B * 4 * o.nblk * o.nsp > INT32_MAX) return hipErrorInvalidValue;
+  hipError_t e = a.dtype == 0 ? launch_io<float>(a, p, o.L) : launch_io<uint16_t>(a, p, o.L);
   if (e != hipSuccess) return e;
   const int C4 = (int)(4 * a.D);
   hipLaunchKernelGGL(bwd_params, dim3((unsigned)((C4 * a.N + 255) / 256)), dim3(256), 0, a.stream, a.A_log, p.dAp,
-                     p.dbp, p.dDp, a.dA_log, a.ddt_bias, a.dDs, (int)a.B, C4, (int)a.N);
+                     p.dbp, p.dDp, a.dA_log, a.ddt_bias, a.dDs, (int)(a.B * o.nsp), C4, (int)a.N);
   return hipGetLastError();
 }
 

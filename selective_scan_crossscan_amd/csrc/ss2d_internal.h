@@ -124,6 +124,8 @@ struct BackwardArgs {
   hipStream_t stream;
 };
 size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N);
+// Segments each backward sequence is cut into (1: one workgroup walks the whole map).
+int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N);
 hipError_t launch_backward(const BackwardArgs& a, void* scratch);
 
 // x (B*D planes of H x W) -> xT (planes of W x H).
