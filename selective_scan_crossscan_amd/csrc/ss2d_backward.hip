@@ -98,6 +98,21 @@ constexpr int kCT = 8;                // steps per lane in a chunk
 constexpr int kChunk = 16 * kCT;      // steps per chunk
 constexpr int kPad = kChunk + 16;     // LDS row: one pad slot per lane's run, so a row's lanes hit distinct banks
 
+// Sums over the four rows of a wave (its four channels), by halves.  The 32-lane
+// swap exchanges lanes 32-63 of x with lanes 0-31 of y; adding the two results
+// leaves x summed over rows r and r + 2 in lanes 0-31 and y summed likewise in
+// lanes 32-63.  The 16-lane swap exchanges the odd rows of x with the even rows of
+// y; adding leaves x summed over rows r and r + 1 in rows 0 and 2 and y in rows 1
+// and 3.
+__device__ __forceinline__ float swap_add32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_add16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dppf(float old, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xf, 0xf, false));
@@ -140,7 +155,7 @@ template <typename S, int MODE>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   __shared__ float sB[16][kPad];
   __shared__ float sC[16][kPad];
-  __shared__ float red[2][16][kPad];
+  __shared__ float wred[2][4][2][kPad];  // [state parity][wave][dCs, dBs][step]: the waves' four-channel sums
   __shared__ float carry_q[16][16], carry_a[16][16], dA_s[16][16], a2s[16][16];
   __shared__ float adj_p[16][16], adj_q[16][16];  // kSegMaps: the adjoint map of the chunks walked so far
   const int tid = threadIdx.x, s = tid & 15, ch = tid >> 4;
@@ -176,17 +191,27 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
   auto cdl = [&](int c) -> float& { return p.cdl[(((int64_t)bk * nch + c) * D + ds) * 16 + s]; };
   const int j0 = s * kCT, jp0 = j0 + s;  // first step of this lane in the chunk, and its padded LDS slot
 
-  float del[kCT], uu[kCT], gg[kCT], sig[kCT];
+  // Per lane and chunk: delta, u, xu = delta * u (the input's factor of every
+  // state), g and sigmoid(dt + bias).  (Reading u and dt again at the chunk's end
+  // instead of keeping them measured slower.)
+  float del[kCT], uu[kCT], xu[kCT], gg[kCT], sig[kCT];
+  auto lane_step = [&](int c, int i, int& li, int& xi) {
+    const int l = c * kChunk + j0 + i;
+    const bool in = dval && l < L;
+    li = in ? l : 0;
+    xi = in ? (k >= 2 ? L - 1 - l : l) : 0;
+    return in;
+  };
   auto load_lane = [&](int c, bool with_g) {
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
-      const int l = c * kChunk + j0 + i;
-      const bool in = dval && l < L;
-      const int li = in ? l : 0, xi = in ? (k >= 2 ? L - 1 - l : l) : 0;
+      int li, xi;
+      const bool in = lane_step(c, i, li, xi);
       const float pre = Io<S>::ld(dtr, li) + bias;
       del[i] = in ? softplus_f32(pre) : 0.f;
-      sig[i] = in ? 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;
       uu[i] = in ? Io<S>::ld(xs, xi) : 0.f;
+      sig[i] = in ? 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;
+      xu[i] = del[i] * uu[i];
       gg[i] = in && with_g ? Io<S>::ld(gs, xi) : 0.f;
     }
   };
@@ -230,7 +255,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < kCT; ++i) {
           a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
-          Q = fmaf(a[i], Q, del[i] * uu[i] * sB[n][jp0 + i]);
+          Q = fmaf(a[i], Q, xu[i] * sB[n][jp0 + i]);
         }
         if (seg) {
           // the lane's adjoint map r -> Pl r + R (r enters after its last step),
@@ -267,18 +292,23 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
     __syncthreads();
   }
 
+  // Per step, over the states: tq = sum_n q Bs and sa = sum_n q A a h_{l-1}, so
+  // that du = delta tq + Ds g and ddelta = sa + u tq take no per-state product.
   float dbias = 0.f, dD = 0.f;
   for (int c = c1 - 1; c >= c0; --c) {
     stage(c, true);
     load_lane(c, true);
     __syncthreads();
-    float du[kCT], dd[kCT];
+    float tq[kCT], sa[kCT];
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) du[i] = dd[i] = 0.f;
+    for (int i = 0; i < kCT; ++i) tq[i] = sa[i] = 0.f;
+    float sd1 = 0.f;  // delta summed over the lane's steps after its first
+#pragma unroll
+    for (int i = 1; i < kCT; ++i) sd1 += del[i];
     const float cum = MODE == kSegGrads && dval ? cdl(c) : 0.f;
     for (int n = 0; n < N; ++n) {
       const float A2 = a2s[ch][n], A = A2 * kLn2;
-      float a[kCT], h[kCT];
+      float a[kCT], h[kCT], cg[kCT];
       float h_in = dval ? hck(c, n) : 0.f;
       // a segment's stored states start from zero: add the entering state's decayed part
       if (MODE == kSegGrads) h_in = fmaf(__builtin_amdgcn_exp2f(A2 * cum), adj_q[ch][n], h_in);
@@ -286,34 +316,34 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < kCT; ++i) {
         a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
-        hv = fmaf(a[i], hv, del[i] * uu[i] * sB[n][jp0 + i]);
+        hv = fmaf(a[i], hv, xu[i] * sB[n][jp0 + i]);
         h[i] = hv;
       }
       const float acar = carry_a[ch][n], qcar = carry_q[ch][n];
       const float a_right = dppf<kRowShl + 1>(acar, a[0]);  // decay of the step after this lane's last
-      float P = 1.f, Q = 0.f;
+      // the lane's map q_after -> P q_after + Q: P is the decay over its steps after the first, then a_right
+      float P = a_right * __builtin_amdgcn_exp2f(A2 * sd1), Q = 0.f;
 #pragma unroll
       for (int i = kCT - 1; i >= 0; --i) {
         const float an = i == kCT - 1 ? a_right : a[i + 1];
-        Q = fmaf(an, Q, sC[n][jp0 + i] * gg[i]);
-        P *= an;
+        cg[i] = sC[n][jp0 + i] * gg[i];
+        Q = fmaf(an, Q, cg[i]);
       }
       scan_maps<kRowShl>(P, Q);
       const float Pe = dppf<kRowShl + 1>(1.f, P), Qe = dppf<kRowShl + 1>(0.f, Q);
       float q = fmaf(Pe, qcar, Qe);  // adjoint at the step after this lane's last
-      float dA = 0.f;
+      float dA = 0.f, hg[kCT], qx[kCT];  // the dCs and dBs terms of each step
 #pragma unroll
       for (int i = kCT - 1; i >= 0; --i) {
         const float an = i == kCT - 1 ? a_right : a[i + 1];
-        const float Bv = sB[n][jp0 + i];
-        q = fmaf(an, q, sC[n][jp0 + i] * gg[i]);
+        q = fmaf(an, q, cg[i]);
         const float hp = i > 0 ? h[i - 1] : h_in;
-        const float qd = q * del[i];
-        du[i] = fmaf(qd, Bv, du[i]);
-        dd[i] = fmaf(q, fmaf(A * a[i], hp, Bv * uu[i]), dd[i]);
-        dA = fmaf(qd * a[i], hp, dA);
-        red[0][ch][jp0 + i] = h[i] * gg[i];
-        red[1][ch][jp0 + i] = qd * uu[i];
+        const float w = q * a[i] * hp;
+        tq[i] = fmaf(q, sB[n][jp0 + i], tq[i]);
+        sa[i] = fmaf(A, w, sa[i]);
+        dA = fmaf(del[i], w, dA);
+        hg[i] = h[i] * gg[i];
+        qx[i] = q * xu[i];
       }
       const float q0 = row_lane(q, 0), a0 = row_lane(a[0], 0);
       dA = row_sum16(dA);
@@ -322,28 +352,42 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
         carry_a[ch][n] = a0;
         dA_s[ch][n] += dA;
       }
+      // the terms summed over the wave's four channels: after the two swap rounds,
+      // lane (row r, s) holds, for t = 0..3, the sum for step 2t + (r & 1) of lane
+      // s's run, of dCs for r < 2 and of dBs for r >= 2
+      float h2[kCT];
+#pragma unroll
+      for (int m = 0; m < kCT; ++m) h2[m] = swap_add32(hg[m], qx[m]);
+      {
+        const int r = (tid >> 4) & 3;
+        float* wr = &wred[n & 1][tid >> 6][r >> 1][jp0 + (r & 1)];
+#pragma unroll
+        for (int t = 0; t < kCT / 2; ++t) wr[2 * t] = swap_add16(h2[2 * t], h2[2 * t + 1]);
+      }
+      // One barrier per state: the next state writes the other buffer, and the one
+      // after it writes this buffer only past the next barrier, which every thread
+      // reaches after reading this one.
       __syncthreads();
-      for (int o = tid; o < 2 * kChunk; o += 256) {
-        const int which = o / kChunk, j = o - which * kChunk;
+      {
+        static_assert(2 * kChunk == 256, "one dCs or dBs sum per thread");
+        const int which = tid / kChunk, j = tid - which * kChunk;
         const int l = c * kChunk + j;
         if (l < L) {
           const int jp = j + j / kCT;
-          float sum = 0.f;
-#pragma unroll
-          for (int c2 = 0; c2 < 16; ++c2) sum += red[which][c2][jp];
+          const float sum = ((wred[n & 1][0][which][jp] + wred[n & 1][1][which][jp]) + wred[n & 1][2][which][jp]) +
+                            wred[n & 1][3][which][jp];
           float* dst = which == 0 ? p.dCp : p.dBp;
           dst[(((int64_t)bk * p.nblk + blk) * N + n) * L + l] = sum;
         }
       }
-      __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
-      const int l = c * kChunk + j0 + i;
-      if (dval && l < L) {
-        const float ddt = dd[i] * sig[i];
-        Io<S>::st(static_cast<S*>(p.ddt), row + l, ddt);
-        p.du[row + l] = fmaf(Dsk, gg[i], du[i]);
+      int li, xi;
+      if (lane_step(c, i, li, xi)) {
+        const float ddt = fmaf(uu[i], tq[i], sa[i]) * sig[i];
+        Io<S>::st(static_cast<S*>(p.ddt), row + li, ddt);
+        p.du[row + li] = fmaf(del[i], tq[i], Dsk * gg[i]);
         dbias += ddt;
         dD = fmaf(gg[i], uu[i], dD);
       }
@@ -402,23 +446,45 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ d
   }
 }
 
-// dx[b, d, p] = du of directions 0, 1, 2, 3 at the steps that visit p, added in that order.
+// dx[b, d, p] = du of directions 0, 1, 2, 3 at the steps that visit p, added in that
+// order.  A workgroup takes a kMergeTile x kMergeTile pixel tile of one (b, d)
+// plane: the column directions' values are read along their walk (down the tile's
+// columns) into LDS and read back across its rows, so every global access is
+// contiguous (rows of odd LDS length: both sides free of bank conflicts).
+constexpr int kMergeTile = 32;
+
 template <typename S>
-__global__ __launch_bounds__(256) void bwd_merge(const float* __restrict__ du, S* __restrict__ dx, int64_t BD,
-                                                int D, int H, int W) {
+__global__ __launch_bounds__(256) void bwd_merge(const float* __restrict__ du, S* __restrict__ dx, int D, int H,
+                                                int W, int tiles_w, int tiles) {
+  __shared__ float t1[kMergeTile][kMergeTile + 1], t3[kMergeTile][kMergeTile + 1];  // [w][h]
+  const int64_t bd = blockIdx.x / tiles;
+  const int t = (int)(blockIdx.x - bd * tiles);
+  const int h0 = (t / tiles_w) * kMergeTile, w0 = (t % tiles_w) * kMergeTile;
+  const int64_t b = bd / D, d = bd - b * D;
   const int L = H * W;
-  const int64_t total = BD * L;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t bd = e / L;
-    const int px = (int)(e - bd * L);
-    const int64_t b = bd / D, d = bd - b * D;
-    const int hh = px / W, ww = px - hh * W;
-    const int lc = ww * H + hh;
-    const float* r0 = du + ((b * 4 + 0) * D + d) * L;
-    const float* r1 = du + ((b * 4 + 1) * D + d) * L;
-    const float* r2 = du + ((b * 4 + 2) * D + d) * L;
-    const float* r3 = du + ((b * 4 + 3) * D + d) * L;
-    Io<S>::st(dx, e, ((r0[px] + r1[lc]) + r2[L - 1 - px]) + r3[L - 1 - lc]);
+  const float* r0 = du + ((b * 4 + 0) * D + d) * L;
+  const float* r1 = du + ((b * 4 + 1) * D + d) * L;
+  const float* r2 = du + ((b * 4 + 2) * D + d) * L;
+  const float* r3 = du + ((b * 4 + 3) * D + d) * L;
+  const int a = threadIdx.x & 31, c = threadIdx.x >> 5;
+#pragma unroll
+  for (int m = 0; m < kMergeTile / 8; ++m) {  // pixel (h0 + a, w0 + ww) is step (w0 + ww) * H + h0 + a of the column walk
+    const int ww = c + 8 * m;
+    if (h0 + a < H && w0 + ww < W) {
+      const int lc = (w0 + ww) * H + h0 + a;
+      t1[ww][a] = r1[lc];
+      t3[ww][a] = r3[L - 1 - lc];
+    }
+  }
+  __syncthreads();
+  S* out = dx + bd * L;
+#pragma unroll
+  for (int m = 0; m < kMergeTile / 8; ++m) {
+    const int hh = c + 8 * m;
+    if (h0 + hh < H && w0 + a < W) {
+      const int px = (h0 + hh) * W + w0 + a;
+      Io<S>::st(out, px, ((r0[px] + t1[a][hh]) + r2[L - 1 - px]) + t3[a][hh]);
+    }
   }
 }
 
@@ -471,8 +537,10 @@ hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L) {
   hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, static_cast<S*>(a.dBs),
                      static_cast<S*>(a.dCs), a.B * 4, p.nblk, (int)a.N, (int)L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_merge<S>), dim3(4096), dim3(256), 0, a.stream, p.du, static_cast<S*>(a.dx), a.B * a.D,
-                     (int)a.D, (int)a.H, (int)a.W);
+  const int tiles_w = (int)((a.W + kMergeTile - 1) / kMergeTile);
+  const int tiles = (int)((a.H + kMergeTile - 1) / kMergeTile) * tiles_w;
+  hipLaunchKernelGGL((bwd_merge<S>), dim3((unsigned)(a.B * a.D * tiles)), dim3(256), 0, a.stream, p.du,
+                     static_cast<S*>(a.dx), (int)a.D, (int)a.H, (int)a.W, tiles_w, tiles);
   return hipGetLastError();
 }
 
@@ -567,7 +635,8 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.nblk = (int)o.nblk;
   p.nsp = (int)o.nsp;
   p.cps = (int)o.cps;
-  if (a.B * 4 * o.nblk * o.nsp > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t merge_tiles = ((a.H + kMergeTile - 1) / kMergeTile) * ((a.W + kMergeTile - 1) / kMergeTile);
+  if (a.B * 4 * o.nblk * o.nsp > INT32_MAX || a.B * a.D * merge_tiles > INT32_MAX) return hipErrorInvalidValue;
   hipError_t e = a.dtype == 0 ? launch_io<float>(a, p, o.L) : launch_io<uint16_t>(a, p, o.L);
   if (e != hipSuccess) return e;
   const int C4 = (int)(4 * a.D);
