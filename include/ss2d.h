@@ -199,7 +199,8 @@ int ss2d_version(void);
  * ss2d_describe -- write a one-line, NUL-terminated description of how
  * ss2d_forward would run this shape (kernel variant, lanes per sequence,
  * channels per workgroup, grid size, LDS and temporary sizes), followed by the
- * number of segments ss2d_backward cuts each sequence into, into buf[0..len).
+ * number of segments ss2d_backward cuts each sequence into and the number of
+ * 16-channel blocks each of its workgroups takes, into buf[0..len).
  * Host only; no device work.  Returns SS2D_OK or a validation code.
  */
 int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,

@@ -146,11 +146,12 @@ int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dty
   snprintf(buf, (size_t)len,
            "kernel=chunked_dpp_scan lanes_per_seq=%d steps_per_lane=%d waves=%d chans_per_block=%d "
            "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu "
-           "backward_segments=%lld",
+           "backward_segments=%lld backward_blocks_per_workgroup=%lld",
            pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.xtrans ? 1 : 0,
            pl.transpose ? 1 : 0,
            (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes,
-           (long long)ss2d::backward_segments(B, D, H, W, N));
+           (long long)ss2d::backward_segments(B, D, H, W, N, dtype),
+           (long long)ss2d::backward_blocks_per_workgroup(B, D, H, W, N, dtype));
   return SS2D_OK;
 }
 
@@ -422,7 +423,7 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
   if (rc != SS2D_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* tmp = nullptr;
-  hipError_t e = hipMallocAsync(&tmp, ss2d::backward_scratch_bytes(B, D, H, W, N), st);
+  hipError_t e = hipMallocAsync(&tmp, ss2d::backward_scratch_bytes(B, D, H, W, N, dtype), st);
   if (e != hipSuccess) {
     remember(e);
     return SS2D_ERR_HIP;

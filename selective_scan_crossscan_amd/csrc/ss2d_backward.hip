@@ -64,7 +64,7 @@ struct BwdParams {
   void* ddt;   // (B, 4, D, L) out
   float* du;   // (B, 4, D, L) temporary
   float* hck;  // (B*4, nseg, D, N, 16) temporary: state entering each lane's steps of each chunk
-  float* dBp;  // (B*4, nblk, N, L) temporary
+  float* dBp;  // (B*4, ceil(nblk / CPB), N, L) temporary: one partial per workgroup's channel blocks
   float* dCp;
   float* dAp;  // (B, nsp, 4D, N) temporary
   float* dbp;  // (B, nsp, 4D) temporary
@@ -148,71 +148,123 @@ constexpr int kRowShl = 0x100;  // row_shl:n = 0x100 + n (from lane i + n)
 
 // MODE kWhole: one workgroup walks every chunk, pass A then pass B.  kSegMaps: pass
 // A over one segment from a zero state, with the segment's maps as records.
-// kSegGrads: pass B over one segment, from the chained records.
+// kSegGrads: pass B over one segment, from the chained records.  CPB channel
+// blocks per workgroup share each chunk's Bs/Cs staging and write one dBs/dCs
+// partial between them.
 enum BwdMode { kWhole = 0, kSegMaps = 1, kSegGrads = 2 };
 
-template <typename S, int MODE>
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
+// One channel as seen by the lanes of its DPP row: validity, parameters and the
+// rows it reads.
+template <typename S>
+struct BwdChan {
+  bool valid;
+  int d, c_idx;  // channel (0 when invalid) and its index k * D + d in the per-channel parameters
+  float bias, dsk;
+  const S* xs;   // u along the direction's walk (x or its transpose)
+  const S* gs;   // g likewise
+  const S* dtr;  // dt row
+  int64_t row;   // start of the (b, k, d) row in (B, 4, D, L) tensors
+  __device__ BwdChan(const BwdParams& p, int bk, int dd) {
+    const int k = bk & 3, b = bk >> 2, D = p.D, L = p.L;
+    valid = dd < D;
+    d = valid ? dd : 0;
+    c_idx = k * D + d;
+    bias = p.dt_bias[c_idx];
+    dsk = p.Ds[c_idx];
+    xs = static_cast<const S*>((k & 1) ? p.xT : p.x) + ((int64_t)b * D + d) * L;
+    gs = static_cast<const S*>((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + d) * L;
+    dtr = static_cast<const S*>(p.dt) + ((int64_t)bk * D + d) * L;
+    row = ((int64_t)bk * D + d) * L;
+  }
+};
+
+// Per channel block, lane s's register copy of what belongs to state s of its
+// row's channel (read by the row's lanes with row_lane), and the lane's sums.
+struct BwdRegs {
+  float a2;      // A * log2(e)
+  float h;       // pass A: the state carried to the next chunk; kSegGrads: the state entering the segment
+  float q, a;    // pass B: the adjoint and the decay at the first step of the chunk walked last
+  float dA;      // sum of q delta a h_{l-1}
+  float ap, aq;  // kSegMaps: the adjoint map of the chunks walked so far
+  float dbias, dD;
+};
+
+// At most 168 VGPRs (three waves per SIMD): two blocks per workgroup would
+// otherwise take 188 and run at two; the few values spilled are reloaded per
+// chunk, outside the state loop.
+template <typename S, int MODE, int CPB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_chunk_kernel(BwdParams p) {
   __shared__ float sB[16][kPad];
   __shared__ float sC[16][kPad];
-  __shared__ float wred[2][4][2][kPad];  // [state parity][wave][dCs, dBs][step]: the waves' four-channel sums
-  __shared__ float carry_q[16][16], carry_a[16][16], dA_s[16][16], a2s[16][16];
-  __shared__ float adj_p[16][16], adj_q[16][16];  // kSegMaps: the adjoint map of the chunks walked so far
+  __shared__ float wred[2][4][2][kPad];    // [state parity][wave][dCs, dBs][step]: the waves' four-channel sums
+  __shared__ float acc[CPB > 1 ? 16 : 1][256];  // [state][thread]: the earlier blocks' sums at the thread's step
+  // The blocks take turns in one register set: after each block the thread swaps
+  // it with its stash slot (the other block's, CPB = 2), so the loop over blocks
+  // stays rolled and the registers those of one block.
+  __shared__ BwdRegs stash[CPB > 1 ? 256 : 1];
+  static_assert(CPB == 1 || CPB == 2, "one or two channel blocks per workgroup");
   const int tid = threadIdx.x, s = tid & 15, ch = tid >> 4;
   const int sg = blockIdx.x % p.nsp;
   const int grp = blockIdx.x / p.nsp;
-  const int blk = grp % p.nblk;
-  const int bk = grp / p.nblk;  // b * 4 + k
+  const int ngrp = (p.nblk + CPB - 1) / CPB;
+  const int blk0 = (grp % ngrp) * CPB;  // this workgroup's first channel block
+  const int bk = grp / ngrp;            // b * 4 + k
   const int k = bk & 3, b = bk >> 2;
   const int D = p.D, L = p.L, N = p.N, nch = p.nseg;
   const int c0 = sg * p.cps, c1 = min(nch, c0 + p.cps);
-  const int d = blk * kBwdChans + ch;
-  const bool dval = d < D;
-  const int ds = dval ? d : 0;
-  const int c_idx = k * D + ds;
-  const int64_t rec = (((int64_t)bk * p.nsp + sg) * D + ds) * N + s;  // this lane's segment record (state s)
-  const bool rval = dval && s < N;
-  a2s[ch][s] = rval ? -expf(p.A_log[(int64_t)c_idx * N + s]) * kLog2e : 0.f;
-  carry_q[ch][s] = MODE == kSegGrads && rval ? p.segR[rec] : 0.f;
-  carry_a[ch][s] = 1.f;
-  dA_s[ch][s] = 0.f;
-  adj_p[ch][s] = 1.f;
-  adj_q[ch][s] = MODE == kSegGrads && rval ? p.segF[rec] : 0.f;  // kSegGrads: the state entering the segment
-  const float bias = p.dt_bias[c_idx], Dsk = p.Ds[c_idx];
-  const S* xs = static_cast<const S*>((k & 1) ? p.xT : p.x) + ((int64_t)b * D + ds) * L;
-  const S* gs = static_cast<const S*>((k & 1) ? p.dyT : p.dy) + ((int64_t)b * D + ds) * L;
-  const S* dtr = static_cast<const S*>(p.dt) + ((int64_t)bk * D + ds) * L;
+  const int j0 = s * kCT, jp0 = j0 + s;  // first step of this lane in the chunk, and its padded LDS slot
   const S* Bb = static_cast<const S*>(p.Bs) + (int64_t)bk * N * L;
   const S* Cb = static_cast<const S*>(p.Cs) + (int64_t)bk * N * L;
-  const int64_t row = ((int64_t)bk * D + ds) * L;
-  auto hck = [&](int c, int n) -> float& {
-    return p.hck[((((int64_t)bk * nch + c) * D + ds) * N + n) * 16 + s];
+  // this thread's dCs (tid < kChunk) or dBs output step in a chunk
+  static_assert(2 * kChunk == 256, "one dCs or dBs sum per thread");
+  const int which = tid / kChunk, jo = tid - which * kChunk, jpo = jo + jo / kCT;
+
+  BwdRegs rr;  // the current block's
+  auto next_block = [&]() {  // rr <-> stash (CPB = 2): blocks 0, 1, 0, 1, ...
+    if (CPB > 1) {
+      const BwdRegs t = stash[tid];
+      stash[tid] = rr;
+      rr = t;
+    }
   };
-  auto cdl = [&](int c) -> float& { return p.cdl[(((int64_t)bk * nch + c) * D + ds) * 16 + s]; };
-  const int j0 = s * kCT, jp0 = j0 + s;  // first step of this lane in the chunk, and its padded LDS slot
+#pragma unroll 1
+  for (int cb = 0; cb < CPB; ++cb) {
+    const BwdChan<S> cn(p, bk, (blk0 + cb) * kBwdChans + ch);
+    const bool rval = cn.valid && s < N;
+    const int64_t rec = (((int64_t)bk * p.nsp + sg) * D + cn.d) * N + s;  // this lane's segment record (state s)
+    rr.a2 = rval ? -expf(p.A_log[(int64_t)cn.c_idx * N + s]) * kLog2e : 0.f;
+    rr.h = MODE == kSegGrads && rval ? p.segF[rec] : 0.f;
+    rr.q = MODE == kSegGrads && rval ? p.segR[rec] : 0.f;
+    rr.a = 1.f;
+    rr.dA = 0.f;
+    rr.ap = 1.f;
+    rr.aq = 0.f;
+    rr.dbias = rr.dD = 0.f;
+    next_block();
+  }
 
   // Per lane and chunk: delta, u, xu = delta * u (the input's factor of every
   // state), g and sigmoid(dt + bias).  (Reading u and dt again at the chunk's end
   // instead of keeping them measured slower.)
   float del[kCT], uu[kCT], xu[kCT], gg[kCT], sig[kCT];
-  auto lane_step = [&](int c, int i, int& li, int& xi) {
+  auto lane_step = [&](const BwdChan<S>& cn, int c, int i, int& li, int& xi) {
     const int l = c * kChunk + j0 + i;
-    const bool in = dval && l < L;
+    const bool in = cn.valid && l < L;
     li = in ? l : 0;
     xi = in ? (k >= 2 ? L - 1 - l : l) : 0;
     return in;
   };
-  auto load_lane = [&](int c, bool with_g) {
+  auto load_lane = [&](const BwdChan<S>& cn, int c, bool with_g) {
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
       int li, xi;
-      const bool in = lane_step(c, i, li, xi);
-      const float pre = Io<S>::ld(dtr, li) + bias;
+      const bool in = lane_step(cn, c, i, li, xi);
+      const float pre = Io<S>::ld(cn.dtr, li) + cn.bias;
       del[i] = in ? softplus_f32(pre) : 0.f;
-      uu[i] = in ? Io<S>::ld(xs, xi) : 0.f;
+      uu[i] = in ? Io<S>::ld(cn.xs, xi) : 0.f;
       sig[i] = in ? 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;
       xu[i] = del[i] * uu[i];
-      gg[i] = in && with_g ? Io<S>::ld(gs, xi) : 0.f;
+      gg[i] = in && with_g ? Io<S>::ld(cn.gs, xi) : 0.f;
     }
   };
   auto stage = [&](int c, bool with_c) {
@@ -226,180 +278,201 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdParams p) {
       if (with_c) sC[n][jp] = in ? Io<S>::ld(Cb, off) : 0.f;
     }
   };
-  __syncthreads();
+  auto hck = [&](const BwdChan<S>& cn, int c, int n) -> float& {
+    return p.hck[((((int64_t)bk * nch + c) * D + cn.d) * N + n) * 16 + s];
+  };
+  auto cdl = [&](const BwdChan<S>& cn, int c) -> float& {
+    return p.cdl[(((int64_t)bk * nch + c) * D + cn.d) * 16 + s];
+  };
 
   if (MODE != kSegGrads) {
     // pass A: the state entering each lane's steps of every chunk
     constexpr bool seg = MODE == kSegMaps;
+    static_assert(MODE != kSegMaps || CPB == 1, "segment maps take one block per workgroup");
     float cum = 0.f;  // kSegMaps: delta summed over the segment's chunks before this one
     for (int c = c0; c < c1; ++c) {
       stage(c, seg);
-      load_lane(c, seg);
-      __syncthreads();
-      float sdel = 0.f;
+#pragma unroll 1
+      for (int cb = 0; cb < CPB; ++cb) {
+        const BwdChan<S> cn(p, bk, (blk0 + cb) * kBwdChans + ch);
+        load_lane(cn, c, seg);
+        if (cb == 0) __syncthreads();  // the chunk's Bs (and Cs) staged
+        float sdel = 0.f;
 #pragma unroll
-      for (int i = 0; i < kCT; ++i) sdel += del[i];
-      if (seg) {
-        float incl = sdel;  // inclusive prefix over the row
-        incl += dppf<kRowShr + 1>(0.f, incl);
-        incl += dppf<kRowShr + 2>(0.f, incl);
-        incl += dppf<kRowShr + 4>(0.f, incl);
-        incl += dppf<kRowShr + 8>(0.f, incl);
-        if (dval) cdl(c) = cum + (incl - sdel);
-        cum += row_lane(incl, 15);
-      }
-      for (int n = 0; n < N; ++n) {
-        const float A2 = a2s[ch][n];
-        const float Pl = __builtin_amdgcn_exp2f(A2 * sdel);
-        float P = Pl, Q = 0.f, a[kCT];
-#pragma unroll
-        for (int i = 0; i < kCT; ++i) {
-          a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
-          Q = fmaf(a[i], Q, xu[i] * sB[n][jp0 + i]);
-        }
+        for (int i = 0; i < kCT; ++i) sdel += del[i];
         if (seg) {
-          // the lane's adjoint map r -> Pl r + R (r enters after its last step),
-          // composed over the row: lane 0 holds the chunk's
-          float Pb = Pl, R = 0.f;
-#pragma unroll
-          for (int i = kCT - 1; i >= 0; --i) R = a[i] * fmaf(sC[n][jp0 + i], gg[i], R);
-          scan_maps<kRowShl>(Pb, R);
-          if (s == 0) {  // the chunks so far, then this one: (P1, Q1) o (Pb, R)
-            const float P1 = adj_p[ch][n];
-            adj_q[ch][n] = fmaf(P1, R, adj_q[ch][n]);
-            adj_p[ch][n] = P1 * Pb;
-          }
+          float incl = sdel;  // inclusive prefix over the row
+          incl += dppf<kRowShr + 1>(0.f, incl);
+          incl += dppf<kRowShr + 2>(0.f, incl);
+          incl += dppf<kRowShr + 4>(0.f, incl);
+          incl += dppf<kRowShr + 8>(0.f, incl);
+          if (cn.valid) cdl(cn, c) = cum + (incl - sdel);
+          cum += row_lane(incl, 15);
         }
-        scan_maps<kRowShr>(P, Q);
-        const float Pe = dppf<kRowShr + 1>(1.f, P), Qe = dppf<kRowShr + 1>(0.f, Q);
-        const float hc = carry_q[ch][n];
-        if (dval) hck(c, n) = fmaf(Pe, hc, Qe);
-        const float hout = fmaf(P, hc, Q);  // lane 15: the state leaving the chunk
-        if (s == 15) carry_q[ch][n] = hout;
+        for (int n = 0; n < N; ++n) {
+          const float A2 = row_lane(rr.a2, n);
+          const float Pl = __builtin_amdgcn_exp2f(A2 * sdel);
+          float P = Pl, Q = 0.f, a[kCT];
+#pragma unroll
+          for (int i = 0; i < kCT; ++i) {
+            a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
+            Q = fmaf(a[i], Q, xu[i] * sB[n][jp0 + i]);
+          }
+          if (seg) {
+            // the lane's adjoint map r -> Pl r + R (r enters after its last step),
+            // composed over the row: lane 0 holds the chunk's
+            float Pb = Pl, R = 0.f;
+#pragma unroll
+            for (int i = kCT - 1; i >= 0; --i) R = a[i] * fmaf(sC[n][jp0 + i], gg[i], R);
+            scan_maps<kRowShl>(Pb, R);
+            const float Pb0 = row_lane(Pb, 0), R0 = row_lane(R, 0);
+            if (s == n) {  // the chunks so far, then this one: (ap, aq) o (Pb0, R0)
+              rr.aq = fmaf(rr.ap, R0, rr.aq);
+              rr.ap *= Pb0;
+            }
+          }
+          scan_maps<kRowShr>(P, Q);
+          const float Pe = dppf<kRowShr + 1>(1.f, P), Qe = dppf<kRowShr + 1>(0.f, Q);
+          const float hc = row_lane(rr.h, n);
+          if (cn.valid) hck(cn, c, n) = fmaf(Pe, hc, Qe);
+          const float hout = row_lane(fmaf(P, hc, Q), 15);  // the state leaving the chunk (lane 15's)
+          if (s == n) rr.h = hout;
+        }
+        next_block();
       }
-      __syncthreads();
+      __syncthreads();  // the next chunk's staging overwrites Bs/Cs
     }
     if (seg) {
-      if (rval) {
-        p.segP[rec] = adj_p[ch][s];
-        p.segF[rec] = carry_q[ch][s];
-        p.segR[rec] = adj_q[ch][s];
+      const BwdChan<S> cn(p, bk, blk0 * kBwdChans + ch);
+      if (cn.valid && s < N) {
+        const int64_t rec = (((int64_t)bk * p.nsp + sg) * D + cn.d) * N + s;
+        p.segP[rec] = rr.ap;
+        p.segF[rec] = rr.h;
+        p.segR[rec] = rr.aq;
       }
       return;
     }
-    // pass B: chunks from the last; the adjoint enters each lane from the right
-    carry_q[ch][s] = 0.f;
-    __syncthreads();
   }
 
+  // pass B: chunks from the last; the adjoint enters each lane from the right.
   // Per step, over the states: tq = sum_n q Bs and sa = sum_n q A a h_{l-1}, so
   // that du = delta tq + Ds g and ddelta = sa + u tq take no per-state product.
-  float dbias = 0.f, dD = 0.f;
+  int par = 0;  // consecutive states use alternate wred buffers
   for (int c = c1 - 1; c >= c0; --c) {
     stage(c, true);
-    load_lane(c, true);
-    __syncthreads();
-    float tq[kCT], sa[kCT];
+    const int lo = c * kChunk + jo;  // this thread's dCs/dBs step
+#pragma unroll 1
+    for (int cb = 0; cb < CPB; ++cb) {
+      const BwdChan<S> cn(p, bk, (blk0 + cb) * kBwdChans + ch);
+      load_lane(cn, c, true);
+      if (cb == 0) __syncthreads();  // the chunk's Bs/Cs staged
+      float tq[kCT], sa[kCT];
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) tq[i] = sa[i] = 0.f;
-    float sd1 = 0.f;  // delta summed over the lane's steps after its first
+      for (int i = 0; i < kCT; ++i) tq[i] = sa[i] = 0.f;
+      float sd1 = 0.f;  // delta summed over the lane's steps after its first
 #pragma unroll
-    for (int i = 1; i < kCT; ++i) sd1 += del[i];
-    const float cum = MODE == kSegGrads && dval ? cdl(c) : 0.f;
-    for (int n = 0; n < N; ++n) {
-      const float A2 = a2s[ch][n], A = A2 * kLn2;
-      float a[kCT], h[kCT], cg[kCT];
-      float h_in = dval ? hck(c, n) : 0.f;
-      // a segment's stored states start from zero: add the entering state's decayed part
-      if (MODE == kSegGrads) h_in = fmaf(__builtin_amdgcn_exp2f(A2 * cum), adj_q[ch][n], h_in);
-      float hv = h_in;
+      for (int i = 1; i < kCT; ++i) sd1 += del[i];
+      const float cum = MODE == kSegGrads && cn.valid ? cdl(cn, c) : 0.f;
+      for (int n = 0; n < N; ++n) {
+        const float A2 = row_lane(rr.a2, n), A = A2 * kLn2;
+        float a[kCT], h[kCT], cg[kCT];
+        float h_in = cn.valid ? hck(cn, c, n) : 0.f;
+        // a segment's stored states start from zero: add the entering state's decayed part
+        if (MODE == kSegGrads) h_in = fmaf(__builtin_amdgcn_exp2f(A2 * cum), row_lane(rr.h, n), h_in);
+        float hv = h_in;
+#pragma unroll
+        for (int i = 0; i < kCT; ++i) {
+          a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
+          hv = fmaf(a[i], hv, xu[i] * sB[n][jp0 + i]);
+          h[i] = hv;
+        }
+        const float acar = row_lane(rr.a, n), qcar = row_lane(rr.q, n);
+        const float a_right = dppf<kRowShl + 1>(acar, a[0]);  // decay of the step after this lane's last
+        // the lane's map q_after -> P q_after + Q: P is the decay over its steps after the first, then a_right
+        float P = a_right * __builtin_amdgcn_exp2f(A2 * sd1), Q = 0.f;
+#pragma unroll
+        for (int i = kCT - 1; i >= 0; --i) {
+          const float an = i == kCT - 1 ? a_right : a[i + 1];
+          cg[i] = sC[n][jp0 + i] * gg[i];
+          Q = fmaf(an, Q, cg[i]);
+        }
+        scan_maps<kRowShl>(P, Q);
+        const float Pe = dppf<kRowShl + 1>(1.f, P), Qe = dppf<kRowShl + 1>(0.f, Q);
+        float q = fmaf(Pe, qcar, Qe);  // adjoint at the step after this lane's last
+        float dA = 0.f, hg[kCT], qx[kCT];  // the dCs and dBs terms of each step
+#pragma unroll
+        for (int i = kCT - 1; i >= 0; --i) {
+          const float an = i == kCT - 1 ? a_right : a[i + 1];
+          q = fmaf(an, q, cg[i]);
+          const float hp = i > 0 ? h[i - 1] : h_in;
+          const float w = q * a[i] * hp;
+          tq[i] = fmaf(q, sB[n][jp0 + i], tq[i]);
+          sa[i] = fmaf(A, w, sa[i]);
+          dA = fmaf(del[i], w, dA);
+          hg[i] = h[i] * gg[i];
+          qx[i] = q * xu[i];
+        }
+        const float q0 = row_lane(q, 0), a0 = row_lane(a[0], 0);
+        dA = row_sum16(dA);
+        if (s == n) {  // carried to the chunk before
+          rr.q = q0;
+          rr.a = a0;
+          rr.dA += dA;
+        }
+        // the terms summed over the wave's four channels: after the two swap rounds,
+        // lane (row r, s) holds, for t = 0..3, the sum for step 2t + (r & 1) of lane
+        // s's run, of dCs for r < 2 and of dBs for r >= 2
+        float h2[kCT];
+#pragma unroll
+        for (int m = 0; m < kCT; ++m) h2[m] = swap_add32(hg[m], qx[m]);
+        {
+          const int rw = ch & 3;
+          float* wr = &wred[par][tid >> 6][rw >> 1][jp0 + (rw & 1)];
+#pragma unroll
+          for (int t = 0; t < kCT / 2; ++t) wr[2 * t] = swap_add16(h2[2 * t], h2[2 * t + 1]);
+        }
+        // One barrier per state: the next state writes the other buffer, and the one
+        // after it writes this buffer only past the next barrier, which every thread
+        // reaches after reading this one.
+        __syncthreads();
+        if (lo < L) {
+          float sum = ((wred[par][0][which][jpo] + wred[par][1][which][jpo]) + wred[par][2][which][jpo]) +
+                      wred[par][3][which][jpo];
+          if (cb > 0) sum = acc[n][tid] + sum;  // the earlier blocks first
+          if (cb + 1 < CPB) {
+            acc[n][tid] = sum;  // this thread's own entry
+          } else {
+            float* dst = which == 0 ? p.dCp : p.dBp;
+            dst[(((int64_t)bk * ngrp + blk0 / CPB) * N + n) * L + lo] = sum;
+          }
+        }
+        par ^= 1;
+      }
 #pragma unroll
       for (int i = 0; i < kCT; ++i) {
-        a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
-        hv = fmaf(a[i], hv, xu[i] * sB[n][jp0 + i]);
-        h[i] = hv;
-      }
-      const float acar = carry_a[ch][n], qcar = carry_q[ch][n];
-      const float a_right = dppf<kRowShl + 1>(acar, a[0]);  // decay of the step after this lane's last
-      // the lane's map q_after -> P q_after + Q: P is the decay over its steps after the first, then a_right
-      float P = a_right * __builtin_amdgcn_exp2f(A2 * sd1), Q = 0.f;
-#pragma unroll
-      for (int i = kCT - 1; i >= 0; --i) {
-        const float an = i == kCT - 1 ? a_right : a[i + 1];
-        cg[i] = sC[n][jp0 + i] * gg[i];
-        Q = fmaf(an, Q, cg[i]);
-      }
-      scan_maps<kRowShl>(P, Q);
-      const float Pe = dppf<kRowShl + 1>(1.f, P), Qe = dppf<kRowShl + 1>(0.f, Q);
-      float q = fmaf(Pe, qcar, Qe);  // adjoint at the step after this lane's last
-      float dA = 0.f, hg[kCT], qx[kCT];  // the dCs and dBs terms of each step
-#pragma unroll
-      for (int i = kCT - 1; i >= 0; --i) {
-        const float an = i == kCT - 1 ? a_right : a[i + 1];
-        q = fmaf(an, q, cg[i]);
-        const float hp = i > 0 ? h[i - 1] : h_in;
-        const float w = q * a[i] * hp;
-        tq[i] = fmaf(q, sB[n][jp0 + i], tq[i]);
-        sa[i] = fmaf(A, w, sa[i]);
-        dA = fmaf(del[i], w, dA);
-        hg[i] = h[i] * gg[i];
-        qx[i] = q * xu[i];
-      }
-      const float q0 = row_lane(q, 0), a0 = row_lane(a[0], 0);
-      dA = row_sum16(dA);
-      if (s == 0) {
-        carry_q[ch][n] = q0;
-        carry_a[ch][n] = a0;
-        dA_s[ch][n] += dA;
-      }
-      // the terms summed over the wave's four channels: after the two swap rounds,
-      // lane (row r, s) holds, for t = 0..3, the sum for step 2t + (r & 1) of lane
-      // s's run, of dCs for r < 2 and of dBs for r >= 2
-      float h2[kCT];
-#pragma unroll
-      for (int m = 0; m < kCT; ++m) h2[m] = swap_add32(hg[m], qx[m]);
-      {
-        const int r = (tid >> 4) & 3;
-        float* wr = &wred[n & 1][tid >> 6][r >> 1][jp0 + (r & 1)];
-#pragma unroll
-        for (int t = 0; t < kCT / 2; ++t) wr[2 * t] = swap_add16(h2[2 * t], h2[2 * t + 1]);
-      }
-      // One barrier per state: the next state writes the other buffer, and the one
-      // after it writes this buffer only past the next barrier, which every thread
-      // reaches after reading this one.
-      __syncthreads();
-      {
-        static_assert(2 * kChunk == 256, "one dCs or dBs sum per thread");
-        const int which = tid / kChunk, j = tid - which * kChunk;
-        const int l = c * kChunk + j;
-        if (l < L) {
-          const int jp = j + j / kCT;
-          const float sum = ((wred[n & 1][0][which][jp] + wred[n & 1][1][which][jp]) + wred[n & 1][2][which][jp]) +
-                            wred[n & 1][3][which][jp];
-          float* dst = which == 0 ? p.dCp : p.dBp;
-          dst[(((int64_t)bk * p.nblk + blk) * N + n) * L + l] = sum;
+        int li, xi;
+        if (lane_step(cn, c, i, li, xi)) {
+          const float ddt = fmaf(uu[i], tq[i], sa[i]) * sig[i];
+          Io<S>::st(static_cast<S*>(p.ddt), cn.row + li, ddt);
+          p.du[cn.row + li] = fmaf(del[i], tq[i], cn.dsk * gg[i]);
+          rr.dbias += ddt;
+          rr.dD = fmaf(gg[i], uu[i], rr.dD);
         }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < kCT; ++i) {
-      int li, xi;
-      if (lane_step(c, i, li, xi)) {
-        const float ddt = fmaf(uu[i], tq[i], sa[i]) * sig[i];
-        Io<S>::st(static_cast<S*>(p.ddt), row + li, ddt);
-        p.du[row + li] = fmaf(del[i], tq[i], Dsk * gg[i]);
-        dbias += ddt;
-        dD = fmaf(gg[i], uu[i], dD);
-      }
+      next_block();
     }
   }
-  dbias = row_sum16(dbias);
-  dD = row_sum16(dD);
-  const int64_t pc = ((int64_t)b * p.nsp + sg) * 4 * D + c_idx;  // this channel's per-(batch, segment) slot
-  if (rval) p.dAp[pc * N + s] = dA_s[ch][s];
-  if (dval && s == 0) {
-    p.dbp[pc] = dbias;
-    p.dDp[pc] = dD;
+#pragma unroll 1
+  for (int cb = 0; cb < CPB; ++cb) {
+    const BwdChan<S> cn(p, bk, (blk0 + cb) * kBwdChans + ch);
+    const float dbias = row_sum16(rr.dbias), dD = row_sum16(rr.dD);
+    const int64_t pc = ((int64_t)b * p.nsp + sg) * 4 * D + cn.c_idx;  // this channel's per-(batch, segment) slot
+    if (cn.valid && s < N) p.dAp[pc * N + s] = rr.dA;
+    if (cn.valid && s == 0) {
+      p.dbp[pc] = dbias;
+      p.dDp[pc] = dD;
+    }
+    next_block();
   }
 }
 
@@ -427,7 +500,7 @@ __global__ __launch_bounds__(256) void bwd_seg_carry(const float* __restrict__ s
   }
 }
 
-// dBs / dCs: the channel blocks' partials summed in block order.
+// dBs / dCs: the workgroups' partials (one per channel-block group) summed in order.
 template <typename S>
 __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ dBp, const float* __restrict__ dCp,
                                                     S* __restrict__ dBs, S* __restrict__ dCs, int64_t BK,
@@ -514,28 +587,32 @@ __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_lo
 // chunked scan (one launch, or three for a segmented map), the dBs/dCs sums and
 // the dx merge.
 template <typename S>
-hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L) {
+hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L, int cpb) {
   hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(const_cast<void*>(p.xT)),
                                      (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
   if (e != hipSuccess) return e;
   e = launch_transpose<S>(static_cast<const S*>(a.dy), static_cast<S*>(const_cast<void*>(p.dyT)), (int)(a.B * a.D),
                           (int)a.H, (int)a.W, a.stream);
   if (e != hipSuccess) return e;
-  const unsigned blocks = (unsigned)(a.B * 4 * p.nblk * p.nsp);
+  const int ngrp = (p.nblk + cpb - 1) / cpb;
+  const unsigned blocks = (unsigned)(a.B * 4 * ngrp * p.nsp);
   if (p.nsp == 1) {
-    hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole>), dim3(blocks), dim3(256), 0, a.stream, p);
+    if (cpb == 2)
+      hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole, 2>), dim3(blocks), dim3(256), 0, a.stream, p);
+    else
+      hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole, 1>), dim3(blocks), dim3(256), 0, a.stream, p);
   } else {
-    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegMaps>), dim3(blocks), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegMaps, 1>), dim3(blocks), dim3(256), 0, a.stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t cols = a.B * 4 * a.D * a.N;
     hipLaunchKernelGGL(bwd_seg_carry, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, a.stream, p.segP, p.segF,
                        p.segR, cols, a.D * a.N, p.nsp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegGrads>), dim3(blocks), dim3(256), 0, a.stream, p);
+    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegGrads, 1>), dim3(blocks), dim3(256), 0, a.stream, p);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, static_cast<S*>(a.dBs),
-                     static_cast<S*>(a.dCs), a.B * 4, p.nblk, (int)a.N, (int)L);
+                     static_cast<S*>(a.dCs), a.B * 4, ngrp, (int)a.N, (int)L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tiles_w = (int)((a.W + kMergeTile - 1) / kMergeTile);
   const int tiles = (int)((a.H + kMergeTile - 1) / kMergeTile) * tiles_w;
@@ -548,13 +625,15 @@ hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L) {
 // six per compute unit is cut into segments of at least kMinSegChunks chunks.
 constexpr int64_t kBwdTargetBlocks = 1536;
 constexpr int64_t kMinSegChunks = 4;
+// Workgroups that fill the chip once at three per compute unit.
+constexpr int64_t kBwdPairBlocks = 768;
 
 struct BwdLayout {
-  int64_t L, nch, nblk, nsp, cps;
+  int64_t L, nch, nblk, nsp, cps, cpb;
   size_t du, hck, dBp, dCp, dAp, dbp, dDp, cdl, segP, segF, segR, xT, dyT, total;  // byte offsets
 };
 
-BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
+BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
   BwdLayout o;
   o.L = H * W;
   o.nch = (o.L + kChunk - 1) / kChunk;
@@ -565,6 +644,11 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
   if (nsp < 2) nsp = 1;
   o.cps = (o.nch + nsp - 1) / nsp;
   o.nsp = (o.nch + o.cps - 1) / o.cps;  // no empty segment
+  // two channel blocks per workgroup (sharing Bs/Cs staging and the dBs/dCs
+  // partial) where that still leaves a full round of workgroups; fp32 storage
+  // only (with bf16 the kernel spills more and ran slower than the partials save)
+  o.cpb = dtype == 0 && o.nsp == 1 && B * 4 * ((o.nblk + 1) / 2) >= kBwdPairBlocks ? 2 : 1;
+  const int64_t ngrp = (o.nblk + o.cpb - 1) / o.cpb;
   auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
   size_t off = 0;
   auto take = [&](size_t& at, int64_t floats) {
@@ -573,8 +657,8 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
   };
   take(o.du, B * 4 * D * o.L);
   take(o.hck, B * 4 * o.nch * D * N * 16);
-  take(o.dBp, B * 4 * o.nblk * N * o.L);
-  take(o.dCp, B * 4 * o.nblk * N * o.L);
+  take(o.dBp, B * 4 * ngrp * N * o.L);
+  take(o.dCp, B * 4 * ngrp * N * o.L);
   take(o.dAp, B * o.nsp * 4 * D * N);
   take(o.dbp, B * o.nsp * 4 * D);
   take(o.dDp, B * o.nsp * 4 * D);
@@ -591,16 +675,20 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
 
 }  // namespace
 
-size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
-  return bwd_layout(B, D, H, W, N).total;
+size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
+  return bwd_layout(B, D, H, W, N, dtype).total;
 }
 
-int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N) {
-  return bwd_layout(B, D, H, W, N).nsp;
+int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
+  return bwd_layout(B, D, H, W, N, dtype).nsp;
+}
+
+int64_t backward_blocks_per_workgroup(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
+  return bwd_layout(B, D, H, W, N, dtype).cpb;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
-  const BwdLayout o = bwd_layout(a.B, a.D, a.H, a.W, a.N);
+  const BwdLayout o = bwd_layout(a.B, a.D, a.H, a.W, a.N, a.dtype);
   char* base = static_cast<char*>(scratch);
   auto f = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   BwdParams p;
@@ -637,7 +725,7 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.cps = (int)o.cps;
   const int64_t merge_tiles = ((a.H + kMergeTile - 1) / kMergeTile) * ((a.W + kMergeTile - 1) / kMergeTile);
   if (a.B * 4 * o.nblk * o.nsp > INT32_MAX || a.B * a.D * merge_tiles > INT32_MAX) return hipErrorInvalidValue;
-  hipError_t e = a.dtype == 0 ? launch_io<float>(a, p, o.L) : launch_io<uint16_t>(a, p, o.L);
+  hipError_t e = a.dtype == 0 ? launch_io<float>(a, p, o.L, (int)o.cpb) : launch_io<uint16_t>(a, p, o.L, (int)o.cpb);
   if (e != hipSuccess) return e;
   const int C4 = (int)(4 * a.D);
   hipLaunchKernelGGL(bwd_params, dim3((unsigned)((C4 * a.N + 255) / 256)), dim3(256), 0, a.stream, a.A_log, p.dAp,

@@ -123,9 +123,11 @@ struct BackwardArgs {
   int dtype;
   hipStream_t stream;
 };
-size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N);
+size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype);
 // Segments each backward sequence is cut into (1: one workgroup walks the whole map).
-int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N);
+int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype);
+// Channel blocks of 16 channels each backward workgroup takes (1 or 2).
+int64_t backward_blocks_per_workgroup(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype);
 hipError_t launch_backward(const BackwardArgs& a, void* scratch);
 
 // x (B*D planes of H x W) -> xT (planes of W x H).

@@ -89,10 +89,14 @@ def test_backward_bf16_at_stage2_size_per_batch():
     _run(1, 384, 28, 28, 16, seed=2, a_log="s4d", dtype="bf16")
 
 
-def _segments(B, D, H, W, N):
+def _plan(B, D, H, W, N, dtype=0):
     import selective_scan_crossscan_amd as ss2d
-    desc = ss2d.describe(B, D, H, W, N)
-    return int(desc.split("backward_segments=")[1].split()[0])
+    desc = ss2d.describe(B, D, H, W, N, dtype)
+    return {k: int(desc.split(k + "=")[1].split()[0]) for k in ("backward_segments", "backward_blocks_per_workgroup")}
+
+
+def _segments(B, D, H, W, N):
+    return _plan(B, D, H, W, N)["backward_segments"]
 
 
 # (B, D, H, W, N, dtype): maps cut into segments -- two segments of four chunks,
@@ -152,3 +156,36 @@ def test_backward_full_size_sampled_channels(cfg, segmented):
         e = float(np.linalg.norm(g - r) / np.linalg.norm(r))
         print(k, f"{e:.2e}", flush=True)
         assert e <= TOL[k], (k, e)
+
+
+@pytest.mark.parametrize("cfg,cpb", [(1, 2), (2, 2), (3, 1)],
+                         ids=["vmamba_t_stage1", "vmamba_t_stage3", "vmamba_t_stage2_bf16"])
+def test_backward_full_size_batch_element(cfg, cpb):
+    # a full-size shape in the plan the benchmark times (one segment; fp32: two
+    # channel blocks per workgroup sharing one dBs/dCs partial); the oracle
+    # recomputes batch element 0 on its own (its dx, ddt, dBs and dCs depend only on
+    # its inputs)
+    shape = ss2d_inputs.CONFIGS[cfg]
+    B, D, H, W, N = shape.B, shape.D, shape.H, shape.W, shape.N
+    bf16 = shape.dtype == "bf16"
+    assert _plan(B, D, H, W, N, 1 if bf16 else 0) == {"backward_segments": 1, "backward_blocks_per_workgroup": cpb}
+    print(f"[backward full size, batch element 0] {shape}", flush=True)
+    inp = ss2d_inputs.generate(shape, seed=6)
+    rng = np.random.default_rng(7)
+    dy = rng.standard_normal((B, D, H, W)).astype(np.float32)
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    if bf16:
+        dy = ss2d_inputs.round_to_bf16(dy)
+    import selective_scan_crossscan_amd as ss2d
+    d = {k: (torch.from_numpy(v).to(tdt) if k in ("x", "dt", "Bs", "Cs") else torch.from_numpy(v)).cuda()
+         for k, v in inp.items()}
+    got = ss2d.backward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"],
+                        torch.from_numpy(dy).to(tdt).cuda())
+    torch.cuda.synchronize()
+    sub = {k: (v[:1] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in inp.items()}
+    ref = backward.ss2d_backward_f64(**sub, dy=dy[:1])
+    for k in ("dx", "ddt", "dBs", "dCs"):
+        g = got[k][:1].double().cpu().numpy()
+        e = float(np.linalg.norm(g - ref[k]) / np.linalg.norm(ref[k]))
+        print(k, f"{e:.2e}", flush=True)
+        assert e <= (1e-2 if bf16 else TOL[k]), (k, e)
