@@ -169,10 +169,11 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
  * Every output is fully overwritten (no accumulation into existing values) and
  * must not overlap an input or another output (SS2D_ERR_ALIAS).  All arithmetic
  * is fp32; bf16 outputs are rounded once.  N is 1..16.  All sums run in a fixed
- * order, so results are deterministic.  Takes a stream-ordered temporary of
- * about B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*N*L + 16*B*4*D*N*ceil(L/128) fp32
- * values (du, transposed copies of x and dy, per-channel-block partials of dBs
- * and dCs, the state entering every 8 steps) and runs six kernels on `stream`.
+ * order, so results are deterministic.  Takes a stream-ordered temporary of at
+ * most about B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*N*L + 16*B*4*D*N*ceil(L/128)
+ * fp32 values (du, transposed copies of x and dy, dBs and dCs partials, one per
+ * workgroup of one or two 16-channel blocks, the state entering every 8 steps)
+ * and runs six kernels on `stream`.
  * When B*4*ceil(D/16) is small, each sequence is cut into S segments of at least
  * 512 steps (S from ss2d_describe): two more kernels, and about
  * 16*B*4*D*ceil(L/128) + 3*B*4*S*D*N more temporary values.
