@@ -158,17 +158,18 @@ def test_backward_full_size_sampled_channels(cfg, segmented):
         assert e <= TOL[k], (k, e)
 
 
-@pytest.mark.parametrize("cfg,cpb", [(1, 2), (2, 2), (3, 1)],
-                         ids=["vmamba_t_stage1", "vmamba_t_stage3", "vmamba_t_stage2_bf16"])
-def test_backward_full_size_batch_element(cfg, cpb):
-    # a full-size shape in the plan the benchmark times (one segment; fp32: two
-    # channel blocks per workgroup sharing one dBs/dCs partial); the oracle
-    # recomputes batch element 0 on its own (its dx, ddt, dBs and dCs depend only on
-    # its inputs)
-    shape = ss2d_inputs.CONFIGS[cfg]
+@pytest.mark.parametrize("cfg,nsp,cpb", [(1, 1, 2), (2, 1, 2), (3, 1, 1), ("2x192x90x90", 16, 1)],
+                         ids=["vmamba_t_stage1", "vmamba_t_stage3", "vmamba_t_stage2_bf16", "segmented_2x192x90x90"])
+def test_backward_full_size_batch_element(cfg, nsp, cpb):
+    # a full-size shape in the plan the benchmark times (fp32: two channel blocks
+    # per workgroup sharing one dBs/dCs partial), and a 90 x 90 map cut into 16
+    # segments as the 256 x 256 map is; the oracle recomputes batch element 0 on its
+    # own (its dx, ddt, dBs and dCs depend only on its inputs)
+    shape = (ss2d_inputs.CONFIGS[cfg] if isinstance(cfg, int)
+             else ss2d_inputs.Shape("segmented", 2, 192, 90, 90, 16, "f32"))
     B, D, H, W, N = shape.B, shape.D, shape.H, shape.W, shape.N
     bf16 = shape.dtype == "bf16"
-    assert _plan(B, D, H, W, N, 1 if bf16 else 0) == {"backward_segments": 1, "backward_blocks_per_workgroup": cpb}
+    assert _plan(B, D, H, W, N, 1 if bf16 else 0) == {"backward_segments": nsp, "backward_blocks_per_workgroup": cpb}
     print(f"[backward full size, batch element 0] {shape}", flush=True)
     inp = ss2d_inputs.generate(shape, seed=6)
     rng = np.random.default_rng(7)
