@@ -82,6 +82,16 @@ def test_lanes_override_knob():
     assert "lanes_per_seq=32" in ss2d.describe(32, 192, 56, 56, 16)
 
 
+def test_describe_lanes_rule():
+    # 16 lanes beyond 512 steps when the 16-channel blocks give >= 768 workgroups
+    # and at most 64 steps are left after whole 256-step chunks
+    assert "lanes_per_seq=16" in ss2d.describe(64, 384, 28, 28, 16, ss2d.SS2D_BF16)  # 1536 blocks, 16 left
+    assert "lanes_per_seq=16" in ss2d.describe(32, 384, 40, 40, 16)   # 768 blocks, 64 left
+    assert "lanes_per_seq=32" in ss2d.describe(32, 192, 28, 28, 16)   # 384 blocks
+    assert "lanes_per_seq=32" in ss2d.describe(32, 768, 44, 44, 16)   # 144 left
+    assert "lanes_per_seq=16" in ss2d.describe(1, 8, 15, 20, 16)      # under 512 steps
+
+
 # fake, well-aligned, non-overlapping addresses (never dereferenced: validation fails first)
 BASE = 1 << 40
 X, DT, AL, BI, BS, CS, DS, Y = (BASE + i * (1 << 34) for i in range(8))
