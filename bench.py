@@ -110,6 +110,71 @@ PROFILE_COMMANDS = {
 }
 COPY_PROBE_MIB = 512
 
+# Shader counters of the step's kernels, two passes of at most eight SQ counters each
+# (one counter block per pass: the hardware takes no more).
+SQ_PASSES = {
+    "sq1": "SQ_WAVES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU SQ_INSTS_LDS "
+           "SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR",
+    "sq2": "SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_LDS "
+           "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INST_LEVEL_LDS",
+}
+SQ_COMMAND = ("rocprofv3 --pmc {counters} -f csv -d {d} -o {name} -- python bench.py --config {c}{x} --steps 3 "
+              "--warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks")
+
+
+def summarize_counters(folder: str, cfg: int, path: str = "scan") -> int:
+    """Write the SQ-counter summary of the step's dominant kernel into profiles/: the
+    instruction mix per state update and the VALU's share of the CUs' busy cycles."""
+    shape = ss2d_inputs.CONFIGS[cfg]
+    bwd = path == "backward"
+    kernel = "bwd_chunk_kernel" if bwd else KERNEL_PREFIX
+    workload = shape.name + ("_backward" if bwd else "")
+    extra = " --path backward" if bwd else ""
+    cmds = [SQ_COMMAND.format(counters=SQ_PASSES[n], d=folder, name=n, c=cfg, x=extra) for n in SQ_PASSES]
+    vals = {}  # counter -> summed over the kernel's template instances, averaged over dispatches
+    for name in SQ_PASSES:
+        inst = {}
+        for r in _counter_rows(folder, name):
+            if _is_kernel(r["Kernel_Name"], kernel):
+                inst.setdefault((r["Counter_Name"], r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        for (cn, _), v in inst.items():
+            vals[cn] = vals.get(cn, 0.0) + sum(v) / len(v)
+    upd = shape.updates
+    lines = [f"# {kernel} — {workload} — shader counters (rocprofv3)", "",
+             f"Workload: {shape}.  State updates per step: {upd:.4e}"
+             + (" ((b,k,d,n,l) terms; the backward runs more work per term)." if bwd else "."), "",
+             "Two counter runs, from the repository root:", "", "```", *cmds, "```", "",
+             "Per step, summed over the kernel's template instances and averaged over its dispatches:", "",
+             "| counter | value |", "|---|---|"]
+    for cn in sorted(vals):
+        lines.append(f"| {cn} | {vals[cn]:.4e} |")
+    valu = vals.get("SQ_INSTS_VALU", 0.0)
+    trans = vals.get("SQ_INSTS_VALU_TRANS_F32", 0.0)
+    busy = vals.get("SQ_BUSY_CU_CYCLES", 0.0)
+    lines += ["", "Derived:", "",
+              f"* VALU instructions per state update: {valu * 64 / upd:.2f} (SQ_INSTS_VALU x 64 lanes / updates), "
+              f"{trans * 64 / upd:.2f} of them transcendental (SQ_INSTS_VALU_TRANS_F32);",
+              f"* LDS instructions per update: {vals.get('SQ_INSTS_LDS', 0.0) * 64 / upd:.3f}; vector memory "
+              f"reads {vals.get('SQ_INSTS_VMEM_RD', 0.0) * 64 / upd:.3f}, writes "
+              f"{vals.get('SQ_INSTS_VMEM_WR', 0.0) * 64 / upd:.3f};"]
+    if busy > 0:
+        act = vals.get("SQ_ACTIVE_INST_VALU", 0.0)
+        lines.append(f"* VALU issue share of the SIMDs: SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES = {act / busy:.3f}. "
+                     "SQ_ACTIVE_INST_VALU counts 4-cycle units (one per wave64 VALU instruction, two per "
+                     f"transcendental: here {act / max(valu + trans, 1.0):.3f} of SQ_INSTS_VALU + "
+                     "SQ_INSTS_VALU_TRANS_F32), summed over the waves; SQ_BUSY_CU_CYCLES counts cycles summed "
+                     "over the CUs, so the ratio is the fraction of the four SIMDs' cycles spent issuing VALU "
+                     "instructions;")
+    if vals.get("SQ_LDS_IDX_ACTIVE", 0.0) > 0:
+        lines.append(f"* LDS bank-conflict cycles per LDS-active cycle: "
+                     f"{vals.get('SQ_LDS_BANK_CONFLICT', 0.0) / vals['SQ_LDS_IDX_ACTIVE']:.3f}.")
+    lines.append("")
+    out = os.path.join(PROFILES, f"{kernel}_{workload}_sq_counters.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out}: {valu * 64 / upd:.2f} VALU per update")
+    return 0
+
 
 def _is_kernel(name: str, kernel: str) -> bool:
     """Whether a rocprofv3 kernel name is `kernel` (a template instance or a plain function)."""
@@ -287,9 +352,13 @@ def main() -> int:
                     help="also time the channel-last LayerNorm epilogue on the forward's output")
     ap.add_argument("--summarize-kind", choices=["scan", "from_x", "backward", "epilogue"], default=None,
                     help="which kernel --summarize-profile summarises (default: --path)")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="write the SQ-counter summary (two rocprofv3 --pmc runs in DIR) into profiles/ and exit")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="turn the rocprofv3 output of PROFILE_COMMANDS in DIR into the summaries under profiles/")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.config, args.path)
     if args.summarize_profile:
         return summarize_profile(args.summarize_profile, args.config, args.summarize_kind or args.path)
 
