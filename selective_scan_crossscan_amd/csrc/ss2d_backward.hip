@@ -13,9 +13,11 @@
 //   dDs = sum_{b,l} g_l u_l,  dx = the merge of du.
 //
 // How it runs (the forward's decomposition, run twice).
-//   * A workgroup is 16 channels of one (batch, direction); a DPP row of 16 lanes
-//     owns one channel, lane s the 8 consecutive steps 8s.. of each 128-step
-//     chunk, and every lane loops over the states.
+//   * A workgroup takes one or two blocks of 16 channels of one (batch,
+//     direction); a DPP row of 16 lanes owns one channel, lane s the 8
+//     consecutive steps 8s.. of each 128-step chunk, and every lane loops over
+//     the states.  What belongs to state n of a channel (its A, carries, dA) is
+//     held by lane n of the row.
 //   * Pass A walks the chunks forwards: per state each lane folds its steps into
 //     one affine map h -> P h + Q, an inclusive prefix scan of the row's maps
 //     (DPP row_shr) gives every lane its entering state, which is stored; lane
@@ -26,13 +28,15 @@
 //     every lane the adjoint entering from its right, and the lane walks its
 //     steps backwards accumulating du and ddelta over the states in registers.
 //     Lane 0 carries q and a of the chunk's first step to the chunk before.
-//   * dBs/dCs partials are summed over the workgroup's 16 channels through LDS per
-//     state and chunk and written per channel block; a second kernel sums the
-//     blocks in a fixed order, so results are deterministic (no atomics).
+//   * dBs/dCs terms are summed per state and chunk over a wave's four channels
+//     with lane swaps, over the four waves through LDS, and over the workgroup's
+//     blocks in a per-thread LDS accumulator, then written as one partial per
+//     workgroup; a second kernel sums the partials in a fixed order, so results
+//     are deterministic (no atomics).
 //   * Column walks read transposed copies of x and dy (made first), so every
 //     operand load is contiguous along the steps.
-//   * du goes to a temporary; a gather kernel merges it into dx, and a small
-//     kernel sums the per-batch parameter gradients.
+//   * du goes to a temporary; a tiled kernel merges it into dx, and a small
+//     kernel sums the per-batch (and per-segment) parameter gradients.
 //   * Maps too long for one workgroup per channel block to fill the chip are cut
 //     into segments of consecutive chunks, one workgroup each, in three launches:
 //     pass A from a zero state, which also folds the segment's whole forward map
@@ -48,7 +52,7 @@
 namespace ss2d {
 namespace {
 
-constexpr int kBwdChans = 16;  // channels per workgroup
+constexpr int kBwdChans = 16;  // channels per channel block (a workgroup takes one or two)
 
 struct BwdParams {
   const void* x;  // x, dt, Bs, Cs, dy, xT, dyT and ddt in the storage type
@@ -73,8 +77,9 @@ struct BwdParams {
   float* segP;  // (B*4, nsp, D, N): the segment's decay, forward offset, adjoint offset; the carry kernel
   float* segF;  //   turns F into the state entering the segment and R into the adjoint entering it
   float* segR;
-  int D, H, W, L, N, nseg, nblk;
-  int nsp, cps;  // segments, chunks per segment
+  int D, H, W, L, N;
+  int nseg, nblk;  // 128-step chunks per sequence, 16-channel blocks
+  int nsp, cps;    // segments, chunks per segment
 };
 
 // Sum over the 16 lanes of a DPP row (four rotations).
