@@ -129,27 +129,33 @@ __device__ __forceinline__ float row_lane(float v, int j) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & ~15) + j) << 2, __float_as_int(v)));
 }
 
-// Inclusive scans over a row of maps x -> P x + Q.  Prefix: lane i composes lanes
-// 0..i, the lower lanes applied first.  Suffix: lane i composes lanes i..15, the
-// higher lanes applied first (the adjoint runs from the end).  A lane past the
-// row edge contributes the identity (1, 0).
-template <int SHIFT_BASE>
-__device__ __forceinline__ void scan_maps(float& P, float& Q) {
-#pragma unroll
-  for (int lv = 0; lv < 4; ++lv) {
-    float Pk, Qk;
-    switch (lv) {
-      case 0: Pk = dppf<SHIFT_BASE + 1>(1.f, P); Qk = dppf<SHIFT_BASE + 1>(0.f, Q); break;
-      case 1: Pk = dppf<SHIFT_BASE + 2>(1.f, P); Qk = dppf<SHIFT_BASE + 2>(0.f, Q); break;
-      case 2: Pk = dppf<SHIFT_BASE + 4>(1.f, P); Qk = dppf<SHIFT_BASE + 4>(0.f, Q); break;
-      default: Pk = dppf<SHIFT_BASE + 8>(1.f, P); Qk = dppf<SHIFT_BASE + 8>(0.f, Q); break;
-    }
-    Q = fmaf(P, Qk, Q);
-    P = P * Pk;
-  }
-}
 constexpr int kRowShr = 0x110;  // row_shr:n = 0x110 + n (from lane i - n)
 constexpr int kRowShl = 0x100;  // row_shl:n = 0x100 + n (from lane i + n)
+
+// Scans over a row of maps x -> P x + Q.  Prefix: scan_inclusive<16> (lane i
+// composes lanes 0..i, the lower lanes applied first) and incoming_state<16> (the
+// previous lane's map applied to a carry).  Suffix, for the adjoint, which runs
+// from the end: the same fused levels reading from the right (row_shl), lane i
+// composing lanes i..15, the higher lanes applied first; a lane past the row edge
+// is not written, which is the identity.  Wait states as in the prefix forms.
+__device__ __forceinline__ void scan_suffix16(float& P, float& Q) {
+  asm volatile("s_nop 1\n\t" SS2D_SCAN_STEP("row_shl:1 row_mask:0xf") SS2D_SCAN_NEXT("row_shl:2 row_mask:0xf")
+                   SS2D_SCAN_NEXT("row_shl:4 row_mask:0xf") SS2D_SCAN_NEXT("row_shl:8 row_mask:0xf")
+               : "+v"(P), "+v"(Q));
+}
+
+// The next lane's map applied to carry: P[i+1] * carry + Q[i+1]; lane 15 keeps
+// carry (its source is past the row edge).
+__device__ __forceinline__ float from_right16(float P, float Q, float carry) {
+  float h = carry;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %1, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_add_f32_dpp %0, %2, %0 row_shl:1 row_mask:0xf bank_mask:0xf"
+      : "+v"(h)
+      : "v"(P), "v"(Q));
+  return h;
+}
 
 // MODE kWhole: one workgroup walks every chunk, pass A then pass B.  kSegMaps: pass
 // A over one segment from a zero state, with the segment's maps as records.
@@ -329,17 +335,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
             float Pb = Pl, R = 0.f;
 #pragma unroll
             for (int i = kCT - 1; i >= 0; --i) R = a[i] * fmaf(sC[n][jp0 + i], gg[i], R);
-            scan_maps<kRowShl>(Pb, R);
+            scan_suffix16(Pb, R);
             const float Pb0 = row_lane(Pb, 0), R0 = row_lane(R, 0);
             if (s == n) {  // the chunks so far, then this one: (ap, aq) o (Pb0, R0)
               rr.aq = fmaf(rr.ap, R0, rr.aq);
               rr.ap *= Pb0;
             }
           }
-          scan_maps<kRowShr>(P, Q);
-          const float Pe = dppf<kRowShr + 1>(1.f, P), Qe = dppf<kRowShr + 1>(0.f, Q);
+          scan_inclusive<16>(P, Q);
           const float hc = row_lane(rr.h, n);
-          if (cn.valid) hck(cn, c, n) = fmaf(Pe, hc, Qe);
+          const float hin = incoming_state<16>(P, Q, hc, s);
+          if (cn.valid) hck(cn, c, n) = hin;
           const float hout = row_lane(fmaf(P, hc, Q), 15);  // the state leaving the chunk (lane 15's)
           if (s == n) rr.h = hout;
         }
@@ -401,9 +407,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
           cg[i] = sC[n][jp0 + i] * gg[i];
           Q = fmaf(an, Q, cg[i]);
         }
-        scan_maps<kRowShl>(P, Q);
-        const float Pe = dppf<kRowShl + 1>(1.f, P), Qe = dppf<kRowShl + 1>(0.f, Q);
-        float q = fmaf(Pe, qcar, Qe);  // adjoint at the step after this lane's last
+        scan_suffix16(P, Q);
+        float q = from_right16(P, Q, qcar);  // adjoint at the step after this lane's last
         float dA = 0.f, hg[kCT], qx[kCT];  // the dCs and dBs terms of each step
 #pragma unroll
         for (int i = kCT - 1; i >= 0; --i) {
