@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       const float pre = Io<S>::ld(cn.dtr, li) + cn.bias;
       del[i] = in ? softplus_f32(pre) : 0.f;
       uu[i] = in ? Io<S>::ld(cn.xs, xi) : 0.f;
-      sig[i] = in ? 1.f / (1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;
+      sig[i] = in ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;  // 1-ulp reciprocal
       xu[i] = del[i] * uu[i];
       gg[i] = in && with_g ? Io<S>::ld(cn.gs, xi) : 0.f;
     }
