@@ -190,3 +190,46 @@ def test_backward_full_size_batch_element(cfg, nsp, cpb):
         e = float(np.linalg.norm(g - ref[k]) / np.linalg.norm(ref[k]))
         print(k, f"{e:.2e}", flush=True)
         assert e <= (1e-2 if bf16 else TOL[k]), (k, e)
+
+
+def _check_batch_element_and_channels(shape, idx, seed):
+    """Full GPU backward of `shape`; the oracle on batch element 0 (dx, ddt, dBs, dCs)
+    and on the channels `idx` alone (dA_log, ddt_bias, dDs, summed over the batch)."""
+    B, D, H, W, N = shape.B, shape.D, shape.H, shape.W, shape.N
+    inp = ss2d_inputs.generate(shape, seed=seed, a_log="s4d")
+    rng = np.random.default_rng(seed + 1)
+    dy = rng.standard_normal((B, D, H, W)).astype(np.float32)
+    import selective_scan_crossscan_amd as ss2d
+    d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    got = ss2d.backward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"],
+                        torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    sub = {k: (v[:1] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in inp.items()}
+    ref = backward.ss2d_backward_f64(**sub, dy=dy[:1])
+    for k in ("dx", "ddt", "dBs", "dCs"):
+        g = got[k][:1].double().cpu().numpy()
+        e = float(np.linalg.norm(g - ref[k]) / np.linalg.norm(ref[k]))
+        print(k, f"{e:.2e}", flush=True)
+        assert e <= TOL[k], (k, e)
+    idx = np.asarray(idx)
+    per_k = lambda v: v.reshape(4, D, *v.shape[1:])[:, idx].reshape(4 * len(idx), *v.shape[1:])
+    sub = dict(x=inp["x"][:, idx], dt=inp["dt"][:, :, idx], A_log=per_k(inp["A_log"]),
+               dt_bias=per_k(inp["dt_bias"]), Bs=inp["Bs"], Cs=inp["Cs"], Ds=per_k(inp["Ds"]))
+    ref = backward.ss2d_backward_f64(**sub, dy=dy[:, idx])
+    cols = torch.from_numpy(np.concatenate([k * D + idx for k in range(4)]))
+    for k in ("dA_log", "ddt_bias", "dDs"):
+        g = got[k][cols].double().cpu().numpy()
+        e = float(np.linalg.norm(g - ref[k]) / np.linalg.norm(ref[k]))
+        print(k, f"{e:.2e}", flush=True)
+        assert e <= TOL[k], (k, e)
+
+
+@pytest.mark.parametrize("dims", [(32, 192, 16, 16, 5), (28, 200, 16, 16, 16)], ids=["N5", "D200_odd_blocks"])
+def test_backward_two_blocks_edge_cases(dims):
+    # two channel blocks per workgroup with N < 16, and with an odd number of
+    # 16-channel blocks (D = 200: the last workgroup's second block lies past D)
+    B, D, H, W, N = dims
+    assert _plan(B, D, H, W, N) == {"backward_segments": 1, "backward_blocks_per_workgroup": 2}
+    print(f"[backward two blocks] {dims}", flush=True)
+    _check_batch_element_and_channels(ss2d_inputs.Shape("t", B, D, H, W, N, "f32"), [0, 17, D - 1],
+                                      seed=sum(dims))
