@@ -150,6 +150,8 @@ EDGE = [
     (1, 8, 64, 33, 16, "bf16"),   # 2112 steps: a 64-step prefetched remainder
     (3, 9, 45, 48, 7, "f32"),     # D past the channel block, odd N, ragged remainder
     (1, 4, 8, 264, 16, "f32"),    # H = 8: a lane's steps span columns of the copy
+    # 16 lanes past 512 steps (768 channel blocks, at most 64 steps after whole chunks)
+    (32, 384, 24, 24, 16, "f32"),  # 576 steps: 2 chunks + a 64-step remainder
 ]
 
 
@@ -176,6 +178,8 @@ LANE_CASES = [
     (64, (1, 2, 64, 64, 16, "f32")),   # 64 x 16, 4 chunks
     (64, (1, 3, 40, 40, 16, "bf16")),
     (16, (1, 3, 24, 32, 16, "bf16")),
+    (16, (1, 3, 40, 40, 16, "f32")),   # 16 x 16, 6 chunks + a 64-step remainder (not prefetched)
+    (16, (1, 4, 28, 28, 16, "bf16")),  # 16 x 16, 3 chunks + a 16-step remainder
 ]
 
 
