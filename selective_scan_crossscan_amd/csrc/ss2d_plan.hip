@@ -12,14 +12,19 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   (void)N;
   Plan pl;
   const int64_t L = H * W;
-  // 16 lanes per sequence: short sequences, or longer ones when the 16-channel
-  // blocks still give at least three workgroups per CU and little is left after
-  // whole 256-step chunks (the 16-lane remainder is not prefetched).  Then each
-  // workgroup shares its Bs/Cs staging among twice the channels and the scan
-  // across lanes is one level shorter; measured 2-15% faster on 24x24 to 48x48
-  // maps, slower when either condition fails.
+  // 16 lanes per sequence: short sequences, or longer ones when little is left
+  // after whole 256-step chunks (the 16-lane remainder is not prefetched) and
+  // either the 16-channel blocks still give at least three workgroups per CU or a
+  // 32-lane plan would be cut into segments anyway.  Each workgroup then shares
+  // its Bs/Cs staging among twice the channels, the scan across lanes is one
+  // level shorter, and segmented maps can take twice the segments.  Measured
+  // 2-15% faster on 24x24 to 48x48 maps and up to 16% on segmented ones (never
+  // more than 0.3% slower there); slower on unsegmented maps with fewer blocks or
+  // longer remainders.
   const int64_t units16 = B * ((D + kWaves * 4 - 1) / (kWaves * 4));
-  int G = (L < 512 || (units16 >= 768 && L % 256 <= 64)) ? 16 : 32;
+  const int64_t units32 = B * ((D + kWaves * 2 - 1) / (kWaves * 2));
+  const bool seg32 = L % 4 == 0 && units32 < 512 && L / 512 >= 8;  // a 32-lane plan would be segmented
+  int G = (L < 512 || ((units16 >= 768 || seg32) && L % 256 <= 64)) ? 16 : 32;
   if (lanes_override == 16 || lanes_override == 32 || lanes_override == 64) G = lanes_override;
   // Steps per lane: 16, unless the remainder after whole 16-step chunks would fill
   // at least one 8-step chunk, which then runs at full speed instead of in the

@@ -90,6 +90,8 @@ def test_describe_lanes_rule():
     assert "lanes_per_seq=32" in ss2d.describe(32, 192, 28, 28, 16)   # 384 blocks
     assert "lanes_per_seq=32" in ss2d.describe(32, 768, 44, 44, 16)   # 144 left
     assert "lanes_per_seq=16" in ss2d.describe(1, 8, 15, 20, 16)      # under 512 steps
+    assert "lanes_per_seq=16" in ss2d.describe(2, 192, 256, 256, 16)  # segmented either way
+    assert "lanes_per_seq=32" in ss2d.describe(1, 11, 96, 100, 16)    # segmented, 128 steps left
 
 
 def test_describe_backward_plan():
