@@ -6,9 +6,10 @@ import this package.  The HIP library never calls it and shares no code with it.
 Three independent formulations of the scan, and the projections, live here:
   * `ss2d_f64`      -- plain C loops in double precision (ss2d_oracle.c),
                         OpenMP across (b, d) planes only.  The reference result.
-  * `ops_numpy`     -- the page's tensor-op formulation (stack / transpose / flip
-                        / cat for the scan, flip / transpose / sum for the merge)
-                        with a vectorised time loop, in float64.
+  * `ops_numpy`     -- each direction as a permutation of the pixel indices
+                        (the grid of pixel numbers read along that direction),
+                        the sequences gathered and the outputs scattered back
+                        through it, with a vectorised time loop, in float64.
   * `brute`         -- an O(L^2) unrolled sum with no recurrence at all, for tiny
                         maps, walking the map in the orders the direction table
                         describes.

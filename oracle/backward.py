@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ops_numpy import cross_merge, cross_scan
+from .ops_numpy import merge_sequences, scan_sequences
 
 
 def _sigmoid(v):
@@ -44,8 +44,8 @@ def ss2d_backward_f64(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy):
     B, D, H, W = x.shape
     L = H * W
     N = A_log.shape[1]
-    u = cross_scan(x)                 # (B, 4, D, L)
-    g = cross_scan(dy)                # the merge's adjoint
+    u = scan_sequences(x)             # (B, 4, D, L)
+    g = scan_sequences(dy)            # the merge's adjoint
     bias = dt_bias.reshape(4, D)
     pre = dt + bias[None, :, :, None]
     delta = np.logaddexp(0.0, pre)    # (B, 4, D, L)
@@ -76,7 +76,7 @@ def ss2d_backward_f64(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy):
     dA = (q * delta[:, :, :, None, :] * a * h_prev).sum(axis=(0, 4))     # (4, D, N)
     ddt = ddelta * _sigmoid(pre)
     return {
-        "dx": cross_merge(du, H, W).reshape(B, D, H, W),
+        "dx": merge_sequences(du, H, W).reshape(B, D, H, W),
         "ddt": ddt,
         "dA_log": (dA * A).reshape(4 * D, N),
         "ddt_bias": ddt.sum(axis=(0, 3)).reshape(4 * D),

@@ -117,7 +117,7 @@ MUTATIONS = {
     "B_and_C_grads_swapped": ('"dBs": dBs,\n        "dCs": dCs,', '"dBs": dCs,\n        "dCs": dBs,'),
     "state_term_sign": ("(A[None, :, :, :, None] * a * h_prev + Bk", "(-A[None, :, :, :, None] * a * h_prev + Bk"),
     "skip_missing_in_du": ("+ Ds.reshape(4, D)[None, :, :, None] * g", "+ 0.0 * g"),
-    "merge_adjoint_not_scanned": ("g = cross_scan(dy)", "g = np.repeat(dy.reshape(B, 1, D, L), 4, axis=1)"),
+    "merge_adjoint_not_scanned": ("g = scan_sequences(dy)", "g = np.repeat(dy.reshape(B, 1, D, L), 4, axis=1)"),
     "h_instead_of_h_prev": ("dA = (q * delta[:, :, :, None, :] * a * h_prev)", "dA = (q * delta[:, :, :, None, :] * a * h)"),
 }
 

@@ -221,8 +221,8 @@ def test_scan_and_merge_are_adjoint():
     for (H, W) in [(3, 5), (6, 2), (1, 4)]:
         x = rng.standard_normal((2, 3, H, W))
         o = rng.standard_normal((2, 4, 3, H * W))
-        lhs = np.sum(ops_numpy.cross_scan(x) * o)
-        rhs = np.sum(x.reshape(2, 3, H * W) * ops_numpy.cross_merge(o, H, W))
+        lhs = np.sum(ops_numpy.scan_sequences(x) * o)
+        rhs = np.sum(x.reshape(2, 3, H * W) * ops_numpy.merge_sequences(o, H, W))
         assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + 1)
 
 
@@ -245,7 +245,7 @@ def test_causality_one_hot():
 def test_page_cross_scan_assertions():
     g = json.load(open(os.path.join(GOLDEN, "page_cross_scan.json")))
     x = np.random.default_rng(81).standard_normal(g["input_shape"])
-    xs = ops_numpy.cross_scan(x)
+    xs = ops_numpy.scan_sequences(x)
     assert list(xs.shape) == g["output_shape"]
     for b in range(x.shape[0]):
         for c in (0, 17, 63):
@@ -258,7 +258,7 @@ def test_page_cross_scan_assertions():
     inp["Bs"][:] = 0.0
     inp["Ds"][:] = 1.0
     _, out_k = _run(inp, want_out_k=True)
-    np.testing.assert_array_equal(out_k[0], ops_numpy.cross_scan(inp["x"].astype(np.float64))[0])
+    np.testing.assert_array_equal(out_k[0], ops_numpy.scan_sequences(inp["x"].astype(np.float64))[0])
 
 
 # ---------------------------------------------------------------- P12, P13: limits

@@ -141,13 +141,13 @@ def test_generated_weights_follow_the_recipe():
 
 SRC = projection.__file__
 MUTATIONS = {
-    "split_order_swapped": ("dts, Bs, Cs = np.split(x_dbl, [R, R + N], axis=2)",
-                            "Bs, Cs, dts = np.split(x_dbl, [N, 2 * N], axis=2)"),
-    "B_and_C_swapped": ("dts, Bs, Cs = np.split(", "dts, Cs, Bs = np.split("),
-    "no_cross_scan": ("    xs = cross_scan(x)\n", "    xs = np.repeat(x.reshape(x.shape[0], 1, x.shape[1], -1), 4, axis=1)\n"),
-    "one_weight_for_all_directions": ('"bkdl,kcd->bkcl", xs, w,', '"bkdl,cd->bkcl", xs, w[0],'),
-    "dt_map_transposed": ('"bkrl,kdr->bkdl", dts, wdt,', '"bkrl,kdr->bkdl", dts[:, :, ::-1], wdt,'),
-    "dt_directions_crossed": ('"bkrl,kdr->bkdl", dts, wdt,', '"bkrl,kdr->bkdl", dts, wdt[[1, 0, 3, 2]],'),
+    "split_order_swapped": ("rows_dt, rows_B, rows_C = slice(0, R), slice(R, R + N), slice(R + N, C)",
+                            "rows_dt, rows_B, rows_C = slice(2 * N, C), slice(0, N), slice(N, 2 * N)"),
+    "B_and_C_swapped": ("Bs, Cs = proj[:, :, rows_B], proj[:, :, rows_C]", "Bs, Cs = proj[:, :, rows_C], proj[:, :, rows_B]"),
+    "no_cross_scan": ("    seq = scan_sequences(x)", "    seq = np.repeat(x.reshape(x.shape[0], 1, x.shape[1], -1), 4, axis=1)"),
+    "one_weight_for_all_directions": ("np.matmul(w[k], seq[:, k])", "np.matmul(w[0], seq[:, k])"),
+    "dt_map_transposed": ("np.matmul(wdt[k], low_rank[:, k])", "np.matmul(wdt[k], low_rank[:, k, ::-1])"),
+    "dt_directions_crossed": ("np.matmul(wdt[k], low_rank[:, k])", "np.matmul(wdt[k ^ 1], low_rank[:, k])"),
 }
 
 
