@@ -31,13 +31,24 @@ import ss2d_inputs  # noqa: E402
 # MI355X peaks (vendor figures: 256 CUs, 2.4 GHz, 8 TB/s HBM3E).
 CUS, CLOCK_HZ = 256, 2.4e9
 HBM_PEAK_GBPS = 8000.0
-# FP32 VALU issue: 128 lanes/clk/CU (157.3 TFLOP/s fp32 vector = 256 CU x 2.4 GHz x 128 FMA x 2).
-VALU_LANES_PER_CLK = 128
-# Transcendentals run at a quarter of that rate and take the same issue slots.
-TRANS_SLOTS = 4
-# Minimal work of one state update: exp2(delta*A) plus 4 VALU (delta*A, du*B, h fma, y fma).
-SLOTS_PER_UPDATE = 4 + TRANS_SLOTS
-PEAK_UPDATES_PER_S = CUS * CLOCK_HZ * VALU_LANES_PER_CLK / SLOTS_PER_UPDATE  # 9.83e12
+# FP32 VALU issue without packed FP32 (every source here is built without it): 64 lanes/clk/CU,
+# i.e. one wave64 instruction per 4 clocks on each of the 4 SIMDs.  The vendor's 157.3 TFLOP/s
+# fp32 vector figure (128 lanes/clk/CU) counts packed FP32 and is out of reach here.
+VALU_LANES_PER_CLK = 64
+# Transcendentals (v_exp_f32) issue at half that rate on CDNA4: 32 lanes/clk/CU.
+TRANS_LANES_PER_CLK = 32
+# Minimal work of one state update: one exp2(delta*A) plus 4 VALU (delta*A, du*B, h fma, y fma).
+CLK_PER_UPDATE_PER_CU = 1.0 / TRANS_LANES_PER_CLK + 4.0 / VALU_LANES_PER_CLK
+PEAK_UPDATES_PER_S = CUS * CLOCK_HZ / CLK_PER_UPDATE_PER_CU  # 6.55e12
+PEAK_UNIT = ("Gupdates/s; peak = 256 CU x 2.4 GHz / (1/32 + 4/64) clk per update: one exp2 at 32 "
+             "lanes/clk/CU plus 4 non-packed fp32 VALU at 64 lanes/clk/CU")
+# The backward, per (b,k,d,n,l) term: the forward's exp2 and 3 VALU recomputed (delta*A, du*B,
+# h fma), the adjoint's 2 (C*g, q fma) and 7 for the gradient terms (dCs, dBs, du, ddelta's
+# two products, dA's two): one exp2 plus 12 VALU.
+BWD_CLK_PER_TERM_PER_CU = 1.0 / TRANS_LANES_PER_CLK + 12.0 / VALU_LANES_PER_CLK
+BWD_PEAK_TERMS_PER_S = CUS * CLOCK_HZ / BWD_CLK_PER_TERM_PER_CU  # 2.81e12
+BWD_PEAK_UNIT = ("Gterms/s of (b,k,d,n,l); peak = 256 CU x 2.4 GHz / (1/32 + 12/64) clk per term: one exp2 "
+                 "plus 12 non-packed fp32 VALU (forward recompute 3, adjoint 2, gradient terms 7)")
 FP32_MFMA_PEAK = 157.3e12  # dense fp32 matrix FLOP/s
 
 _CSRC = os.path.join("selective_scan_crossscan_amd", "csrc")
@@ -61,6 +72,52 @@ def traffic_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
     return os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.md")
 
 
+def kernel_stats_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{workload}_kernel_stats.md")
+
+
+def bench_shape(args):
+    """The workload of this run: configuration args.config, with N = args.n if given."""
+    shape = ss2d_inputs.CONFIGS[args.config]
+    if args.n:
+        shape = ss2d_inputs.Shape(f"{shape.name}_n{args.n}", shape.B, shape.D, shape.H, shape.W, args.n, shape.dtype)
+    return shape
+
+
+def bench_workload(shape, path: str) -> str:
+    return shape.name + ("" if path == "scan" else "_" + path)
+
+
+def bench_flags(args, path: str) -> str:
+    """Command-line flags that select this workload and path (for the recorded commands)."""
+    return ((f" --n {args.n}" if args.n else "") + (" --epilogue" if path == "epilogue" else
+                                                   f" --path {path}" if path != "scan" else ""))
+
+
+def algorithmic_bytes(shape, K: int = 4) -> int:
+    """Bytes a forward over K directions must move: x and y once, dt, Bs, Cs, fp32 parameters."""
+    s = shape.elem_bytes
+    return s * shape.B * shape.L * ((2 + K) * shape.D + 2 * K * shape.N) + 4 * K * shape.D * (shape.N + 2)
+
+
+def _record(path: str):
+    try:
+        with open(path) as f:
+            m = re.search(r"```json\n(.*?)\n```", f.read(), re.S)
+        return json.loads(m.group(1)) if m else None
+    except (OSError, ValueError):
+        return None
+
+
+def measured_kernel_time(workload: str, kernel: str = KERNEL_PREFIX):
+    """The committed rocprofv3 kernel-trace record of `kernel` on `workload` (average launch
+    duration); None when absent or the kernel changed since."""
+    rec = _record(kernel_stats_file(workload, kernel))
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash(kernel) or rec.get("workload") != workload:
+        return None
+    return rec
+
+
 def kernel_source_hash(kernel: str = "ss2d_forward_kernel") -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -73,13 +130,7 @@ def measured_traffic(workload: str, kernel: str = KERNEL_PREFIX):
     """HBM bytes per launch of `kernel` from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters, scaled by the copy-kernel calibration; None when absent or the kernel
     changed since."""
-    try:
-        with open(traffic_file(workload, kernel)) as f:
-            text = f.read()
-        m = re.search(r"```json\n(.*?)\n```", text, re.S)
-        rec = json.loads(m.group(1)) if m else {}
-    except (OSError, ValueError):
-        return None
+    rec = _record(traffic_file(workload, kernel)) or {}
     if rec.get("kernel_source_hash") != kernel_source_hash(kernel) or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -122,15 +173,16 @@ SQ_COMMAND = ("rocprofv3 --pmc {counters} -f csv -d {d} -o {name} -- python benc
               "--warmup 1 --no-cpu-baseline --flush-steps 0 --no-peaks")
 
 
-def summarize_counters(folder: str, cfg: int, path: str = "scan") -> int:
+def summarize_counters(folder: str, args) -> int:
     """Write the SQ-counter summary of the step's dominant kernel into profiles/: the
     instruction mix per state update and the VALU's share of the CUs' busy cycles."""
-    shape = ss2d_inputs.CONFIGS[cfg]
+    path = args.path
+    shape = bench_shape(args)
     bwd = path == "backward"
     kernel = "bwd_chunk_kernel" if bwd else KERNEL_PREFIX
-    workload = shape.name + ("_backward" if bwd else "")
-    extra = " --path backward" if bwd else ""
-    cmds = [SQ_COMMAND.format(counters=SQ_PASSES[n], d=folder, name=n, c=cfg, x=extra) for n in SQ_PASSES]
+    workload = bench_workload(shape, path)
+    extra = bench_flags(args, path)
+    cmds = [SQ_COMMAND.format(counters=SQ_PASSES[n], d=folder, name=n, c=args.config, x=extra) for n in SQ_PASSES]
     vals = {}  # counter -> summed over the kernel's template instances, averaged over dispatches
     for name in SQ_PASSES:
         inst = {}
@@ -139,7 +191,7 @@ def summarize_counters(folder: str, cfg: int, path: str = "scan") -> int:
                 inst.setdefault((r["Counter_Name"], r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         for (cn, _), v in inst.items():
             vals[cn] = vals.get(cn, 0.0) + sum(v) / len(v)
-    upd = shape.updates
+    upd = (2 if path == "bidir" else 4) * shape.B * shape.D * shape.L * shape.N
     lines = [f"# {kernel} — {workload} — shader counters (rocprofv3)", "",
              f"Workload: {shape}.  State updates per step: {upd:.4e}"
              + (" ((b,k,d,n,l) terms; the backward runs more work per term)." if bwd else "."), "",
@@ -195,18 +247,21 @@ def _counter_rows(folder: str, prefix: str):
         return list(csv.DictReader(f))
 
 
-def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
+def summarize_profile(folder: str, args, path: str = "scan") -> int:
     """Write the rocprofv3 summaries of one workload into profiles/ (text only).
     path "scan": the scan kernel of the forward; "from_x": the projection kernel of
-    the forward from x and the projection weights."""
+    the forward from x and the projection weights; "backward": the chunked backward
+    kernel; "epilogue": the channel-last kernel; "bidir": the scan kernel of the
+    two-path scan."""
     import csv
-    shape = ss2d_inputs.CONFIGS[cfg]
+    shape = bench_shape(args)
+    cfg = args.config
     os.makedirs(PROFILES, exist_ok=True)
     from_x, bwd, epi = path == "from_x", path == "backward", path == "epilogue"
     kernel = ("project_kernel" if from_x else "bwd_chunk_kernel" if bwd else "channel_last_kernel" if epi
               else KERNEL_PREFIX)
-    workload = shape.name + ("" if path == "scan" else "_" + path)
-    extra = " --epilogue" if epi else f" --path {path}" if path != "scan" else ""
+    workload = bench_workload(shape, path)
+    extra = bench_flags(args, path)
     cmds = {k: v.format(d=folder, c=cfg, x=extra) for k, v in PROFILE_COMMANDS.items()}
 
     # Kernel-trace statistics, next to the bench line printed by the same run.
@@ -228,8 +283,12 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
         work = (f"Backward per launch: {shape.updates:.4e} (b,k,d,n,l) terms; algorithmic bytes {alg_bytes:.4e} "
                 "(x, dy, dt, Bs, Cs read once; dx, ddt, dBs, dCs written once).")
     else:
-        alg_bytes = shape.algorithmic_bytes
-        work = f"Updates per launch: {shape.updates:.4e}; algorithmic bytes per launch: {alg_bytes:.4e}."
+        K = 2 if path == "bidir" else 4
+        alg_bytes = algorithmic_bytes(shape, K)
+        upd = K * shape.B * shape.D * shape.L * shape.N
+        work = (f"Updates per step: {upd:.4e}; algorithmic bytes per step: {alg_bytes:.4e} (one launch of the "
+                "scan kernel per block of 16 states, or a carry pass and one launch per direction on segmented "
+                "maps).")
     lines = [f"# {kernel} — {workload} — rocprofv3 kernel trace", "", f"Workload: {shape}.  {work}", "",
              "Command (from the repository root):", "", "```", cmds["stats"], "```", "",
              "| kernel | calls | average µs | min µs | max µs | share |", "|---|---|---|---|---|---|"]
@@ -269,8 +328,13 @@ def summarize_profile(folder: str, cfg: int, path: str = "scan") -> int:
                   f"({alg_flops / (kern_avg * 1e-6) / FP32_MFMA_PEAK:.3f} of the fp32 MFMA peak) and "
                   f"{alg_bytes / (kern_avg * 1e-6) / 1e9:.0f} GB/s of algorithmic bytes "
                   f"({alg_bytes / (kern_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s).", ""]
-    lines += ["Bench line of this run:", "", "```json", bench_line, "```", ""]
-    with open(os.path.join(PROFILES, f"{kernel}_{workload}_kernel_stats.md"), "w") as f:
+    lines += ["Bench line of this run:", "", "```", bench_line, "```", ""]
+    krec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
+            "kernel_avg_us": kern_avg, "step_kernels_us": per_step,
+            "note": "kernel_avg_us: sum over the kernel's template instances of their average launch duration"}
+    lines += ["Record read by bench.py (valid only while the kernel sources hash to the value below):", "",
+              "```json", json.dumps(krec, indent=1), "```", ""]
+    with open(kernel_stats_file(workload, kernel), "w") as f:
         f.write("\n".join(lines))
 
     # HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), calibrated on a plain device copy
@@ -337,10 +401,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = VMamba-T stage-1")
-    ap.add_argument("--path", choices=["scan", "from_x", "backward"], default="scan",
+    ap.add_argument("--path", choices=["scan", "from_x", "backward", "bidir"], default="scan",
                     help="scan: the forward from x, dt, Bs, Cs (the headline); from_x: the forward from x and the "
                          "projection weights (projections on the matrix cores, then the scan); backward: the "
-                         "gradients of the forward given dy (fp32 workloads)")
+                         "gradients of the forward given dy; bidir: the two-path scan (forward and backward "
+                         "recursion over the L = H*W tokens, ss2d_bidir_forward)")
+    ap.add_argument("--n", type=int, default=0, help="state size N of the workload (0: its own, 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity")
     ap.add_argument("--lanes", type=int, default=0, help="force lanes per sequence chunk (16/32/64; 0 = auto)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -350,7 +416,7 @@ def main() -> int:
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device roofline probes")
     ap.add_argument("--epilogue", action="store_true",
                     help="also time the channel-last LayerNorm epilogue on the forward's output")
-    ap.add_argument("--summarize-kind", choices=["scan", "from_x", "backward", "epilogue"], default=None,
+    ap.add_argument("--summarize-kind", choices=["scan", "from_x", "backward", "epilogue", "bidir"], default=None,
                     help="which kernel --summarize-profile summarises (default: --path)")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
                     help="write the SQ-counter summary (two rocprofv3 --pmc runs in DIR) into profiles/ and exit")
@@ -358,9 +424,9 @@ def main() -> int:
                     help="turn the rocprofv3 output of PROFILE_COMMANDS in DIR into the summaries under profiles/")
     args = ap.parse_args()
     if args.summarize_counters:
-        return summarize_counters(args.summarize_counters, args.config, args.path)
+        return summarize_counters(args.summarize_counters, args)
     if args.summarize_profile:
-        return summarize_profile(args.summarize_profile, args.config, args.summarize_kind or args.path)
+        return summarize_profile(args.summarize_profile, args, args.summarize_kind or args.path)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -376,13 +442,18 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
-    if args.lanes:
-        ss2d.set_lanes_per_seq(args.lanes)
-    shape = ss2d_inputs.CONFIGS[args.config]
+    shape = bench_shape(args)
     print(f"[bench] workload {shape}", file=sys.stderr, flush=True)
     from_x = args.path == "from_x"
     bwd = args.path == "backward"
-    inp = ss2d_inputs.generate_projected(shape, seed=0) if from_x else ss2d_inputs.generate(shape, seed=0)
+    bidir = args.path == "bidir"
+    K = 2 if bidir else 4
+    if from_x:
+        inp = ss2d_inputs.generate_projected(shape, seed=0)
+    elif bidir:
+        inp = ss2d_inputs.bidir_random(shape.B, shape.D, shape.L, shape.N, seed=0, dtype=shape.dtype, a_log="s4d")
+    else:
+        inp = ss2d_inputs.generate(shape, seed=0)
     tdt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
     d = {}
     for k, v in inp.items():
@@ -405,10 +476,16 @@ def main() -> int:
         def step():
             ss2d.forward_from_x(d["x"], d["x_proj_weight"], d["dt_projs_weight"], d["A_log"], d["dt_bias"],
                                 d["Ds"], out=y, stream=stream)
+    elif bidir:
+        yb = y.view(shape.B, shape.D, shape.L)
+
+        def step():
+            ss2d.bidir_forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], out=yb,
+                               stream=stream)
     else:
         def step():
             ss2d.forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], out=y,
-                         stream=stream)
+                         stream=stream, lanes=args.lanes)
 
     for _ in range(args.warmup):
         step()
@@ -512,10 +589,13 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    plan = dict(kv.split("=") for kv in ss2d.describe(shape.B, shape.D, shape.H, shape.W, shape.N,
-                                                       1 if shape.dtype == "bf16" else 0).split())
+    code = 1 if shape.dtype == "bf16" else 0
+    plan_text = ss2d.describe(shape.B, shape.D, shape.H, shape.W, shape.N, code, lanes=args.lanes)
+    plan = dict(kv.split("=") for kv in plan_text.split())
     nseg = int(plan["segments"])
-    launches = int(plan["x_transposed"]) + (1 if nseg == 1 else 5 + int(plan["plane_transposed"]))
+    blocks = int(plan["state_blocks"])
+    per_block = 1 if nseg == 1 else 1 + K + int(plan["plane_transposed"])  # scan, or carry + one per direction
+    launches = int(plan["x_transposed"]) + blocks * per_block
     if bwd:
         # two transposes, the chunked scan (or, on a segmented map, its two passes
         # and the segment carry), the dBs/dCs sum, the dx merge, the parameter sums
@@ -523,15 +603,18 @@ def main() -> int:
     if from_x:
         launches += 1 + (1 - int(plan["x_transposed"]))  # the projection, and its own transpose of x
     ms_per_step = wall * 1e3 / args.steps
-    kernel_s = ev_ms * 1e-3 / args.steps  # one kernel launch per step, same stream
-    updates = shape.updates
+    step_s = ev_ms * 1e-3 / args.steps  # all launches of one step, same stream
+    updates = K * shape.B * shape.D * shape.L * shape.N
+    alg_bytes = algorithmic_bytes(shape, K)
     value = updates * args.steps / wall
-    achieved = updates / kernel_s
-    hbm_gbps = shape.algorithmic_bytes / kernel_s / 1e9
-    # the counters of the step's dominant kernel: the scan (forward, from_x) or the
-    # chunked backward kernel
-    traffic = (measured_traffic(shape.name + "_backward", "bwd_chunk_kernel") if bwd
-               else measured_traffic(shape.name))
+    achieved = updates / step_s
+    hbm_gbps = alg_bytes / step_s / 1e9
+    peak = BWD_PEAK_TERMS_PER_S if bwd else PEAK_UPDATES_PER_S
+    workload = bench_workload(shape, args.path)
+    # the committed rocprofv3 records of the step's dominant kernel (valid while its sources are unchanged)
+    dom = "bwd_chunk_kernel" if bwd else KERNEL_PREFIX
+    traffic = measured_traffic(workload, dom)
+    kstats = measured_kernel_time(workload, dom)
 
     result = {
         "metric": "SS2D state-updates/s (B·4·D·L·N) and achieved HBM GB/s % of peak",
@@ -546,16 +629,15 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic (seeded numpy PCG64, VMamba-shaped value recipe)",
-        "config": {"workload": shape.name + ("_from_x" if from_x else "_backward" if bwd else ""), "path": args.path, "B": shape.B, "D": shape.D, "H": shape.H, "W": shape.W,
-                   "N": shape.N, "K": 4, "L": shape.L, "io_dtype": shape.dtype,
-                   "plan": ss2d.describe(shape.B, shape.D, shape.H, shape.W, shape.N,
-                                         1 if shape.dtype == "bf16" else 0)},
+        "config": {"workload": workload, "path": args.path, "B": shape.B, "D": shape.D,
+                   "H": shape.H, "W": shape.W, "N": shape.N, "K": K, "L": shape.L, "io_dtype": shape.dtype,
+                   "plan": plan_text},
         "roofline": {
             "bound": "alu",
             "achieved": achieved / 1e9,
-            "peak": PEAK_UPDATES_PER_S / 1e9,
-            "unit": "Gupdates/s (1 exp2 + 4 fp32 VALU per update = 8 of 128 issue slots/clk/CU)",
-            "frac": achieved / PEAK_UPDATES_PER_S,
+            "peak": peak / 1e9,
+            "unit": BWD_PEAK_UNIT if bwd else PEAK_UNIT,
+            "frac": achieved / peak,
             "traffic": traffic,
             "timed": f"HIP events around each step on the launch stream: {launches} launch(es) " + (
                      "(transposes of x and dy, the chunked backward kernel, the dBs/dCs sum, the dx merge, the "
@@ -563,20 +645,22 @@ def main() -> int:
                      "(the scan kernel, after a transpose of x on maps of 2048+ pixels; traffic is the scan "
                      "kernel's own)"),
         },
-        "hbm": {"algorithmic_bytes": shape.algorithmic_bytes, "achieved_GBps": hbm_gbps,
+        "hbm": {"algorithmic_bytes": alg_bytes, "achieved_GBps": hbm_gbps,
                 "frac_of_peak": hbm_gbps / HBM_PEAK_GBPS, "peak_GBps": HBM_PEAK_GBPS},
-        "kernel_us": kernel_s * 1e6,
+        "kernel_us": step_s * 1e6,
     }
-    if bwd:
-        result["roofline"]["unit"] += ("; backward: each (b,k,d,n,l) counted once, though the backward recomputes "
-                                       "the forward twice and adds the adjoint walk")
+    if kstats is not None:
+        # the dominant kernel alone, from the committed rocprofv3 kernel trace of this workload
+        result["roofline"]["kernel_only"] = {
+            "kernel": dom, "us": kstats["kernel_avg_us"], "frac": updates / (kstats["kernel_avg_us"] * 1e-6) / peak,
+            "source": os.path.relpath(kernel_stats_file(workload, dom), ROOT)}
     if epi is not None:
         result["epilogue"] = epi
     if proj is not None:
         result["projection"] = proj
         result["roofline"]["unit"] += "; from_x: the whole path (transpose, projection, scan) per step"
     if flushed is not None:
-        flushed["frac_of_roofline_peak"] = updates / (flushed["median_us"] * 1e-6) / PEAK_UPDATES_PER_S
+        flushed["frac_of_roofline_peak"] = updates / (flushed["median_us"] * 1e-6) / peak
         result["flushed"] = flushed
     if peaks is not None:
         result["measured_peaks"] = {
@@ -584,11 +668,12 @@ def main() -> int:
             "fma_Gps": peaks["fma_per_s"] / 1e9, "hbm_read_GBps": peaks["hbm_read_Bps"] / 1e9,
             "hbm_copy_GBps": peaks["hbm_copy_Bps"] / 1e9, "lds_read_GBps": peaks["lds_read_Bps"] / 1e9,
             "compute_units": peaks["compute_units"]}
-        result["roofline_measured"] = {
-            "bound": "alu", "achieved": achieved / 1e9, "peak": peaks["update_mix_per_s"] / 1e9,
-            "unit": "Gupdates/s (peak = the probe kernel running the update's exp2 + 4 VALU mix on this device)",
-            "frac": achieved / peaks["update_mix_per_s"],
-            "hbm_frac_of_measured_copy": hbm_gbps * 1e9 / peaks["hbm_copy_Bps"]}
+        if not bwd:
+            result["roofline_measured"] = {
+                "bound": "alu", "achieved": achieved / 1e9, "peak": peaks["update_mix_per_s"] / 1e9,
+                "unit": "Gupdates/s (peak = the probe kernel running the update's exp2 + 4 VALU mix on this device)",
+                "frac": achieved / peaks["update_mix_per_s"],
+                "hbm_frac_of_measured_copy": hbm_gbps * 1e9 / peaks["hbm_copy_Bps"]}
 
     if not args.no_cpu_baseline:
         import oracle
@@ -596,37 +681,52 @@ def main() -> int:
         x64 = {k: np.ascontiguousarray(v, dtype=np.float64) for k, v in inp.items()}
         threads = oracle.threads()
         t0 = time.perf_counter()
+        nb_sample = shape.B
         if bwd:
             # a bounded sample: the float64 backward oracle on the first batch element
             from oracle import backward as obwd
             x1 = {k: (v[:1] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in x64.items()}
             refs = obwd.ss2d_backward_f64(**x1, dy=dy[:1].double().cpu().numpy())
-            cpu_s = (time.perf_counter() - t0) * shape.B
+            nb_sample = 1
             ref = refs["dx"]
         elif from_x:
             from oracle import projection
             ref = projection.ss2d_from_x_f64(**x64)
-            cpu_s = time.perf_counter() - t0
+        elif bidir:
+            # a bounded sample: the float64 numpy two-path oracle on the first batch elements
+            from oracle import bidir as obidir
+            nb_sample = min(shape.B, 4)
+            xs = {k: (v[:nb_sample] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in x64.items()}
+            ref = obidir.bidir_f64(**xs)
         else:
-            ref = oracle.ss2d_f64(**x64)
-            cpu_s = time.perf_counter() - t0
-        got = (grads["dx"][:1] if bwd else y).double().cpu().numpy()
+            # whole workload unless it is more than ~5e9 updates: then the first batch elements
+            nb_sample = shape.B if updates <= 5e9 else max(1, int(shape.B * 5e9 // updates))
+            xs = {k: (v[:nb_sample] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in x64.items()}
+            ref = oracle.ss2d_f64(**xs)
+        sample_s = time.perf_counter() - t0
+        cpu_s = sample_s * shape.B / nb_sample
+        got = (grads["dx"] if bwd else y).double().cpu().numpy()[:nb_sample]
+        if bidir:
+            got = got.reshape(ref.shape)
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         max_abs = float(np.max(np.abs(got - ref)))
+        scaled = f", scaled by {shape.B}/{nb_sample}" if nb_sample != shape.B else ""
         result["cpu_baseline"] = {
             "value": updates / cpu_s,
             "unit": "state-updates/s",
-            "cores": 1 if bwd else threads,
+            "cores": 1 if (bwd or bidir) else threads,
             "kind": "oracle",
-            "sample": (f"the float64 numpy backward oracle on 1 of {shape.B} batch elements, scaled by {shape.B}; "
-                       f"{cpu_s / shape.B:.2f} s for the sample on {cpu_model()}") if bwd else
-                      (f"the whole workload ({shape.B}x{shape.D} planes, {updates:.3e} updates), "
-                       + ("numpy float64 projections (einsum), then " if from_x else "")
-                       + f"fp64 C loops, OpenMP over (b,d) planes; {cpu_s:.2f} s on {cpu_model()}"),
+            "sample": (f"the float64 numpy backward oracle on 1 of {shape.B} batch elements{scaled}; "
+                       f"{sample_s:.2f} s for the sample on {cpu_model()}") if bwd else
+                      (f"the float64 numpy two-path oracle on {nb_sample} of {shape.B} batch elements{scaled}; "
+                       f"{sample_s:.2f} s for the sample on {cpu_model()}") if bidir else
+                      (f"{nb_sample} of {shape.B} batch elements ({shape.D} planes each){scaled}, "
+                       + ("numpy float64 projections, then " if from_x else "")
+                       + f"fp64 C loops, OpenMP over (b,d) planes; {sample_s:.2f} s on {cpu_model()}"),
         }
         result["parity"] = {"rel_l2": rel, "max_abs": max_abs, "max_abs_y": float(np.max(np.abs(ref))),
-                            "vs": "fp64 backward oracle, dx of batch element 0" if bwd else
-                            "fp64 oracle, whole output"}
+                            "vs": ("fp64 backward oracle, dx of batch element 0" if bwd else
+                                   f"fp64 oracle, batch elements 0..{nb_sample - 1}")}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -36,7 +36,7 @@ typedef enum {
   SS2D_ERR_NULL = -1,           /* a required pointer is NULL                     */
   SS2D_ERR_SHAPE = -2,          /* B, D, H or W < 1, H*W > 2^25 - 1, or a size    */
                                 /* overflows int64                                */
-  SS2D_ERR_UNSUPPORTED_N = -3,  /* N outside 1..16                                */
+  SS2D_ERR_UNSUPPORTED_N = -3,  /* N outside 1..256 (forward), 1..16 (others)     */
   SS2D_ERR_DTYPE = -4,          /* dtype is not an ss2d_dtype value               */
   SS2D_ERR_ALIAS = -5,          /* y overlaps one of the inputs                   */
   SS2D_ERR_ALIGN = -6,          /* a pointer is not aligned to its element size   */
@@ -60,27 +60,85 @@ typedef enum {
  *   Ds      [4*D]          fp32
  *   y       [B, D, H, W]   dtype  output; fully overwritten, never read.  Must not
  *                                 overlap any input.
- *   N       number of states, 1..16.
+ *   N       number of states, 1..256.  Up to 16 states run in one pass; larger N
+ *           runs in passes over blocks of 16 states whose outputs are summed in
+ *           fp32 in a fixed order (y is linear in each state's contribution).
+ *           d_state = 256 is the large-state setting of the [VSSD] page
+ *           ("项目概述：当视觉Transformer遇到状态空间模型", §4.1).
  *   stream  a hipStream_t (NULL = the default stream).
+ *
+ * Alignment: every pointer must be aligned to its element size (SS2D_ERR_ALIGN
+ * otherwise).  Bases aligned to 16 bytes (fp32) or 8 bytes (bf16) -- as torch
+ * allocations are -- with L % 4 == 0 take the vector/DMA path; other
+ * element-aligned bases take a slower scalar path with the same results.
  *
  * Behaviour: arguments are validated before any device work (codes above).  On
  * SS2D_OK the work has been enqueued asynchronously; execution faults surface at
  * the caller's next synchronisation.  Nothing is printed, thrown or aborted.
  * Each call takes a stream-ordered temporary of B*D*H*W fp32 values (2*B*D*H*W
- * for bf16) for the merge.  When a long map is cut into segments it also holds
- * 32 fp32 values per (batch, direction, channel, segment), a copy of x with H
- * and W swapped, and an fp32 B*D*H*W transposed merge plane (ss2d_describe shows
- * the plan and the exact size).  The temporary is allocated and freed on
- * `stream` from the device's default memory pool (whose release threshold the
- * library raises so freed blocks are reused).  A call then runs one kernel, or
- * seven for segmented maps (a transpose of x, a carry pass, one launch per
- * direction and a transpose of the merge plane before the last), all on
- * `stream`.  NaN and Inf propagate.  Thread-safe.
+ * for bf16) for the merge.  Maps of 2048 pixels or more add a copy of x with H
+ * and W swapped; when a long map is cut into segments it also holds 32 fp32
+ * values per (batch, direction, channel, segment) and an fp32 B*D*H*W
+ * transposed merge plane (ss2d_describe shows the plan and the exact size).
+ * The temporary is allocated and freed on `stream` from a memory pool the
+ * library creates per device (freed blocks stay reserved there for the next
+ * call until ss2d_trim_memory; the device's default pool is left untouched).
+ * A call then runs one kernel (two with the transpose of x), or seven for
+ * segmented maps (a transpose of x, a carry pass, one launch per direction and
+ * a transpose of the merge plane before the last), per block of 16 states, all
+ * on `stream`.  NaN and Inf propagate.  Thread-safe.
  */
 int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
                  const void* Bs, const void* Cs, const float* Ds, void* y,
                  int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
                  int dtype, void* stream);
+
+/*
+ * ss2d_forward_lanes -- ss2d_forward with the number of lanes that share one
+ * sequence chunk chosen by the caller: 16, 32 or 64 (0 = the automatic choice
+ * ss2d_forward makes).  The result is the same function up to rounding order;
+ * for tests and tuning.  Any other value is SS2D_ERR_SHAPE.  No state is kept
+ * between calls.
+ */
+int ss2d_forward_lanes(const void* x, const void* dt, const float* A_log, const float* dt_bias,
+                       const void* Bs, const void* Cs, const float* Ds, void* y,
+                       int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                       int dtype, int lanes_per_seq, void* stream);
+
+/*
+ * ss2d_bidir_forward -- enqueue the two-direction (bidirectional) selective scan
+ * of a sequence of L tokens on `stream`: a forward path that visits the tokens
+ * t = 0 .. L-1 and a backward path that visits t = L-1 .. 0, each with its own
+ * parameters, and their outputs summed per token.  [VSSD] page "项目概述：当视觉
+ * Transformer遇到状态空间模型", §2.2 (non-causal dual paths; the backward path
+ * changes the recursion direction instead of reversing the input: x is read
+ * backwards in place, never flipped).  The page fuses the two paths with a
+ * learned gate; that gate belongs to the model around this path, and here the
+ * paths are summed as the cross merge sums directions.
+ *   Path j = 0 (forward) or 1 (backward), channel c = j*D + d, step l of path j
+ *   visits token t_j(l) = l (j = 0) or L-1-l (j = 1):
+ *     delta_l = softplus(dt[b,j,d,l] + dt_bias[c]),  A = -exp(A_log[c, n]),
+ *     h_l = exp(delta_l*A) * h_{l-1} + delta_l * Bs[b,j,n,l] * x[b,d,t_j(l)],  h_{-1} = 0,
+ *     out_j[l] = sum_n Cs[b,j,n,l] * h_l + Ds[c] * x[b,d,t_j(l)];
+ *   y[b,d,t] = out_0[t] + out_1[L-1-t]  (fp32, rounded once to `dtype`).
+ * As for ss2d_forward, each path's dt, Bs and Cs are in the order that path
+ * visits the tokens (its scan order).  This is ss2d_forward restricted to its
+ * directions 0 and 2 on a 1 x L map.
+ *   x       [B, D, L]      dtype    (for instance a feature map flattened row by row)
+ *   dt      [B, 2, D, L]   dtype
+ *   A_log   [2*D, N]       fp32
+ *   dt_bias [2*D]          fp32
+ *   Bs, Cs  [B, 2, N, L]   dtype
+ *   Ds      [2*D]          fp32
+ *   y       [B, D, L]      dtype    fully overwritten; must not overlap an input
+ *   N       1..256
+ * Temporaries (none for fp32 output unless L is long enough to be cut into
+ * segments; one fp32 B*D*L plane for bf16), validation, alignment, error
+ * reporting and thread safety as for ss2d_forward with H = 1, W = L.
+ */
+int ss2d_bidir_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
+                       const void* Bs, const void* Cs, const float* Ds, void* y,
+                       int64_t B, int64_t D, int64_t L, int64_t N, int dtype, void* stream);
 
 /*
  * ss2d_project -- enqueue the per-direction input projections of SS2D on `stream`:
@@ -198,22 +256,25 @@ int ss2d_version(void);
 
 /*
  * ss2d_describe -- write a one-line, NUL-terminated description of how
- * ss2d_forward would run this shape (kernel variant, lanes per sequence,
- * channels per workgroup, grid size, LDS and temporary sizes), followed by the
- * number of segments ss2d_backward cuts each sequence into and the number of
- * 16-channel blocks each of its workgroups takes, into buf[0..len).
- * Host only; no device work.  Returns SS2D_OK or a validation code.
+ * ss2d_forward would run this shape with 16/8-byte aligned bases (kernel
+ * variant, lanes per sequence, channels per workgroup, grid size, LDS and
+ * temporary sizes, passes over state blocks), followed by the number of
+ * segments ss2d_backward cuts each sequence into and the number of 16-channel
+ * blocks each of its workgroups takes (0 for N > 16, which the backward does
+ * not take), into buf[0..len).  Host only; no device work.  Returns SS2D_OK or
+ * a validation code.  ss2d_describe_lanes: the same for ss2d_forward_lanes.
  */
 int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
                   char* buf, int64_t len);
+int ss2d_describe_lanes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
+                        int lanes_per_seq, char* buf, int64_t len);
 
 /*
- * ss2d_set_lanes_per_seq -- benchmarking knob: force the number of lanes that
- * share one sequence chunk (16, 32 or 64), or 0 to restore the automatic choice.
- * Process-wide; affects later ss2d_forward and ss2d_describe calls.  Returns
- * SS2D_OK, or SS2D_ERR_SHAPE for any other value.
+ * ss2d_trim_memory -- return the freed blocks the library's memory pools hold
+ * (one pool per device the library has run on) to the system.  Call only when no
+ * library work is in flight.  SS2D_OK or SS2D_ERR_HIP.
  */
-int ss2d_set_lanes_per_seq(int lanes);
+int ss2d_trim_memory(void);
 
 /*
  * ss2d_measure_peaks -- measure, on the current device, the rates the forward is

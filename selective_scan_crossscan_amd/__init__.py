@@ -12,7 +12,7 @@ import os
 import threading
 
 __all__ = ["forward", "ss2d_forward", "project", "ss2d_project", "forward_from_x", "ss2d_forward_from_x",
-           "channel_last", "ss2d_channel_last", "backward", "ss2d_backward", "measure_peaks", "describe", "set_lanes_per_seq", "status_string", "version", "library_path", "lib",
+           "channel_last", "ss2d_channel_last", "backward", "ss2d_backward", "measure_peaks", "describe", "bidir_forward", "ss2d_bidir_forward", "trim_memory", "status_string", "version", "library_path", "lib",
            "SS2D_F32", "SS2D_BF16", "SS2DError"]
 
 SS2D_F32 = 0
@@ -62,8 +62,14 @@ def lib():
             L.ss2d_version.restype = ctypes.c_int
             L.ss2d_describe.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.c_char_p, i64]
             L.ss2d_describe.restype = ctypes.c_int
-            L.ss2d_set_lanes_per_seq.argtypes = [ctypes.c_int]
-            L.ss2d_set_lanes_per_seq.restype = ctypes.c_int
+            L.ss2d_describe_lanes.argtypes = [i64] * 5 + [ctypes.c_int, ctypes.c_int, ctypes.c_char_p, i64]
+            L.ss2d_describe_lanes.restype = ctypes.c_int
+            L.ss2d_forward_lanes.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, ctypes.c_int, vp]
+            L.ss2d_forward_lanes.restype = ctypes.c_int
+            L.ss2d_bidir_forward.argtypes = [vp] * 8 + [i64] * 4 + [ctypes.c_int, vp]
+            L.ss2d_bidir_forward.restype = ctypes.c_int
+            L.ss2d_trim_memory.argtypes = []
+            L.ss2d_trim_memory.restype = ctypes.c_int
             L.ss2d_project.argtypes = [vp] * 6 + [i64] * 6 + [ctypes.c_int, vp]
             L.ss2d_project.restype = ctypes.c_int
             L.ss2d_forward_from_x.argtypes = [vp] * 7 + [i64] * 6 + [ctypes.c_int, vp]
@@ -87,24 +93,36 @@ def version() -> int:
     return lib().ss2d_version()
 
 
-def describe(B, D, H, W, N, dtype=SS2D_F32) -> str:
+def describe(B, D, H, W, N, dtype=SS2D_F32, lanes: int = 0) -> str:
+    """The launch plan of a forward of this shape (lanes: 0 = automatic, else 16/32/64)."""
     buf = ctypes.create_string_buffer(512)
-    rc = lib().ss2d_describe(B, D, H, W, N, int(dtype), buf, len(buf))
+    if lanes:
+        rc = lib().ss2d_describe_lanes(B, D, H, W, N, int(dtype), int(lanes), buf, len(buf))
+    else:
+        rc = lib().ss2d_describe(B, D, H, W, N, int(dtype), buf, len(buf))
     if rc != 0:
         raise SS2DError(rc, status_string(rc))
     return buf.value.decode()
 
 
-def set_lanes_per_seq(lanes: int) -> None:
-    """Benchmarking knob: force 16/32/64 lanes per sequence chunk (0 = automatic)."""
-    rc = lib().ss2d_set_lanes_per_seq(int(lanes))
+def trim_memory() -> None:
+    """Return the freed temporaries the library's memory pools hold to the system."""
+    rc = lib().ss2d_trim_memory()
     if rc != 0:
-        raise SS2DError(rc, status_string(rc))
+        _raise(rc)
 
 
-def ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, stream) -> int:
+def ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, stream, lanes: int = 0) -> int:
     """Raw C-ABI call with integer device addresses; returns the status code."""
+    if lanes:
+        return lib().ss2d_forward_lanes(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype),
+                                        int(lanes), stream)
     return lib().ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype), stream)
+
+
+def ss2d_bidir_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, L, N, dtype, stream) -> int:
+    """Raw C-ABI call with integer device addresses; returns the status code."""
+    return lib().ss2d_bidir_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, L, N, int(dtype), stream)
 
 
 def ss2d_project(x, x_proj_weight, dt_projs_weight, dt, Bs, Cs, B, D, H, W, N, R, dtype, stream) -> int:
@@ -301,13 +319,33 @@ def _raise(rc: int):
     raise SS2DError(rc, msg)
 
 
-def forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, out=None, stream=None):
+def forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, out=None, stream=None, lanes: int = 0):
     """SS2D forward on torch tensors.
 
     x (B,D,H,W), dt (B,4,D,H*W), Bs/Cs (B,4,N,H*W): float32 or bfloat16, all the same;
     A_log (4D,N), dt_bias (4D,), Ds (4D,): float32.  All contiguous, on one ROCm device.
+    N may be 1..256.  lanes: 0 (automatic) or 16/32/64 lanes per sequence chunk.
     Returns y (B,D,H,W) in x's dtype (written into `out` if given).
     """
+    return _forward_k(4, x, dt, A_log, dt_bias, Bs, Cs, Ds, out, stream, lanes)
+
+
+def bidir_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, out=None, stream=None):
+    """Two-direction (bidirectional) selective scan on torch tensors (ss2d_bidir_forward).
+
+    x (B,D,L), dt (B,2,D,L), Bs/Cs (B,2,N,L): float32 or bfloat16, all the same; path 1's
+    dt/Bs/Cs are in its own visiting order (token L-1-l at step l).  A_log (2D,N),
+    dt_bias (2D,), Ds (2D,): float32.  Returns y (B,D,L) in x's dtype.
+    """
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    B, D, L = x.shape
+    y = _forward_k(2, x.reshape(B, D, 1, L), dt, A_log, dt_bias, Bs, Cs, Ds,
+                   None if out is None else out.view(B, D, 1, L), stream, 0)
+    return y.view(B, D, L) if out is None else out
+
+
+def _forward_k(K, x, dt, A_log, dt_bias, Bs, Cs, Ds, out, stream, lanes):
     import torch
 
     if x.dim() != 4:
@@ -336,20 +374,23 @@ def forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, out=None, stream=None):
         if t.dtype != torch.float32:
             raise TypeError("A_log, dt_bias, Ds must be float32")
     L = H * W
-    if tuple(dt.shape) != (B, 4, D, L) or tuple(Bs.shape) != (B, 4, N, L) or tuple(Cs.shape) != (B, 4, N, L):
-        raise ValueError("dt must be (B,4,D,L) and Bs, Cs (B,4,N,L)")
-    if tuple(A_log.shape) != (4 * D, N) or tuple(dt_bias.shape) != (4 * D,) or tuple(Ds.shape) != (4 * D,):
-        raise ValueError("A_log must be (4D,N); dt_bias and Ds (4D,)")
+    if tuple(dt.shape) != (B, K, D, L) or tuple(Bs.shape) != (B, K, N, L) or tuple(Cs.shape) != (B, K, N, L):
+        raise ValueError(f"dt must be (B,{K},D,L) and Bs, Cs (B,{K},N,L)")
+    if tuple(A_log.shape) != (K * D, N) or tuple(dt_bias.shape) != (K * D,) or tuple(Ds.shape) != (K * D,):
+        raise ValueError(f"A_log must be ({K}D,N); dt_bias and Ds ({K}D,)")
     if out is None:
         out = torch.empty((B, D, H, W), dtype=x.dtype, device=x.device)
     elif tuple(out.shape) != (B, D, H, W) or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous (B,D,H,W) tensor of x's dtype")
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
+    ptrs = (x.data_ptr(), dt.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(), Bs.data_ptr(), Cs.data_ptr(),
+            Ds.data_ptr(), out.data_ptr())
     with torch.cuda.device(x.device):
-        rc = ss2d_forward(x.data_ptr(), dt.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(), Bs.data_ptr(),
-                          Cs.data_ptr(), Ds.data_ptr(), out.data_ptr(), B, D, H, W, N, code,
-                          stream.cuda_stream)
+        if K == 2:
+            rc = ss2d_bidir_forward(*ptrs, B, D, L, N, code, stream.cuda_stream)
+        else:
+            rc = ss2d_forward(*ptrs, B, D, H, W, N, code, stream.cuda_stream, lanes=lanes)
     if rc != 0:
         _raise(rc)
     return out

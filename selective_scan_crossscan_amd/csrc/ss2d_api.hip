@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;  // 1.0.0
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;  // 1.1.0
 thread_local char g_last_hip_error[256] = "";
 
 void remember(hipError_t e) {
@@ -27,8 +27,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
-// Shape checks shared by ss2d_forward and ss2d_describe.
-int check_shape(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
+// Shape checks shared by the entry points; max_n: the largest N the caller takes.
+int check_shape(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int64_t max_n = 16) {
   if (B < 1 || D < 1 || H < 1 || W < 1) return SS2D_ERR_SHAPE;
   int64_t L, t;
   // Every element count and byte count must fit comfortably: the kernels use
@@ -38,7 +38,7 @@ int check_shape(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype
   if (!mul_ok(H, W, &L) || L > INT32_MAX / 64) return SS2D_ERR_SHAPE;
   if (!mul_ok(B, 4, &t) || !mul_ok(t, D, &t) || !mul_ok(t, L, &t) || !mul_ok(t, 4, &t)) return SS2D_ERR_SHAPE;
   if (B > INT32_MAX / 4 || D > INT32_MAX / 4) return SS2D_ERR_SHAPE;
-  if (N < 1 || N > 16) return SS2D_ERR_UNSUPPORTED_N;
+  if (N < 1 || N > max_n) return SS2D_ERR_UNSUPPORTED_N;
   if (dtype != SS2D_F32 && dtype != SS2D_BF16) return SS2D_ERR_DTYPE;
   return SS2D_OK;
 }
@@ -50,11 +50,19 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 struct DeviceInfo {
   int device = -1;
+  hipMemPool_t pool = nullptr;  // the library's own memory pool on that device
 };
 
-// Per-device one-time setup (stream-ordered memory pool keeps freed scratch).
+// Per-device one-time setup, done with that device current: the library's own
+// stream-ordered memory pool for its temporaries (its release threshold keeps
+// freed blocks for the next call; other users of the device's default pool are
+// not affected).
+struct DevState {
+  bool ready = false;
+  hipMemPool_t pool = nullptr;
+};
 std::mutex g_dev_mutex;
-bool g_dev_ready[64];
+DevState g_dev[64];
 
 int device_info(DeviceInfo* out) {
   int dev = -1;
@@ -64,27 +72,43 @@ int device_info(DeviceInfo* out) {
     return SS2D_ERR_NO_DEVICE;
   }
   std::lock_guard<std::mutex> lk(g_dev_mutex);
-  if (!g_dev_ready[dev]) {
-    hipMemPool_t pool;
-    e = hipDeviceGetDefaultMemPool(&pool, dev);
+  DevState& st = g_dev[dev];
+  if (!st.ready) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
     if (e != hipSuccess) {
       remember(e);
       return SS2D_ERR_NO_DEVICE;
     }
-    // Keep freed scratch in the pool between calls instead of returning it to the system.
     uint64_t threshold = UINT64_MAX;
     e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
     if (e != hipSuccess) {
       remember(e);
+      (void)hipMemPoolDestroy(pool);
       return SS2D_ERR_NO_DEVICE;
     }
-    g_dev_ready[dev] = true;
+    st.pool = pool;
+    st.ready = true;
   }
   out->device = dev;
+  out->pool = st.pool;
   return SS2D_OK;
 }
 
-std::atomic<int> g_lanes_override{0};
+// Stream-ordered temporary from the library's pool (nothing for 0 bytes).
+hipError_t tmp_alloc(const DeviceInfo& di, void** p, size_t bytes, hipStream_t st) {
+  *p = nullptr;
+  if (bytes == 0) return hipSuccess;
+  return hipMallocFromPoolAsync(p, bytes, di.pool, st);
+}
+
+hipError_t tmp_free(void* p, hipStream_t st) { return p ? hipFreeAsync(p, st) : hipSuccess; }
 
 }  // namespace
 
@@ -92,9 +116,16 @@ extern "C" {
 
 int ss2d_version(void) { return kVersion; }
 
-int ss2d_set_lanes_per_seq(int lanes) {
-  if (lanes != 0 && lanes != 16 && lanes != 32 && lanes != 64) return SS2D_ERR_SHAPE;
-  g_lanes_override.store(lanes);
+int ss2d_trim_memory(void) {
+  std::lock_guard<std::mutex> lk(g_dev_mutex);
+  for (int d = 0; d < 64; ++d) {
+    if (!g_dev[d].ready) continue;
+    const hipError_t e = hipMemPoolTrimTo(g_dev[d].pool, 0);
+    if (e != hipSuccess) {
+      remember(e);
+      return SS2D_ERR_HIP;
+    }
+  }
   return SS2D_OK;
 }
 
@@ -127,7 +158,7 @@ const char* ss2d_status_string(int status) {
     case SS2D_OK: return "ok";
     case SS2D_ERR_NULL: return "a required pointer is NULL";
     case SS2D_ERR_SHAPE: return "invalid shape: B, D, H, W must be >= 1 and sizes must fit";
-    case SS2D_ERR_UNSUPPORTED_N: return "unsupported state size N (supported: 1..16)";
+    case SS2D_ERR_UNSUPPORTED_N: return "unsupported state size N (forward: 1..256; projection and backward: 1..16)";
     case SS2D_ERR_DTYPE: return "unknown dtype (0 = fp32, 1 = bf16)";
     case SS2D_ERR_ALIAS: return "output y overlaps an input";
     case SS2D_ERR_ALIGN: return "a pointer is not aligned to its element size";
@@ -137,34 +168,23 @@ const char* ss2d_status_string(int status) {
   }
 }
 
-int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, char* buf,
-                  int64_t len) {
-  if (!buf || len < 1) return SS2D_ERR_NULL;
-  const int rc = check_shape(B, D, H, W, N, dtype);
-  if (rc != SS2D_OK) return rc;
-  const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
-  snprintf(buf, (size_t)len,
-           "kernel=chunked_dpp_scan lanes_per_seq=%d steps_per_lane=%d waves=%d chans_per_block=%d "
-           "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu "
-           "backward_segments=%lld backward_blocks_per_workgroup=%lld",
-           pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.xtrans ? 1 : 0,
-           pl.transpose ? 1 : 0,
-           (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes,
-           (long long)ss2d::backward_segments(B, D, H, W, N, dtype),
-           (long long)ss2d::backward_blocks_per_workgroup(B, D, H, W, N, dtype));
-  return SS2D_OK;
-}
+}  // extern "C"
 
-int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
-                 const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W,
-                 int64_t N, int dtype, void* stream) {
+namespace {
+
+// Validation shared by the forward entry points (K directions).  *aligned: every
+// storage-type base allows the vector paths (16-byte fp32 / 8-byte bf16
+// alignment); element-aligned bases that are not take the scalar path.
+int check_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                  const void* Cs, const float* Ds, const void* y, int64_t B, int64_t D, int64_t H, int64_t W,
+                  int64_t N, int dtype, int K, bool* aligned) {
   if (!x || !dt || !A_log || !dt_bias || !Bs || !Cs || !Ds || !y) return SS2D_ERR_NULL;
-  int rc = check_shape(B, D, H, W, N, dtype);
+  const int rc = check_shape(B, D, H, W, N, dtype, ss2d::kMaxStates);
   if (rc != SS2D_OK) return rc;
   const int64_t L = H * W;
   const int64_t s = dtype == SS2D_BF16 ? 2 : 4;
-  const int64_t xbytes = B * D * L * s, dtbytes = B * 4 * D * L * s, bcbytes = B * 4 * N * L * s;
-  const int64_t pbytes = 4 * D * N * 4, vbytes = 4 * D * 4;
+  const int64_t xbytes = B * D * L * s, dtbytes = B * K * D * L * s, bcbytes = B * K * N * L * s;
+  const int64_t pbytes = K * D * N * 4, vbytes = K * D * 4;
   if (overlaps(y, xbytes, x, xbytes) || overlaps(y, xbytes, dt, dtbytes) || overlaps(y, xbytes, Bs, bcbytes) ||
       overlaps(y, xbytes, Cs, bcbytes) || overlaps(y, xbytes, A_log, pbytes) ||
       overlaps(y, xbytes, dt_bias, vbytes) || overlaps(y, xbytes, Ds, vbytes))
@@ -173,18 +193,25 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
   if (((uintptr_t)x & m) || ((uintptr_t)dt & m) || ((uintptr_t)Bs & m) || ((uintptr_t)Cs & m) ||
       ((uintptr_t)y & m) || ((uintptr_t)A_log & 3) || ((uintptr_t)dt_bias & 3) || ((uintptr_t)Ds & 3))
     return SS2D_ERR_ALIGN;
-  // Vector paths need 16-byte (fp32) or 8-byte (bf16) aligned bases; torch
-  // allocations are, and anything else takes the same path with the rows
-  // re-based, so insist on it here rather than silently slowing down.
   const uintptr_t vm = (uintptr_t)(4 * s - 1);
-  if (L % 4 == 0 && (((uintptr_t)x & vm) || ((uintptr_t)dt & vm) || ((uintptr_t)Bs & vm) ||
-                     ((uintptr_t)Cs & vm) || ((uintptr_t)y & vm)))
-    return SS2D_ERR_ALIGN;
+  *aligned = !(((uintptr_t)x & vm) || ((uintptr_t)dt & vm) || ((uintptr_t)Bs & vm) || ((uintptr_t)Cs & vm) ||
+               ((uintptr_t)y & vm));
+  return SS2D_OK;
+}
 
+bool lanes_ok(int lanes) { return lanes == 0 || lanes == 16 || lanes == 32 || lanes == 64; }
+
+int forward_impl(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                 const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                 int dtype, int K, int lanes, void* stream) {
+  bool aligned = false;
+  int rc = check_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, K, &aligned);
+  if (rc != SS2D_OK) return rc;
+  if (!lanes_ok(lanes)) return SS2D_ERR_SHAPE;
   DeviceInfo di;
   rc = device_info(&di);
   if (rc != SS2D_OK) return rc;
-  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
+  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, lanes, K, aligned);
 
   ss2d::LaunchArgs a;
   a.x = x;
@@ -203,17 +230,16 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   a.device = di.device;
+  a.K = K;
 
-  float* scratch = nullptr;
-  {
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), plan.scratch_bytes, a.stream);
-    if (e != hipSuccess) {
-      remember(e);
-      return SS2D_ERR_HIP;
-    }
+  void* scratch = nullptr;
+  hipError_t e = tmp_alloc(di, &scratch, plan.scratch_bytes, a.stream);
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
   }
-  hipError_t e = ss2d::launch_forward(a, plan, scratch);
-  hipError_t e2 = hipFreeAsync(scratch, a.stream);
+  e = ss2d::launch_forward(a, plan, static_cast<float*>(scratch));
+  const hipError_t e2 = tmp_free(scratch, a.stream);
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) {
     remember(e);
@@ -221,6 +247,59 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
   }
   return SS2D_OK;
 }
+
+int describe_impl(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes, char* buf,
+                  int64_t len) {
+  if (!buf || len < 1) return SS2D_ERR_NULL;
+  const int rc = check_shape(B, D, H, W, N, dtype, ss2d::kMaxStates);
+  if (rc != SS2D_OK) return rc;
+  if (!lanes_ok(lanes)) return SS2D_ERR_SHAPE;
+  const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, lanes);
+  const bool bwd = N <= 16;  // the backward takes N up to 16
+  snprintf(buf, (size_t)len,
+           "kernel=chunked_dpp_scan lanes_per_seq=%d steps_per_lane=%d waves=%d chans_per_block=%d "
+           "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu "
+           "state_blocks=%d backward_segments=%lld backward_blocks_per_workgroup=%lld",
+           pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.xtrans ? 1 : 0,
+           pl.transpose ? 1 : 0, (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes, pl.state_blocks,
+           bwd ? (long long)ss2d::backward_segments(B, D, H, W, N, dtype) : 0LL,
+           bwd ? (long long)ss2d::backward_blocks_per_workgroup(B, D, H, W, N, dtype) : 0LL);
+  return SS2D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, char* buf, int64_t len) {
+  return describe_impl(B, D, H, W, N, dtype, 0, buf, len);
+}
+
+int ss2d_describe_lanes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_per_seq,
+                        char* buf, int64_t len) {
+  return describe_impl(B, D, H, W, N, dtype, lanes_per_seq, buf, len);
+}
+
+int ss2d_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                 const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W,
+                 int64_t N, int dtype, void* stream) {
+  return forward_impl(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, 4, 0, stream);
+}
+
+int ss2d_forward_lanes(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                       const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W,
+                       int64_t N, int dtype, int lanes_per_seq, void* stream) {
+  return forward_impl(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, 4, lanes_per_seq, stream);
+}
+
+int ss2d_bidir_forward(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                       const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t L, int64_t N,
+                       int dtype, void* stream) {
+  // one row of L pixels: the row walk is the sequence order, its reverse the backward path
+  return forward_impl(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, 1, L, N, dtype, 2, 0, stream);
+}
+
+}  // extern "C"
 
 namespace {
 
@@ -236,6 +315,8 @@ int check_projection(int64_t D, int64_t N, int64_t R, const float* wx, const flo
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
+
+extern "C" {
 
 int ss2d_project(const void* x, const float* x_proj_weight, const float* dt_projs_weight, void* dt, void* Bs,
                  void* Cs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int64_t R, int dtype,
@@ -266,7 +347,7 @@ int ss2d_project(const void* x, const float* x_proj_weight, const float* dt_proj
   if (rc != SS2D_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* xT = nullptr;
-  hipError_t e = hipMallocAsync(&xT, (size_t)xbytes, st);
+  hipError_t e = tmp_alloc(di, &xT, (size_t)xbytes, st);
   if (e != hipSuccess) {
     remember(e);
     return SS2D_ERR_HIP;
@@ -276,7 +357,7 @@ int ss2d_project(const void* x, const float* x_proj_weight, const float* dt_proj
     ss2d::ProjectArgs pa{x, xT, x_proj_weight, dt_projs_weight, dt, Bs, Cs, B, D, H, W, N, R, dtype, st};
     e = ss2d::launch_project(pa);
   }
-  hipError_t e2 = hipFreeAsync(xT, st);
+  hipError_t e2 = tmp_free(xT, st);
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) {
     remember(e);
@@ -306,19 +387,21 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
   if (((uintptr_t)x & m) || ((uintptr_t)y & m) || ((uintptr_t)A_log & 3) || ((uintptr_t)dt_bias & 3) ||
       ((uintptr_t)Ds & 3))
     return SS2D_ERR_ALIGN;
+  // dt, Bs and Cs live in the library's (aligned) temporary; x and y may be
+  // element-aligned only, which takes the scalar paths
   const uintptr_t vm = (uintptr_t)(4 * s - 1);
-  if (L % 4 == 0 && (((uintptr_t)x & vm) || ((uintptr_t)y & vm))) return SS2D_ERR_ALIGN;
+  const bool aligned = !(((uintptr_t)x & vm) || ((uintptr_t)y & vm));
 
   DeviceInfo di;
   rc = device_info(&di);
   if (rc != SS2D_OK) return rc;
-  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, g_lanes_override.load());
+  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, 0, 4, aligned);
   // one temporary: x transposed, dt, Bs, Cs, then what the scan itself needs
   const size_t o_dt = up256((size_t)xbytes), o_b = o_dt + up256((size_t)dtbytes);
   const size_t o_c = o_b + up256((size_t)bcbytes), o_scan = o_c + up256((size_t)bcbytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* tmp = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&tmp), o_scan + plan.scratch_bytes, st);
+  hipError_t e = tmp_alloc(di, reinterpret_cast<void**>(&tmp), o_scan + plan.scratch_bytes, st);
   if (e != hipSuccess) {
     remember(e);
     return SS2D_ERR_HIP;
@@ -351,7 +434,7 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
     // the scan's column walks read the transposed copy made for the projections
     e = ss2d::launch_forward(a, plan, reinterpret_cast<float*>(tmp + o_scan), xT);
   }
-  hipError_t e2 = hipFreeAsync(tmp, st);
+  hipError_t e2 = tmp_free(tmp, st);
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) {
     remember(e);
@@ -423,7 +506,7 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
   if (rc != SS2D_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* tmp = nullptr;
-  hipError_t e = hipMallocAsync(&tmp, ss2d::backward_scratch_bytes(B, D, H, W, N, dtype), st);
+  hipError_t e = tmp_alloc(di, &tmp, ss2d::backward_scratch_bytes(B, D, H, W, N, dtype), st);
   if (e != hipSuccess) {
     remember(e);
     return SS2D_ERR_HIP;
@@ -431,7 +514,7 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
   ss2d::BackwardArgs a{x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs,
                        B, D, H, W, N, dtype, st};
   e = ss2d::launch_backward(a, tmp);
-  hipError_t e2 = hipFreeAsync(tmp, st);
+  hipError_t e2 = tmp_free(tmp, st);
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) {
     remember(e);

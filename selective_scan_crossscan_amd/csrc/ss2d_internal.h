@@ -21,6 +21,13 @@ struct LaunchArgs {
   int dtype;  // 0 = fp32, 1 = bf16
   hipStream_t stream;
   int device;  // current device of the calling thread
+  // Directions: 4 (the cross scan) or 2 (the row walk and its reverse; the
+  // per-direction tensors then hold two slots).
+  int K = 4;
+  // State block of one launch: N states from n0 of Nt (A_log rows and the Bs/Cs
+  // (batch, direction) slices have Nt states).  launch_forward sets these.
+  int64_t Nt = 0, n0 = 0;
+  bool skip = true, acc = false, final_out = true;
 };
 
 // How a shape is mapped onto the machine.
@@ -39,7 +46,14 @@ struct Plan {
   bool transpose;        // the column merge plane is transposed before the last direction (segmented plans)
   size_t xt_offset;      // byte offsets of those copies in the temporary
   size_t pct_offset;
+  bool vec;              // rows and bases aligned for 16-byte (fp32) / 8-byte (bf16) access: the DMA path
+  int state_blocks;      // launches over blocks of at most 16 states (N > 16)
 };
+
+// Largest N one kernel launch takes; larger N runs in blocks of this many states.
+constexpr int kStatesPerLaunch = 16;
+// Largest N the forward accepts.
+constexpr int kMaxStates = 256;
 
 // Device buffers of one forward, carved from the temporary.
 struct Scratch {
@@ -61,7 +75,11 @@ struct PeakRates {
 hipError_t measure_peaks(PeakRates* out, int64_t hbm_bytes, hipStream_t stream);
 
 // lanes_override: 0 = automatic, else 16, 32 or 64 lanes per sequence.
-Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override);
+// K: directions (4 or 2).  aligned: the caller's bases allow the vector paths
+// (with L % 4 == 0 they then take the DMA path).  no_copies: no transposed
+// copies in the temporary (the column walks and the final merge gather instead).
+Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override, int K = 4,
+               bool aligned = true, bool no_copies = false);
 
 // Enqueue the forward.  `scratch` holds plan.scratch_bytes.  `xT`, when not null,
 // already holds x with H and W swapped (B*D planes of W x H): column walks then

@@ -220,6 +220,16 @@ struct Params {
   const float* pcolT;
   int seg_chunks, nseg;
   int kdir;  // the one direction of a segment output launch
+  // Directions: K = 4 (the cross scan: 1, 3, 0, 2) or K = 2 (the row walk and its
+  // reverse only: 0, 2, whose per-direction tensors are slots 0 and 1).
+  int K;
+  // State block: this launch runs states n0 .. n0+N-1 of Nt (the row stride of
+  // A_log and the (batch, direction) stride of Bs/Cs are Nt).  skip: add Ds*u
+  // (the first block only); acc: the row plane already holds earlier blocks'
+  // sums, so direction 0 adds to it; final_out: the last block, which writes y
+  // in the storage type (earlier bf16 blocks leave their fp32 sums in the row
+  // plane).
+  int Nt, n0, skip, acc, final_out;
   // Wave priority rotation (0: off): the launch fits one round of prio_levels
   // resident workgroups on each of prio_ncu CUs.
   int prio_ncu, prio_levels;
@@ -719,10 +729,13 @@ __device__ __forceinline__ void store_outputs(float* plane, bool rev, bool add, 
 // visits pixel L-1-l0-i.  The row plane holds direction 0 (it is y itself for
 // fp32 output: each element is read, then written, by the same lane), the
 // column plane directions 1 + 3, so y = (y0 + y2) + (y1 + y3).
-// pct: the column plane transposed to row-major order, or null (then gathered).
+// pct: the column plane transposed to row-major order, or null (then gathered);
+// both null: no column directions (K = 2), y = y0 + y2.
+// yf: with bf16 storage, an fp32 destination instead of y (a state block before
+// the last leaves its sums in the row plane); null otherwise.
 template <typename S, int T, bool VEC, bool FULL>
-__device__ __forceinline__ void store_final(const float* prow, const float* pcol, const float* pct, S* y, int l0,
-                                            int L, int H, int W, const float (&yv)[T]) {
+__device__ __forceinline__ void store_final(const float* prow, const float* pcol, const float* pct, S* y, float* yf,
+                                            int l0, int L, int H, int W, const float (&yv)[T]) {
   if constexpr (VEC && (T % 4 == 0)) {
     // pixels s_lo .. s_lo+T-1; pixel s_lo+j holds yv[T-1-j].  A partial chunk's
     // pixels below 0 come in whole groups of 4 (see load_x) and are skipped.
@@ -747,7 +760,7 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
         v[j + 2] += o.z;
         v[j + 3] += o.w;
       }
-    } else {
+    } else if (pcol != nullptr) {
       const int s0 = FULL ? s_lo : max(s_lo, 0);
       int h = s0 / W;
       int w = s0 - h * W;
@@ -761,16 +774,32 @@ __device__ __forceinline__ void store_final(const float* prow, const float* pcol
         h += wrap ? 1 : 0;
       }
     }
+    if (sizeof(S) != 4 && yf != nullptr) {
 #pragma unroll
-    for (int j = 0; j < T; j += 4)
-      if (FULL || s_lo + j >= 0) Io<S>::st4(y, s_lo + j, make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]));
+      for (int j = 0; j < T; j += 4)
+        if (FULL || s_lo + j >= 0) Io<float>::st4(yf, s_lo + j, make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < T; j += 4)
+        if (FULL || s_lo + j >= 0) Io<S>::st4(y, s_lo + j, make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]));
+    }
   } else {
     int pix = L - 1 - (FULL ? l0 : min(l0, L - 1));
     int h = pix / W;
     int w = pix - h * W;
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      if (FULL || l0 + i < L) Io<S>::st(y, pix, (prow[pix] + yv[i]) + (pct != nullptr ? pct[pix] : pcol[w * H + h]));
+      if (FULL || l0 + i < L) {
+        float v = prow[pix] + yv[i];
+        if (pct != nullptr)
+          v += pct[pix];
+        else if (pcol != nullptr)
+          v += pcol[w * H + h];
+        if (sizeof(S) != 4 && yf != nullptr)
+          yf[pix] = v;
+        else
+          Io<S>::st(y, pix, v);
+      }
       --pix;
       --w;
       const bool wrap = w < 0;
@@ -843,7 +872,7 @@ struct Lane {
 template <typename S, int G, int T, int NG0, int TT, bool VEC, int kAreaBytes>
 __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, float* a2s, float* carry,
                                         const S* dtrow, const S* xrow, const S* Bbase, const S* Cbase, float* plane,
-                                        const float* pcol, const float* pct, S* yout, bool rev, bool col, bool add,
+                                        const float* pcol, const float* pct, S* yout, float* yf, bool rev, bool col, bool add,
                                         bool last, float bias,
                                         float dsk, int c0, int L, int H, int W, int N) {
   Lane ln;
@@ -878,7 +907,7 @@ __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid
   }
   if (ln.dvalid) {
     if (last)
-      store_final<S, TT, VEC, false>(plane, pcol, pct, yout, l0, L, H, W, yv);
+      store_final<S, TT, VEC, false>(plane, pcol, pct, yout, yf, l0, L, H, W, yv);
     else
       store_outputs<TT, VEC, false>(plane, rev, add, l0, L, yv);
   }
@@ -890,7 +919,7 @@ __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid
 template <typename S, int G, int TT, bool VEC>
 __device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, const char* bcs, const float (&uv)[TT],
                                                const float* a2s, float* carry, float* plane, const float* pcol,
-                                               const float* pct, S* yout, bool rev, bool add, bool last, float bias,
+                                               const float* pct, S* yout, float* yf, bool rev, bool add, bool last, float bias,
                                                float dsk, int c0,
                                                int L, int H, int W, int N) {
   constexpr int RB = G * TT * (int)sizeof(S);
@@ -908,7 +937,7 @@ __device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, 
   }
   if (ln.dvalid) {
     if (last)
-      store_final<S, TT, VEC, false>(plane, pcol, pct, yout, l0, L, H, W, yv);
+      store_final<S, TT, VEC, false>(plane, pcol, pct, yout, yf, l0, L, H, W, yv);
     else
       store_outputs<TT, VEC, false>(plane, rev, add, l0, L, yv);
   }
@@ -991,6 +1020,8 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   // One direction, specialised at compile time (walk order, merge mode).
   auto direction = [&](auto kc) {
     constexpr int k = decltype(kc)::value;
+    // slot of this direction in the per-direction tensors (K = 2: walks 0 and 2)
+    const int slot = p.K == 4 ? k : (k >> 1);
     // per-direction parameters of the block's channels; the state entering the
     // segment is the composition of the maps of the segments before it
     for (int i = ln.tid; i < CH * kMaxN; i += NTH) {
@@ -998,9 +1029,9 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       const int dg = ln.d0 + dd;
       float v = 0.f, h = 0.f;
       if (dg < D && n < N) {
-        v = -expf(p.A_log[(int64_t)(k * D + dg) * N + n]) * kLog2e;
+        v = -expf(p.A_log[(int64_t)(slot * D + dg) * p.Nt + p.n0 + n]) * kLog2e;
         if (MODE == kSegment) {
-          const float* cr = p.carries + ((int64_t)(ln.b * 4 + k) * D + dg) * p.nseg * (2 * kMaxN);
+          const float* cr = p.carries + ((int64_t)(ln.b * p.K + slot) * D + dg) * p.nseg * (2 * kMaxN);
           for (int j = 0; j < sidx; ++j) h = fmaf(cr[j * 2 * kMaxN + 2 * n], h, cr[j * 2 * kMaxN + 2 * n + 1]);
         }
       }
@@ -1010,16 +1041,21 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     }
     for (int i = ln.tid; i < CH; i += NTH) {
       const int dg = ln.d0 + i;
-      biass[i] = dg < D ? p.dt_bias[k * D + dg] : 0.f;
-      dss[i] = dg < D ? p.Ds[k * D + dg] : 0.f;
+      biass[i] = dg < D ? p.dt_bias[slot * D + dg] : 0.f;
+      dss[i] = (dg < D && p.skip) ? p.Ds[slot * D + dg] : 0.f;
     }
     __syncthreads();
 
-    constexpr bool rev = k >= 2, col = (k & 1) != 0, add = k == 3, last = k == 2;
+    constexpr bool rev = k >= 2, col = (k & 1) != 0, last = k == 2;
+    // direction 3 adds to the column plane direction 1 wrote; direction 0 adds to
+    // the row plane when earlier state blocks left their sums there
+    const bool add = k == 3 || (k == 0 && p.acc != 0);
     float* plane = (col ? p.pcol : p.prow) + plane_off;
-    const float* pcol = p.pcol + plane_off;
+    const float* pcol = p.K == 4 ? p.pcol + plane_off : nullptr;  // null: no column plane to merge
     S* yout = static_cast<S*>(p.y) + plane_off;
-    const S* dtdir = static_cast<const S*>(p.dt) + (int64_t)(ln.b * 4 + k) * D * L;
+    // bf16 state blocks before the last keep fp32 sums in the row plane
+    float* yf = (sizeof(S) != 4 && !p.final_out) ? p.prow + plane_off : nullptr;
+    const S* dtdir = static_cast<const S*>(p.dt) + (int64_t)(ln.b * p.K + slot) * D * L;
     const S* dtrow = dtdir + (int64_t)ln.dsafe * L;
     // column walks over the transposed copy of x read contiguous rows; direction 2
     // reads a transposed column plane when there is one
@@ -1027,8 +1063,9 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     const S* xsrc = xt ? static_cast<const S*>(p.xT) + plane_off : xrow;
     const bool xcol = col && !xt;
     const float* pct = p.pcolT != nullptr ? p.pcolT + plane_off : nullptr;
-    const S* Bbase = static_cast<const S*>(p.Bs) + (int64_t)(ln.b * 4 + k) * N * L;
-    const S* Cbase = static_cast<const S*>(p.Cs) + (int64_t)(ln.b * 4 + k) * N * L;
+    const int64_t bc_off = ((int64_t)(ln.b * p.K + slot) * p.Nt + p.n0) * L;
+    const S* Bbase = static_cast<const S*>(p.Bs) + bc_off;
+    const S* Cbase = static_cast<const S*>(p.Cs) + bc_off;
     const float bias = biass[ln.dl];
     const float dsk = dss[ln.dl];
     const int ngrp = (N + NG - 1) / NG;
@@ -1200,7 +1237,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         if (!PART && tailpf && c + 1 == cend) load_tail_x(xn);
         if (MODE != kCarry && ln.dvalid) {
           if (last)
-            store_final<S, T, VEC, !PART>(plane, pcol, pct, yout, c * GT + ln.seg * T, L, H, W, yv);
+            store_final<S, T, VEC, !PART>(plane, pcol, pct, yout, yf, c * GT + ln.seg * T, L, H, W, yv);
           else
             store_outputs<T, VEC, !PART>(plane, rev, add, c * GT + ln.seg * T, L, yv);
         }
@@ -1219,7 +1256,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
             float uv[TT];
 #pragma unroll
             for (int i = 0; i < TT; ++i) uv[i] = xn[i];
-            tail_chunk_lds<S, G, TT, VEC>(ln, dtb, bcs, uv, a2s, carry, plane, pcol, pct, yout, rev, add, last, bias,
+            tail_chunk_lds<S, G, TT, VEC>(ln, dtb, bcs, uv, a2s, carry, plane, pcol, pct, yout, yf, rev, add, last, bias,
                                           dsk, c0, L, H, W, N);
           }
         };
@@ -1236,7 +1273,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       // ---------------- rows not 16-byte aligned: every chunk staged through registers
       for (; c0 + GT <= L; c0 += GT)
         tail_chunk<S, G, T, NG, T, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
-                                        plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
+                                        plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
     }
 
     if constexpr (MODE == kCarry) {
@@ -1246,7 +1283,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         const int dd = i / kMaxN, n = i - dd * kMaxN;
         const int dg = ln.d0 + dd;
         if (dg < D && n < N) {
-          float* cr = p.carries + (((int64_t)(ln.b * 4 + k) * D + dg) * p.nseg + sidx) * (2 * kMaxN);
+          float* cr = p.carries + (((int64_t)(ln.b * p.K + slot) * D + dg) * p.nseg + sidx) * (2 * kMaxN);
           cr[2 * n] = aprod[i];
           cr[2 * n + 1] = carry[i];
         }
@@ -1262,22 +1299,22 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     // ---------------- remainder chunks (fewer steps per lane)
     while (L - c0 >= G * 8) {
       tail_chunk<S, G, T, NG, 8, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
-                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
+                                      plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 8;
     }
     if (L - c0 >= G * 4) {
       tail_chunk<S, G, T, NG, 4, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
-                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
+                                      plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 4;
     }
     if (L - c0 >= G * 2) {
       tail_chunk<S, G, T, NG, 2, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
-                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
+                                      plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 2;
     }
     while (c0 < L) {
       tail_chunk<S, G, T, NG, 1, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
-                                      plane, pcol, pct, yout, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
+                                      plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G;
     }
     __syncthreads();  // this direction's plane writes are complete and visible to the block
@@ -1292,8 +1329,10 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     }
   } else {
     // column pair, then row pair: the last direction finishes the merge
-    direction(std::integral_constant<int, 1>{});
-    direction(std::integral_constant<int, 3>{});
+    if (p.K == 4) {
+      direction(std::integral_constant<int, 1>{});
+      direction(std::integral_constant<int, 3>{});
+    }
     direction(std::integral_constant<int, 0>{});
     direction(std::integral_constant<int, 2>{});
   }
@@ -1466,6 +1505,12 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, const Scratch& 
   p.seg_chunks = plan.seg_chunks;
   p.nseg = plan.nseg;
   p.kdir = 0;
+  p.K = a.K;
+  p.Nt = (int)a.Nt;
+  p.n0 = (int)a.n0;
+  p.skip = a.skip ? 1 : 0;
+  p.acc = a.acc ? 1 : 0;
+  p.final_out = a.final_out ? 1 : 0;
   constexpr int NG = group_states<G, T>();
   const int64_t units = plan.blocks / plan.nseg;  // (batch, channel block) pairs
   // priority rotation for launches of at most one round (see the kernel)
@@ -1506,9 +1551,11 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, const Scratch& 
                        dim3(kWaves * 64), 0, a.stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int order[4] = {1, 3, 0, 2};
+    const int order4[4] = {1, 3, 0, 2}, order2[2] = {0, 2};
+    const int* order = a.K == 4 ? order4 : order2;
     rotation(reinterpret_cast<const void*>(&ss2d_forward_kernel<S, G, T, NG, VEC, kSegment>), units * plan.nseg);
-    for (int k : order) {
+    for (int i = 0; i < a.K; ++i) {
+      const int k = order[i];
       p.kdir = k;
       if (k == 2 && s.pcolT) {
         // the column plane is complete after direction 3; as pixels [W][H] -> [H][W]
@@ -1528,7 +1575,7 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, const Scratch& 
 
 template <typename S, int G, int T>
 hipError_t launch_gt(const LaunchArgs& a, const Plan& plan, const Scratch& s) {
-  if ((a.H * a.W) % 4 == 0) return launch_variant<S, G, T, true>(a, plan, s);
+  if (plan.vec) return launch_variant<S, G, T, true>(a, plan, s);
   return launch_variant<S, G, T, false>(a, plan, s);
 }
 

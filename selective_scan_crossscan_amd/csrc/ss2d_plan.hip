@@ -8,8 +8,8 @@ namespace ss2d {
 // more than the gathers it saves: measured on 14x14 and 28x28 maps).
 constexpr int64_t kTransposeXFrom = 2048;
 
-Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override) {
-  (void)N;
+Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int lanes_override, int K,
+               bool aligned, bool no_copies) {
   Plan pl;
   const int64_t L = H * W;
   // 16 lanes per sequence: short sequences, or longer ones when little is left
@@ -35,7 +35,9 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   pl.steps_per_lane = T;
   pl.waves = kWaves;
   pl.chans_per_block = kWaves * (64 / G);
-  const bool vec = L % 4 == 0;  // the ABI layer guarantees base alignment for this case
+  const bool vec = L % 4 == 0 && aligned;
+  pl.vec = vec;
+  pl.state_blocks = (int)((N + kStatesPerLaunch - 1) / kStatesPerLaunch);
   // Too few (batch, channel block) pairs to fill the machine and long sequences:
   // cut each sequence into segments of at least four full chunks, aiming at about
   // three workgroups per CU; a carry pass then supplies each segment's entering
@@ -55,16 +57,18 @@ Plan make_plan(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
   }
   pl.blocks = units * pl.nseg;
   pl.lds_bytes = dtype == 0 ? lds_bytes_s<float>(G, T, vec) : lds_bytes_s<uint16_t>(G, T, vec);
-  const size_t planes = (size_t)(dtype == 0 ? 1 : 2) * (size_t)(B * D * L) * sizeof(float);
+  // fp32 planes: the column plane (K = 4), and for bf16 output the row plane
+  const size_t nplanes = (size_t)(K == 4 ? 1 : 0) + (size_t)(dtype == 0 ? 0 : 1);
+  const size_t planes = nplanes * (size_t)(B * D * L) * sizeof(float);
   pl.carry_offset = planes;
-  pl.scratch_bytes = planes + (pl.nseg > 1 ? (size_t)(B * 4 * D) * pl.nseg * 2 * kMaxN * sizeof(float) : 0);
+  pl.scratch_bytes = planes + (pl.nseg > 1 ? (size_t)(B * K * D) * pl.nseg * 2 * kMaxN * sizeof(float) : 0);
   // A column walk reading x in place touches one cache line per step and lane;
   // those gathers load the same L1 path the Bs/Cs copies use.  So on large maps
   // x is transposed once first and the column walks read the copy.  Segmented
   // plans (large maps, whose working set outgrows L2) also transpose the column
   // merge plane before direction 2.
-  pl.xtrans = vec && (pl.nseg > 1 || L >= kTransposeXFrom);
-  pl.transpose = pl.nseg > 1;
+  pl.xtrans = K == 4 && !no_copies && vec && (pl.nseg > 1 || L >= kTransposeXFrom);
+  pl.transpose = K == 4 && !no_copies && pl.nseg > 1;
   pl.xt_offset = pl.pct_offset = 0;
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
   if (pl.xtrans) {
@@ -82,16 +86,37 @@ hipError_t launch_forward(const LaunchArgs& a, const Plan& plan, float* scratch,
   const int64_t plane = a.B * a.D * a.H * a.W;
   char* base = reinterpret_cast<char*>(scratch);
   Scratch s;
-  // planes: row-major (directions 0, 2), column-major (directions 1, 3)
-  s.prow = a.dtype == 0 ? static_cast<float*>(a.y) : scratch + plane;
-  s.pcol = scratch;
+  // planes: column-major (directions 1, 3; K = 4 only), then row-major
+  // (directions 0, 2): y itself for fp32 output
+  const int64_t ncol = a.K == 4 ? 1 : 0;
+  s.pcol = a.K == 4 ? scratch : nullptr;
+  s.prow = a.dtype == 0 ? static_cast<float*>(a.y) : scratch + ncol * plane;
   s.carries = reinterpret_cast<float*>(base + plan.carry_offset);
   s.xT = xT ? const_cast<void*>(xT) : plan.xtrans ? static_cast<void*>(base + plan.xt_offset) : nullptr;
   s.xT_given = xT != nullptr;
   s.pcolT = plan.transpose ? reinterpret_cast<float*>(base + plan.pct_offset) : nullptr;
   const bool t8 = plan.steps_per_lane == 8;
-  if (a.dtype == 0) return t8 ? launch_f32_t8(a, plan, s) : launch_f32_t16(a, plan, s);
-  return t8 ? launch_bf16_t8(a, plan, s) : launch_bf16_t16(a, plan, s);
+  // N > 16: one launch sequence per block of at most 16 states.  y is linear in
+  // each state's contribution, so the blocks' outputs add up: the first block
+  // adds the skip term Ds*u, later blocks add onto the row plane, and only the
+  // last rounds to the storage type.
+  for (int blk = 0; blk < plan.state_blocks; ++blk) {
+    LaunchArgs b = a;
+    b.Nt = a.N;
+    b.n0 = (int64_t)blk * kStatesPerLaunch;
+    b.N = a.N - b.n0 < kStatesPerLaunch ? a.N - b.n0 : kStatesPerLaunch;
+    b.skip = blk == 0;
+    b.acc = blk > 0;
+    b.final_out = blk + 1 == plan.state_blocks;
+    hipError_t e;
+    if (a.dtype == 0)
+      e = t8 ? launch_f32_t8(b, plan, s) : launch_f32_t16(b, plan, s);
+    else
+      e = t8 ? launch_bf16_t8(b, plan, s) : launch_bf16_t16(b, plan, s);
+    if (e != hipSuccess) return e;
+    s.xT_given = s.xT != nullptr;  // transposed once, by the first block's launches
+  }
+  return hipSuccess;
 }
 
 }  // namespace ss2d

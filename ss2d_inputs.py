@@ -96,25 +96,27 @@ def _f32(a: np.ndarray) -> np.ndarray:
 
 
 def generate(shape: Shape, seed: int = 0, a_log: str = "s4d", dt_min: float = 1e-3,
-             dt_max: float = 1e-1) -> dict:
+             dt_max: float = 1e-1, K: int = 4) -> dict:
     """Draw one input set.  Returns float32 numpy arrays (bf16-rounded where the
-    shape says so) keyed x, dt, A_log, dt_bias, Bs, Cs, Ds."""
+    shape says so) keyed x, dt, A_log, dt_bias, Bs, Cs, Ds.  K: direction slots
+    of the per-direction tensors (4 for the cross scan, 2 for the two-path scan,
+    whose x is then used as (B, D, H*W))."""
     B, D, H, W, N, L = shape.B, shape.D, shape.H, shape.W, shape.N, shape.L
     rng = np.random.default_rng(seed)
     x = _f32(rng.standard_normal((B, D, H, W)))
-    dt = _f32(rng.standard_normal((B, 4, D, L)) * 0.5)
-    U = rng.random(4 * D)
+    dt = _f32(rng.standard_normal((B, K, D, L)) * 0.5)
+    U = rng.random(K * D)
     dt0 = np.exp(U * (math.log(dt_max) - math.log(dt_min)) + math.log(dt_min))
     dt_bias = _f32(dt0 + np.log(-np.expm1(-dt0)))
-    Bs = _f32(rng.standard_normal((B, 4, N, L)))
-    Cs = _f32(rng.standard_normal((B, 4, N, L)))
+    Bs = _f32(rng.standard_normal((B, K, N, L)))
+    Cs = _f32(rng.standard_normal((B, K, N, L)))
     if a_log == "s4d":
-        A_log = _f32(np.broadcast_to(np.log(np.arange(1, N + 1, dtype=np.float64)), (4 * D, N)))
+        A_log = _f32(np.broadcast_to(np.log(np.arange(1, N + 1, dtype=np.float64)), (K * D, N)))
     elif a_log == "random":
-        A_log = _f32(rng.uniform(-1.0, 2.5, size=(4 * D, N)))
+        A_log = _f32(rng.uniform(-1.0, 2.5, size=(K * D, N)))
     else:
         raise ValueError(f"unknown a_log recipe {a_log!r}")
-    Ds = np.ones(4 * D, dtype=np.float32)
+    Ds = np.ones(K * D, dtype=np.float32)
     if shape.dtype == "bf16":
         x, dt, Bs, Cs = (round_to_bf16(v) for v in (x, dt, Bs, Cs))
     return dict(x=x, dt=dt, A_log=np.ascontiguousarray(A_log), dt_bias=dt_bias, Bs=Bs, Cs=Cs, Ds=Ds)
@@ -156,6 +158,13 @@ def generate_projected(shape: Shape, seed: int = 0, R: int | None = None, dt_min
 
 
 def tiny_random(B: int, D: int, H: int, W: int, N: int, seed: int, dtype: str = "f32",
-                a_log: str = "random") -> dict:
+                a_log: str = "random", K: int = 4) -> dict:
     """Small inputs of arbitrary shape (non-square maps, ragged lengths) for tests."""
-    return generate(Shape("tiny_random", B, D, H, W, N, dtype), seed=seed, a_log=a_log)
+    return generate(Shape("tiny_random", B, D, H, W, N, dtype), seed=seed, a_log=a_log, K=K)
+
+
+def bidir_random(B: int, D: int, L: int, N: int, seed: int, dtype: str = "f32", a_log: str = "random") -> dict:
+    """Inputs of the two-path scan: x (B, D, L) and two direction slots per tensor."""
+    inp = generate(Shape("bidir", B, D, 1, L, N, dtype), seed=seed, a_log=a_log, K=2)
+    inp["x"] = inp["x"].reshape(B, D, L)
+    return inp

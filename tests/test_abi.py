@@ -3,6 +3,10 @@
 The library must load without a GPU, export every function include/ss2d.h
 declares, and reject bad arguments with the documented codes before touching
 the device.  Fake (never dereferenced) addresses are used for pointers.
+
+Calls that pass validation reach the device query and report SS2D_ERR_NO_DEVICE
+(-7) here; on a machine with a GPU the same calls would launch kernels on the
+fake addresses, so every test that expects -7 is skipped where a device exists.
 """
 import ctypes
 import os
@@ -16,6 +20,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ss2d.h")
 
 
+def _no_device_here():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+NO_DEVICE = _no_device_here()
+# valid calls launch kernels where a GPU exists: only run them where none does
+needs_no_device = pytest.mark.skipif(not NO_DEVICE, reason="a valid call would launch kernels on fake addresses")
+
+
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -24,9 +41,10 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == sorted(["ss2d_forward", "ss2d_status_string", "ss2d_last_hip_error", "ss2d_version",
-                            "ss2d_describe", "ss2d_set_lanes_per_seq", "ss2d_measure_peaks", "ss2d_project",
-                            "ss2d_forward_from_x", "ss2d_channel_last", "ss2d_backward"])
+    assert names == sorted(["ss2d_forward", "ss2d_forward_lanes", "ss2d_bidir_forward", "ss2d_status_string",
+                            "ss2d_last_hip_error", "ss2d_version", "ss2d_describe", "ss2d_describe_lanes",
+                            "ss2d_trim_memory", "ss2d_measure_peaks", "ss2d_project", "ss2d_forward_from_x",
+                            "ss2d_channel_last", "ss2d_backward"])
     lib = ctypes.CDLL(ss2d.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -71,15 +89,23 @@ def test_describe_segmented_plan_includes_transposed_copies():
     assert int(fields["scratch_bytes"]) == pct + B * D * L * 4
 
 
-def test_lanes_override_knob():
-    lib = ss2d.lib()
-    assert lib.ss2d_set_lanes_per_seq(64) == 0
-    try:
-        assert "lanes_per_seq=64" in ss2d.describe(32, 192, 56, 56, 16)
-        assert lib.ss2d_set_lanes_per_seq(48) == -2
-    finally:
-        assert lib.ss2d_set_lanes_per_seq(0) == 0
-    assert "lanes_per_seq=32" in ss2d.describe(32, 192, 56, 56, 16)
+def test_lanes_per_call():
+    """The lanes choice is an argument of the call, not library state."""
+    assert "lanes_per_seq=64" in ss2d.describe(32, 192, 56, 56, 16, lanes=64)
+    assert "lanes_per_seq=16" in ss2d.describe(32, 192, 56, 56, 16, lanes=16)
+    assert "lanes_per_seq=32" in ss2d.describe(32, 192, 56, 56, 16)   # unaffected by the calls above
+    buf = ctypes.create_string_buffer(512)
+    assert ss2d.lib().ss2d_describe_lanes(2, 3, 4, 5, 16, 0, 48, buf, len(buf)) == -2
+
+
+def test_describe_state_blocks():
+    """N > 16 runs over blocks of 16 states; the backward figures are 0 (it takes N <= 16)."""
+    f = dict(kv.split("=") for kv in ss2d.describe(2, 32, 8, 8, 256).split())
+    assert f["state_blocks"] == "16" and f["backward_segments"] == "0"
+    f = dict(kv.split("=") for kv in ss2d.describe(2, 32, 8, 8, 17).split())
+    assert f["state_blocks"] == "2"
+    f = dict(kv.split("=") for kv in ss2d.describe(2, 32, 8, 8, 16).split())
+    assert f["state_blocks"] == "1" and f["backward_segments"] == "1"
 
 
 def test_describe_lanes_rule():
@@ -133,9 +159,15 @@ def test_bad_shape(shape):
     assert _call(B=B, D=D, H=H, W=W) == -2
 
 
-@pytest.mark.parametrize("N", [0, -1, 17, 256])
+@pytest.mark.parametrize("N", [0, -1, 257, 1 << 20])
 def test_unsupported_state_size(N):
     assert _call(N=N) == -3
+
+
+@needs_no_device
+@pytest.mark.parametrize("N", [1, 17, 64, 256])
+def test_large_state_sizes_are_accepted(N):
+    assert _call(N=N) == -7
 
 
 @pytest.mark.parametrize("dtype", [2, -1, 7])
@@ -151,24 +183,58 @@ def test_output_aliasing_an_input():
 
 
 def test_misaligned_pointers():
+    # only element misalignment is an error
     assert _call(x=X + 2) == -6
     assert _call(al=AL + 1) == -6
-    # bf16 elements need 2-byte alignment; with L % 4 == 0 rows need 8-byte alignment
     assert _call(x=X + 1, dtype=1) == -6
-    assert _call(x=X + 4, dtype=1, H=4, W=4) == -6
-    # fp32 with L % 4 == 0 needs 16-byte aligned bases
-    assert _call(dt=DT + 4, H=4, W=4) == -6
+    assert _call(y=Y + 3, H=4, W=4) == -6
 
 
-def _no_device_here():
-    try:
-        import torch
-        return torch.cuda.device_count() == 0
-    except Exception:
-        return True
+@needs_no_device
+def test_element_aligned_bases_are_accepted():
+    """Bases aligned to their element but not to 16 (fp32) / 8 (bf16) bytes take the
+    scalar path instead of being rejected."""
+    assert _call(x=X + 4, dtype=1, H=4, W=4) == -7
+    assert _call(dt=DT + 4, H=4, W=4) == -7
+    assert _call(y=Y + 8, bs=BS + 4, H=8, W=8) == -7
 
 
-@pytest.mark.skipif(not _no_device_here(), reason="only meaningful where no GPU is present")
+# the two-path scan: x (B, D, L), per-path tensors with two slots
+def _bidir(x=X, dt=DT, al=AL, bi=BI, bs=BS, cs=CS, ds=DS, y=Y, B=2, D=3, L=20, N=16, dtype=0):
+    return ss2d.ss2d_bidir_forward(x, dt, al, bi, bs, cs, ds, y, B, D, L, N, dtype, None)
+
+
+def test_bidir_validation():
+    for i in range(8):
+        args = [X, DT, AL, BI, BS, CS, DS, Y]
+        args[i] = None
+        assert _bidir(*args) == -1
+    assert _bidir(L=0) == -2
+    assert _bidir(N=0) == -3
+    assert _bidir(N=257) == -3
+    assert _bidir(dtype=3) == -4
+    assert _bidir(y=DT + 8) == -5
+    assert _bidir(x=X + 2) == -6
+
+
+@needs_no_device
+def test_bidir_valid_calls_without_device_report_no_device():
+    assert _bidir() == -7
+    assert _bidir(N=256, dtype=1) == -7
+    # the (B, 2, D, L) dt ends where a (B, 4, D, L) one would still run on: y may start there
+    assert _bidir(y=DT + 2 * 2 * 3 * 20 * 4) == -7
+
+
+@needs_no_device
+def test_forward_lanes_call():
+    L = ss2d.lib()
+    args = (X, DT, AL, BI, BS, CS, DS, Y, 2, 3, 4, 5, 16, 0)
+    assert L.ss2d_forward_lanes(*args, 48, None) == -2
+    for lanes in (0, 16, 32, 64):
+        assert L.ss2d_forward_lanes(*args, lanes, None) == -7
+
+
+@needs_no_device
 def test_measure_peaks_validates_before_touching_a_device():
     L = ss2d.lib()
     p = ss2d.Peaks()
@@ -178,6 +244,7 @@ def test_measure_peaks_validates_before_touching_a_device():
     assert L.ss2d_measure_peaks(ctypes.byref(p), 1 << 20, None) == -7  # no GPU in this container
 
 
+@needs_no_device
 def test_valid_call_without_device_reports_no_device():
     assert _call() == -7
 
@@ -214,7 +281,7 @@ def test_projection_rank_and_row_limits(call):
     assert call(R=-3) == -2
     assert call(N=16, R=33) == -2     # 2 * (33 + 32) = 130 rows > 128
     assert call(N=1, R=63) == -2      # 2 * (63 + 2) = 130
-    assert call(N=17) == -3
+    assert call(N=17) == -3           # the projections take N <= 16
     assert call(dtype=3) == -4
     assert call(B=0) == -2
 
@@ -228,13 +295,15 @@ def test_projection_aliasing_and_alignment():
     assert _fromx(y=X) == -5
     assert _fromx(y=WDT) == -5
     assert _fromx(wdt=WDT + 1) == -6
-    assert _fromx(x=X + 4, H=4, W=4) == -6   # fp32, L % 4 == 0: 16-byte bases
+    assert _fromx(x=X + 2) == -6
 
 
+@needs_no_device
 def test_projection_valid_calls_without_device_report_no_device():
     assert _proj() == -7
     assert _proj(N=16, R=32) == -7     # exactly 128 rows is allowed
     assert _fromx() == -7
+    assert _fromx(x=X + 4, H=4, W=4) == -7   # element-aligned x takes the scalar paths
 
 
 # the channel-last epilogue
@@ -259,10 +328,11 @@ def test_channel_last_validation():
     assert _epi(out=GM) == -5
     assert _epi(y=X + 1, dtype=1) == -6
     assert _epi(g=GM + 2) == -6
-    assert _epi(out=OUT + 4, D=8) == -7             # element alignment is enough (then: no device)
 
 
+@needs_no_device
 def test_channel_last_valid_calls_without_device_report_no_device():
+    assert _epi(out=OUT + 4, D=8) == -7             # element alignment is enough (then: no device)
     assert _epi() == -7
     assert _epi(g=None, b=None) == -7               # scale and shift are optional
     assert _epi(norm=0, eps=-1.0) == -7             # eps is unused without the normalisation
@@ -287,7 +357,6 @@ def test_backward_validation():
     p = [X, DT, AL, BI, BS, CS, DS] + GRAD
     p[0] = X + 1                          # bf16 tensors need 2-byte alignment
     assert _bwd(p, dtype=1) == -6
-    assert _bwd(dtype=1) == -7            # bf16 is accepted (then: no device)
     assert _bwd(N=17) == -3
     assert _bwd(W=0) == -2
     p = [X, DT, AL, BI, BS, CS, DS] + GRAD
@@ -299,4 +368,9 @@ def test_backward_validation():
     p = [X, DT, AL, BI, BS, CS, DS] + GRAD
     p[10] = GRAD[3] + 2                   # dA_log misaligned
     assert _bwd(p) == -6
-    assert _bwd() == -7                   # valid, no device here
+
+
+@needs_no_device
+def test_backward_valid_calls_without_device_report_no_device():
+    assert _bwd(dtype=1) == -7            # bf16 is accepted
+    assert _bwd() == -7

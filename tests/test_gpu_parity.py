@@ -35,9 +35,10 @@ def _dev(inp, dtype):
     return out
 
 
-def gpu_forward(inp, dtype, stream=None):
+def gpu_forward(inp, dtype, stream=None, lanes=0):
     d = _dev(inp, dtype)
-    y = _lib().forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], stream=stream)
+    y = _lib().forward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], stream=stream,
+                       lanes=lanes)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64)
 
@@ -187,19 +188,16 @@ LANE_CASES = [
 def test_lane_variants(lanes, shape):
     B, D, H, W, N, dtype = shape
     lib = _lib()
-    print(f"[case] lanes={lanes} {shape} plan: {lib.describe(B, D, H, W, N, 1 if dtype == 'bf16' else 0)}", flush=True)
+    code = 1 if dtype == "bf16" else 0
+    print(f"[case] lanes={lanes} {shape} automatic plan: {lib.describe(B, D, H, W, N, code)}", flush=True)
+    print(f"[case] forced plan: {lib.describe(B, D, H, W, N, code, lanes=lanes)}", flush=True)
     inp = ss2d_inputs.tiny_random(B, D, H, W, N, seed=lanes + H, dtype=dtype)
-    lib.set_lanes_per_seq(lanes)
-    try:
-        print(f"[case] forced plan: {lib.describe(B, D, H, W, N, 1 if dtype == 'bf16' else 0)}", flush=True)
-        y = gpu_forward(inp, dtype)
-        ref = oracle.ss2d_inputs_f64(inp)
-        check(y, ref, dtype, f"lanes={lanes} {shape}")
-        inp["Ds"][:] = 0.0
-        y = gpu_forward(inp, dtype)
-        check_scan_only(y, oracle.ss2d_inputs_f64(inp), dtype, f"lanes={lanes} {shape}")
-    finally:
-        lib.set_lanes_per_seq(0)
+    y = gpu_forward(inp, dtype, lanes=lanes)
+    ref = oracle.ss2d_inputs_f64(inp)
+    check(y, ref, dtype, f"lanes={lanes} {shape}")
+    inp["Ds"][:] = 0.0
+    y = gpu_forward(inp, dtype, lanes=lanes)
+    check_scan_only(y, oracle.ss2d_inputs_f64(inp), dtype, f"lanes={lanes} {shape}")
 
 
 @pytest.mark.parametrize("bias", [-14.0, -6.0, 0.0, 3.0, 12.0, 25.0])

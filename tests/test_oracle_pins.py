@@ -93,9 +93,11 @@ def _lti_inputs(B, D, H, W, N, seed):
     return x, dt, A_log, bias, Bs, Cs, Ds, Bv, Cv
 
 
-def test_lti_constant_input_geometric_sum():
-    """u constant too: h_l[n] = delta B_n u (1 - a_n^(l+1)) / (1 - a_n)."""
-    B, D, H, W, N = 2, 2, 3, 5, 4
+@pytest.mark.parametrize("N", [4, 64])
+def test_lti_constant_input_geometric_sum(N):
+    """u constant too: h_l[n] = delta B_n u (1 - a_n^(l+1)) / (1 - a_n).  N = 64: a
+    large state (the [VSSD] page's §4.1 recommends d_state 256)."""
+    B, D, H, W = 2, 2, 3, 5
     x, dt, A_log, bias, Bs, Cs, Ds, Bv, Cv = _lti_inputs(B, D, H, W, N, seed=3)
     x[:] = np.random.default_rng(4).standard_normal((B, D, 1, 1))
     y = oracle.ss2d_f64(x, dt, A_log, bias, Bs, Cs, Ds)
@@ -150,8 +152,33 @@ def test_brute_force_small_maps(H, W):
     np.testing.assert_allclose(y, yb, rtol=1e-11, atol=1e-12)
 
 
+def test_brute_force_large_state():
+    """N past 16 (blocks of states on the GPU): the O(L^2) form with N = 20."""
+    inp = _rand(1, 2, 2, 3, 20, seed=77)
+    inp["Ds"] = np.random.default_rng(78).standard_normal(inp["Ds"].shape)
+    np.testing.assert_allclose(_run(inp), brute.ss2d(**inp), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,cuts", [(40, (16, 32)), (256, (16, 100, 255))])
+def test_states_add_up(N, cuts):
+    """y is Ds*u plus one term per state, so the forward over all N states equals the
+    sum of forwards over any split of the states, the skip term taken once.  (The GPU
+    runs N > 16 in blocks of 16 states and adds the blocks.)"""
+    inp = _rand(2, 3, 3, 4, N, seed=N)
+    inp["Ds"] = np.random.default_rng(N + 1).standard_normal(inp["Ds"].shape)
+    whole = _run(inp)
+    bounds = (0,) + cuts + (N,)
+    parts = 0.0
+    for i in range(len(bounds) - 1):
+        lo, hi = bounds[i], bounds[i + 1]
+        sub = dict(inp, A_log=inp["A_log"][:, lo:hi], Bs=inp["Bs"][:, :, lo:hi], Cs=inp["Cs"][:, :, lo:hi],
+                   Ds=inp["Ds"] if i == 0 else np.zeros_like(inp["Ds"]))
+        parts = parts + _run(sub)
+    np.testing.assert_allclose(parts, whole, rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("H,W,N,dtype", [(5, 3, 4, "f32"), (1, 9, 2, "f32"), (6, 6, 16, "bf16"),
-                                         (4, 7, 1, "f32")])
+                                         (4, 7, 1, "f32"), (3, 4, 48, "f32")])
 def test_c_oracle_matches_tensor_op_formulation(H, W, N, dtype):
     inp = ss2d_inputs.tiny_random(2, 3, H, W, N, seed=H * 100 + W, dtype=dtype)
     y, ok = _run(inp, want_out_k=True)
