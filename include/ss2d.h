@@ -41,7 +41,9 @@ typedef enum {
   SS2D_ERR_ALIAS = -5,          /* y overlaps one of the inputs                   */
   SS2D_ERR_ALIGN = -6,          /* a pointer is not aligned to its element size   */
   SS2D_ERR_NO_DEVICE = -7,      /* no HIP device, or the device query failed      */
-  SS2D_ERR_HIP = -8             /* a HIP call or kernel launch failed             */
+  SS2D_ERR_HIP = -8,            /* a HIP call or kernel launch failed             */
+  SS2D_ERR_NOALLOC_LIMIT = -9   /* ss2d_forward_noalloc: the shape's temporary    */
+                                /* exceeds the library's static array (128 MiB)   */
 } ss2d_status;
 
 /*
@@ -104,6 +106,30 @@ int ss2d_forward_lanes(const void* x, const void* dt, const float* A_log, const 
                        const void* Bs, const void* Cs, const float* Ds, void* y,
                        int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
                        int dtype, int lanes_per_seq, void* stream);
+
+/*
+ * ss2d_forward_noalloc -- ss2d_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): it calls no hipMalloc, hipFree or allocating library
+ * routine.  Its temporary is a static device array of 128 MiB that the library
+ * holds on every device it runs on until the process ends, so only shapes whose
+ * temporary fits run: it holds the fp32 merge plane(s) (B*D*H*W fp32 values, twice
+ * that for bf16 output) and, for long maps cut into segments, 32 fp32 values per
+ * (batch, direction, channel, segment).  Larger shapes return
+ * SS2D_ERR_NOALLOC_LIMIT before any device work (VMamba-T stage-1 fp32, 77 MB,
+ * and 2 x 192 x 256 x 256 fp32, 107 MB, fit; bf16 B=64, D=384, 28 x 28 does not).
+ * Unlike ss2d_forward it makes no transposed copies: column walks and the final
+ * merge gather from x and the column plane in place.  Same arguments, results
+ * (the same function up to rounding order), validation and error codes as
+ * ss2d_forward.  Every call on a device uses that device's one array, and nothing
+ * in it needs to start at any value; calls whose work overlaps on one device
+ * (other streams, other threads) race on it and must be serialised by the
+ * caller.
+ */
+int ss2d_forward_noalloc(const void* x, const void* dt, const float* A_log, const float* dt_bias,
+                         const void* Bs, const void* Cs, const float* Ds, void* y,
+                         int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
+                         int dtype, void* stream);
 
 /*
  * ss2d_bidir_forward -- enqueue the two-direction (bidirectional) selective scan

@@ -12,7 +12,7 @@ import os
 import threading
 
 __all__ = ["forward", "ss2d_forward", "project", "ss2d_project", "forward_from_x", "ss2d_forward_from_x",
-           "channel_last", "ss2d_channel_last", "backward", "ss2d_backward", "measure_peaks", "describe", "bidir_forward", "ss2d_bidir_forward", "trim_memory", "status_string", "version", "library_path", "lib",
+           "channel_last", "ss2d_channel_last", "backward", "ss2d_backward", "measure_peaks", "describe", "bidir_forward", "ss2d_bidir_forward", "ss2d_forward_noalloc", "trim_memory", "status_string", "version", "library_path", "lib",
            "SS2D_F32", "SS2D_BF16", "SS2DError"]
 
 SS2D_F32 = 0
@@ -68,6 +68,8 @@ def lib():
             L.ss2d_forward_lanes.restype = ctypes.c_int
             L.ss2d_bidir_forward.argtypes = [vp] * 8 + [i64] * 4 + [ctypes.c_int, vp]
             L.ss2d_bidir_forward.restype = ctypes.c_int
+            L.ss2d_forward_noalloc.argtypes = [vp] * 8 + [i64] * 5 + [ctypes.c_int, vp]
+            L.ss2d_forward_noalloc.restype = ctypes.c_int
             L.ss2d_trim_memory.argtypes = []
             L.ss2d_trim_memory.restype = ctypes.c_int
             L.ss2d_project.argtypes = [vp] * 6 + [i64] * 6 + [ctypes.c_int, vp]
@@ -118,6 +120,11 @@ def ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, str
         return lib().ss2d_forward_lanes(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype),
                                         int(lanes), stream)
     return lib().ss2d_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype), stream)
+
+
+def ss2d_forward_noalloc(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, stream) -> int:
+    """Raw C-ABI call of the no-allocation forward; returns the status code."""
+    return lib().ss2d_forward_noalloc(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, int(dtype), stream)
 
 
 def ss2d_bidir_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, L, N, dtype, stream) -> int:

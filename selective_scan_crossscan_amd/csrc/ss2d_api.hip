@@ -48,18 +48,28 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
+// The temporary of the no-allocation forward (ss2d_forward_noalloc), for callers
+// that cannot allocate: one array on every device the library runs on, held until
+// the process ends.  Host code never passes its name to a kernel or a copy (on
+// the host it only stands for the device variable); it uses the device address
+// hipGetSymbolAddress returns for the device in question, kept per device.
+constexpr size_t kNoAllocBytes = (size_t)128 << 20;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
 struct DeviceInfo {
   int device = -1;
   hipMemPool_t pool = nullptr;  // the library's own memory pool on that device
+  void* noalloc = nullptr;      // device address of `scratch` on that device
 };
 
 // Per-device one-time setup, done with that device current: the library's own
 // stream-ordered memory pool for its temporaries (its release threshold keeps
 // freed blocks for the next call; other users of the device's default pool are
-// not affected).
+// not affected), and the device address of the no-allocation array.
 struct DevState {
   bool ready = false;
   hipMemPool_t pool = nullptr;
+  void* noalloc = nullptr;
 };
 std::mutex g_dev_mutex;
 DevState g_dev[64];
@@ -93,11 +103,20 @@ int device_info(DeviceInfo* out) {
       (void)hipMemPoolDestroy(pool);
       return SS2D_ERR_NO_DEVICE;
     }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      remember(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      (void)hipMemPoolDestroy(pool);
+      return SS2D_ERR_NO_DEVICE;
+    }
     st.pool = pool;
+    st.noalloc = ptr;
     st.ready = true;
   }
   out->device = dev;
   out->pool = st.pool;
+  out->noalloc = st.noalloc;
   return SS2D_OK;
 }
 
@@ -164,6 +183,7 @@ const char* ss2d_status_string(int status) {
     case SS2D_ERR_ALIGN: return "a pointer is not aligned to its element size";
     case SS2D_ERR_NO_DEVICE: return "no usable HIP device";
     case SS2D_ERR_HIP: return "a HIP call or kernel launch failed";
+    case SS2D_ERR_NOALLOC_LIMIT: return "the shape needs more temporary memory than ss2d_forward_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -201,17 +221,21 @@ int check_forward(const void* x, const void* dt, const float* A_log, const float
 
 bool lanes_ok(int lanes) { return lanes == 0 || lanes == 16 || lanes == 32 || lanes == 64; }
 
+// noalloc: run from the per-device static array (no transposed copies, so the
+// temporary is the merge planes and segment maps only), or fail with
+// SS2D_ERR_NOALLOC_LIMIT before touching the device when it does not fit.
 int forward_impl(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
                  const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
-                 int dtype, int K, int lanes, void* stream) {
+                 int dtype, int K, int lanes, void* stream, bool noalloc = false) {
   bool aligned = false;
   int rc = check_forward(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, K, &aligned);
   if (rc != SS2D_OK) return rc;
   if (!lanes_ok(lanes)) return SS2D_ERR_SHAPE;
+  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, lanes, K, aligned, noalloc);
+  if (noalloc && plan.scratch_bytes > kNoAllocBytes) return SS2D_ERR_NOALLOC_LIMIT;
   DeviceInfo di;
   rc = device_info(&di);
   if (rc != SS2D_OK) return rc;
-  const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, lanes, K, aligned);
 
   ss2d::LaunchArgs a;
   a.x = x;
@@ -232,14 +256,22 @@ int forward_impl(const void* x, const void* dt, const float* A_log, const float*
   a.device = di.device;
   a.K = K;
 
-  void* scratch = nullptr;
-  hipError_t e = tmp_alloc(di, &scratch, plan.scratch_bytes, a.stream);
+  if (noalloc) {
+    const hipError_t e = ss2d::launch_forward(a, plan, static_cast<float*>(di.noalloc));
+    if (e != hipSuccess) {
+      remember(e);
+      return SS2D_ERR_HIP;
+    }
+    return SS2D_OK;
+  }
+  void* tmp = nullptr;
+  hipError_t e = tmp_alloc(di, &tmp, plan.scratch_bytes, a.stream);
   if (e != hipSuccess) {
     remember(e);
     return SS2D_ERR_HIP;
   }
-  e = ss2d::launch_forward(a, plan, static_cast<float*>(scratch));
-  const hipError_t e2 = tmp_free(scratch, a.stream);
+  e = ss2d::launch_forward(a, plan, static_cast<float*>(tmp));
+  const hipError_t e2 = tmp_free(tmp, a.stream);
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) {
     remember(e);
@@ -284,6 +316,12 @@ int ss2d_forward(const void* x, const void* dt, const float* A_log, const float*
                  const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W,
                  int64_t N, int dtype, void* stream) {
   return forward_impl(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, 4, 0, stream);
+}
+
+int ss2d_forward_noalloc(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                         const void* Cs, const float* Ds, void* y, int64_t B, int64_t D, int64_t H, int64_t W,
+                         int64_t N, int dtype, void* stream) {
+  return forward_impl(x, dt, A_log, dt_bias, Bs, Cs, Ds, y, B, D, H, W, N, dtype, 4, 0, stream, true);
 }
 
 int ss2d_forward_lanes(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,

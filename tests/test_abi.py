@@ -41,7 +41,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert names == sorted(["ss2d_forward", "ss2d_forward_lanes", "ss2d_bidir_forward", "ss2d_status_string",
+    assert names == sorted(["ss2d_forward", "ss2d_forward_lanes", "ss2d_forward_noalloc", "ss2d_bidir_forward",
+                            "ss2d_status_string",
                             "ss2d_last_hip_error", "ss2d_version", "ss2d_describe", "ss2d_describe_lanes",
                             "ss2d_trim_memory", "ss2d_measure_peaks", "ss2d_project", "ss2d_forward_from_x",
                             "ss2d_channel_last", "ss2d_backward"])
@@ -52,7 +53,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_strings():
     assert ss2d.version() >= 10000
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = ss2d.status_string(code)
         assert isinstance(s, str) and s
     assert ss2d.status_string(123) == "unknown status"
@@ -374,3 +375,28 @@ def test_backward_validation():
 def test_backward_valid_calls_without_device_report_no_device():
     assert _bwd(dtype=1) == -7            # bf16 is accepted
     assert _bwd() == -7
+
+
+# the no-allocation forward: same validation, plus the static array's limit
+def _noalloc(x=X, dt=DT, al=AL, bi=BI, bs=BS, cs=CS, ds=DS, y=Y, B=2, D=3, H=4, W=5, N=16, dtype=0):
+    return ss2d.ss2d_forward_noalloc(x, dt, al, bi, bs, cs, ds, y, B, D, H, W, N, dtype, None)
+
+
+def test_noalloc_validation_and_limit():
+    assert _noalloc(x=None) == -1
+    assert _noalloc(H=0) == -2
+    assert _noalloc(N=257) == -3
+    assert _noalloc(dtype=9) == -4
+    assert _noalloc(y=X) == -5
+    assert _noalloc(x=X + 2) == -6
+    # two fp32 planes of 64 x 384 x 28 x 28 (bf16 output) = 154 MB > 128 MiB: refused before any device work
+    assert _noalloc(B=64, D=384, H=28, W=28, dtype=1) == -9
+    assert _noalloc(B=64, D=192, H=56, W=56) == -9       # one fp32 plane of 64 x 192 x 3136 is 154 MB
+    assert "128 MiB" in open(HEADER).read()
+
+
+@needs_no_device
+def test_noalloc_valid_calls_without_device_report_no_device():
+    assert _noalloc() == -7
+    assert _noalloc(B=32, D=192, H=56, W=56) == -7       # VMamba-T stage-1 fp32: 77 MB
+    assert _noalloc(B=2, D=192, H=256, W=256) == -7      # segmented 256 x 256 map: 107 MB
