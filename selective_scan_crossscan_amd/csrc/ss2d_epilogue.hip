@@ -8,12 +8,19 @@
 //   out[b, p, d] = (y[b, d, p] - m) / sqrt(v + eps) * gamma[d] + beta[d],
 // or out[b, p, d] = y[b, d, p] without the normalisation.
 //
-// How it runs.  A workgroup takes TP consecutive pixels of one batch with all D
-// channels into LDS (rows of TP + 1 floats, so reading down a row's pixels is
-// free of bank conflicts), eight loads in flight per thread.  The statistics are
-// two passes over LDS in fp32 (mean, then the squared deviations), 256 / TP
-// threads per pixel.  The output is written pixel by pixel, D contiguous values
-// each, consecutive threads on consecutive channels.
+// How it runs (channel_last_vec_kernel, rows and bases aligned for vector
+// access).  A workgroup takes TP = 16 consecutive pixels of one batch with all D
+// channels.  Loads read V consecutive pixels of a channel per lane (V = 4 fp32,
+// 8 bf16: 16-byte loads) into an LDS tile stored pixel-major, [TP][D + 4], so the
+// output side reads V consecutive channels of a pixel with 16-byte LDS reads and
+// writes them with one vector store; a tile's output rows are one contiguous
+// block.  The statistics are per pixel over K = threads / TP consecutive lanes,
+// mean then squared deviations, each reduced across the K lanes with shuffles
+// (no serial loop, no barrier between the two).  Consecutive tiles run on one
+// XCD (they share 128-byte lines of y).  bf16 output uses the hardware packed
+// round-to-nearest-even conversion.  Other shapes (L or D not a multiple of V,
+// unaligned bases, D above 900) take channel_last_kernel: channel-major tiles
+// of up to 64 pixels, scalar stores.
 #include "ss2d_kernels.h"
 
 namespace ss2d {
@@ -177,6 +184,190 @@ __global__ __launch_bounds__(kEpiThreads) void channel_last_kernel(EpiParams p) 
   }
 }
 
+// ------------------------------------------------------------------ vector path
+// V consecutive elements of storage type S as floats, and back.
+template <typename S, int V>
+struct VecIo;
+template <>
+struct VecIo<float, 4> {
+  static __device__ __forceinline__ void ld(const float* p, int64_t i, float (&v)[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p + i);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+  static __device__ __forceinline__ void st(float* p, int64_t i, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <>
+struct VecIo<uint16_t, 4> {
+  static __device__ __forceinline__ void ld(const uint16_t* p, int64_t i, float (&v)[4]) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p + i);
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, int64_t i, const float (&v)[4]) {
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
+  }
+};
+template <>
+struct VecIo<uint16_t, 8> {
+  static __device__ __forceinline__ void ld(const uint16_t* p, int64_t i, float (&v)[8]) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p + i);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void st(uint16_t* p, int64_t i, const float (&v)[8]) {
+    *reinterpret_cast<uint4*>(p + i) = make_uint4(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]),
+                                                  bf16x2_rne(v[4], v[5]), bf16x2_rne(v[6], v[7]));
+  }
+};
+
+constexpr int kVecTile = 16;   // pixels per workgroup
+constexpr int kVecMaxD = 900;   // [16][D + 4] fp32 tile plus gamma and beta: up to 64 KB of dynamic LDS
+
+// Sum over the K consecutive lanes of a group (K a power of two up to 64).
+template <int K>
+__device__ __forceinline__ float lane_group_sum(float v) {
+#pragma unroll
+  for (int o = K / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename S, int V, int NT, bool NORM>
+__global__ __launch_bounds__(NT) void channel_last_vec_kernel(EpiParams p) {
+  constexpr int TP = kVecTile;
+  constexpr int K = NT / TP;  // lanes per pixel in the statistics
+  extern __shared__ __align__(16) float vtile[];  // [TP][D + 4], then gamma and beta (D each)
+  __shared__ float mean_s[TP], rstd_s[TP];
+  const int D = p.D, L = p.L, ldd = D + 4;
+  const int tid = threadIdx.x;
+  float* gam = vtile + TP * ldd;
+  float* bet = gam + D;
+  if (NORM) {
+    for (int i = tid; i < D; i += NT) {
+      gam[i] = p.gamma ? p.gamma[i] : 1.f;
+      bet[i] = p.beta ? p.beta[i] : 0.f;
+    }
+  }
+  // consecutive tiles (which share lines of y) on one XCD; workgroups are dealt
+  // round-robin over the 8 XCDs
+  const int nb = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = nb >> 3, rem = nb & 7;
+  const int wid = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int t = wid % p.tiles;
+  const int64_t b = wid / p.tiles;
+  const int p0 = t * TP;
+  const int np = L - p0 < TP ? L - p0 : TP;  // a multiple of V: L % V == 0
+  const S* yb = static_cast<const S*>(p.y) + b * D * L;
+
+  // load: vector e = d * (TP / V) + jv (channel d, pixels V*jv ..), U in flight per thread
+  {
+    constexpr int GV = TP / V;
+    constexpr int U = 32 / V;
+    const int nv = D * GV;
+    constexpr int DQ = NT / GV;  // NT is a multiple of GV
+    int d = tid / GV;
+    const int jv = tid % GV;
+    for (int e0 = tid; e0 < nv; e0 += U * NT) {
+      float v[U][V];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int dd = d + u * DQ;
+        const bool ok = e0 + u * NT < nv && V * jv < np;
+        VecIo<S, V>::ld(yb, ok ? (int64_t)dd * L + p0 + V * jv : 0, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (e0 + u * NT < nv) {
+          float* r = vtile + V * jv * ldd + d + u * DQ;
+#pragma unroll
+          for (int i = 0; i < V; ++i) r[i * ldd] = v[u][i];
+        }
+      }
+      d += U * DQ;
+    }
+  }
+  __syncthreads();
+
+  if (NORM) {
+    const int q = tid % K, j = tid / K;
+    const float* row = vtile + j * ldd;
+    float s0 = 0.f, s1 = 0.f;
+    int dd = q;
+    for (; dd + K < D; dd += 2 * K) {
+      s0 += row[dd];
+      s1 += row[dd + K];
+    }
+    if (dd < D) s0 += row[dd];
+    const float m = lane_group_sum<K>(s0 + s1) / (float)D;
+    float c0 = 0.f, c1 = 0.f;
+    dd = q;
+    for (; dd + K < D; dd += 2 * K) {
+      const float a0 = row[dd] - m, a1 = row[dd + K] - m;
+      c0 = fmaf(a0, a0, c0);
+      c1 = fmaf(a1, a1, c1);
+    }
+    if (dd < D) {
+      const float a0 = row[dd] - m;
+      c0 = fmaf(a0, a0, c0);
+    }
+    const float var = lane_group_sum<K>(c0 + c1) / (float)D;
+    if (q == 0) {
+      mean_s[j] = m;
+      rstd_s[j] = 1.f / sqrtf(var + p.eps);
+    }
+    __syncthreads();
+  }
+
+  // store: vector o = j * (D / V) + c (pixel j, channels V*c ..); the tile's output
+  // rows are consecutive, so the workgroup writes one contiguous block
+  S* ob = static_cast<S*>(p.out) + (b * L + p0) * (int64_t)D;
+  const int DV = D / V, mv = np * DV;
+  const int oq = NT / DV, orr = NT - oq * DV;
+  int j = tid / DV, c = tid - (tid / DV) * DV;
+  for (int o = tid; o < mv; o += NT) {
+    const float* src = vtile + j * ldd + V * c;
+    float w[V];
+#pragma unroll
+    for (int i = 0; i < V; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(src + i);
+      w[i] = a.x; w[i + 1] = a.y; w[i + 2] = a.z; w[i + 3] = a.w;
+    }
+    if (NORM) {
+      const float m = mean_s[j], r = rstd_s[j];
+#pragma unroll
+      for (int i = 0; i < V; i += 4) {
+        const float4 g = *reinterpret_cast<const float4*>(gam + V * c + i);
+        const float4 be = *reinterpret_cast<const float4*>(bet + V * c + i);
+        w[i] = fmaf((w[i] - m) * r, g.x, be.x);
+        w[i + 1] = fmaf((w[i + 1] - m) * r, g.y, be.y);
+        w[i + 2] = fmaf((w[i + 2] - m) * r, g.z, be.z);
+        w[i + 3] = fmaf((w[i + 3] - m) * r, g.w, be.w);
+      }
+    }
+    VecIo<S, V>::st(ob, (int64_t)o * V, w);
+    j += oq;
+    c += orr;
+    if (c >= DV) {
+      c -= DV;
+      ++j;
+    }
+  }
+}
+
+template <typename S, int V, int NT>
+hipError_t launch_vec(const EpiParams& p, bool norm, unsigned blocks, hipStream_t stream) {
+  const size_t lds = ((size_t)kVecTile * (p.D + 4) + 2 * (size_t)p.D) * sizeof(float);
+  if (norm)
+    hipLaunchKernelGGL((channel_last_vec_kernel<S, V, NT, true>), dim3(blocks), dim3(NT), lds, stream, p);
+  else
+    hipLaunchKernelGGL((channel_last_vec_kernel<S, V, NT, false>), dim3(blocks), dim3(NT), lds, stream, p);
+  return hipGetLastError();
+}
+
 template <typename S, bool VEC>
 hipError_t launch_epi(const EpiParams& p, bool norm, unsigned blocks, hipStream_t stream) {
   if (norm)
@@ -199,6 +390,29 @@ hipError_t launch_channel_last(const EpilogueArgs& a) {
   p.eps = a.eps;
   p.D = (int)a.D;
   p.L = (int)(a.H * a.W);
+  {
+    // the vector path: V-element accesses along pixels (loads) and channels (stores)
+    const int V = (a.dtype == 1 && p.L % 8 == 0 && p.D % 8 == 0) ? 8 : 4;
+    const uintptr_t va = a.dtype == 0 ? 15 : (uintptr_t)(2 * V - 1);
+    const bool vec_ok = p.L % V == 0 && p.D % V == 0 && p.D <= kVecMaxD && !((uintptr_t)a.y & va) &&
+                        !((uintptr_t)a.out & va);
+    if (vec_ok) {
+      p.TP = kVecTile;
+      p.tiles = (p.L + kVecTile - 1) / kVecTile;
+      const int64_t blocks = a.B * p.tiles;
+      if (blocks > INT32_MAX) return hipErrorInvalidValue;
+      // 256 threads (16 lanes per pixel) for up to 256 channels, else 512 (32 lanes)
+      const bool wide = p.D > 256;
+      if (a.dtype == 0)
+        return wide ? launch_vec<float, 4, 512>(p, a.normalize, (unsigned)blocks, a.stream)
+                    : launch_vec<float, 4, 256>(p, a.normalize, (unsigned)blocks, a.stream);
+      if (V == 8)
+        return wide ? launch_vec<uint16_t, 8, 512>(p, a.normalize, (unsigned)blocks, a.stream)
+                    : launch_vec<uint16_t, 8, 256>(p, a.normalize, (unsigned)blocks, a.stream);
+      return wide ? launch_vec<uint16_t, 4, 512>(p, a.normalize, (unsigned)blocks, a.stream)
+                  : launch_vec<uint16_t, 4, 256>(p, a.normalize, (unsigned)blocks, a.stream);
+    }
+  }
   // pixels per workgroup: the most (up to 64, a power of two) whose tile fits the LDS
   int tp = 64;
   while (tp > 1 && (int64_t)p.D * (tp + 1) > kEpiLdsFloats) tp >>= 1;

@@ -73,6 +73,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// Two floats to two packed bf16, rounded to nearest even by the hardware's packed
+// conversion (one instruction on gfx950).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2_v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
+}
+
 template <typename S>
 struct Io;
 
@@ -98,10 +108,7 @@ struct Io<uint16_t> {
   }
   static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_rne(v); }
   static __device__ __forceinline__ void st4(uint16_t* p, int64_t i, float4 v) {  // i % 4 == 0
-    uint2 u;
-    u.x = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
-    u.y = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
-    *reinterpret_cast<uint2*>(p + i) = u;
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(bf16x2_rne(v.x, v.y), bf16x2_rne(v.z, v.w));
   }
 };
 

@@ -43,10 +43,15 @@ def _dev(a, dtype=None):
     return t.cuda()
 
 
-# (B, D, H, W): 64 / 32 / 16 / 1 pixels per workgroup, ragged last tiles,
-# odd D, the largest D
+# (B, D, H, W).  Channel-major fallback tiles (L or D not a multiple of the vector
+# width, D above 956): 64 / 32 / 16 / 1 pixels per workgroup, ragged last tiles, odd
+# D, the largest D.  Vector path (16-pixel pixel-major tiles): whole tiles, a 4- or
+# 12-pixel last tile, 256- and 512-thread workgroups, bf16 with 8- and 4-element
+# vectors, D at the vector path's limit (900) and just past it (904).
 SHAPES = [(2, 16, 8, 8), (1, 192, 7, 9), (2, 384, 5, 7), (1, 768, 3, 5), (1, 3, 1, 37), (1, 4096, 2, 3),
-          (3, 100, 6, 11)]
+          (3, 100, 6, 11),
+          (2, 192, 8, 10), (1, 384, 6, 6), (2, 768, 4, 7), (1, 900, 4, 4), (1, 904, 2, 8), (3, 100, 4, 9),
+          (1, 12, 2, 2), (4, 256, 16, 16), (2, 260, 4, 4)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -87,3 +92,42 @@ def test_full_size_stage1_after_the_forward():
     torch.cuda.synchronize()
     ref = epilogue.layer_norm_channel_last(y.double().cpu().numpy(), g.cpu().numpy(), b.cpu().numpy(), eps=1e-5)
     assert np.all(np.abs(out.double().cpu().numpy() - ref) <= 1e-5 * (1 + np.abs(ref)))
+
+
+def _offset(a, dtype):
+    """A contiguous device tensor holding a whose base is one element past a 256-byte
+    boundary (aligned to its element only)."""
+    t = torch.bfloat16 if dtype == "bf16" else torch.float32
+    flat = torch.zeros(a.size + 64, dtype=t, device="cuda")
+    v = flat[1:1 + a.size].view(a.shape)
+    v.copy_(torch.from_numpy(np.ascontiguousarray(a)).to(t))
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_element_aligned_bases_take_the_scalar_tiles(dtype):
+    B, D, H, W = 2, 192, 8, 8
+    y, g, b = _case(B, D, H, W, dtype, seed=9)
+    ss2d = _lib()
+    out = _offset(np.zeros((B, H, W, D), np.float32), dtype)
+    ss2d.channel_last(_offset(y, dtype), _dev(g), _dev(b), eps=1e-5, out=out)
+    torch.cuda.synchronize()
+    ref = epilogue.layer_norm_channel_last(y, g, b, eps=1e-5)
+    extra = 2.0 ** -8 * np.abs(ref) if dtype == "bf16" else 0.0
+    assert np.all(np.abs(out.double().cpu().numpy() - ref) <= 1e-5 * (1 + np.abs(ref)) + extra)
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4])
+def test_workload_shapes(ci):
+    """The four workload shapes (the vector path) on random values, against the oracle on
+    two batch elements."""
+    shape = ss2d_inputs.CONFIGS[ci]
+    B, D, H, W = 2, shape.D, shape.H, shape.W
+    y, g, b = _case(B, D, H, W, shape.dtype, seed=ci)
+    out = _lib().channel_last(_dev(y, shape.dtype), _dev(g), _dev(b), eps=1e-5)
+    plain = _lib().channel_last(_dev(y, shape.dtype), normalize=False)
+    torch.cuda.synchronize()
+    ref = epilogue.layer_norm_channel_last(y, g, b, eps=1e-5)
+    extra = 2.0 ** -8 * np.abs(ref) if shape.dtype == "bf16" else 0.0
+    assert np.all(np.abs(out.double().cpu().numpy() - ref) <= 1e-5 * (1 + np.abs(ref)) + extra)
+    assert np.array_equal(plain.double().cpu().numpy(), epilogue.channel_last(y))
