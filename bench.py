@@ -90,8 +90,8 @@ def bench_workload(shape, path: str) -> str:
 
 def bench_flags(args, path: str) -> str:
     """Command-line flags that select this workload and path (for the recorded commands)."""
-    return ((f" --n {args.n}" if args.n else "") + (" --epilogue" if path == "epilogue" else
-                                                   f" --path {path}" if path != "scan" else ""))
+    return ((" --epilogue" if path == "epilogue" else f" --path {path}" if path != "scan" else "")
+            + (f" --n {args.n}" if args.n else ""))
 
 
 def algorithmic_bytes(shape, K: int = 4) -> int:
@@ -127,13 +127,13 @@ def kernel_source_hash(kernel: str = "ss2d_forward_kernel") -> str:
 
 
 def measured_traffic(workload: str, kernel: str = KERNEL_PREFIX):
-    """HBM bytes per launch of `kernel` from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    """HBM bytes per step (all launches) of `kernel` from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     counters, scaled by the copy-kernel calibration; None when absent or the kernel
     changed since."""
     rec = _record(traffic_file(workload, kernel)) or {}
     if rec.get("kernel_source_hash") != kernel_source_hash(kernel) or rec.get("workload") != workload:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_step")
 
 
 def cpu_model() -> str:
@@ -260,9 +260,21 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
     from_x, bwd, epi = path == "from_x", path == "backward", path == "epilogue"
     kernel = ("project_kernel" if from_x else "bwd_chunk_kernel" if bwd else "channel_last_kernel" if epi
               else KERNEL_PREFIX)
+    # the kernel's template instances and variants (the epilogue has a vector and a general kernel)
+    names = ("channel_last_vec_kernel", "channel_last_kernel") if epi else (kernel,)
     workload = bench_workload(shape, path)
     extra = bench_flags(args, path)
     cmds = {k: v.format(d=folder, c=cfg, x=extra) for k, v in PROFILE_COMMANDS.items()}
+
+    def executions(steps, warmup, flush):
+        """How many times a run executes the path that launches `kernel`: the timed and
+        warm-up steps and the flushed steps; the epilogue runs warm-up + timed steps after
+        them; the projection also runs alone, warm-up + timed."""
+        if epi:
+            return warmup + steps
+        if from_x:
+            return (warmup + steps + flush) + (warmup + steps)
+        return warmup + steps + flush
 
     # Kernel-trace statistics, next to the bench line printed by the same run.
     with open(_find(folder, "stats_kernel_stats.csv")) as f:
@@ -292,29 +304,35 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
     lines = [f"# {kernel} — {workload} — rocprofv3 kernel trace", "", f"Workload: {shape}.  {work}", "",
              "Command (from the repository root):", "", "```", cmds["stats"], "```", "",
              "| kernel | calls | average µs | min µs | max µs | share |", "|---|---|---|---|---|---|"]
-    # Each template instance of the kernel runs once per step (a segmented backward
-    # runs two: its two passes), so its time per step is the sum of their averages.
-    kern_avg = None
-    per_step = 0.0  # fused plans launch each of a forward's kernels once per step
+    # Per step: a kernel's summed duration over the run divided by the executions of the
+    # path (a step may launch it several times: once per block of 16 states, or a carry
+    # pass and one launch per direction on segmented maps).
+    n_exec = executions(bench["steps"], bench["warmup"], (bench.get("flushed") or {}).get("steps", 0))
+    kern_total = None
+    step_total = 0.0
     present = []
     for r in stats:
         name = r["Name"]
         if len(name) > 90:
             name = name[:87] + "..."
         avg = float(r["AverageNs"]) / 1e3
-        if _is_kernel(r["Name"], kernel):
-            kern_avg = (kern_avg or 0.0) + avg
+        tot = avg * int(r["Calls"])
+        if any(_is_kernel(r["Name"], k) for k in names):
+            kern_total = (kern_total or 0.0) + tot
         for k in STEP_KERNELS:
             if _is_kernel(r["Name"], k):
-                per_step += avg
+                step_total += tot
                 present.append(k)
         lines.append(f"| `{name}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    kern_avg = kern_total / n_exec
+    per_step = step_total / n_exec
     lines += ["", f"bench.py's own HIP-event average over the timed steps of this run: "
                   f"{bench['kernel_us']:.1f} µs per step (roofline frac {bench['roofline']['frac']:.3f}).",
-              f"rocprofv3 average over all launches (warm-up included): {kern_avg:.1f} µs for {kernel}; "
-              f"{per_step:.1f} µs per step as the sum of the average durations of the step's kernels, one launch each "
-              f"({', '.join(sorted(present))}).", ""]
+              f"rocprofv3, summed over the run's {n_exec} executions of the path (warm-up and flushed steps "
+              f"included): {kern_avg:.1f} µs per execution in {'/'.join(names)}"
+              + ("" if (epi or from_x) else f"; {per_step:.1f} µs per step in all of the step's kernels "
+                 f"({', '.join(sorted(set(present)))})") + ".", ""]
     if epi:
         ej = bench["epilogue"]
         lines += [f"The epilogue timed by bench.py with HIP events: {ej['us']:.1f} µs; {kernel} by rocprofv3: "
@@ -330,8 +348,9 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
                   f"({alg_bytes / (kern_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s).", ""]
     lines += ["Bench line of this run:", "", "```", bench_line, "```", ""]
     krec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
-            "kernel_avg_us": kern_avg, "step_kernels_us": per_step,
-            "note": "kernel_avg_us: sum over the kernel's template instances of their average launch duration"}
+            "kernel_avg_us": kern_avg, "step_kernels_us": per_step, "executions": n_exec,
+            "note": "kernel_avg_us: the kernel's summed duration per execution of the path (all its launches "
+                    "in one step)"}
     lines += ["Record read by bench.py (valid only while the kernel sources hash to the value below):", "",
               "```json", json.dumps(krec, indent=1), "```", ""]
     with open(kernel_stats_file(workload, kernel), "w") as f:
@@ -342,37 +361,35 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
     per = {}
     for counter, prefix in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = [r for r in _counter_rows(folder, prefix) if r["Counter_Name"] == counter]
-        inst = {}  # template instance -> its dispatches' values
-        for r in rows:
-            if _is_kernel(r["Kernel_Name"], kernel):
-                inst.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        vals = [float(r["Counter_Value"]) for r in rows if any(_is_kernel(r["Kernel_Name"], k) for k in names)]
         copies = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         probe_kib, probe_name = max(copies)
         expected_kib = COPY_PROBE_MIB * 1024.0
-        per[counter] = {"kernel_kib_per_dispatch": sum(sum(v) / len(v) for v in inst.values()),
-                        "dispatches": sum(len(v) for v in inst.values()), "instances": len(inst),
+        # the counter runs time 3 steps after 1 warm-up step, no flushed steps
+        n_cnt = executions(3, 1, 0)
+        per[counter] = {"kernel_kib_per_step": sum(vals) / n_cnt, "dispatches": len(vals), "executions": n_cnt,
                         "copy_probe_kib": probe_kib, "copy_probe_kernel": probe_name,
                         "copy_expected_kib": expected_kib, "scale": expected_kib / probe_kib}
-    fetch_b = per["FETCH_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["FETCH_SIZE"]["scale"]
-    write_b = per["WRITE_SIZE"]["kernel_kib_per_dispatch"] * 1024 * per["WRITE_SIZE"]["scale"]
+    fetch_b = per["FETCH_SIZE"]["kernel_kib_per_step"] * 1024 * per["FETCH_SIZE"]["scale"]
+    write_b = per["WRITE_SIZE"]["kernel_kib_per_step"] * 1024 * per["WRITE_SIZE"]["scale"]
     rec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
            "kernel_sources": KERNEL_SOURCES[kernel],
-           "hbm_bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
+           "hbm_bytes_per_step": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
            "algorithmic_bytes": alg_bytes, "counters": per}
     lines = [f"# {kernel} — {workload} — HBM traffic (rocprofv3 counters)", "",
              "Two counter runs, one counter each, from the repository root:", "", "```", cmds["fetch"],
              cmds["write"], "```", "",
              f"Each run also performs one {COPY_PROBE_MIB} MiB device-to-device copy; the scale factor is the "
-             "copy's known size divided by what the same counter reads for it.  Where the kernel has several "
-             "template instances in a step (the two passes of a segmented backward), the per-dispatch figure "
-             "is the sum of the instances' averages.", "",
-             "| counter | kernel KiB / dispatch | copy probe KiB | copy expected KiB | scale | kernel bytes |",
+             "copy's known size divided by what the same counter reads for it.  The kernel's figures are "
+             "summed over all its dispatches in the run and divided by the executions of the path (3 timed "
+             "steps and 1 warm-up), i.e. per step, all of the step's launches of the kernel.", "",
+             "| counter | kernel KiB / step | copy probe KiB | copy expected KiB | scale | kernel bytes |",
              "|---|---|---|---|---|---|"]
     for counter, b in (("FETCH_SIZE", fetch_b), ("WRITE_SIZE", write_b)):
         c = per[counter]
-        lines.append(f"| {counter} | {c['kernel_kib_per_dispatch']:.0f} | {c['copy_probe_kib']:.0f} | "
+        lines.append(f"| {counter} | {c['kernel_kib_per_step']:.0f} | {c['copy_probe_kib']:.0f} | "
                      f"{c['copy_expected_kib']:.0f} | {c['scale']:.4f} | {b / 1e6:.1f} MB |")
-    lines += ["", f"HBM traffic per launch: {(fetch_b + write_b) / 1e6:.1f} MB against "
+    lines += ["", f"HBM traffic per step: {(fetch_b + write_b) / 1e6:.1f} MB against "
                   f"{alg_bytes / 1e6:.1f} MB algorithmic "
                   f"(ratio {(fetch_b + write_b) / alg_bytes:.2f}).", "",
               "Record read by bench.py (valid only while the kernel sources hash to the value below):", "",
