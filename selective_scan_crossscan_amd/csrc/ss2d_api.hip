@@ -352,6 +352,9 @@ int check_projection(int64_t D, int64_t N, int64_t R, const float* wx, const flo
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Largest rank for which ss2d_forward_from_x hands the scan the low-rank rows.
+constexpr int64_t kFromXLowRankUpTo = 8;
+
 }  // namespace
 
 extern "C" {
@@ -434,8 +437,13 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
   rc = device_info(&di);
   if (rc != SS2D_OK) return rc;
   const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, 0, 4, aligned);
-  // one temporary: x transposed, dt, Bs, Cs, then what the scan itself needs
-  const size_t o_dt = up256((size_t)xbytes), o_b = o_dt + up256((size_t)dtbytes);
+  // Low-rank step input: for small ranks the projection writes the R rows and the
+  // scan forms dt from them, instead of writing and reading back the D rows of dt
+  // (measured faster up to kFromXLowRankUpTo; see the design notes).
+  const bool lowrank = R <= kFromXLowRankUpTo && R <= ss2d::kMaxLowRankInput && R <= plan.chans_per_block;
+  const int64_t dtrows_bytes = lowrank ? B * 4 * R * L * s : dtbytes;
+  // one temporary: x transposed, dt (or its low-rank rows), Bs, Cs, then what the scan itself needs
+  const size_t o_dt = up256((size_t)xbytes), o_b = o_dt + up256((size_t)dtrows_bytes);
   const size_t o_c = o_b + up256((size_t)bcbytes), o_scan = o_c + up256((size_t)bcbytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* tmp = nullptr;
@@ -448,11 +456,15 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
   void *dt = tmp + o_dt, *Bs = tmp + o_b, *Cs = tmp + o_c;
   e = ss2d::launch_transpose_x(x, xT, B * D, H, W, dtype, st);
   if (e == hipSuccess) {
-    ss2d::ProjectArgs pa{x, xT, x_proj_weight, dt_projs_weight, dt, Bs, Cs, B, D, H, W, N, R, dtype, st};
+    ss2d::ProjectArgs pa{x, xT, x_proj_weight, dt_projs_weight, lowrank ? nullptr : dt, Bs, Cs, B, D, H, W, N, R,
+                         dtype, st};
+    pa.dts = lowrank ? dt : nullptr;
     e = ss2d::launch_project(pa);
   }
   if (e == hipSuccess) {
     ss2d::LaunchArgs a;
+    a.R = lowrank ? (int)R : 0;
+    a.wdt = dt_projs_weight;
     a.x = x;
     a.dt = dt;
     a.A_log = A_log;

@@ -28,7 +28,15 @@ struct LaunchArgs {
   // (batch, direction) slices have Nt states).  launch_forward sets these.
   int64_t Nt = 0, n0 = 0;
   bool skip = true, acc = false, final_out = true;
+  // Low-rank step input: R > 0 means dt holds the R rows dts (B, K, R, L) and the
+  // scan forms dt = wdt (K, D, R) times them itself (R <= kMaxLowRankInput and at
+  // most the plan's channels per workgroup).
+  int R = 0;
+  const float* wdt = nullptr;
 };
+
+// Largest rank of the low-rank step input the scan expands itself.
+constexpr int kMaxLowRankInput = 8;
 
 // How a shape is mapped onto the machine.
 struct Plan {
@@ -93,12 +101,13 @@ struct ProjectArgs {
   const void* xT;
   const float* wx;   // (4, R + 2N, D)
   const float* wdt;  // (4, D, R)
-  void* dt;          // (B, 4, D, L)
+  void* dt;          // (B, 4, D, L), or null when dts is given
   void* Bs;          // (B, 4, N, L)
   void* Cs;          // (B, 4, N, L)
   int64_t B, D, H, W, N, R;
   int dtype;
   hipStream_t stream;
+  void* dts = nullptr;  // (B, 4, R, L): the low-rank rows instead of the dt map
 };
 hipError_t launch_project(const ProjectArgs& a);
 // Largest 2 * (R + 2N) the projection kernel takes.

@@ -54,6 +54,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxN = 16;
 constexpr int kWaves = 4;
+// Largest rank of the low-rank step input the scan expands itself (see Params::R).
+constexpr int kMaxLowRank = 8;
 
 // LDS floats per lane segment for T steps: multiples of 4 get a stride whose
 // 16-byte slot count is odd, so 16-byte reads by consecutive lanes do not
@@ -237,6 +239,12 @@ struct Params {
   // in the storage type (earlier bf16 blocks leave their fp32 sums in the row
   // plane).
   int Nt, n0, skip, acc, final_out;
+  // Low-rank step input (R > 0): dt points to the R rows dts (B, K, R, L) in scan
+  // order, and the scan forms dt[b,k,d,l] = sum_r wdt[k,d,r] * dts[b,k,r,l] itself
+  // ([SS2D] §3.2: dt_projs applied to the low-rank rows) instead of reading a
+  // (B, K, D, L) dt.  R <= kMaxLowRank and R <= channels per workgroup.
+  int R;
+  const float* wdt;  // (K, D, R)
   // Wave priority rotation (0: off): the launch fits one round of prio_levels
   // resident workgroups on each of prio_ncu CUs.
   int prio_ncu, prio_levels;
@@ -282,7 +290,7 @@ struct Layout {
   static constexpr int kRing0Bytes = kGroupBytes > kStagedBytes ? (kGroupBytes > kTileBytes ? kGroupBytes : kTileBytes)
                                                                 : (kStagedBytes > kTileBytes ? kStagedBytes : kTileBytes);
   static constexpr int kDtBytes = C::kChans * kGT * (int)sizeof(S);
-  static constexpr int kParFloats = 3 * C::kChans * kMaxN + 2 * C::kChans;
+  static constexpr int kParFloats = 3 * C::kChans * kMaxN + 2 * C::kChans + C::kChans * kMaxLowRank;
   static constexpr int kBytes = kRing0Bytes + kGroupBytes + kDtBytes + 4 * kParFloats;
 };
 
@@ -593,20 +601,54 @@ __device__ __forceinline__ void load_x_col(__amdgpu_buffer_rsrc_t rx, uint32_t x
   }
 }
 
+// T values of a row from l0 (zero past L).
 template <typename S, int T, bool VEC, bool FULL>
-__device__ __forceinline__ void load_inputs(const S* dtrow, const S* xrow, bool rev, bool col, int l0, int L, int H,
-                                            int W, float (&dtv)[T], float (&uv)[T]) {
+__device__ __forceinline__ void load_row(const S* row, int l0, int L, float (&v)[T]) {
   if constexpr (VEC && (T % 4 == 0)) {  // groups of 4 wholly inside or outside (see load_x)
 #pragma unroll
     for (int i = 0; i < T; i += 4) {
       float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (FULL || l0 + i < L) q = Io<S>::ld4(dtrow, l0 + i);
-      dtv[i] = q.x; dtv[i + 1] = q.y; dtv[i + 2] = q.z; dtv[i + 3] = q.w;
+      if (FULL || l0 + i < L) q = Io<S>::ld4(row, l0 + i);
+      v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < T; ++i) dtv[i] = (FULL || l0 + i < L) ? Io<S>::ld(dtrow, l0 + i) : 0.f;
+    for (int i = 0; i < T; ++i) v[i] = (FULL || l0 + i < L) ? Io<S>::ld(row, l0 + i) : 0.f;
   }
+}
+
+// Where a lane's dt comes from: its channel's dt row, or (R > 0) the R low-rank
+// rows of its (batch, direction) and its channel's R weights (in LDS).
+template <typename S>
+struct DtSrc {
+  const S* row;    // dt row of the lane's channel (R == 0)
+  const S* lr;     // first low-rank row (R > 0); row r at lr + r * L
+  const float* w;  // the lane's channel's weights, w[r]
+  int R;
+};
+
+template <typename S, int T, bool VEC, bool FULL>
+__device__ __forceinline__ void load_dt(const DtSrc<S>& src, int l0, int L, float (&dtv)[T]) {
+  if (src.R == 0) {
+    load_row<S, T, VEC, FULL>(src.row, l0, L, dtv);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < T; ++i) dtv[i] = 0.f;
+#pragma unroll 1
+  for (int r = 0; r < src.R; ++r) {
+    float v[T];
+    load_row<S, T, VEC, FULL>(src.lr + (int64_t)r * L, l0, L, v);
+    const float w = src.w[r];
+#pragma unroll
+    for (int i = 0; i < T; ++i) dtv[i] = fmaf(w, v[i], dtv[i]);
+  }
+}
+
+template <typename S, int T, bool VEC, bool FULL>
+__device__ __forceinline__ void load_inputs(const DtSrc<S>& dsrc, const S* xrow, bool rev, bool col, int l0, int L,
+                                            int H, int W, float (&dtv)[T], float (&uv)[T]) {
+  load_dt<S, T, VEC, FULL>(dsrc, l0, L, dtv);
   load_x<S, T, VEC, FULL>(xrow, rev, col, l0, L, H, W, uv);
 }
 
@@ -878,7 +920,7 @@ struct Lane {
 // values in fewer, callee-saved registers, and the callee spill to scratch.
 template <typename S, int G, int T, int NG0, int TT, bool VEC, int kAreaBytes>
 __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid, float* smem, float* a2s, float* carry,
-                                        const S* dtrow, const S* xrow, const S* Bbase, const S* Cbase, float* plane,
+                                        const DtSrc<S>& dsrc, const S* xrow, const S* Bbase, const S* Cbase, float* plane,
                                         const float* pcol, const float* pct, S* yout, float* yf, bool rev, bool col, bool add,
                                         bool last, float bias,
                                         float dsk, int c0, int L, int H, int W, int N) {
@@ -895,7 +937,7 @@ __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid
   constexpr int SS = seg_stride<TT>();
   const int l0 = c0 + ln.seg * TT;
   float dtv[TT], uv[TT];
-  load_inputs<S, TT, VEC, false>(dtrow, xrow, rev, col, l0, L, H, W, dtv, uv);
+  load_inputs<S, TT, VEC, false>(dsrc, xrow, rev, col, l0, L, H, W, dtv, uv);
   float delta[TT], du[TT], yv[TT];
   const float sdelta = prepare_steps<TT>(dtv, uv, bias, dsk, ln.dvalid, L - l0, delta, du, yv);
   for (int n0 = 0; n0 < N; n0 += NG) {
@@ -924,7 +966,8 @@ __device__ __forceinline__ void tail_chunk(int tid, int seg, int dl, bool dvalid
 // dt (one plain row per channel) at dts, Bs then Cs (kMaxN plain rows each) at
 // bcs, and x already in uv.  No global load waits here.
 template <typename S, int G, int TT, bool VEC>
-__device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, const char* bcs, const float (&uv)[TT],
+__device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, int R, const float* wl, const char* bcs,
+                                               const float (&uv)[TT],
                                                const float* a2s, float* carry, float* plane, const float* pcol,
                                                const float* pct, S* yout, float* yf, bool rev, bool add, bool last, float bias,
                                                float dsk, int c0,
@@ -932,7 +975,20 @@ __device__ __forceinline__ void tail_chunk_lds(const Lane& ln, const char* dts, 
   constexpr int RB = G * TT * (int)sizeof(S);
   const int l0 = c0 + ln.seg * TT;
   float dtv[TT];
-  read_plain<S, TT>(dts + ln.dl * RB, ln.seg, dtv);
+  if (R == 0) {
+    read_plain<S, TT>(dts + ln.dl * RB, ln.seg, dtv);
+  } else {  // low-rank rows 0..R-1 of the plain copy, weighted by the channel's weights
+#pragma unroll
+    for (int i = 0; i < TT; ++i) dtv[i] = 0.f;
+#pragma unroll 1
+    for (int r = 0; r < R; ++r) {
+      float v[TT];
+      read_plain<S, TT>(dts + r * RB, ln.seg, v);
+      const float w = wl[r];
+#pragma unroll
+      for (int i = 0; i < TT; ++i) dtv[i] = fmaf(w, v[i], dtv[i]);
+    }
+  }
   float delta[TT], du[TT], yv[TT];
   const float sdelta = prepare_steps<TT>(dtv, uv, bias, dsk, true, L - l0, delta, du, yv);
 #pragma unroll 1
@@ -977,6 +1033,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   float* biass = carry + CH * kMaxN;
   float* dss = biass + CH;
   float* aprod = dss + CH;
+  float* wts = aprod + CH * kMaxN;  // low-rank weights: [CH][kMaxLowRank]
 
   // Work id: consecutive ids (same batch and segment, neighbouring channel blocks,
   // which share Bs/Cs) stay on one XCD; workgroups are dealt round-robin over the
@@ -1051,6 +1108,11 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       biass[i] = dg < D ? p.dt_bias[slot * D + dg] : 0.f;
       dss[i] = (dg < D && p.skip) ? p.Ds[slot * D + dg] : 0.f;
     }
+    for (int i = ln.tid; i < CH * kMaxLowRank; i += NTH) {
+      const int dd = i / kMaxLowRank, r = i - dd * kMaxLowRank;
+      const int dg = ln.d0 + dd;
+      wts[i] = (dg < D && r < p.R) ? p.wdt[(int64_t)(slot * D + dg) * p.R + r] : 0.f;
+    }
     __syncthreads();
 
     constexpr bool rev = k >= 2, col = (k & 1) != 0, last = k == 2;
@@ -1062,8 +1124,14 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     S* yout = static_cast<S*>(p.y) + plane_off;
     // bf16 state blocks before the last keep fp32 sums in the row plane
     float* yf = (sizeof(S) != 4 && !p.final_out) ? p.prow + plane_off : nullptr;
-    const S* dtdir = static_cast<const S*>(p.dt) + (int64_t)(ln.b * p.K + slot) * D * L;
-    const S* dtrow = dtdir + (int64_t)ln.dsafe * L;
+    // dt rows of this (batch, direction), or its R low-rank rows
+    const int drows_all = p.R > 0 ? p.R : D;
+    const S* dtdir = static_cast<const S*>(p.dt) + (int64_t)(ln.b * p.K + slot) * drows_all * L;
+    DtSrc<S> dsrc;
+    dsrc.row = dtdir + (int64_t)(p.R > 0 ? 0 : ln.dsafe) * L;
+    dsrc.lr = dtdir;
+    dsrc.w = wts + ln.dl * kMaxLowRank;
+    dsrc.R = p.R;
     // column walks over the transposed copy of x read contiguous rows; direction 2
     // reads a transposed column plane when there is one
     const bool xt = col && p.xT != nullptr;
@@ -1085,10 +1153,14 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
       // stands in past N).  Resources cover this (batch, direction) only.
       const int nval = D - ln.d0 < CH ? D - ln.d0 : CH;
       const uint32_t rowsz = (uint32_t)L * (uint32_t)sizeof(S);
-      const __amdgpu_buffer_rsrc_t rdt = make_rsrc(dtdir + (int64_t)ln.d0 * L, (uint32_t)nval * rowsz);
+      // staged dt rows: the block's channels (a valid row stands in past D), or the
+      // R low-rank rows (row 0 stands in for the CH - R rows past them)
+      const int nrow = p.R > 0 ? p.R : nval;
+      const __amdgpu_buffer_rsrc_t rdt =
+          make_rsrc(dtdir + (int64_t)(p.R > 0 ? 0 : ln.d0) * L, (uint32_t)nrow * rowsz);
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bbase, (uint32_t)N * rowsz);
       const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cbase, (uint32_t)N * rowsz);
-      auto dt_rows = [=](int r) { return RowRef{rdt, (uint32_t)(r < nval ? r : 0) * rowsz}; };
+      auto dt_rows = [=](int r) { return RowRef{rdt, (uint32_t)(r < nrow ? r : 0) * rowsz}; };
       auto bc_rows = [=](int g) {
         return [=](int r) {
           const int n = g * NG + (r < NG ? r : r - NG);
@@ -1181,7 +1253,20 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
         constexpr bool PART = decltype(part_c)::value;
         rotate_priority();
         float dtn[T];
-        read_seg<S, T>(dtb + ln.dl * GT * (int)sizeof(S), ln.seg, dtn);
+        if (p.R == 0) {
+          read_seg<S, T>(dtb + ln.dl * GT * (int)sizeof(S), ln.seg, dtn);
+        } else {  // dt from the staged low-rank rows and the channel's weights
+#pragma unroll
+          for (int i = 0; i < T; ++i) dtn[i] = 0.f;
+#pragma unroll 1
+          for (int r = 0; r < p.R; ++r) {
+            float v[T];
+            read_seg<S, T>(dtb + r * GT * (int)sizeof(S), ln.seg, v);
+            const float w = dsrc.w[r];
+#pragma unroll
+            for (int i = 0; i < T; ++i) dtn[i] = fmaf(w, v[i], dtn[i]);
+          }
+        }
         float delta[T], du[T], yv[T];
         // Lanes of a channel past D work on channel d0's data and store nothing; a
         // group of G lanes never mixes channels, so no masking is needed here.
@@ -1263,7 +1348,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
             float uv[TT];
 #pragma unroll
             for (int i = 0; i < TT; ++i) uv[i] = xn[i];
-            tail_chunk_lds<S, G, TT, VEC>(ln, dtb, bcs, uv, a2s, carry, plane, pcol, pct, yout, yf, rev, add, last, bias,
+            tail_chunk_lds<S, G, TT, VEC>(ln, dtb, p.R, wts + ln.dl * kMaxLowRank, bcs, uv, a2s, carry, plane, pcol, pct, yout, yf, rev, add, last, bias,
                                           dsk, c0, L, H, W, N);
           }
         };
@@ -1279,7 +1364,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
     } else {
       // ---------------- rows not 16-byte aligned: every chunk staged through registers
       for (; c0 + GT <= L; c0 += GT)
-        tail_chunk<S, G, T, NG, T, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+        tail_chunk<S, G, T, NG, T, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dsrc, xsrc, Bbase, Cbase,
                                         plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
     }
 
@@ -1305,22 +1390,22 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
 
     // ---------------- remainder chunks (fewer steps per lane)
     while (L - c0 >= G * 8) {
-      tail_chunk<S, G, T, NG, 8, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 8, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dsrc, xsrc, Bbase, Cbase,
                                       plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 8;
     }
     if (L - c0 >= G * 4) {
-      tail_chunk<S, G, T, NG, 4, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 4, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dsrc, xsrc, Bbase, Cbase,
                                       plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 4;
     }
     if (L - c0 >= G * 2) {
-      tail_chunk<S, G, T, NG, 2, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 2, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dsrc, xsrc, Bbase, Cbase,
                                       plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G * 2;
     }
     while (c0 < L) {
-      tail_chunk<S, G, T, NG, 1, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dtrow, xsrc, Bbase, Cbase,
+      tail_chunk<S, G, T, NG, 1, VEC, Y::kRing0Bytes>(ln.tid, ln.seg, ln.dl, ln.dvalid, smem, a2s, carry, dsrc, xsrc, Bbase, Cbase,
                                       plane, pcol, pct, yout, yf, rev, xcol, add, last, bias, dsk, c0, L, H, W, N);
       c0 += G;
     }
@@ -1513,6 +1598,8 @@ hipError_t launch_variant(const LaunchArgs& a, const Plan& plan, const Scratch& 
   p.nseg = plan.nseg;
   p.kdir = 0;
   p.K = a.K;
+  p.R = a.R;
+  p.wdt = a.wdt;
   p.Nt = (int)a.Nt;
   p.n0 = (int)a.n0;
   p.skip = a.skip ? 1 : 0;

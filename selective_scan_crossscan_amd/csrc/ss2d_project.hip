@@ -49,6 +49,7 @@ struct ProjParams {
   void* dt;          // (B, 4, D, L)
   void* Bs;          // (B, 4, N, L)
   void* Cs;          // (B, 4, N, L)
+  void* dts;         // (B, 4, R, L) or null: write the low-rank rows instead of the dt map
   int D, L, N, R, C, strips;
   int tiles;  // 16-row tiles of the 2C stacked rows
 };
@@ -176,8 +177,11 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
         const int kk = m >= C ? 1 : 0;
         const int c = m - kk * C;
         const float4 v = make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
-        if (c < R) {
+        if (c < R && p.dts == nullptr) {
           *reinterpret_cast<float4*>(dts + (kk * R + c) * kStrip + 4 * col) = v;
+        } else if (c < R) {  // the low-rank rows themselves, in scan order
+          const int64_t bk = (int64_t)b * 4 + o + 2 * kk;
+          put4<S, VEC>(static_cast<S*>(p.dts) + (bk * R + c) * L, pos, L, kk == 1, v);
         } else {
           const int64_t bk = (int64_t)b * 4 + o + 2 * kk;
           S* row = c < R + N ? static_cast<S*>(p.Bs) + (bk * N + (c - R)) * L
@@ -187,6 +191,7 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
       }
     }
   }
+  if (p.dts != nullptr) return;  // the scan forms dt from the low-rank rows itself
   __syncthreads();
 
   // dt = W_dt (D x R) times the R rows, per direction, 16 channels at a time.
@@ -266,6 +271,7 @@ hipError_t launch_project(const ProjectArgs& a) {
   p.dt = a.dt;
   p.Bs = a.Bs;
   p.Cs = a.Cs;
+  p.dts = a.dts;
   p.D = (int)a.D;
   p.L = (int)(a.H * a.W);
   p.N = (int)a.N;
@@ -276,10 +282,11 @@ hipError_t launch_project(const ProjectArgs& a) {
   if (p.tiles > kMaxTiles) return hipErrorInvalidValue;
   const int64_t blocks = a.B * 2 * p.strips;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  const size_t lds = (size_t)2 * p.R * kStrip * sizeof(float);
+  const size_t lds = a.dts ? 0 : (size_t)2 * p.R * kStrip * sizeof(float);
   const uintptr_t am = a.dtype == 0 ? 15 : 7;
+  const void* dtout = a.dts ? a.dts : a.dt;
   const bool vec = p.L % 4 == 0 && p.D % 4 == 0 && !((uintptr_t)a.x & am) && !((uintptr_t)a.xT & am) &&
-                   !((uintptr_t)a.dt & am) && !((uintptr_t)a.Bs & am) && !((uintptr_t)a.Cs & am) &&
+                   !((uintptr_t)dtout & am) && !((uintptr_t)a.Bs & am) && !((uintptr_t)a.Cs & am) &&
                    !((uintptr_t)a.wx & 15);
   if (a.dtype == 0)
     return vec ? launch_tiles<float, true>(p, (unsigned)blocks, lds, a.stream)

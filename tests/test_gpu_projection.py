@@ -119,9 +119,9 @@ def test_forward_from_x_segmented_map():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_forward_from_x_equals_forward_on_projected_inputs(dtype):
-    # same projections, same scan arithmetic: reading x through the transposed
-    # copy must not change a bit
-    inp = _inputs(2, 32, 12, 20, 16, 2, dtype, seed=9)
+    # rank 9 (past the low-rank input's limit of 8): same projections, same scan
+    # arithmetic, so reading x through the transposed copy must not change a bit
+    inp = _inputs(2, 32, 12, 20, 16, 9, dtype, seed=9)
     d = _dev(inp, dtype)
     ss2d = _lib()
     y1 = ss2d.forward_from_x(d["x"], d["x_proj_weight"], d["dt_projs_weight"], d["A_log"], d["dt_bias"], d["Ds"])
@@ -131,6 +131,37 @@ def test_forward_from_x_equals_forward_on_projected_inputs(dtype):
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert torch.equal(y1, y3)
+
+
+# Ranks up to 8 hand the scan the low-rank rows, which forms dt itself (R FMAs per
+# channel and step): fused plans with remainder chunks, a prefetched remainder,
+# the register-staged path (L % 4 != 0), a segmented plan, bf16, R at the limit.
+LOW_RANK = [
+    (1, 16, 40, 40, 16, 6, "f32"),   # 1600 steps: 3 chunks and a prefetched 64-step remainder
+    (2, 24, 9, 14, 16, 3, "f32"),    # L % 4 != 0: every chunk through the register-staged path
+    (1, 32, 28, 28, 16, 8, "bf16"),  # R = 8, bf16, 16 lanes
+    (1, 16, 72, 72, 16, 4, "f32"),   # segmented: the carry pass and the per-direction launches
+    (2, 40, 14, 14, 7, 5, "f32"),    # one partial chunk, odd N
+]
+
+
+@pytest.mark.parametrize("shape", LOW_RANK, ids=lambda s: "x".join(map(str, s)))
+def test_forward_from_x_low_rank_input(shape):
+    """The low-rank path against the oracle, and against the forward on the projected
+    inputs (dt formed by the projection kernel) to the forward's tolerances."""
+    B, D, H, W, N, R, dtype = shape
+    print(f"[from_x low rank] {shape} {_lib().describe(B, D, H, W, N, 1 if dtype == 'bf16' else 0)}", flush=True)
+    inp = _inputs(B, D, H, W, N, R, dtype, seed=R + H)
+    y = _check_forward(inp, dtype).double().cpu().numpy()
+    d = _dev(inp, dtype)
+    ss2d = _lib()
+    dt, Bs, Cs = ss2d.project(d["x"], d["x_proj_weight"], d["dt_projs_weight"], N)
+    y2 = ss2d.forward(d["x"], dt, d["A_log"], d["dt_bias"], Bs, Cs, d["Ds"])
+    torch.cuda.synchronize()
+    y2 = y2.double().cpu().numpy()
+    rel = float(np.linalg.norm(y - y2) / np.linalg.norm(y2))
+    print(f"[from_x low rank] vs forward on projected inputs: rel_l2 {rel:.3e}", flush=True)
+    assert rel <= (2e-2 if dtype == "bf16" else 1e-5)
 
 
 @pytest.mark.parametrize("cfg", [1, 3], ids=["vmamba_t_stage1", "vmamba_t_stage2_bf16"])
