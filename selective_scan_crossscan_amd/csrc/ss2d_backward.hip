@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   __shared__ float sB[16][kPad];
   __shared__ float sC[16][kPad];
   __shared__ float wred[2][4][2][kPad];    // [state parity][wave][dCs, dBs][step]: the waves' four-channel sums
-  __shared__ float acc[CPB > 1 ? 16 : 1][256];  // [state][thread]: the earlier blocks' sums at the thread's step
+  __shared__ float acc[16][256];  // [state][thread]: the sums at the thread's step, over the blocks so far
   // The blocks take turns in one register set: after each block the thread swaps
   // it with its stash slot (the other block's, CPB = 2), so the loop over blocks
   // stays rolled and the registers those of one block.
@@ -265,28 +265,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     xi = in ? (k >= 2 ? L - 1 - l : l) : 0;
     return in;
   };
+  // Every load is issued first, at in-bounds (clamped) indices, so that all of
+  // them are in flight together; steps past the end are zeroed afterwards.
+  // (Loads under a per-step condition were issued and waited for one by one.)
   auto load_lane = [&](const BwdChan<S>& cn, int c, bool with_g) {
+    float dtv[kCT];
+    bool inr[kCT];
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
       int li, xi;
-      const bool in = lane_step(cn, c, i, li, xi);
-      const float pre = Io<S>::ld(cn.dtr, li) + cn.bias;
+      inr[i] = lane_step(cn, c, i, li, xi);
+      dtv[i] = Io<S>::ld(cn.dtr, li);
+      uu[i] = Io<S>::ld(cn.xs, xi);
+      gg[i] = with_g ? Io<S>::ld(cn.gs, xi) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) {
+      const float pre = dtv[i] + cn.bias;
+      const bool in = inr[i];
       del[i] = in ? softplus_f32(pre) : 0.f;
-      uu[i] = in ? Io<S>::ld(cn.xs, xi) : 0.f;
+      uu[i] = in ? uu[i] : 0.f;
       sig[i] = in ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-pre * kLog2e)) : 0.f;  // 1-ulp reciprocal
       xu[i] = del[i] * uu[i];
-      gg[i] = in && with_g ? Io<S>::ld(cn.gs, xi) : 0.f;
+      gg[i] = in ? gg[i] : 0.f;
     }
   };
+  // Bs (and Cs) of chunk c into LDS: element e = tid + 256 r is state 2 r + tid / 128
+  // at step tid % 128, so a wave reads 64 consecutive steps of one state row.  All
+  // of a thread's loads are in flight together, as in load_lane; the row offsets
+  // are wave-uniform (scalar), and past the end the address is clamped in bounds.
   auto stage = [&](int c, bool with_c) {
-    for (int e = tid; e < 16 * kChunk; e += 256) {
-      const int n = e / kChunk, j = e - n * kChunk;
-      const int l = c * kChunk + j;
+    constexpr int kPer = 16 * kChunk / 256;  // elements per thread and tensor
+    const int hi = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int j = tid & (kChunk - 1), l = c * kChunk + j;
+    const int lc = l < L ? l : L - 1;
+    float vb[kPer], vc[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int n = 2 * r + hi, nc = n < N ? n : N - 1;
+      vb[r] = Io<S>::ld(Bb + lc, (int64_t)nc * L);
+      vc[r] = with_c ? Io<S>::ld(Cb + lc, (int64_t)nc * L) : 0.f;
+    }
+    const int jp = j + j / kCT;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int n = 2 * r + hi;
       const bool in = n < N && l < L;
-      const int64_t off = in ? (int64_t)n * L + l : 0;
-      const int jp = j + j / kCT;
-      sB[n][jp] = in ? Io<S>::ld(Bb, off) : 0.f;
-      if (with_c) sC[n][jp] = in ? Io<S>::ld(Cb, off) : 0.f;
+      sB[n][jp] = in ? vb[r] : 0.f;
+      if (with_c) sC[n][jp] = in ? vc[r] : 0.f;
     }
   };
   auto hck = [&](const BwdChan<S>& cn, int c, int n) -> float& {
@@ -320,34 +346,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
           if (cn.valid) cdl(cn, c) = cum + (incl - sdel);
           cum += row_lane(incl, 15);
         }
-        for (int n = 0; n < N; ++n) {
-          const float A2 = row_lane(rr.a2, n);
-          const float Pl = __builtin_amdgcn_exp2f(A2 * sdel);
-          float P = Pl, Q = 0.f, a[kCT];
+        // Two states per iteration (n and n1 = n + 1, or n again for an odd last
+        // one): their chains are independent, so the scheduler can interleave them.
+        // Every LDS and cross-lane read of both comes first (the scans' asm blocks
+        // order memory accesses around them); stores and lane updates come after
+        // both.  Lane n1's carried state is read before lane n's is updated, which
+        // it does not depend on.
+        for (int n = 0; n < N; n += 2) {
+          const int n1 = n + 1 < N ? n + 1 : n;
+          const int nn[2] = {n, n1};
+          float hin[2], hout[2], Pb0[2], R0[2], A2v[2], hcv[2], bv[2][kCT], cv[2][kCT];
 #pragma unroll
-          for (int i = 0; i < kCT; ++i) {
-            a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
-            Q = fmaf(a[i], Q, xu[i] * sB[n][jp0 + i]);
-          }
-          if (seg) {
-            // the lane's adjoint map r -> Pl r + R (r enters after its last step),
-            // composed over the row: lane 0 holds the chunk's
-            float Pb = Pl, R = 0.f;
+          for (int t = 0; t < 2; ++t) {
+            A2v[t] = row_lane(rr.a2, nn[t]);
+            hcv[t] = row_lane(rr.h, nn[t]);
 #pragma unroll
-            for (int i = kCT - 1; i >= 0; --i) R = a[i] * fmaf(sC[n][jp0 + i], gg[i], R);
-            scan_suffix16(Pb, R);
-            const float Pb0 = row_lane(Pb, 0), R0 = row_lane(R, 0);
-            if (s == n) {  // the chunks so far, then this one: (ap, aq) o (Pb0, R0)
-              rr.aq = fmaf(rr.ap, R0, rr.aq);
-              rr.ap *= Pb0;
+            for (int i = 0; i < kCT; ++i) {
+              bv[t][i] = sB[nn[t]][jp0 + i];
+              cv[t][i] = seg ? sC[nn[t]][jp0 + i] : 0.f;
             }
           }
-          scan_inclusive<16>(P, Q);
-          const float hc = row_lane(rr.h, n);
-          const float hin = incoming_state<16>(P, Q, hc, s);
-          if (cn.valid) hck(cn, c, n) = hin;
-          const float hout = row_lane(fmaf(P, hc, Q), 15);  // the state leaving the chunk (lane 15's)
-          if (s == n) rr.h = hout;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float A2 = A2v[t], hc = hcv[t];
+            const float Pl = __builtin_amdgcn_exp2f(A2 * sdel);
+            float P = Pl, Q = 0.f, a[kCT];
+#pragma unroll
+            for (int i = 0; i < kCT; ++i) {
+              a[i] = __builtin_amdgcn_exp2f(del[i] * A2);
+              Q = fmaf(a[i], Q, xu[i] * bv[t][i]);
+            }
+            if (seg) {
+              // the lane's adjoint map r -> Pl r + R (r enters after its last step),
+              // composed over the row: lane 0 holds the chunk's
+              float Pb = Pl, R = 0.f;
+#pragma unroll
+              for (int i = kCT - 1; i >= 0; --i) R = a[i] * fmaf(cv[t][i], gg[i], R);
+              scan_suffix16(Pb, R);
+              Pb0[t] = row_lane(Pb, 0);
+              R0[t] = row_lane(R, 0);
+            }
+            scan_inclusive<16>(P, Q);
+            hin[t] = incoming_state<16>(P, Q, hc, s);
+            hout[t] = row_lane(fmaf(P, hc, Q), 15);  // the state leaving the chunk (lane 15's)
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if (t == 1 && n1 == n) break;
+            const int m = nn[t];
+            if (seg && s == m) {  // the chunks so far, then this one: (ap, aq) o (Pb0, R0)
+              rr.aq = fmaf(rr.ap, R0[t], rr.aq);
+              rr.ap *= Pb0[t];
+            }
+            if (s == m) rr.h = hout[t];
+            if (cn.valid) hck(cn, c, m) = hin[t];
+          }
         }
         next_block();
       }
@@ -369,6 +422,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   // Per step, over the states: tq = sum_n q Bs and sa = sum_n q A a h_{l-1}, so
   // that du = delta tq + Ds g and ddelta = sa + u tq take no per-state product.
   int par = 0;  // consecutive states use alternate wred buffers
+  // The four waves' sums of state n (buffer b) at this thread's step, added to
+  // the earlier blocks' in the thread's own accumulator entry.
+  auto wave_sums = [&](int b, int n, int cb) {
+    const float sum = ((wred[b][0][which][jpo] + wred[b][1][which][jpo]) + wred[b][2][which][jpo]) +
+                      wred[b][3][which][jpo];
+    acc[n][tid] = cb > 0 ? acc[n][tid] + sum : sum;  // the earlier blocks first
+  };
   for (int c = c1 - 1; c >= c0; --c) {
     stage(c, true);
     const int lo = c * kChunk + jo;  // this thread's dCs/dBs step
@@ -384,12 +444,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 #pragma unroll
       for (int i = 1; i < kCT; ++i) sd1 += del[i];
       const float cum = MODE == kSegGrads && cn.valid ? cdl(cn, c) : 0.f;
+      // the stored state of the next state index is loaded one iteration ahead
+      // (the channel index is clamped, so the address is in bounds)
+      // and what it reads from the row's other lanes likewise (lane n + 1's carries
+      // are not changed by iteration n, which only updates lane n's)
+      float h_next = hck(cn, c, 0);
+      float A2n = row_lane(rr.a2, 0), acn = row_lane(rr.a, 0), qcn = row_lane(rr.q, 0);
+      float hsn = MODE == kSegGrads ? row_lane(rr.h, 0) : 0.f;
       for (int n = 0; n < N; ++n) {
-        const float A2 = row_lane(rr.a2, n), A = A2 * kLn2;
+        const float A2 = A2n, A = A2 * kLn2, acar = acn, qcar = qcn, hseg = hsn;
         float a[kCT], h[kCT], cg[kCT];
-        float h_in = cn.valid ? hck(cn, c, n) : 0.f;
+        float h_in = cn.valid ? h_next : 0.f;
+        if (n + 1 < N) {
+          h_next = hck(cn, c, n + 1);
+          A2n = row_lane(rr.a2, n + 1);
+          acn = row_lane(rr.a, n + 1);
+          qcn = row_lane(rr.q, n + 1);
+          if (MODE == kSegGrads) hsn = row_lane(rr.h, n + 1);
+        }
         // a segment's stored states start from zero: add the entering state's decayed part
-        if (MODE == kSegGrads) h_in = fmaf(__builtin_amdgcn_exp2f(A2 * cum), row_lane(rr.h, n), h_in);
+        if (MODE == kSegGrads) h_in = fmaf(__builtin_amdgcn_exp2f(A2 * cum), hseg, h_in);
         float hv = h_in;
 #pragma unroll
         for (int i = 0; i < kCT; ++i) {
@@ -397,7 +471,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
           hv = fmaf(a[i], hv, xu[i] * sB[n][jp0 + i]);
           h[i] = hv;
         }
-        const float acar = row_lane(rr.a, n), qcar = row_lane(rr.q, n);
         const float a_right = dppf<kRowShl + 1>(acar, a[0]);  // decay of the step after this lane's last
         // the lane's map q_after -> P q_after + Q: P is the decay over its steps after the first, then a_right
         float P = a_right * __builtin_amdgcn_exp2f(A2 * sd1), Q = 0.f;
@@ -441,22 +514,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 #pragma unroll
           for (int t = 0; t < kCT / 2; ++t) wr[2 * t] = swap_add16(h2[2 * t], h2[2 * t + 1]);
         }
-        // One barrier per state: the next state writes the other buffer, and the one
-        // after it writes this buffer only past the next barrier, which every thread
-        // reaches after reading this one.
+        // The previous state's four wave sums (written before the last barrier) are
+        // summed while this state's are being written; one barrier per state: the
+        // next state writes the other buffer, and the one after it writes this one
+        // only past the next barrier, which every thread reaches after reading it.
+        if (n > 0) wave_sums(par ^ 1, n - 1, cb);
         __syncthreads();
-        if (lo < L) {
-          float sum = ((wred[par][0][which][jpo] + wred[par][1][which][jpo]) + wred[par][2][which][jpo]) +
-                      wred[par][3][which][jpo];
-          if (cb > 0) sum = acc[n][tid] + sum;  // the earlier blocks first
-          if (cb + 1 < CPB) {
-            acc[n][tid] = sum;  // this thread's own entry
-          } else {
-            float* dst = which == 0 ? p.dCp : p.dBp;
-            dst[(((int64_t)bk * ngrp + blk0 / CPB) * N + n) * L + lo] = sum;
-          }
-        }
         par ^= 1;
+      }
+      wave_sums(par ^ 1, N - 1, cb);
+      if (cb + 1 == CPB && lo < L) {
+        // the workgroup's partial, one row per state, written after the state loop
+        // (no global store inside it, so its only memory wait is the prefetched state)
+        float* dst = (which == 0 ? p.dCp : p.dBp) + ((int64_t)bk * ngrp + blk0 / CPB) * N * L + lo;
+        for (int n = 0; n < N; ++n) dst[(int64_t)n * L] = acc[n][tid];
       }
 #pragma unroll
       for (int i = 0; i < kCT; ++i) {
