@@ -215,8 +215,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   __shared__ BwdRegs stash[CPB > 1 ? 256 : 1];
   static_assert(CPB == 1 || CPB == 2, "one or two channel blocks per workgroup");
   const int tid = threadIdx.x, s = tid & 15, ch = tid >> 4;
-  const int sg = blockIdx.x % p.nsp;
-  const int grp = blockIdx.x / p.nsp;
+  // Workgroups are dealt round-robin over the 8 XCDs; consecutive work ids (the
+  // segments and channel groups of one batch and direction, which read the same
+  // Bs/Cs, then the directions of one batch, which read the same x and dy) are
+  // put on one XCD, so that they share its L2.
+  const int nb = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = nb >> 3, rem = nb & 7;
+  const int wid = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int sg = wid % p.nsp;
+  const int grp = wid / p.nsp;
   const int ngrp = (p.nblk + CPB - 1) / CPB;
   const int blk0 = (grp % ngrp) * CPB;  // this workgroup's first channel block
   const int bk = grp / ngrp;            // b * 4 + k
@@ -650,11 +656,14 @@ __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_lo
   const int e = blockIdx.x * 256 + threadIdx.x;  // (c, n)
   if (e >= C4 * N) return;
   const int c = e / N, n = e - c * N;
+  // sums in batch order; unrolled so that eight loads are in flight at a time
   float s = 0.f;
+#pragma unroll 8
   for (int b = 0; b < B; ++b) s += dAp[((int64_t)b * C4 + c) * N + n];
   dA_log[e] = -expf(A_log[e]) * s;
   if (n == 0) {
     float sb = 0.f, sd = 0.f;
+#pragma unroll 8
     for (int b = 0; b < B; ++b) {
       sb += dbp[(int64_t)b * C4 + c];
       sd += dDp[(int64_t)b * C4 + c];
