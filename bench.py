@@ -100,6 +100,13 @@ def algorithmic_bytes(shape, K: int = 4) -> int:
     return s * shape.B * shape.L * ((2 + K) * shape.D + 2 * K * shape.N) + 4 * K * shape.D * (shape.N + 2)
 
 
+def backward_algorithmic_bytes(shape) -> int:
+    """Bytes the backward must move: x, dy, dt, Bs, Cs read once, dx, ddt, dBs, dCs written
+    once (storage type), and the fp32 parameters read and their gradients written."""
+    s = shape.elem_bytes
+    return s * shape.B * shape.L * (11 * shape.D + 16 * shape.N) + 2 * 4 * 4 * shape.D * (shape.N + 2)
+
+
 def _record(path: str):
     try:
         with open(path) as f:
@@ -291,7 +298,7 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
         work = (f"Epilogue per launch: algorithmic bytes {alg_bytes:.4e} (y read once, the channel-last output "
                 "written once, gamma and beta).")
     elif bwd:
-        alg_bytes = 4 * shape.B * shape.L * (11 * shape.D + 16 * shape.N)
+        alg_bytes = backward_algorithmic_bytes(shape)
         work = (f"Backward per launch: {shape.updates:.4e} (b,k,d,n,l) terms; algorithmic bytes {alg_bytes:.4e} "
                 "(x, dy, dt, Bs, Cs read once; dx, ddt, dBs, dCs written once).")
     else:
@@ -622,7 +629,7 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     step_s = ev_ms * 1e-3 / args.steps  # all launches of one step, same stream
     updates = K * shape.B * shape.D * shape.L * shape.N
-    alg_bytes = algorithmic_bytes(shape, K)
+    alg_bytes = backward_algorithmic_bytes(shape) if bwd else algorithmic_bytes(shape, K)
     value = updates * args.steps / wall
     achieved = updates / step_s
     hbm_gbps = alg_bytes / step_s / 1e9
