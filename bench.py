@@ -334,6 +334,17 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
     kern_avg = kern_total / n_exec
     per_step = step_total / n_exec
+    if from_x:
+        # the run's projection launches in time order: first those inside the forward from x
+        # (warm-up, timed and flushed steps), then ss2d_project alone (warm-up and timed)
+        with open(_find(folder, "stats_kernel_trace.csv")) as f:
+            tr = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in csv.DictReader(f)
+                        if _is_kernel(r["Kernel_Name"], kernel))
+        n_fx = bench["warmup"] + bench["steps"] + (bench.get("flushed") or {}).get("steps", 0)
+        fx_us = [(e - b) / 1e3 for b, e in tr[:n_fx]]
+        alone_us = [(e - b) / 1e3 for b, e in tr[n_fx:]]
+        fx_avg, kern_avg = sum(fx_us) / len(fx_us), sum(alone_us) / len(alone_us)
+        lowrank = ss2d_inputs.default_rank(shape.D) <= FROM_X_LOWRANK_MAX
     lines += ["", f"bench.py's own HIP-event average over the timed steps of this run: "
                   f"{bench['kernel_us']:.1f} µs per step (roofline frac {bench['roofline']['frac']:.3f}).",
               f"rocprofv3, summed over the run's {n_exec} executions of the path (warm-up and flushed steps "
@@ -347,17 +358,28 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
                   f"({alg_bytes / (kern_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s).", ""]
     if from_x:
         pj = bench["projection"]
-        lines += [f"The projection alone, timed by bench.py with HIP events (transpose of x + {kernel}): "
-                  f"{pj['us']:.1f} µs; {kernel} by rocprofv3: {kern_avg:.1f} µs, i.e. "
+        lr_bytes = lowrank_projection_bytes(shape)
+        lines += [f"The projection alone (ss2d_project, the dt map written), timed by bench.py with HIP events "
+                  f"(transpose of x + {kernel}): {pj['us']:.1f} µs; its {len(alone_us)} launches of {kernel} by "
+                  f"rocprofv3: {kern_avg:.1f} µs on average, i.e. "
                   f"{alg_flops / (kern_avg * 1e-6) / 1e12:.1f} TFLOP/s "
                   f"({alg_flops / (kern_avg * 1e-6) / FP32_MFMA_PEAK:.3f} of the fp32 MFMA peak) and "
                   f"{alg_bytes / (kern_avg * 1e-6) / 1e9:.0f} GB/s of algorithmic bytes "
-                  f"({alg_bytes / (kern_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s).", ""]
+                  f"({alg_bytes / (kern_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s).",
+                  f"Inside the forward from x ({len(fx_us)} launches): {fx_avg:.1f} µs on average"
+                  + (f"; at rank {ss2d_inputs.default_rank(shape.D)} it writes the low-rank rows instead of the "
+                     f"dt map ({lr_bytes / 1e6:.1f} MB algorithmic, "
+                     f"{lr_bytes / (fx_avg * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s)." if lowrank
+                     else " (the same dt map: the rank is above the scan's low-rank limit)."), ""]
     lines += ["Bench line of this run:", "", "```", bench_line, "```", ""]
     krec = {"workload": workload, "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
             "kernel_avg_us": kern_avg, "step_kernels_us": per_step, "executions": n_exec,
             "note": "kernel_avg_us: the kernel's summed duration per execution of the path (all its launches "
                     "in one step)"}
+    if from_x:
+        krec["from_x_avg_us"] = fx_avg
+        krec["note"] = ("kernel_avg_us: ss2d_project alone (the dt map); from_x_avg_us: the launches inside the "
+                        "forward from x")
     lines += ["Record read by bench.py (valid only while the kernel sources hash to the value below):", "",
               "```json", json.dumps(krec, indent=1), "```", ""]
     with open(kernel_stats_file(workload, kernel), "w") as f:
@@ -368,12 +390,17 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
     per = {}
     for counter, prefix in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = [r for r in _counter_rows(folder, prefix) if r["Counter_Name"] == counter]
-        vals = [float(r["Counter_Value"]) for r in rows if any(_is_kernel(r["Kernel_Name"], k) for k in names)]
+        kr = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                    if any(_is_kernel(r["Kernel_Name"], k) for k in names))
+        if from_x:
+            # the counter runs: 1 + 3 steps of the forward from x, then 1 + 3 of ss2d_project alone
+            kr = kr[len(kr) // 2:]
+        vals = [v for _, v in kr]
         copies = [(float(r["Counter_Value"]), r["Kernel_Name"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         probe_kib, probe_name = max(copies)
         expected_kib = COPY_PROBE_MIB * 1024.0
         # the counter runs time 3 steps after 1 warm-up step, no flushed steps
-        n_cnt = executions(3, 1, 0)
+        n_cnt = 4 if from_x else executions(3, 1, 0)
         per[counter] = {"kernel_kib_per_step": sum(vals) / n_cnt, "dispatches": len(vals), "executions": n_cnt,
                         "copy_probe_kib": probe_kib, "copy_probe_kernel": probe_name,
                         "copy_expected_kib": expected_kib, "scale": expected_kib / probe_kib}
@@ -389,7 +416,9 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
              f"Each run also performs one {COPY_PROBE_MIB} MiB device-to-device copy; the scale factor is the "
              "copy's known size divided by what the same counter reads for it.  The kernel's figures are "
              "summed over all its dispatches in the run and divided by the executions of the path (3 timed "
-             "steps and 1 warm-up), i.e. per step, all of the step's launches of the kernel.", "",
+             "steps and 1 warm-up), i.e. per step, all of the step's launches of the kernel"
+             + (" (for the projection: the launches of ss2d_project alone, which writes the dt map)." if from_x
+                else "."), "",
              "| counter | kernel KiB / step | copy probe KiB | copy expected KiB | scale | kernel bytes |",
              "|---|---|---|---|---|---|"]
     for counter, b in (("FETCH_SIZE", fetch_b), ("WRITE_SIZE", write_b)):
@@ -406,6 +435,20 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
     print(f"wrote profiles for {workload}: {kernel} avg {kern_avg:.1f} us, step {per_step:.1f} us, "
           f"traffic {(fetch_b + write_b) / 1e6:.1f} MB")
     return 0
+
+
+# ranks up to which the forward from x has the scan form dt from the low-rank rows
+# (the library's own limit; ss2d_describe does not report it)
+FROM_X_LOWRANK_MAX = 8
+
+
+def lowrank_projection_bytes(shape, R=None):
+    """Algorithmic bytes of the projection inside the forward from x at a low rank: x read once,
+    the R low-rank rows, Bs and Cs written once (storage type), fp32 weights."""
+    R = ss2d_inputs.default_rank(shape.D) if R is None else R
+    C = R + 2 * shape.N
+    return (shape.elem_bytes * shape.B * shape.L * (shape.D + 4 * C)
+            + 4 * 4 * (C * shape.D + shape.D * R))
 
 
 def projection_work(shape, R=None):
@@ -454,7 +497,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the SS2D forward shards by (batch, channel) with no exchange; see the design notes)",
+              "(the SS2D forward would shard by (batch, channel) with no exchange between GPUs)",
               file=sys.stderr)
         return 2
 

@@ -439,7 +439,8 @@ int ss2d_forward_from_x(const void* x, const float* x_proj_weight, const float* 
   const ss2d::Plan plan = ss2d::make_plan(B, D, H, W, N, dtype, 0, 4, aligned);
   // Low-rank step input: for small ranks the projection writes the R rows and the
   // scan forms dt from them, instead of writing and reading back the D rows of dt
-  // (measured faster up to kFromXLowRankUpTo; see the design notes).
+  // (measured: faster at rank 6 on 56x56 and 256x256 maps; larger ranks add R
+  // FMAs per channel and step to an ALU-bound scan and keep the dt map).
   const bool lowrank = R <= kFromXLowRankUpTo && R <= ss2d::kMaxLowRankInput && R <= plan.chans_per_block;
   const int64_t dtrows_bytes = lowrank ? B * 4 * R * L * s : dtbytes;
   // one temporary: x transposed, dt (or its low-rank rows), Bs, Cs, then what the scan itself needs
