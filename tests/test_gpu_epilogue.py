@@ -44,7 +44,7 @@ def _dev(a, dtype=None):
 
 
 # (B, D, H, W).  Channel-major fallback tiles (L or D not a multiple of the vector
-# width, D above 956): 64 / 32 / 16 / 1 pixels per workgroup, ragged last tiles, odd
+# width, D above 900): 64 / 32 / 16 / 1 pixels per workgroup, ragged last tiles, odd
 # D, the largest D.  Vector path (16-pixel pixel-major tiles): whole tiles, a 4- or
 # 12-pixel last tile, 256- and 512-thread workgroups, bf16 with 8- and 4-element
 # vectors, D at the vector path's limit (900) and just past it (904).
