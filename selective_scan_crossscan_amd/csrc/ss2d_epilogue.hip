@@ -14,9 +14,11 @@
 // 8 bf16: 16-byte loads) into an LDS tile stored pixel-major, [TP][D + 4], so the
 // output side reads V consecutive channels of a pixel with 16-byte LDS reads and
 // writes them with one vector store; a tile's output rows are one contiguous
-// block.  The statistics are per pixel over K = threads / TP consecutive lanes,
-// mean then squared deviations, each reduced across the K lanes with shuffles
-// (no serial loop, no barrier between the two).  Consecutive tiles run on one
+// block.  The statistics are per pixel over K = threads / TP consecutive lanes:
+// each lane reads its share of the pixel's channels once, with 16-byte LDS
+// reads, into registers, and the mean and then the squared deviations are
+// reduced across the K lanes with shuffles (no second LDS pass, no barrier
+// between the two).  256 threads up to 512 channels, 512 above.  Consecutive tiles run on one
 // XCD (they share 128-byte lines of y).  bf16 output uses the hardware packed
 // round-to-nearest-even conversion.  Other shapes (L or D not a multiple of V,
 // unaligned bases, D above 900) take channel_last_kernel: channel-major tiles
@@ -228,6 +230,8 @@ struct VecIo<uint16_t, 8> {
 
 constexpr int kVecTile = 16;   // pixels per workgroup
 constexpr int kVecMaxD = 900;   // [16][D + 4] fp32 tile plus gamma and beta: up to 64 KB of dynamic LDS
+constexpr int kVecStatF4 = 8;   // 16-byte values per lane in the statistics: D <= 32 K (K lanes per pixel)
+constexpr int kVecNarrowMaxD = 4 * kVecStatF4 * (256 / kVecTile);  // widest D the 256-thread form takes (512)
 
 // Sum over the K consecutive lanes of a group (K a power of two up to 64).
 template <int K>
@@ -293,28 +297,34 @@ __global__ __launch_bounds__(NT) void channel_last_vec_kernel(EpiParams p) {
   __syncthreads();
 
   if (NORM) {
+    // the pixel's channels are read once, 4 at a time (16-byte LDS reads), into
+    // registers: lane q of the pixel's K holds channels 4(q + K m) .. + 3
+    static_assert(4 * K * kVecStatF4 >= (NT == 256 ? kVecNarrowMaxD : kVecMaxD),
+                  "the statistics registers cover every channel the launch allows");
     const int q = tid % K, j = tid / K;
     const float* row = vtile + j * ldd;
-    float s0 = 0.f, s1 = 0.f;
-    int dd = q;
-    for (; dd + K < D; dd += 2 * K) {
-      s0 += row[dd];
-      s1 += row[dd + K];
+    const int D4 = D >> 2;
+    float4 xv[kVecStatF4];
+    float sum = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < kVecStatF4; ++mm) {
+      const int c4 = q + K * mm;
+      xv[mm] = c4 < D4 ? *reinterpret_cast<const float4*>(row + 4 * c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      sum += (xv[mm].x + xv[mm].y) + (xv[mm].z + xv[mm].w);
     }
-    if (dd < D) s0 += row[dd];
-    const float m = lane_group_sum<K>(s0 + s1) / (float)D;
-    float c0 = 0.f, c1 = 0.f;
-    dd = q;
-    for (; dd + K < D; dd += 2 * K) {
-      const float a0 = row[dd] - m, a1 = row[dd + K] - m;
-      c0 = fmaf(a0, a0, c0);
-      c1 = fmaf(a1, a1, c1);
+    const float m = lane_group_sum<K>(sum) / (float)D;
+    float sq = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < kVecStatF4; ++mm) {
+      if (q + K * mm < D4) {
+        const float a0 = xv[mm].x - m, a1 = xv[mm].y - m, a2 = xv[mm].z - m, a3 = xv[mm].w - m;
+        sq = fmaf(a0, a0, sq);
+        sq = fmaf(a1, a1, sq);
+        sq = fmaf(a2, a2, sq);
+        sq = fmaf(a3, a3, sq);
+      }
     }
-    if (dd < D) {
-      const float a0 = row[dd] - m;
-      c0 = fmaf(a0, a0, c0);
-    }
-    const float var = lane_group_sum<K>(c0 + c1) / (float)D;
+    const float var = lane_group_sum<K>(sq) / (float)D;
     if (q == 0) {
       mean_s[j] = m;
       rstd_s[j] = 1.f / sqrtf(var + p.eps);
@@ -401,8 +411,9 @@ hipError_t launch_channel_last(const EpilogueArgs& a) {
       p.tiles = (p.L + kVecTile - 1) / kVecTile;
       const int64_t blocks = a.B * p.tiles;
       if (blocks > INT32_MAX) return hipErrorInvalidValue;
-      // 256 threads (16 lanes per pixel) for up to 256 channels, else 512 (32 lanes)
-      const bool wide = p.D > 256;
+      // 256 threads (16 lanes per pixel) for up to 512 channels, else 512 (32 lanes):
+      // the statistics registers of a lane cover 32 K channels
+      const bool wide = p.D > kVecNarrowMaxD;
       if (a.dtype == 0)
         return wide ? launch_vec<float, 4, 512>(p, a.normalize, (unsigned)blocks, a.stream)
                     : launch_vec<float, 4, 256>(p, a.normalize, (unsigned)blocks, a.stream);
