@@ -23,7 +23,8 @@
 //     vector load and holds four consecutive outputs per row for one vector
 //     store.  Sixteen channels are consumed per step: lane group g (lanes
 //     16g..16g+15) feeds channels 4g..4g+3 over four MFMAs, which is one vector
-//     load of the weights too.
+//     load of the weights too.  A wave multiplies only the tiles it holds, and
+//     loads the operands two steps ahead.
 //   * The R rows of the rank-R dt input go to LDS; dt = W_dt (D x R) times
 //     them is a second MFMA product with R in steps of four, its 16-channel
 //     blocks dealt to the four waves.
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
     arow[i] = p.wx + (aval[i] ? ((int64_t)(o + 2 * kk) * C + (m - kk * C)) * D : 0);
   }
   const bool any = wave < MT;  // this wave holds at least one tile
+  const int held = (MT - wave + 3) / 4;  // tiles this wave holds (wave-uniform): only theirs are loaded and multiplied
 
   f32x4 acc[MTW][4];
 #pragma unroll
@@ -138,38 +140,48 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
 
   if (any) {
     // operands of 16 channels: x rows dg..dg+3 at this lane's positions, and the
-    // weights of this lane's rows at channels dg..dg+3 (dg = d0 + 4g); the next
-    // step's are loaded before this step's products
-    Operand bv[4], av[MTW];
-    auto load_step = [&](int d0) {
+    // weights of this lane's rows at channels dg..dg+3 (dg = d0 + 4g), in two
+    // register sets: the operands two steps ahead are loaded before this step's
+    // products
+    Operand bv[2][4], av[2][MTW] = {};
+    auto load_step = [&](int d0, int set) {
       const int dg = d0 + 4 * g;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = dg + j;
-        bv[j] = ld4_operand<S, VEC>(src + (int64_t)(d < D ? d : 0) * L, pos, L, d < D);
+        bv[set][j] = ld4_operand<S, VEC>(src + (int64_t)(d < D ? d : 0) * L, pos, L, d < D);
       }
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) av[i] = ld4_operand<float, VEC>(arow[i], dg, D, aval[i]);
+      for (int i = 0; i < MTW; ++i)
+        if (i < held) av[set][i] = ld4_operand<float, VEC>(arow[i], dg, D, aval[i]);
     };
-    load_step(0);
-    for (int d0 = 0; d0 < D; d0 += 16) {
+    auto mma_step = [&](int d0, int set) {
       float4 bc[4], ac[MTW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bc[j] = bv[j].get();
+      for (int j = 0; j < 4; ++j) bc[j] = bv[set][j].get();
 #pragma unroll
-      for (int i = 0; i < MTW; ++i) ac[i] = av[i].get();
-      if (d0 + 16 < D) load_step(d0 + 16);
+      for (int i = 0; i < MTW; ++i) ac[i] = i < held ? av[set][i].get() : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (d0 + 32 < D) load_step(d0 + 32, set);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < MTW; ++i) {
+        if (i >= held) break;
 #pragma unroll
-        for (int i = 0; i < MTW; ++i)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc[i][t] = mfma_16x16x4(comp(ac[i], j), comp(bc[j], t), acc[i][t]);
+      }
+    };
+    load_step(0, 0);
+    if (16 < D) load_step(16, 1);
+    for (int d0 = 0; d0 < D; d0 += 32) {
+      mma_step(d0, 0);
+      if (d0 + 16 < D) mma_step(d0 + 16, 1);
     }
 
     // lane (g, col) holds stacked rows mt*16 + 4g + r at positions pos..pos+3
 #pragma unroll
     for (int i = 0; i < MTW; ++i) {
+      if (i >= held) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = (wave + 4 * i) * 16 + 4 * g + r;
