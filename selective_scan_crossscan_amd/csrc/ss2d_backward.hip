@@ -735,9 +735,8 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int 
   o.cps = (o.nch + nsp - 1) / nsp;
   o.nsp = (o.nch + o.cps - 1) / o.cps;  // no empty segment
   // two channel blocks per workgroup (sharing Bs/Cs staging and the dBs/dCs
-  // partial) where that still leaves a full round of workgroups; fp32 storage
-  // only (with bf16 the kernel spills more and ran slower than the partials save)
-  o.cpb = dtype == 0 && o.nsp == 1 && B * 4 * ((o.nblk + 1) / 2) >= kBwdPairBlocks ? 2 : 1;
+  // partial) where that still leaves a full round of workgroups
+  o.cpb = o.nsp == 1 && B * 4 * ((o.nblk + 1) / 2) >= kBwdPairBlocks ? 2 : 1;
   const int64_t ngrp = (o.nblk + o.cpb - 1) / o.cpb;
   auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
   size_t off = 0;

@@ -123,14 +123,14 @@ def test_describe_lanes_rule():
 
 def test_describe_backward_plan():
     # the backward cuts long maps into segments when its channel blocks alone give
-    # fewer than 1536 workgroups, and pairs channel blocks (fp32, one segment) while
-    # that still leaves 768 workgroups
+    # fewer than 1536 workgroups, and pairs channel blocks (one segment) while that
+    # still leaves 768 workgroups
     def plan(*a):
         f = dict(kv.split("=") for kv in ss2d.describe(*a).split())
         return int(f["backward_segments"]), int(f["backward_blocks_per_workgroup"])
     assert plan(32, 192, 56, 56, 16, ss2d.SS2D_F32) == (1, 2)    # 1536 blocks
     assert plan(32, 768, 14, 14, 16, ss2d.SS2D_F32) == (1, 2)
-    assert plan(64, 384, 28, 28, 16, ss2d.SS2D_BF16) == (1, 1)   # bf16 keeps one block
+    assert plan(64, 384, 28, 28, 16, ss2d.SS2D_BF16) == (1, 2)   # bf16 pairs too
     assert plan(2, 192, 256, 256, 16, ss2d.SS2D_F32) == (16, 1)  # 96 blocks: 16 segments
     assert plan(1, 192, 56, 56, 16, ss2d.SS2D_F32) == (5, 1)
     assert plan(1, 16, 8, 8, 16, ss2d.SS2D_F32) == (1, 1)        # one chunk: nothing to cut

@@ -158,11 +158,11 @@ def test_backward_full_size_sampled_channels(cfg, segmented):
         assert e <= TOL[k], (k, e)
 
 
-@pytest.mark.parametrize("cfg,nsp,cpb", [(1, 1, 2), (2, 1, 2), (3, 1, 1), ("2x192x90x90", 16, 1)],
+@pytest.mark.parametrize("cfg,nsp,cpb", [(1, 1, 2), (2, 1, 2), (3, 1, 2), ("2x192x90x90", 16, 1)],
                          ids=["vmamba_t_stage1", "vmamba_t_stage3", "vmamba_t_stage2_bf16", "segmented_2x192x90x90"])
 def test_backward_full_size_batch_element(cfg, nsp, cpb):
-    # a full-size shape in the plan the benchmark times (fp32: two channel blocks
-    # per workgroup sharing one dBs/dCs partial), and a 90 x 90 map cut into 16
+    # a full-size shape in the plan the benchmark times (two channel blocks per
+    # workgroup sharing one dBs/dCs partial), and a 90 x 90 map cut into 16
     # segments as the 256 x 256 map is; the oracle recomputes batch element 0 on its
     # own (its dx, ddt, dBs and dCs depend only on its inputs)
     shape = (ss2d_inputs.CONFIGS[cfg] if isinstance(cfg, int)
@@ -193,16 +193,23 @@ def test_backward_full_size_batch_element(cfg, nsp, cpb):
 
 
 def _check_batch_element_and_channels(shape, idx, seed):
-    """Full GPU backward of `shape`; the oracle on batch element 0 (dx, ddt, dBs, dCs)
-    and on the channels `idx` alone (dA_log, ddt_bias, dDs, summed over the batch)."""
+    """Full GPU backward of `shape` (storage type as the shape says); the oracle on batch
+    element 0 (dx, ddt, dBs, dCs) and on the channels `idx` alone (dA_log, ddt_bias, dDs,
+    summed over the batch).  bf16 storage: the per-element gradients to 1e-2 (their
+    output rounding), the fp32 parameter gradients as for fp32."""
     B, D, H, W, N = shape.B, shape.D, shape.H, shape.W, shape.N
+    bf16 = shape.dtype == "bf16"
     inp = ss2d_inputs.generate(shape, seed=seed, a_log="s4d")
     rng = np.random.default_rng(seed + 1)
     dy = rng.standard_normal((B, D, H, W)).astype(np.float32)
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    if bf16:
+        dy = ss2d_inputs.round_to_bf16(dy)
     import selective_scan_crossscan_amd as ss2d
-    d = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    d = {k: (torch.from_numpy(v).to(tdt) if k in ("x", "dt", "Bs", "Cs") else torch.from_numpy(v)).cuda()
+         for k, v in inp.items()}
     got = ss2d.backward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"],
-                        torch.from_numpy(dy).cuda())
+                        torch.from_numpy(dy).to(tdt).cuda())
     torch.cuda.synchronize()
     sub = {k: (v[:1] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in inp.items()}
     ref = backward.ss2d_backward_f64(**sub, dy=dy[:1])
@@ -210,7 +217,7 @@ def _check_batch_element_and_channels(shape, idx, seed):
         g = got[k][:1].double().cpu().numpy()
         e = float(np.linalg.norm(g - ref[k]) / np.linalg.norm(ref[k]))
         print(k, f"{e:.2e}", flush=True)
-        assert e <= TOL[k], (k, e)
+        assert e <= (1e-2 if bf16 else TOL[k]), (k, e)
     idx = np.asarray(idx)
     per_k = lambda v: v.reshape(4, D, *v.shape[1:])[:, idx].reshape(4 * len(idx), *v.shape[1:])
     sub = dict(x=inp["x"][:, idx], dt=inp["dt"][:, :, idx], A_log=per_k(inp["A_log"]),
@@ -224,12 +231,16 @@ def _check_batch_element_and_channels(shape, idx, seed):
         assert e <= TOL[k], (k, e)
 
 
-@pytest.mark.parametrize("dims", [(32, 192, 16, 16, 5), (28, 200, 16, 16, 16)], ids=["N5", "D200_odd_blocks"])
-def test_backward_two_blocks_edge_cases(dims):
+@pytest.mark.parametrize("dims,dtype", [((32, 192, 16, 16, 5), "f32"), ((28, 200, 16, 16, 16), "f32"),
+                                        ((28, 200, 12, 16, 7), "bf16")],
+                         ids=["N5", "D200_odd_blocks", "bf16_D200_N7"])
+def test_backward_two_blocks_edge_cases(dims, dtype):
     # two channel blocks per workgroup with N < 16, and with an odd number of
-    # 16-channel blocks (D = 200: the last workgroup's second block lies past D)
+    # 16-channel blocks (D = 200: the last workgroup's second block lies past D),
+    # in both storage types
     B, D, H, W, N = dims
-    assert _plan(B, D, H, W, N) == {"backward_segments": 1, "backward_blocks_per_workgroup": 2}
-    print(f"[backward two blocks] {dims}", flush=True)
-    _check_batch_element_and_channels(ss2d_inputs.Shape("t", B, D, H, W, N, "f32"), [0, 17, D - 1],
+    assert _plan(B, D, H, W, N, 1 if dtype == "bf16" else 0) == {"backward_segments": 1,
+                                                                  "backward_blocks_per_workgroup": 2}
+    print(f"[backward two blocks] {dims} {dtype}", flush=True)
+    _check_batch_element_and_channels(ss2d_inputs.Shape("t", B, D, H, W, N, dtype), [0, 17, D - 1],
                                       seed=sum(dims))
