@@ -304,7 +304,7 @@ int ss2d_trim_memory(void);
 
 /*
  * ss2d_measure_peaks -- measure, on the current device, the rates the forward is
- * judged against (its roofline), one probe kernel per rate, each timed with HIP
+ * measured against (its roofline), one probe kernel per rate, each timed with HIP
  * events as the best of three runs on `stream`:
  *   exp_per_s         v_exp_f32 results per second (8 independent chains per lane)
  *   fma_per_s         plain fp32 FMA results per second
