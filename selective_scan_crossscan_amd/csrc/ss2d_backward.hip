@@ -648,6 +648,52 @@ __global__ __launch_bounds__(256) void bwd_merge(const float* __restrict__ du, S
   }
 }
 
+// The same merge with one workgroup per (b, d) plane, for planes that fit LDS with H
+// and W multiples of 4 and a 16-byte (fp32) or 8-byte (bf16) aligned dx: the column
+// directions' values are read along their walk four at a time (four consecutive h
+// of one column) into a row-major LDS copy, then each thread sums four consecutive
+// pixels of a row in the same order as above and writes them with one store.
+constexpr int kMergePlaneMax = 4096;  // pixels: two fp32 planes of LDS (32 KB)
+
+template <typename S>
+__global__ __launch_bounds__(256) void bwd_merge_plane(const float* __restrict__ du, S* __restrict__ dx, int D,
+                                                       int H, int W) {
+  __shared__ __align__(16) float t1[kMergePlaneMax], t3[kMergePlaneMax];  // row-major pixels
+  const int64_t bd = blockIdx.x;
+  const int64_t b = bd / D, d = bd - b * D;
+  const int L = H * W, L4 = L >> 2;
+  const float* r0 = du + ((b * 4 + 0) * D + d) * L;
+  const float* r1 = du + ((b * 4 + 1) * D + d) * L;
+  const float* r2 = du + ((b * 4 + 2) * D + d) * L;
+  const float* r3 = du + ((b * 4 + 3) * D + d) * L;
+  for (int q = threadIdx.x; q < L4; q += 256) {
+    // column-walk steps 4q .. 4q+3: pixels (h .. h+3, w) with 4q = w H + h
+    const int w = (4 * q) / H, h = 4 * q - w * H;
+    const float4 a = *reinterpret_cast<const float4*>(r1 + 4 * q);
+    const float4 c = *reinterpret_cast<const float4*>(r3 + (L - 4 - 4 * q));  // steps 4q+3 .. 4q, reversed
+    const int p = h * W + w;
+    t1[p] = a.x;
+    t1[p + W] = a.y;
+    t1[p + 2 * W] = a.z;
+    t1[p + 3 * W] = a.w;
+    t3[p] = c.w;
+    t3[p + W] = c.z;
+    t3[p + 2 * W] = c.y;
+    t3[p + 3 * W] = c.x;
+  }
+  __syncthreads();
+  S* out = dx + bd * L;
+  for (int q = threadIdx.x; q < L4; q += 256) {
+    const int p = 4 * q;  // pixels p .. p+3 of one row (W % 4 == 0)
+    const float4 v0 = *reinterpret_cast<const float4*>(r0 + p);
+    const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));  // pixels p+3 .. p, reversed
+    const float4 v1 = *reinterpret_cast<const float4*>(t1 + p);
+    const float4 v3 = *reinterpret_cast<const float4*>(t3 + p);
+    Io<S>::st4(out, p, make_float4(((v0.x + v1.x) + v2.w) + v3.x, ((v0.y + v1.y) + v2.z) + v3.y,
+                                   ((v0.z + v1.z) + v2.y) + v3.z, ((v0.w + v1.w) + v2.x) + v3.w));
+  }
+}
+
 // Per-channel parameter gradients: sums over the batch in batch order.
 __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_log, const float* __restrict__ dAp,
                                                  const float* __restrict__ dbp, const float* __restrict__ dDp,
@@ -704,6 +750,12 @@ hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L, int c
   hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp, static_cast<S*>(a.dBs),
                      static_cast<S*>(a.dCs), a.B * 4, ngrp, (int)a.N, (int)L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const uintptr_t am = sizeof(S) == 4 ? 15 : 7;
+  if (L <= kMergePlaneMax && a.H % 4 == 0 && a.W % 4 == 0 && !((uintptr_t)a.dx & am)) {
+    hipLaunchKernelGGL((bwd_merge_plane<S>), dim3((unsigned)(a.B * a.D)), dim3(256), 0, a.stream, p.du,
+                       static_cast<S*>(a.dx), (int)a.D, (int)a.H, (int)a.W);
+    return hipGetLastError();
+  }
   const int tiles_w = (int)((a.W + kMergeTile - 1) / kMergeTile);
   const int tiles = (int)((a.H + kMergeTile - 1) / kMergeTile) * tiles_w;
   hipLaunchKernelGGL((bwd_merge<S>), dim3((unsigned)(a.B * a.D * tiles)), dim3(256), 0, a.stream, p.du,
