@@ -65,7 +65,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
 STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel", "bwd_chunk_kernel",
-                "bwd_seg_carry", "bwd_reduce_bc", "bwd_merge", "bwd_params", "channel_last_kernel"}
+                "bwd_seg_carry", "bwd_reduce_bc", "bwd_reduce_bc4", "bwd_merge", "bwd_merge_plane", "bwd_params",
+                "channel_last_kernel"}
 
 
 def traffic_file(workload: str, kernel: str = KERNEL_PREFIX) -> str:
