@@ -202,8 +202,11 @@ struct BwdRegs {
 
 // At most 168 VGPRs (three waves per SIMD): two blocks per workgroup would
 // otherwise take 188 and run at two; the few values spilled are reloaded per
-// chunk, outside the state loop.
-template <typename S, int MODE, int CPB>
+// chunk, outside the state loop.  VEC: L is a multiple of 4 and the rows are
+// aligned, so a lane's steps (a multiple of 8 from the chunk's start) come in
+// groups of four wholly inside or past the sequence, read and written with one
+// 16-byte (fp32) or 8-byte (bf16) access each, also along the reversed walks.
+template <typename S, int MODE, int CPB, bool VEC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_chunk_kernel(BwdParams p) {
   __shared__ float sB[16][kPad];
   __shared__ float sC[16][kPad];
@@ -277,13 +280,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   auto load_lane = [&](const BwdChan<S>& cn, int c, bool with_g) {
     float dtv[kCT];
     bool inr[kCT];
+    if constexpr (VEC) {
+      static_assert(kCT % 4 == 0, "groups of four steps");
+      const bool rev = k >= 2;
+      float4 dq[kCT / 4], uq[kCT / 4], gq[kCT / 4];
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) {
-      int li, xi;
-      inr[i] = lane_step(cn, c, i, li, xi);
-      dtv[i] = Io<S>::ld(cn.dtr, li);
-      uu[i] = Io<S>::ld(cn.xs, xi);
-      gg[i] = with_g ? Io<S>::ld(cn.gs, xi) : 0.f;
+      for (int g = 0; g < kCT / 4; ++g) {
+        const int l = c * kChunk + j0 + 4 * g;
+        const bool in = cn.valid && l < L;
+        const int li = in ? l : 0, xi = in ? (rev ? L - 4 - l : l) : 0;
+        dq[g] = Io<S>::ld4(cn.dtr, li);
+        uq[g] = Io<S>::ld4(cn.xs, xi);
+        gq[g] = with_g ? Io<S>::ld4(cn.gs, xi) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) inr[4 * g + i] = in;
+      }
+#pragma unroll
+      for (int g = 0; g < kCT / 4; ++g) {
+        const float4 u4 = uq[g], g4 = gq[g];
+        dtv[4 * g] = dq[g].x; dtv[4 * g + 1] = dq[g].y; dtv[4 * g + 2] = dq[g].z; dtv[4 * g + 3] = dq[g].w;
+        uu[4 * g] = rev ? u4.w : u4.x; uu[4 * g + 1] = rev ? u4.z : u4.y;
+        uu[4 * g + 2] = rev ? u4.y : u4.z; uu[4 * g + 3] = rev ? u4.x : u4.w;
+        gg[4 * g] = rev ? g4.w : g4.x; gg[4 * g + 1] = rev ? g4.z : g4.y;
+        gg[4 * g + 2] = rev ? g4.y : g4.z; gg[4 * g + 3] = rev ? g4.x : g4.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kCT; ++i) {
+        int li, xi;
+        inr[i] = lane_step(cn, c, i, li, xi);
+        dtv[i] = Io<S>::ld(cn.dtr, li);
+        uu[i] = Io<S>::ld(cn.xs, xi);
+        gg[i] = with_g ? Io<S>::ld(cn.gs, xi) : 0.f;
+      }
     }
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
@@ -302,6 +331,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   // are wave-uniform (scalar), and past the end the address is clamped in bounds.
   auto stage = [&](int c, bool with_c) {
     constexpr int kPer = 16 * kChunk / 256;  // elements per thread and tensor
+    if constexpr (VEC) {
+      // four steps of kPer / 4 state rows per thread: thread tid reads steps
+      // 4 (tid % 32) .. + 3 of rows tid / 32 + 8 r, so a wave reads two whole rows
+      static_assert(kChunk == 128 && kPer == 8, "a row is 32 groups of four steps");
+      const int j = 4 * (tid & 31), l = c * kChunk + j, n0 = tid >> 5;
+      const bool lin = l < L;  // the four steps are all inside or all past the end
+      const int lc = lin ? l : 0;
+      float4 vb[2], vc[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int n = n0 + 8 * r, nc = n < N ? n : N - 1;
+        vb[r] = Io<S>::ld4(Bb + (int64_t)nc * L, lc);
+        vc[r] = with_c ? Io<S>::ld4(Cb + (int64_t)nc * L, lc) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      const int jp = j + j / kCT;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int n = n0 + 8 * r;
+        const bool in = n < N && lin;
+        const float4 zb = in ? vb[r] : make_float4(0.f, 0.f, 0.f, 0.f);
+        sB[n][jp] = zb.x; sB[n][jp + 1] = zb.y; sB[n][jp + 2] = zb.z; sB[n][jp + 3] = zb.w;
+        if (with_c) {
+          const float4 zc = in ? vc[r] : make_float4(0.f, 0.f, 0.f, 0.f);
+          sC[n][jp] = zc.x; sC[n][jp + 1] = zc.y; sC[n][jp + 2] = zc.z; sC[n][jp + 3] = zc.w;
+        }
+      }
+      return;
+    }
     const int hi = __builtin_amdgcn_readfirstlane(tid >> 7);
     const int j = tid & (kChunk - 1), l = c * kChunk + j;
     const int lc = l < L ? l : L - 1;
@@ -535,15 +592,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
         float* dst = (which == 0 ? p.dCp : p.dBp) + ((int64_t)bk * ngrp + blk0 / CPB) * N * L + lo;
         for (int n = 0; n < N; ++n) dst[(int64_t)n * L] = acc[n][tid];
       }
+      // ddt_bias sums the ddt products as rounded (no fused multiply-add), so that
+      // both access paths add the same values
+      if constexpr (VEC) {
 #pragma unroll
-      for (int i = 0; i < kCT; ++i) {
-        int li, xi;
-        if (lane_step(cn, c, i, li, xi)) {
-          const float ddt = fmaf(uu[i], tq[i], sa[i]) * sig[i];
-          Io<S>::st(static_cast<S*>(p.ddt), cn.row + li, ddt);
-          p.du[cn.row + li] = fmaf(del[i], tq[i], cn.dsk * gg[i]);
-          rr.dbias += ddt;
-          rr.dD = fmaf(gg[i], uu[i], rr.dD);
+        for (int g = 0; g < kCT / 4; ++g) {
+          const int l = c * kChunk + j0 + 4 * g;
+          if (cn.valid && l < L) {
+#pragma clang fp contract(off)
+            float dv[4], uv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int i = 4 * g + t;
+              dv[t] = fmaf(uu[i], tq[i], sa[i]) * sig[i];
+              uv[t] = fmaf(del[i], tq[i], cn.dsk * gg[i]);
+              rr.dbias += dv[t];
+              rr.dD = fmaf(gg[i], uu[i], rr.dD);
+            }
+            Io<S>::st4(static_cast<S*>(p.ddt), cn.row + l, make_float4(dv[0], dv[1], dv[2], dv[3]));
+            *reinterpret_cast<float4*>(p.du + cn.row + l) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kCT; ++i) {
+          int li, xi;
+          if (lane_step(cn, c, i, li, xi)) {
+#pragma clang fp contract(off)
+            const float ddt = fmaf(uu[i], tq[i], sa[i]) * sig[i];
+            Io<S>::st(static_cast<S*>(p.ddt), cn.row + li, ddt);
+            p.du[cn.row + li] = fmaf(del[i], tq[i], cn.dsk * gg[i]);
+            rr.dbias += ddt;
+            rr.dD = fmaf(gg[i], uu[i], rr.dD);
+          }
         }
       }
       next_block();
@@ -742,6 +823,27 @@ __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_lo
   }
 }
 
+// The chunked scan: one launch, or three for a segmented map.
+template <typename S, bool VEC>
+hipError_t launch_chunks(const BackwardArgs& a, const BwdParams& p, int cpb, unsigned blocks) {
+  hipError_t e = hipSuccess;
+  if (p.nsp == 1) {
+    if (cpb == 2)
+      hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole, 2, VEC>), dim3(blocks), dim3(256), 0, a.stream, p);
+    else
+      hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole, 1, VEC>), dim3(blocks), dim3(256), 0, a.stream, p);
+  } else {
+    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegMaps, 1, VEC>), dim3(blocks), dim3(256), 0, a.stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t cols = a.B * 4 * a.D * a.N;
+    hipLaunchKernelGGL(bwd_seg_carry, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, a.stream, p.segP, p.segF,
+                       p.segR, cols, a.D * a.N, p.nsp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegGrads, 1, VEC>), dim3(blocks), dim3(256), 0, a.stream, p);
+  }
+  return hipGetLastError();
+}
+
 // The kernels that read or write the storage type: transposes of x and dy, the
 // chunked scan (one launch, or three for a segmented map), the dBs/dCs sums and
 // the dx merge.
@@ -755,21 +857,13 @@ hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L, int c
   if (e != hipSuccess) return e;
   const int ngrp = (p.nblk + cpb - 1) / cpb;
   const unsigned blocks = (unsigned)(a.B * 4 * ngrp * p.nsp);
-  if (p.nsp == 1) {
-    if (cpb == 2)
-      hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole, 2>), dim3(blocks), dim3(256), 0, a.stream, p);
-    else
-      hipLaunchKernelGGL((bwd_chunk_kernel<S, kWhole, 1>), dim3(blocks), dim3(256), 0, a.stream, p);
-  } else {
-    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegMaps, 1>), dim3(blocks), dim3(256), 0, a.stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t cols = a.B * 4 * a.D * a.N;
-    hipLaunchKernelGGL(bwd_seg_carry, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, a.stream, p.segP, p.segF,
-                       p.segR, cols, a.D * a.N, p.nsp);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegGrads, 1>), dim3(blocks), dim3(256), 0, a.stream, p);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 16-byte (fp32) or 8-byte (bf16) accesses when every row the chunks read or
+  // write starts aligned: L a multiple of 4 and aligned bases
+  const uintptr_t vm = sizeof(S) == 4 ? 15 : 7;
+  const bool vec = L % 4 == 0 && !(((uintptr_t)a.x | (uintptr_t)a.dt | (uintptr_t)a.Bs | (uintptr_t)a.Cs |
+                                    (uintptr_t)a.dy | (uintptr_t)a.ddt | (uintptr_t)p.xT | (uintptr_t)p.dyT) & vm);
+  e = vec ? launch_chunks<S, true>(a, p, cpb, blocks) : launch_chunks<S, false>(a, p, cpb, blocks);
+  if (e != hipSuccess) return e;
   const uintptr_t om = sizeof(S) == 4 ? 15 : 7;
   if ((a.N * L) % 4 == 0 && !((uintptr_t)a.dBs & om) && !((uintptr_t)a.dCs & om))
     hipLaunchKernelGGL((bwd_reduce_bc4<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp,

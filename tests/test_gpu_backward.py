@@ -244,3 +244,40 @@ def test_backward_two_blocks_edge_cases(dims, dtype):
     print(f"[backward two blocks] {dims} {dtype}", flush=True)
     _check_batch_element_and_channels(ss2d_inputs.Shape("t", B, D, H, W, N, dtype), [0, 17, D - 1],
                                       seed=sum(dims))
+
+
+def _offset_copy(t):
+    """t's values in a buffer that starts one element past an aligned base."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dims,dtype", [((2, 20, 12, 12, 16), "f32"), ((1, 16, 32, 32, 16), "f32"),
+                                        ((2, 20, 12, 12, 7), "bf16")],
+                         ids=["whole", "segmented", "bf16"])
+def test_backward_element_aligned_bases(dims, dtype):
+    # L a multiple of 4: aligned inputs take the kernels' 16-byte (8-byte bf16)
+    # accesses, inputs one element past an aligned base the one-element accesses;
+    # both add in the same order, so the gradients are identical, and they match
+    # the oracle
+    B, D, H, W, N = dims
+    print(f"[backward element-aligned bases] {dims} {dtype}", flush=True)
+    got = _run(B, D, H, W, N, seed=sum(dims) + 5, dtype=dtype)
+    inp = ss2d_inputs.tiny_random(B, D, H, W, N, seed=sum(dims) + 5, a_log="random", dtype=dtype)
+    rng = np.random.default_rng(sum(dims) + 5 + 7)
+    dy = rng.standard_normal((B, D, H, W)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if dtype == "bf16":
+        dy = ss2d_inputs.round_to_bf16(dy)
+    d = {k: (torch.from_numpy(v).to(tdt) if k in ("x", "dt", "Bs", "Cs") else torch.from_numpy(v)).cuda()
+         for k, v in inp.items()}
+    off = {k: _offset_copy(d[k]) for k in ("x", "dt", "Bs", "Cs")}
+    assert all(t.data_ptr() % 16 != 0 for t in off.values())
+    import selective_scan_crossscan_amd as ss2d
+    again = ss2d.backward(off["x"], off["dt"], d["A_log"], d["dt_bias"], off["Bs"], off["Cs"], d["Ds"],
+                          _offset_copy(torch.from_numpy(dy).to(tdt).cuda()))
+    torch.cuda.synchronize()
+    for k in got:
+        assert torch.equal(got[k], again[k]), k
