@@ -752,43 +752,53 @@ __global__ __launch_bounds__(256) void bwd_merge(const float* __restrict__ du, S
   }
 }
 
-// The same merge with one workgroup per (b, d) plane, for planes that fit LDS with H
-// and W multiples of 4 and a 16-byte (fp32) or 8-byte (bf16) aligned dx: the column
-// directions' values are read along their walk four at a time (four consecutive h
-// of one column) into a row-major LDS copy, then each thread sums four consecutive
-// pixels of a row in the same order as above and writes them with one store.
+// The same merge with whole (b, d) planes in LDS, for planes of L <= 4096 pixels
+// with L a multiple of 4 and a 16-byte (fp32) or 8-byte (bf16) aligned dx.  TPP
+// threads take one plane (a workgroup 256 / TPP planes): the column directions'
+// values are read along their walk four steps at a time into row-major LDS copies,
+// then each thread sums four consecutive pixels in the same order as above and
+// writes them with one store.  Every global access is a 16-byte (8-byte) one.
 constexpr int kMergePlaneMax = 4096;  // pixels: two fp32 planes of LDS (32 KB)
 
 template <typename S>
-__global__ __launch_bounds__(256) void bwd_merge_plane(const float* __restrict__ du, S* __restrict__ dx, int D,
-                                                       int H, int W) {
-  __shared__ __align__(16) float t1[kMergePlaneMax], t3[kMergePlaneMax];  // row-major pixels
-  const int64_t bd = blockIdx.x;
-  const int64_t b = bd / D, d = bd - b * D;
+__global__ __launch_bounds__(256) void bwd_merge_plane(const float* __restrict__ du, S* __restrict__ dx, int64_t BD,
+                                                       int D, int H, int W, int TPP) {
+  extern __shared__ __align__(16) float mtile[];  // per plane of the workgroup: t1[L], then t3[L]
   const int L = H * W, L4 = L >> 2;
+  const int lt = threadIdx.x % TPP;
+  const int64_t bd = (int64_t)blockIdx.x * (256 / TPP) + threadIdx.x / TPP;
+  float* t1 = mtile + (threadIdx.x / TPP) * 2 * L;
+  float* t3 = t1 + L;
+  const bool live = bd < BD;  // the last workgroup's planes past the end only reach the barrier
+  const int64_t bdc = live ? bd : BD - 1, b = bdc / D, d = bdc - b * D;
   const float* r0 = du + ((b * 4 + 0) * D + d) * L;
   const float* r1 = du + ((b * 4 + 1) * D + d) * L;
   const float* r2 = du + ((b * 4 + 2) * D + d) * L;
   const float* r3 = du + ((b * 4 + 3) * D + d) * L;
-  for (int q = threadIdx.x; q < L4; q += 256) {
-    // column-walk steps 4q .. 4q+3: pixels (h .. h+3, w) with 4q = w H + h
-    const int w = (4 * q) / H, h = 4 * q - w * H;
-    const float4 a = *reinterpret_cast<const float4*>(r1 + 4 * q);
-    const float4 c = *reinterpret_cast<const float4*>(r3 + (L - 4 - 4 * q));  // steps 4q+3 .. 4q, reversed
-    const int p = h * W + w;
-    t1[p] = a.x;
-    t1[p + W] = a.y;
-    t1[p + 2 * W] = a.z;
-    t1[p + 3 * W] = a.w;
-    t3[p] = c.w;
-    t3[p + W] = c.z;
-    t3[p + 2 * W] = c.y;
-    t3[p + 3 * W] = c.x;
+  if (live) {
+    for (int q = lt; q < L4; q += TPP) {
+      // column-walk steps 4q .. 4q+3: step l visits pixel (l mod H, l / H)
+      int w = (4 * q) / H, h = 4 * q - w * H;
+      const float4 a = *reinterpret_cast<const float4*>(r1 + 4 * q);
+      const float4 c = *reinterpret_cast<const float4*>(r3 + (L - 4 - 4 * q));  // steps 4q+3 .. 4q, reversed
+      const float av[4] = {a.x, a.y, a.z, a.w}, cv[4] = {c.w, c.z, c.y, c.x};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int p = h * W + w;
+        t1[p] = av[k];
+        t3[p] = cv[k];
+        if (++h == H) {
+          h = 0;
+          ++w;
+        }
+      }
+    }
   }
   __syncthreads();
+  if (!live) return;
   S* out = dx + bd * L;
-  for (int q = threadIdx.x; q < L4; q += 256) {
-    const int p = 4 * q;  // pixels p .. p+3 of one row (W % 4 == 0)
+  for (int q = lt; q < L4; q += TPP) {
+    const int p = 4 * q;  // pixels p .. p+3 in row-major order
     const float4 v0 = *reinterpret_cast<const float4*>(r0 + p);
     const float4 v2 = *reinterpret_cast<const float4*>(r2 + (L - 4 - p));  // pixels p+3 .. p, reversed
     const float4 v1 = *reinterpret_cast<const float4*>(t1 + p);
@@ -873,9 +883,13 @@ hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L, int c
                        static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * 4, ngrp, (int)a.N, (int)L);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const uintptr_t am = sizeof(S) == 4 ? 15 : 7;
-  if (L <= kMergePlaneMax && a.H % 4 == 0 && a.W % 4 == 0 && !((uintptr_t)a.dx & am)) {
-    hipLaunchKernelGGL((bwd_merge_plane<S>), dim3((unsigned)(a.B * a.D)), dim3(256), 0, a.stream, p.du,
-                       static_cast<S*>(a.dx), (int)a.D, (int)a.H, (int)a.W);
+  if (L <= kMergePlaneMax && L % 4 == 0 && !((uintptr_t)a.dx & am)) {
+    // threads per plane: the fewest of 64, 128, 256 that give each a group of four pixels
+    const int TPP = L / 4 <= 64 ? 64 : (L / 4 <= 128 ? 128 : 256), ppw = 256 / TPP;
+    const int64_t BD = a.B * a.D;
+    const size_t lds = (size_t)ppw * 2 * L * sizeof(float);
+    hipLaunchKernelGGL((bwd_merge_plane<S>), dim3((unsigned)((BD + ppw - 1) / ppw)), dim3(256), lds, a.stream, p.du,
+                       static_cast<S*>(a.dx), BD, (int)a.D, (int)a.H, (int)a.W, TPP);
     return hipGetLastError();
   }
   const int tiles_w = (int)((a.W + kMergeTile - 1) / kMergeTile);

@@ -1522,8 +1522,116 @@ __global__ __launch_bounds__(256) void transpose_small(const S* __restrict__ in,
   }
 }
 
+// The same for planes of n = R C elements with n a multiple of 4 and aligned
+// bases: a workgroup takes P consecutive planes (one contiguous block) per step, and
+// each access moves four consecutive elements (16 bytes fp32, 8 bytes bf16).  A
+// thread's position in the block, as (plane, row, column) on the way in and
+// (plane, column, row) on the way out, advances by a fixed step per 1024 elements
+// without a division.
+constexpr int kSmallGroup = 4096;  // elements per step: P = kSmallGroup / n planes, at least one
+
+template <typename S>
+__global__ __launch_bounds__(256) void transpose_small4(const S* __restrict__ in, S* __restrict__ out, int planes,
+                                                        int R, int C, int P) {
+  extern __shared__ float tile_s[];  // P planes of R rows of C + 1
+  const int n = R * C, ld = C + 1, pst = R * ld;
+  const int tid = threadIdx.x;
+  constexpr int kStep = 4 * 256;
+  // element 4 tid and the step of kStep elements, in (plane, row, column) and in
+  // (plane, column, row) of the output
+  const int ip = (4 * tid) / n, ir = ((4 * tid) - ip * n) / C, ic = (4 * tid) - ip * n - ir * C;
+  const int sp = kStep / n, sr = (kStep - sp * n) / C, sc = kStep - sp * n - sr * C;
+  const int op = ip, oc0 = ((4 * tid) - op * n) / R, or0 = (4 * tid) - op * n - oc0 * R;
+  const int soc = (kStep - sp * n) / R, sor = kStep - sp * n - soc * R;
+  const int64_t groups = ((int64_t)planes + P - 1) / P;
+  for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+    const int64_t pl0 = g * P;
+    const int np = (int)((int64_t)planes - pl0 < P ? (int64_t)planes - pl0 : P);
+    const int m4 = np * n / 4;  // four-element groups of this step
+    const S* src = in + pl0 * n;
+    S* dst = out + pl0 * n;
+    int pl = ip, r = ir, c = ic;
+    for (int q0 = tid; q0 < m4; q0 += 4 * 256) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u * 256;
+        v[u] = Io<S>::ld4(src, q < m4 ? 4 * (int64_t)q : 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (q0 + u * 256 < m4) {
+          float* t = tile_s + pl * pst;
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          int rr = r, cc = c;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {  // n % 4 == 0: the four stay in one plane
+            t[rr * ld + cc] = e[k];
+            if (++cc == C) {
+              cc = 0;
+              ++rr;
+            }
+          }
+        }
+        c += sc;
+        if (c >= C) {
+          c -= C;
+          ++r;
+        }
+        r += sr;
+        if (r >= R) {
+          r -= R;
+          ++pl;
+        }
+        pl += sp;
+      }
+    }
+    __syncthreads();
+    int opl = op, oc = oc0, orow = or0;
+    for (int q = tid; q < m4; q += 256) {  // output element oc R + orow of a plane is input (orow, oc)
+      const float* t = tile_s + opl * pst;
+      float e[4];
+      int rr = orow, cc = oc;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        e[k] = t[rr * ld + cc];
+        if (++rr == R) {
+          rr = 0;
+          ++cc;
+        }
+      }
+      Io<S>::st4(dst, 4 * (int64_t)q, make_float4(e[0], e[1], e[2], e[3]));
+      orow += sor;
+      if (orow >= R) {
+        orow -= R;
+        ++oc;
+      }
+      oc += soc;
+      if (oc >= C) {
+        oc -= C;
+        ++opl;
+      }
+      opl += sp;
+    }
+    __syncthreads();
+  }
+}
+
 template <typename S>
 hipError_t launch_transpose(const S* in, S* out, int planes, int R, int C, hipStream_t stream) {
+  const int64_t n = (int64_t)R * C;
+  const uintptr_t am = sizeof(S) == 4 ? 15 : 7;
+  if (n % 4 == 0 && (int64_t)R * (C + 1) <= kSmallPlane && !(((uintptr_t)in | (uintptr_t)out) & am)) {
+    const int by_lds = (int)(kSmallPlane / ((int64_t)R * (C + 1)));
+    const int by_size = (int)(kSmallGroup / n);
+    const int P = by_size < 1 ? 1 : (by_size < by_lds ? by_size : by_lds);
+    const int64_t groups = ((int64_t)planes + P - 1) / P;
+    const int grid = groups < 4096 ? (int)groups : 4096;
+    const size_t lds = (size_t)P * R * (C + 1) * sizeof(float);
+    hipLaunchKernelGGL((transpose_small4<S>), dim3((unsigned)grid), dim3(256), lds, stream, in, out, planes, R, C,
+                       P);
+    return hipGetLastError();
+  }
   if ((int64_t)R * (C + 1) <= kSmallPlane) {
     const size_t lds = (size_t)R * (C + 1) * sizeof(float);
     const int grid = planes < 2048 ? planes : 2048;
