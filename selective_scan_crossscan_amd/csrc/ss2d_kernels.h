@@ -1467,6 +1467,48 @@ __global__ __launch_bounds__(256) void transpose_planes(const S* __restrict__ in
   }
 }
 
+// The same with R and C multiples of 4 and aligned bases: a thread moves four
+// consecutive elements per access (16 bytes fp32, 8 bytes bf16), 16 threads a
+// 64-element row of the tile.
+template <typename S>
+__global__ __launch_bounds__(256) void transpose_planes4(const S* __restrict__ in, S* __restrict__ out, int R, int C,
+                                                         int tiles_r, int tiles_c) {
+  __shared__ float tile[64][65];
+  const int t = blockIdx.x;
+  const int tc = t % tiles_c;
+  const int rest = t / tiles_c;
+  const int tr = rest % tiles_r;
+  const int64_t plane = rest / tiles_r;
+  const S* src = in + plane * R * C;
+  S* dst = out + plane * R * C;
+  const int r0 = tr * 64, c0 = tc * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {  // rows ty + 16 u, columns 4 tx .. 4 tx + 3 (all inside or all past C)
+    const int r = r0 + ty + 16 * u, c = c0 + 4 * tx;
+    const bool ok = r < R && c < C;
+    v[u] = Io<S>::ld4(src, ok ? (int64_t)r * C + c : 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float* row = &tile[ty + 16 * u][4 * tx];
+    row[0] = v[u].x;
+    row[1] = v[u].y;
+    row[2] = v[u].z;
+    row[3] = v[u].w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {  // output row c = c0 + ty + 16 u, columns r0 + 4 tx .. + 3
+    const int c = c0 + ty + 16 * u, r = r0 + 4 * tx;
+    if (c < C && r < R)
+      Io<S>::st4(dst, (int64_t)c * R + r,
+                 make_float4(tile[4 * tx][ty + 16 * u], tile[4 * tx + 1][ty + 16 * u], tile[4 * tx + 2][ty + 16 * u],
+                             tile[4 * tx + 3][ty + 16 * u]));
+  }
+}
+
 // Whole planes of at most kSmallPlane LDS slots (R rows of C + 1) through LDS: workgroup w
 // transposes planes w, w + gridDim.x, ...  One element per thread and step, so
 // global reads and writes are 256 contiguous bytes per wave (fp32) and the LDS
@@ -1641,8 +1683,12 @@ hipError_t launch_transpose(const S* in, S* out, int planes, int R, int C, hipSt
   const int tiles_r = (R + 63) / 64, tiles_c = (C + 63) / 64;
   const int64_t blocks = (int64_t)planes * tiles_r * tiles_c;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((transpose_planes<S>), dim3((unsigned)blocks), dim3(256), 0, stream, in, out, R, C, tiles_r,
-                     tiles_c);
+  if (R % 4 == 0 && C % 4 == 0 && !(((uintptr_t)in | (uintptr_t)out) & am))
+    hipLaunchKernelGGL((transpose_planes4<S>), dim3((unsigned)blocks), dim3(256), 0, stream, in, out, R, C, tiles_r,
+                       tiles_c);
+  else
+    hipLaunchKernelGGL((transpose_planes<S>), dim3((unsigned)blocks), dim3(256), 0, stream, in, out, R, C, tiles_r,
+                       tiles_c);
   return hipGetLastError();
 }
 
