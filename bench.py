@@ -64,7 +64,8 @@ KERNEL_SOURCES = {
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
-STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_planes", "project_kernel", "bwd_chunk_kernel",
+STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_small4", "transpose_planes", "transpose_planes4",
+                "project_kernel", "bwd_chunk_kernel",
                 "bwd_seg_carry", "bwd_reduce_bc", "bwd_reduce_bc4", "bwd_merge", "bwd_merge_plane", "bwd_params",
                 "channel_last_kernel"}
 
