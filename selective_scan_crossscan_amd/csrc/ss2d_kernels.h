@@ -1564,51 +1564,82 @@ __global__ __launch_bounds__(256) void transpose_small(const S* __restrict__ in,
   }
 }
 
-// The same for planes of n = R C elements with n a multiple of 4 and aligned
-// bases: a workgroup takes P consecutive planes (one contiguous block) per step, and
-// each access moves four consecutive elements (16 bytes fp32, 8 bytes bf16).  A
-// thread's position in the block, as (plane, row, column) on the way in and
-// (plane, column, row) on the way out, advances by a fixed step per 1024 elements
-// without a division.
+// V consecutive elements as floats, and back: 16 bytes (fp32 with V = 4, bf16
+// with V = 8) or 8 bytes (bf16 with V = 4).
+template <typename S, int V>
+__device__ __forceinline__ void ld_vec(const S* p, int64_t i, float (&e)[V]) {
+  if constexpr (V == 8) {
+    static_assert(sizeof(S) == 2, "eight-element accesses are for bf16");
+    const uint4 q = *reinterpret_cast<const uint4*>(p + i);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      e[2 * k] = bf16_to_f32(w[k] & 0xffffu);
+      e[2 * k + 1] = bf16_to_f32(w[k] >> 16);
+    }
+  } else {
+    const float4 v = Io<S>::ld4(p, i);
+    e[0] = v.x;
+    e[1] = v.y;
+    e[2] = v.z;
+    e[3] = v.w;
+  }
+}
+template <typename S, int V>
+__device__ __forceinline__ void st_vec(S* p, int64_t i, const float (&e)[V]) {
+  if constexpr (V == 8) {
+    *reinterpret_cast<uint4*>(p + i) = make_uint4(bf16x2_rne(e[0], e[1]), bf16x2_rne(e[2], e[3]),
+                                                  bf16x2_rne(e[4], e[5]), bf16x2_rne(e[6], e[7]));
+  } else {
+    Io<S>::st4(p, i, make_float4(e[0], e[1], e[2], e[3]));
+  }
+}
+
+// The same for planes of n = R C elements with n a multiple of V and aligned bases:
+// a workgroup takes P consecutive planes (one contiguous block) per step, and each
+// access moves V consecutive elements (V = 4 fp32, 8 bf16: 16 bytes).  A thread's
+// position in the block, as (plane, row, column) on the way in and (plane, column,
+// row) on the way out, advances by a fixed step per 256 V elements without a
+// division.
 constexpr int kSmallGroup = 4096;  // elements per step: P = kSmallGroup / n planes, at least one
 
-template <typename S>
+template <typename S, int V>
 __global__ __launch_bounds__(256) void transpose_small4(const S* __restrict__ in, S* __restrict__ out, int planes,
                                                         int R, int C, int P) {
   extern __shared__ float tile_s[];  // P planes of R rows of C + 1
   const int n = R * C, ld = C + 1, pst = R * ld;
   const int tid = threadIdx.x;
-  constexpr int kStep = 4 * 256;
-  // element 4 tid and the step of kStep elements, in (plane, row, column) and in
+  constexpr int kStep = V * 256;
+  // element V tid and the step of kStep elements, in (plane, row, column) and in
   // (plane, column, row) of the output
-  const int ip = (4 * tid) / n, ir = ((4 * tid) - ip * n) / C, ic = (4 * tid) - ip * n - ir * C;
+  const int e0 = V * tid;
+  const int ip = e0 / n, ir = (e0 - ip * n) / C, ic = e0 - ip * n - ir * C;
   const int sp = kStep / n, sr = (kStep - sp * n) / C, sc = kStep - sp * n - sr * C;
-  const int op = ip, oc0 = ((4 * tid) - op * n) / R, or0 = (4 * tid) - op * n - oc0 * R;
+  const int op = ip, oc0 = (e0 - op * n) / R, or0 = e0 - op * n - oc0 * R;
   const int soc = (kStep - sp * n) / R, sor = kStep - sp * n - soc * R;
   const int64_t groups = ((int64_t)planes + P - 1) / P;
   for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
     const int64_t pl0 = g * P;
     const int np = (int)((int64_t)planes - pl0 < P ? (int64_t)planes - pl0 : P);
-    const int m4 = np * n / 4;  // four-element groups of this step
+    const int mv = np * n / V;  // V-element groups of this step
     const S* src = in + pl0 * n;
     S* dst = out + pl0 * n;
     int pl = ip, r = ir, c = ic;
-    for (int q0 = tid; q0 < m4; q0 += 4 * 256) {
-      float4 v[4];
+    for (int q0 = tid; q0 < mv; q0 += 4 * 256) {
+      float v[4][V];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int q = q0 + u * 256;
-        v[u] = Io<S>::ld4(src, q < m4 ? 4 * (int64_t)q : 0);
+        ld_vec<S, V>(src, q < mv ? (int64_t)V * q : 0, v[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (q0 + u * 256 < m4) {
+        if (q0 + u * 256 < mv) {
           float* t = tile_s + pl * pst;
-          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
           int rr = r, cc = c;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {  // n % 4 == 0: the four stay in one plane
-            t[rr * ld + cc] = e[k];
+          for (int k = 0; k < V; ++k) {  // n % V == 0: the V stay in one plane
+            t[rr * ld + cc] = v[u][k];
             if (++cc == C) {
               cc = 0;
               ++rr;
@@ -1630,19 +1661,19 @@ __global__ __launch_bounds__(256) void transpose_small4(const S* __restrict__ in
     }
     __syncthreads();
     int opl = op, oc = oc0, orow = or0;
-    for (int q = tid; q < m4; q += 256) {  // output element oc R + orow of a plane is input (orow, oc)
+    for (int q = tid; q < mv; q += 256) {  // output element oc R + orow of a plane is input (orow, oc)
       const float* t = tile_s + opl * pst;
-      float e[4];
+      float e[V];
       int rr = orow, cc = oc;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < V; ++k) {
         e[k] = t[rr * ld + cc];
         if (++rr == R) {
           rr = 0;
           ++cc;
         }
       }
-      Io<S>::st4(dst, 4 * (int64_t)q, make_float4(e[0], e[1], e[2], e[3]));
+      st_vec<S, V>(dst, (int64_t)V * q, e);
       orow += sor;
       if (orow >= R) {
         orow -= R;
@@ -1670,8 +1701,13 @@ hipError_t launch_transpose(const S* in, S* out, int planes, int R, int C, hipSt
     const int64_t groups = ((int64_t)planes + P - 1) / P;
     const int grid = groups < 4096 ? (int)groups : 4096;
     const size_t lds = (size_t)P * R * (C + 1) * sizeof(float);
-    hipLaunchKernelGGL((transpose_small4<S>), dim3((unsigned)grid), dim3(256), lds, stream, in, out, planes, R, C,
-                       P);
+    // bf16 planes of a multiple of 8 elements on 16-byte aligned bases: eight per access
+    if (sizeof(S) == 2 && n % 8 == 0 && !(((uintptr_t)in | (uintptr_t)out) & 15))
+      hipLaunchKernelGGL((transpose_small4<S, sizeof(S) == 2 ? 8 : 4>), dim3((unsigned)grid), dim3(256), lds, stream,
+                         in, out, planes, R, C, P);
+    else
+      hipLaunchKernelGGL((transpose_small4<S, 4>), dim3((unsigned)grid), dim3(256), lds, stream, in, out, planes, R,
+                         C, P);
     return hipGetLastError();
   }
   if ((int64_t)R * (C + 1) <= kSmallPlane) {
