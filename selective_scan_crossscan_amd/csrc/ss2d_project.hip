@@ -15,7 +15,8 @@
 // workgroup takes 64 consecutive positions of one orientation (row-major from x,
 // column-major from x transposed) and produces the rows of both directions of
 // that orientation: direction 0 (or 1) at those positions, and direction 2 (or
-// 3) at the mirrored positions L-1-l.
+// 3) at the mirrored positions L-1-l.  On short maps, where the strips give few
+// workgroups, each of the two directions gets a workgroup of its own.
 //   * The projection is a (2C x D) by (D x 64) product in fp32 on
 //     v_mfma_f32_16x16x4_f32: 2C rows in 16-row tiles dealt to the four waves,
 //     the 64 positions as four 16-column tiles whose column j holds position
@@ -39,6 +40,7 @@ namespace {
 constexpr int kStrip = 64;   // positions per workgroup
 constexpr int kMaxTiles = 8;  // 16-row tiles of the stacked projection rows: 2C <= 128
 constexpr int kMaxRSteps = 16;  // steps of four over R in the dt map (R <= 64 follows from 2C <= 128)
+constexpr int64_t kSplitBelow = 512;  // workgroups (B x 2 orientations x strips) under which directions split
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,7 +54,8 @@ struct ProjParams {
   void* Cs;          // (B, 4, N, L)
   void* dts;         // (B, 4, R, L) or null: write the low-rank rows instead of the dt map
   int D, L, N, R, C, strips;
-  int tiles;  // 16-row tiles of the 2C stacked rows
+  int split;  // 1: a workgroup takes one direction of its orientation (C rows), 0: both (2C rows)
+  int tiles;  // 16-row tiles of the workgroup's stacked rows
 };
 
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
@@ -105,15 +108,27 @@ __device__ __forceinline__ void put4(S* row, int pos, int L, bool mirror, float4
 // One workgroup of four waves per 64 positions.  The 16-row tiles of the 2C
 // stacked rows are dealt to the waves (wave w takes tiles w and w + 4: MTW is
 // how many a wave may hold); the dt blocks (direction, 16 channels) likewise.
+// When the strips alone would give few workgroups (short maps), each direction
+// of an orientation gets its own workgroup (split): C stacked rows, its own dt
+// blocks, the same x strip (read twice, the second time mostly from L2).
 // VEC: L and D are multiples of 4 and the bases are aligned for the vector forms.
 template <typename S, int MTW, bool VEC>
 __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
-  extern __shared__ __align__(16) float dts[];  // [2][R][kStrip]
+  extern __shared__ __align__(16) float dts[];  // [directions of the workgroup][R][kStrip]
   const int D = p.D, L = p.L, N = p.N, R = p.R, C = p.C, MT = p.tiles;
   const int strip = blockIdx.x % p.strips;
   const int rest = blockIdx.x / p.strips;
   const int o = rest & 1;  // orientation: 0 row-major (directions 0, 2), 1 column-major (1, 3)
-  const int b = rest >> 1;
+  const bool split = p.split != 0;
+  const int kfix = split ? (rest >> 1) & 1 : 0;  // split: the workgroup's direction is o + 2 kfix
+  const int b = rest >> (split ? 2 : 1);
+  const int nrows = split ? C : 2 * C;  // stacked rows of this workgroup
+  // stacked row m: direction o + 2 kk, row c of it, and its slot kl in the dts buffer
+  auto row_of = [&](int m, int& kk, int& c, int& kl) {
+    kl = split ? 0 : (m >= C ? 1 : 0);
+    kk = split ? kfix : kl;
+    c = m - kl * C;
+  };
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, g = lane >> 4;
   const int pos = strip * kStrip + 4 * col;  // this lane's four positions
@@ -125,9 +140,10 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
     const int m = (wave + 4 * i) * 16 + col;
-    const int kk = m >= C ? 1 : 0;
-    aval[i] = m < 2 * C;
-    arow[i] = p.wx + (aval[i] ? ((int64_t)(o + 2 * kk) * C + (m - kk * C)) * D : 0);
+    int kk, c, kl;
+    row_of(m, kk, c, kl);
+    aval[i] = m < nrows;
+    arow[i] = p.wx + (aval[i] ? ((int64_t)(o + 2 * kk) * C + c) * D : 0);
   }
   const bool any = wave < MT;  // this wave holds at least one tile
   const int held = (MT - wave + 3) / 4;  // tiles this wave holds (wave-uniform): only theirs are loaded and multiplied
@@ -185,12 +201,12 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = (wave + 4 * i) * 16 + 4 * g + r;
-        if (m >= 2 * C) continue;
-        const int kk = m >= C ? 1 : 0;
-        const int c = m - kk * C;
+        if (m >= nrows) continue;
+        int kk, c, kl;
+        row_of(m, kk, c, kl);
         const float4 v = make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
         if (c < R && p.dts == nullptr) {
-          *reinterpret_cast<float4*>(dts + (kk * R + c) * kStrip + 4 * col) = v;
+          *reinterpret_cast<float4*>(dts + (kl * R + c) * kStrip + 4 * col) = v;
         } else if (c < R) {  // the low-rank rows themselves, in scan order
           const int64_t bk = (int64_t)b * 4 + o + 2 * kk;
           put4<S, VEC>(static_cast<S*>(p.dts) + (bk * R + c) * L, pos, L, kk == 1, v);
@@ -210,11 +226,11 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
   // Block jb of the 2 * nd (direction, 16 channels) blocks goes to wave jb % 4;
   // per lane it needs W_dt[k, 16m + col, 4q + g] for the R steps q, and the
   // wave's next block's are loaded before this block's products.
-  const int nd = (D + 15) / 16, nrq = (R + 3) / 4, nblk = 2 * nd;
+  const int nd = (D + 15) / 16, nrq = (R + 3) / 4, nblk = (split ? 1 : 2) * nd;
   float an[kMaxRSteps] = {};
   auto load_a = [&](int jb) {
-    const int kk = jb >= nd ? 1 : 0;
-    const int da = (jb - kk * nd) * 16 + col;
+    const int kl = jb >= nd ? 1 : 0, kk = split ? kfix : kl;
+    const int da = (jb - kl * nd) * 16 + col;
     const float* wrow = p.wdt + ((int64_t)(o + 2 * kk) * D + (da < D ? da : 0)) * R;
 #pragma unroll
     for (int q = 0; q < kMaxRSteps; ++q) {
@@ -224,8 +240,8 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
   };
   if (wave < nblk) load_a(wave);
   for (int jb = wave; jb < nblk; jb += 4) {
-    const int kk = jb >= nd ? 1 : 0;
-    const int dm = (jb - kk * nd) * 16;
+    const int kl = jb >= nd ? 1 : 0, kk = split ? kfix : kl;
+    const int dm = (jb - kl * nd) * 16;
     float ac[kMaxRSteps];
 #pragma unroll
     for (int q = 0; q < kMaxRSteps; ++q) ac[q] = an[q];
@@ -237,7 +253,7 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
     for (int q = 0; q < kMaxRSteps; ++q) {
       if (q >= nrq) continue;
       const int r = 4 * q + g;
-      const float4 v = r < R ? *reinterpret_cast<const float4*>(dts + (kk * R + r) * kStrip + 4 * col)
+      const float4 v = r < R ? *reinterpret_cast<const float4*>(dts + (kl * R + r) * kStrip + 4 * col)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int t = 0; t < 4; ++t) c4[t] = mfma_16x16x4(ac[q], comp(v, t), c4[t]);
@@ -290,11 +306,14 @@ hipError_t launch_project(const ProjectArgs& a) {
   p.R = (int)a.R;
   p.C = (int)(a.R + 2 * a.N);
   p.strips = (p.L + kStrip - 1) / kStrip;
-  p.tiles = (2 * p.C + 15) / 16;
-  if (p.tiles > kMaxTiles) return hipErrorInvalidValue;
-  const int64_t blocks = a.B * 2 * p.strips;
+  // one workgroup per direction when the strips of both orientations give fewer
+  // than two per compute unit (14x14 maps: 256 strips)
+  p.split = a.B * 2 * p.strips < kSplitBelow ? 1 : 0;
+  p.tiles = ((p.split ? 1 : 2) * p.C + 15) / 16;
+  if ((2 * p.C + 15) / 16 > kMaxTiles) return hipErrorInvalidValue;
+  const int64_t blocks = a.B * 2 * p.strips * (p.split ? 2 : 1);
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  const size_t lds = a.dts ? 0 : (size_t)2 * p.R * kStrip * sizeof(float);
+  const size_t lds = a.dts ? 0 : (size_t)(p.split ? 1 : 2) * p.R * kStrip * sizeof(float);
   const uintptr_t am = a.dtype == 0 ? 15 : 7;
   const void* dtout = a.dts ? a.dts : a.dt;
   const bool vec = p.L % 4 == 0 && p.D % 4 == 0 && !((uintptr_t)a.x & am) && !((uintptr_t)a.xT & am) &&
