@@ -41,6 +41,7 @@ constexpr int kStrip = 64;   // positions per workgroup
 constexpr int kMaxTiles = 8;  // 16-row tiles of the stacked projection rows: 2C <= 128
 constexpr int kMaxRSteps = 16;  // steps of four over R in the dt map (R <= 64 follows from 2C <= 128)
 constexpr int64_t kSplitBelow = 512;  // workgroups (B x 2 orientations x strips) under which directions split
+constexpr int kKC = 32;  // STAGED: channels per staged chunk
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -56,6 +57,7 @@ struct ProjParams {
   int D, L, N, R, C, strips;
   int split;  // 1: a workgroup takes one direction of its orientation (C rows), 0: both (2C rows)
   int tiles;  // 16-row tiles of the workgroup's stacked rows
+  int stage_off;  // STAGED: byte offset of the staging buffers in the dynamic LDS (after the dts rows)
 };
 
 __device__ __forceinline__ f32x4 mfma_16x16x4(float a, float b, f32x4 c) {
@@ -112,7 +114,17 @@ __device__ __forceinline__ void put4(S* row, int pos, int L, bool mirror, float4
 // of an orientation gets its own workgroup (split): C stacked rows, its own dt
 // blocks, the same x strip (read twice, the second time mostly from L2).
 // VEC: L and D are multiples of 4 and the bases are aligned for the vector forms.
-template <typename S, int MTW, bool VEC>
+// STAGED (VEC, D a multiple of 32, bf16 rows a multiple of 8): the operands come
+// through LDS instead, 32 channels at a time in two buffers: every wave copies
+// its share of the next chunk's x strip (32 rows of 64 positions) and weight
+// columns (the workgroup's stacked rows, 32 channels each) with the LDS form of
+// the 16-byte buffer load while the current chunk is multiplied, so the loads
+// hold no registers and one wait and barrier per chunk cover them.  The weight
+// rows are 128 bytes, so their 16-byte granules are XOR-swizzled by row pair
+// (granule q of row r sits in slot q ^ ((r / 2) % 8)) and the sixteen rows a
+// lane group reads land in sixteen different bank groups.  The products are the
+// same MFMAs on the same operands in the same order as the register form.
+template <typename S, int MTW, bool VEC, bool STAGED>
 __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
   extern __shared__ __align__(16) float dts[];  // [directions of the workgroup][R][kStrip]
   const int D = p.D, L = p.L, N = p.N, R = p.R, C = p.C, MT = p.tiles;
@@ -154,7 +166,82 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (any) {
+  if constexpr (STAGED) {
+    constexpr int kXB = kKC * kStrip * (int)sizeof(S);  // bytes of a staged x chunk
+    constexpr int kXCopies = kXB / 1024;                // wave-wide 16-byte copies per x chunk
+    constexpr int kXRowB = kStrip * (int)sizeof(S);     // bytes of a staged x row
+    const int wbytes = MT * 16 * kKC * 4;               // bytes of a staged weight chunk
+    char* stg = reinterpret_cast<char*>(dts) + p.stage_off;
+    char* const xbuf0 = stg;
+    char* const wbuf0 = stg + 2 * kXB;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(src, (uint32_t)((int64_t)D * L * (int64_t)sizeof(S)));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.wx, (uint32_t)((int64_t)4 * C * D * 4));
+    const int nwc = MT * 16 / 8;  // weight copies per chunk: eight 128-byte rows each
+    auto issue = [&](int d0, int buf) {
+#pragma unroll
+      for (int j0 = 0; j0 < kXCopies; j0 += 4) {
+        const int j = j0 + wave;
+        if (j < kXCopies) {
+          // lane's 16 bytes: row and first position inside the chunk
+          const int per = 64 * 16 / kXRowB;  // rows per copy
+          const int row = j * per + lane / (64 / per), e = (lane % (64 / per)) * (16 / (int)sizeof(S));
+          const uint32_t voff = (uint32_t)(((int64_t)(d0 + row) * L + strip * kStrip + e) * (int64_t)sizeof(S));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(xbuf0 + buf * kXB + j * 1024), 16, voff, 0, 0,
+                                                   0);
+        }
+      }
+      for (int j = wave; j < nwc; j += 4) {
+        const int r = 8 * j + (lane >> 3);          // stacked row
+        const int q = (lane & 7) ^ ((r >> 1) & 7);  // the granule this lane's slot holds
+        int kk, c, kl;
+        row_of(r < nrows ? r : 0, kk, c, kl);
+        const uint32_t voff = (uint32_t)((((int64_t)(o + 2 * kk) * C + c) * D + d0 + 4 * q) * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_t*)(wbuf0 + buf * wbytes + j * 1024), 16, voff, 0, 0,
+                                                 0);
+      }
+    };
+    const int nck = D / kKC;
+    issue(0, 0);
+    for (int ck = 0; ck < nck; ++ck) {
+      wait_vmem();      // this wave's copies of chunk ck: the only memory operations in flight
+      __syncthreads();  // every wave's copies are visible, and chunk ck - 1's buffers are free
+      if (ck + 1 < nck) issue((ck + 1) * kKC, (ck + 1) & 1);
+      if (!any) continue;
+      const char* xc = xbuf0 + (ck & 1) * kXB;
+      const char* wc = wbuf0 + (ck & 1) * wbytes;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {  // two steps of 16 channels
+        float4 bc[4], ac[MTW];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const char* xp = xc + (16 * st + 4 * g + j) * kXRowB + 4 * col * (int)sizeof(S);
+          if constexpr (sizeof(S) == 4) {
+            bc[j] = *reinterpret_cast<const float4*>(xp);
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(xp);
+            bc[j] = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xffffu),
+                                bf16_to_f32(v.y >> 16));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+          if (i >= held) break;
+          const int r = (wave + 4 * i) * 16 + col;
+          const int qs = (4 * st + g) ^ ((r >> 1) & 7);
+          ac[i] = *reinterpret_cast<const float4*>(wc + r * (kKC * 4) + 16 * qs);
+        }
+#pragma unroll
+        for (int i = 0; i < MTW; ++i) {
+          if (i >= held) break;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[i][t] = mfma_16x16x4(comp(ac[i], j), comp(bc[j], t), acc[i][t]);
+        }
+      }
+    }
+  }
+  if (any && !STAGED) {
     // operands of 16 channels: x rows dg..dg+3 at this lane's positions, and the
     // weights of this lane's rows at channels dg..dg+3 (dg = d0 + 4g), in two
     // register sets: the operands two steps ahead are loaded before this step's
@@ -193,7 +280,8 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
       mma_step(d0, 0);
       if (d0 + 16 < D) mma_step(d0 + 16, 1);
     }
-
+  }
+  if (any) {
     // lane (g, col) holds stacked rows mt*16 + 4g + r at positions pos..pos+3
 #pragma unroll
     for (int i = 0; i < MTW; ++i) {
@@ -268,12 +356,12 @@ __global__ __launch_bounds__(256) void project_kernel(ProjParams p) {
   }
 }
 
-template <typename S, bool VEC>
+template <typename S, bool VEC, bool STAGED>
 hipError_t launch_tiles(const ProjParams& p, unsigned blocks, size_t lds, hipStream_t stream) {
   if (p.tiles <= 4)
-    hipLaunchKernelGGL((project_kernel<S, 1, VEC>), dim3(blocks), dim3(256), lds, stream, p);
+    hipLaunchKernelGGL((project_kernel<S, 1, VEC, STAGED>), dim3(blocks), dim3(256), lds, stream, p);
   else
-    hipLaunchKernelGGL((project_kernel<S, 2, VEC>), dim3(blocks), dim3(256), lds, stream, p);
+    hipLaunchKernelGGL((project_kernel<S, 2, VEC, STAGED>), dim3(blocks), dim3(256), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -300,6 +388,7 @@ hipError_t launch_project(const ProjectArgs& a) {
   p.Bs = a.Bs;
   p.Cs = a.Cs;
   p.dts = a.dts;
+  p.stage_off = 0;
   p.D = (int)a.D;
   p.L = (int)(a.H * a.W);
   p.N = (int)a.N;
@@ -313,17 +402,30 @@ hipError_t launch_project(const ProjectArgs& a) {
   if ((2 * p.C + 15) / 16 > kMaxTiles) return hipErrorInvalidValue;
   const int64_t blocks = a.B * 2 * p.strips * (p.split ? 2 : 1);
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  const size_t lds = a.dts ? 0 : (size_t)(p.split ? 1 : 2) * p.R * kStrip * sizeof(float);
+  size_t lds = a.dts ? 0 : (size_t)(p.split ? 1 : 2) * p.R * kStrip * sizeof(float);
   const uintptr_t am = a.dtype == 0 ? 15 : 7;
   const void* dtout = a.dts ? a.dts : a.dt;
   const bool vec = p.L % 4 == 0 && p.D % 4 == 0 && !((uintptr_t)a.x & am) && !((uintptr_t)a.xT & am) &&
                    !((uintptr_t)dtout & am) && !((uintptr_t)a.Bs & am) && !((uintptr_t)a.Cs & am) &&
                    !((uintptr_t)a.wx & 15);
+  // staged operands: whole 32-channel chunks, 16-byte copies of x rows (a bf16 row
+  // of a multiple of 8 elements), byte offsets inside 32 bits
+  const int esz = a.dtype == 0 ? 4 : 2;
+  const size_t stage_off = (lds + 15) & ~(size_t)15;
+  const size_t staged_lds = stage_off + 2 * ((size_t)kKC * kStrip * esz + (size_t)p.tiles * 16 * kKC * 4);
+  const bool staged = vec && p.D % kKC == 0 && (a.dtype == 0 || p.L % 8 == 0) && staged_lds <= 65536 &&
+                      (int64_t)p.D * p.L * esz < ((int64_t)1 << 31) && (int64_t)4 * p.C * p.D * 4 < ((int64_t)1 << 31);
+  if (staged) {
+    p.stage_off = (int)stage_off;
+    lds = staged_lds;
+  }
   if (a.dtype == 0)
-    return vec ? launch_tiles<float, true>(p, (unsigned)blocks, lds, a.stream)
-               : launch_tiles<float, false>(p, (unsigned)blocks, lds, a.stream);
-  return vec ? launch_tiles<uint16_t, true>(p, (unsigned)blocks, lds, a.stream)
-             : launch_tiles<uint16_t, false>(p, (unsigned)blocks, lds, a.stream);
+    return staged ? launch_tiles<float, true, true>(p, (unsigned)blocks, lds, a.stream)
+                  : vec ? launch_tiles<float, true, false>(p, (unsigned)blocks, lds, a.stream)
+                        : launch_tiles<float, false, false>(p, (unsigned)blocks, lds, a.stream);
+  return staged ? launch_tiles<uint16_t, true, true>(p, (unsigned)blocks, lds, a.stream)
+                : vec ? launch_tiles<uint16_t, true, false>(p, (unsigned)blocks, lds, a.stream)
+                      : launch_tiles<uint16_t, false, false>(p, (unsigned)blocks, lds, a.stream);
 }
 
 }  // namespace ss2d
