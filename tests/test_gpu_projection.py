@@ -83,7 +83,10 @@ def _check_forward(inp, dtype):
 
 # (B, D, H, W, N, R, dtype): several 16-row tiles and 64-position strips, ragged
 # strips (L % 64), L % 4 != 0 (scalar path), D % 16 != 0 (ragged channel step),
-# one row tile (N = 1, R = 1), the 128-row maximum, bf16 storage.
+# one row tile (N = 1, R = 1), the 128-row maximum, bf16 storage.  D a multiple
+# of 32 takes the LDS-staged operands: one workgroup per direction on the small
+# maps, both directions per workgroup on the last two (at least 512 strips), with
+# a ragged last strip, in both storage types.
 SHAPES = [
     (1, 16, 8, 8, 16, 1, "f32"),
     (2, 20, 5, 7, 4, 3, "f32"),
@@ -93,6 +96,8 @@ SHAPES = [
     (1, 33, 7, 9, 16, 5, "f32"),
     (2, 48, 8, 12, 16, 2, "bf16"),
     (1, 20, 5, 7, 3, 2, "bf16"),
+    (40, 32, 20, 20, 16, 4, "f32"),
+    (64, 64, 12, 20, 16, 4, "bf16"),
 ]
 
 
