@@ -101,9 +101,11 @@ def _segments(B, D, H, W, N):
 
 # (B, D, H, W, N, dtype): maps cut into segments -- two segments of four chunks,
 # three with a ragged last segment, a ragged last chunk and a ragged channel block,
-# four segments over two batches, bf16 with N < 16
+# four segments over two batches, bf16 with N < 16; planes too large for one LDS
+# tile, whose transposes of x and dy go in 64 x 64 tiles with ragged edges (W a
+# multiple of 4 or not)
 SEG_SHAPES = [(1, 16, 32, 32, 16, "f32"), (1, 20, 40, 41, 16, "f32"), (2, 16, 48, 48, 16, "f32"),
-              (1, 16, 33, 37, 5, "bf16")]
+              (1, 16, 33, 37, 5, "bf16"), (1, 3, 96, 160, 16, "f32"), (1, 2, 100, 130, 16, "f32")]
 
 
 @pytest.mark.parametrize("shape", SEG_SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -151,6 +151,9 @@ EDGE = [
     (1, 8, 64, 33, 16, "bf16"),   # 2112 steps: a 64-step prefetched remainder
     (3, 9, 45, 48, 7, "f32"),     # D past the channel block, odd N, ragged remainder
     (1, 4, 8, 264, 16, "f32"),    # H = 8: a lane's steps span columns of the copy
+    # planes too large for one LDS tile: transposes in 64 x 64 tiles with ragged edges
+    (1, 3, 96, 160, 16, "f32"),   # H, W multiples of 4: four elements per access
+    (1, 2, 100, 130, 16, "f32"),  # W % 4 != 0: one element per access
     # 16 lanes past 512 steps (768 channel blocks, at most 64 steps after whole chunks)
     (32, 384, 24, 24, 16, "f32"),  # 576 steps: 2 chunks + a 64-step remainder
 ]
