@@ -127,11 +127,21 @@ def measured_kernel_time(workload: str, kernel: str = KERNEL_PREFIX):
     return rec
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and with whitespace runs collapsed, so that a
+    record stays valid across edits of comments alone (the sources hold no string
+    literal with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kernel: str = "ss2d_forward_kernel") -> str:
+    """Hash of the code (comments excluded) of the sources that define `kernel`."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, _CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, _CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,9 +34,12 @@
 //     workgroup; a second kernel sums the partials in a fixed order, so results
 //     are deterministic (no atomics).
 //   * Column walks read transposed copies of x and dy (made first), so every
-//     operand load is contiguous along the steps.
-//   * du goes to a temporary; a tiled kernel merges it into dx, and a small
-//     kernel sums the per-batch (and per-segment) parameter gradients.
+//     operand load is contiguous along the steps; with L a multiple of 4 and
+//     aligned rows a lane's eight steps are two 16-byte (bf16: 8-byte) loads per
+//     operand and two stores per output, also along the reversed walks.
+//   * du goes to a temporary; a merge kernel (whole planes in LDS up to 4096
+//     pixels, else 32 x 32 tiles) sums it into dx, and a small kernel sums the
+//     per-batch (and per-segment) parameter gradients.
 //   * Maps too long for one workgroup per channel block to fill the chip are cut
 //     into segments of consecutive chunks, one workgroup each, in three launches:
 //     pass A from a zero state, which also folds the segment's whole forward map
