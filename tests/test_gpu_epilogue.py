@@ -71,8 +71,9 @@ def test_channel_last_norm_matches_oracle(shape, dtype):
     assert np.array_equal(plain.double().cpu().numpy(), epilogue.channel_last(y))
 
 
-def test_defaults_are_unit_scale_zero_shift():
-    y, _, _ = _case(1, 48, 4, 6, "f32", seed=3)
+@pytest.mark.parametrize("D", [48, 384])  # gamma and beta in LDS, and read through the caches (wide rows)
+def test_defaults_are_unit_scale_zero_shift(D):
+    y, _, _ = _case(1, D, 4, 6, "f32", seed=3)
     out = _lib().channel_last(_dev(y))
     torch.cuda.synchronize()
     ref = epilogue.layer_norm_channel_last(y, eps=1e-5)
