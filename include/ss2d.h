@@ -263,7 +263,10 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
  * 16*B*4*D*ceil(L/128) + 3*B*4*S*D*N more temporary values.
  * Validation, error reporting and thread safety as for ss2d_forward; pointers
  * need element alignment: the storage type for the dtype tensors, 4 bytes for
- * the fp32 ones (SS2D_ERR_ALIGN).
+ * the fp32 ones (SS2D_ERR_ALIGN).  With L a multiple of 4 and bases aligned to
+ * 16 bytes (fp32) or 8 bytes (bf16), as torch allocates them, the kernels move
+ * four elements per access; element-aligned bases take one-element accesses and
+ * give identical results.
  */
 int ss2d_backward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
                   const void* Bs, const void* Cs, const float* Ds, const void* dy,
