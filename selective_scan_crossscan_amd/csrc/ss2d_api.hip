@@ -287,15 +287,14 @@ int describe_impl(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dty
   if (rc != SS2D_OK) return rc;
   if (!lanes_ok(lanes)) return SS2D_ERR_SHAPE;
   const ss2d::Plan pl = ss2d::make_plan(B, D, H, W, N, dtype, lanes);
-  const bool bwd = N <= 16;  // the backward takes N up to 16
   snprintf(buf, (size_t)len,
            "kernel=chunked_dpp_scan lanes_per_seq=%d steps_per_lane=%d waves=%d chans_per_block=%d "
            "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu "
            "state_blocks=%d backward_segments=%lld backward_blocks_per_workgroup=%lld",
            pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.xtrans ? 1 : 0,
            pl.transpose ? 1 : 0, (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes, pl.state_blocks,
-           bwd ? (long long)ss2d::backward_segments(B, D, H, W, N, dtype) : 0LL,
-           bwd ? (long long)ss2d::backward_blocks_per_workgroup(B, D, H, W, N, dtype) : 0LL);
+           (long long)ss2d::backward_segments(B, D, H, W, N, dtype),
+           (long long)ss2d::backward_blocks_per_workgroup(B, D, H, W, N, dtype));
   return SS2D_OK;
 }
 
@@ -529,7 +528,7 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
   if (!x || !dt || !A_log || !dt_bias || !Bs || !Cs || !Ds || !dy || !dx || !ddt || !dA_log || !ddt_bias || !dBs ||
       !dCs || !dDs)
     return SS2D_ERR_NULL;
-  int rc = check_shape(B, D, H, W, N, dtype);
+  int rc = check_shape(B, D, H, W, N, dtype, ss2d::kMaxStates);
   if (rc != SS2D_OK) return rc;
   const int64_t L = H * W;
   const int64_t sz = dtype == SS2D_BF16 ? 2 : 4;

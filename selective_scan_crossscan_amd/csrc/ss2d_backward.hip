@@ -56,6 +56,7 @@ namespace ss2d {
 namespace {
 
 constexpr int kBwdChans = 16;  // channels per channel block (a workgroup takes one or two)
+constexpr int kBwdStates = 16;  // states per pass (a DPP row holds one per lane); larger N runs in passes
 
 struct BwdParams {
   const void* x;  // x, dt, Bs, Cs, dy, xT, dyT and ddt in the storage type
@@ -81,6 +82,9 @@ struct BwdParams {
   float* segF;  //   turns F into the state entering the segment and R into the adjoint entering it
   float* segR;
   int D, H, W, L, N;
+  int Nt, n0;      // all states (the row stride of A_log, Bs, Cs, dA) and this pass's first state
+  int pass;        // state blocks of 16: 0 the only pass, 1 the first of several, 2 a middle one, 3 the last
+  float* ddt_acc;  // (B, 4, D, L) fp32 sum of ddt over the passes so far (passes 1-3)
   int nseg, nblk;  // 128-step chunks per sequence, 16-channel blocks
   int nsp, cps;    // segments, chunks per segment
 };
@@ -236,8 +240,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const int D = p.D, L = p.L, N = p.N, nch = p.nseg;
   const int c0 = sg * p.cps, c1 = min(nch, c0 + p.cps);
   const int j0 = s * kCT, jp0 = j0 + s;  // first step of this lane in the chunk, and its padded LDS slot
-  const S* Bb = static_cast<const S*>(p.Bs) + (int64_t)bk * N * L;
-  const S* Cb = static_cast<const S*>(p.Cs) + (int64_t)bk * N * L;
+  const S* Bb = static_cast<const S*>(p.Bs) + ((int64_t)bk * p.Nt + p.n0) * L;
+  const S* Cb = static_cast<const S*>(p.Cs) + ((int64_t)bk * p.Nt + p.n0) * L;
   // this thread's dCs (tid < kChunk) or dBs output step in a chunk
   static_assert(2 * kChunk == 256, "one dCs or dBs sum per thread");
   const int which = tid / kChunk, jo = tid - which * kChunk, jpo = jo + jo / kCT;
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     const BwdChan<S> cn(p, bk, (blk0 + cb) * kBwdChans + ch);
     const bool rval = cn.valid && s < N;
     const int64_t rec = (((int64_t)bk * p.nsp + sg) * D + cn.d) * N + s;  // this lane's segment record (state s)
-    rr.a2 = rval ? -expf(p.A_log[(int64_t)cn.c_idx * N + s]) * kLog2e : 0.f;
+    rr.a2 = rval ? -expf(p.A_log[(int64_t)cn.c_idx * p.Nt + p.n0 + s]) * kLog2e : 0.f;
     rr.h = MODE == kSegGrads && rval ? p.segF[rec] : 0.f;
     rr.q = MODE == kSegGrads && rval ? p.segR[rec] : 0.f;
     rr.a = 1.f;
@@ -608,11 +612,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
             for (int t = 0; t < 4; ++t) {
               const int i = 4 * g + t;
               dv[t] = fmaf(uu[i], tq[i], sa[i]) * sig[i];
-              uv[t] = fmaf(del[i], tq[i], cn.dsk * gg[i]);
               rr.dbias += dv[t];
               rr.dD = fmaf(gg[i], uu[i], rr.dD);
             }
-            Io<S>::st4(static_cast<S*>(p.ddt), cn.row + l, make_float4(dv[0], dv[1], dv[2], dv[3]));
+            if (p.pass == 0) {  // all states in one pass
+#pragma unroll
+              for (int t = 0; t < 4; ++t) uv[t] = fmaf(del[4 * g + t], tq[4 * g + t], cn.dsk * gg[4 * g + t]);
+              Io<S>::st4(static_cast<S*>(p.ddt), cn.row + l, make_float4(dv[0], dv[1], dv[2], dv[3]));
+            } else {
+              // later state passes add their du and ddt terms to the earlier ones'
+              const float4 du0 = p.pass >= 2 ? *reinterpret_cast<const float4*>(p.du + cn.row + l)
+                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+              const float4 dt0 = p.pass >= 2 ? *reinterpret_cast<const float4*>(p.ddt_acc + cn.row + l)
+                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+              const float du0v[4] = {du0.x, du0.y, du0.z, du0.w}, dt0v[4] = {dt0.x, dt0.y, dt0.z, dt0.w};
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int i = 4 * g + t;
+                uv[t] = p.pass >= 2 ? du0v[t] + del[i] * tq[i] : fmaf(del[i], tq[i], cn.dsk * gg[i]);
+                if (p.pass >= 2) dv[t] = dt0v[t] + dv[t];
+              }
+              if (p.pass == 1 || p.pass == 2)
+                *reinterpret_cast<float4*>(p.ddt_acc + cn.row + l) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+              else
+                Io<S>::st4(static_cast<S*>(p.ddt), cn.row + l, make_float4(dv[0], dv[1], dv[2], dv[3]));
+            }
             *reinterpret_cast<float4*>(p.du + cn.row + l) = make_float4(uv[0], uv[1], uv[2], uv[3]);
           }
         }
@@ -623,8 +647,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
           if (lane_step(cn, c, i, li, xi)) {
 #pragma clang fp contract(off)
             const float ddt = fmaf(uu[i], tq[i], sa[i]) * sig[i];
-            Io<S>::st(static_cast<S*>(p.ddt), cn.row + li, ddt);
-            p.du[cn.row + li] = fmaf(del[i], tq[i], cn.dsk * gg[i]);
+            const float dsum = p.pass >= 2 ? p.ddt_acc[cn.row + li] + ddt : ddt;
+            if (p.pass == 1 || p.pass == 2)
+              p.ddt_acc[cn.row + li] = dsum;
+            else
+              Io<S>::st(static_cast<S*>(p.ddt), cn.row + li, dsum);
+            p.du[cn.row + li] = p.pass >= 2 ? p.du[cn.row + li] + del[i] * tq[i] : fmaf(del[i], tq[i], cn.dsk * gg[i]);
             rr.dbias += ddt;
             rr.dD = fmaf(gg[i], uu[i], rr.dD);
           }
@@ -638,10 +666,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     const BwdChan<S> cn(p, bk, (blk0 + cb) * kBwdChans + ch);
     const float dbias = row_sum16(rr.dbias), dD = row_sum16(rr.dD);
     const int64_t pc = ((int64_t)b * p.nsp + sg) * 4 * D + cn.c_idx;  // this channel's per-(batch, segment) slot
-    if (cn.valid && s < N) p.dAp[pc * N + s] = rr.dA;
+    if (cn.valid && s < N) p.dAp[pc * p.Nt + p.n0 + s] = rr.dA;
     if (cn.valid && s == 0) {
-      p.dbp[pc] = dbias;
-      p.dDp[pc] = dD;
+      // ddt_bias adds every pass's ddt terms (in pass order); the g u sum of dDs
+      // does not depend on the states and is written by the first pass
+      p.dbp[pc] = p.pass >= 2 ? p.dbp[pc] + dbias : dbias;
+      if (p.pass <= 1) p.dDp[pc] = dD;
     }
     next_block();
   }
@@ -671,11 +701,12 @@ __global__ __launch_bounds__(256) void bwd_seg_carry(const float* __restrict__ s
   }
 }
 
-// dBs / dCs: the workgroups' partials (one per channel-block group) summed in order.
+// dBs / dCs: the workgroups' partials (one per channel-block group) summed in order,
+// into rows n0 .. n0 + N - 1 of each (batch, direction)'s Nt rows (orow = Nt L, o0 = n0 L).
 template <typename S>
 __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ dBp, const float* __restrict__ dCp,
                                                     S* __restrict__ dBs, S* __restrict__ dCs, int64_t BK,
-                                                    int nblk, int N, int L) {
+                                                    int nblk, int N, int L, int64_t orow, int64_t o0) {
   const int64_t total = BK * N * L;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int64_t bk = e / ((int64_t)N * L), rest = e - bk * N * L;
@@ -685,8 +716,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ d
       sb += dBp[src];
       sc += dCp[src];
     }
-    Io<S>::st(dBs, e, sb);
-    Io<S>::st(dCs, e, sc);
+    Io<S>::st(dBs, bk * orow + o0 + rest, sb);
+    Io<S>::st(dCs, bk * orow + o0 + rest, sc);
   }
 }
 
@@ -695,7 +726,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float* __restrict__ d
 template <typename S>
 __global__ __launch_bounds__(256) void bwd_reduce_bc4(const float* __restrict__ dBp, const float* __restrict__ dCp,
                                                      S* __restrict__ dBs, S* __restrict__ dCs, int64_t BK,
-                                                     int nblk, int64_t NL) {
+                                                     int nblk, int64_t NL, int64_t orow, int64_t o0) {
   const int64_t total4 = BK * NL / 4;
   for (int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x; e4 < total4; e4 += (int64_t)gridDim.x * 256) {
     const int64_t e = 4 * e4;
@@ -708,8 +739,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc4(const float* __restrict__ 
       sb = make_float4(sb.x + vb.x, sb.y + vb.y, sb.z + vb.z, sb.w + vb.w);
       sc = make_float4(sc.x + vc.x, sc.y + vc.y, sc.z + vc.z, sc.w + vc.w);
     }
-    Io<S>::st4(dBs, e, sb);
-    Io<S>::st4(dCs, e, sc);
+    Io<S>::st4(dBs, bk * orow + o0 + rest, sb);
+    Io<S>::st4(dCs, bk * orow + o0 + rest, sc);
   }
 }
 
@@ -848,20 +879,20 @@ hipError_t launch_chunks(const BackwardArgs& a, const BwdParams& p, int cpb, uns
   } else {
     hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegMaps, 1, VEC>), dim3(blocks), dim3(256), 0, a.stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t cols = a.B * 4 * a.D * a.N;
+    const int64_t cols = a.B * 4 * a.D * p.N;
     hipLaunchKernelGGL(bwd_seg_carry, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, a.stream, p.segP, p.segF,
-                       p.segR, cols, a.D * a.N, p.nsp);
+                       p.segR, cols, a.D * p.N, p.nsp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegGrads, 1, VEC>), dim3(blocks), dim3(256), 0, a.stream, p);
   }
   return hipGetLastError();
 }
 
-// The kernels that read or write the storage type: transposes of x and dy, the
-// chunked scan (one launch, or three for a segmented map), the dBs/dCs sums and
-// the dx merge.
+// The kernels that read or write the storage type: transposes of x and dy, then
+// per block of up to 16 states the chunked scan (one launch, or three for a
+// segmented map) and the dBs/dCs sums, then the dx merge.
 template <typename S>
-hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L, int cpb) {
+hipError_t launch_io(const BackwardArgs& a, BwdParams p, int64_t L, int cpb) {
   hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(const_cast<void*>(p.xT)),
                                      (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
   if (e != hipSuccess) return e;
@@ -875,16 +906,25 @@ hipError_t launch_io(const BackwardArgs& a, const BwdParams& p, int64_t L, int c
   const uintptr_t vm = sizeof(S) == 4 ? 15 : 7;
   const bool vec = L % 4 == 0 && !(((uintptr_t)a.x | (uintptr_t)a.dt | (uintptr_t)a.Bs | (uintptr_t)a.Cs |
                                     (uintptr_t)a.dy | (uintptr_t)a.ddt | (uintptr_t)p.xT | (uintptr_t)p.dyT) & vm);
-  e = vec ? launch_chunks<S, true>(a, p, cpb, blocks) : launch_chunks<S, false>(a, p, cpb, blocks);
-  if (e != hipSuccess) return e;
+  const int Nt = (int)a.N, passes = (Nt + kBwdStates - 1) / kBwdStates;
   const uintptr_t om = sizeof(S) == 4 ? 15 : 7;
-  if ((a.N * L) % 4 == 0 && !((uintptr_t)a.dBs & om) && !((uintptr_t)a.dCs & om))
-    hipLaunchKernelGGL((bwd_reduce_bc4<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp,
-                       static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * 4, ngrp, a.N * L);
-  else
-    hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp,
-                       static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * 4, ngrp, (int)a.N, (int)L);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int ps = 0; ps < passes; ++ps) {
+    // passes in state order: du, ddt and ddt_bias add up over them in that order
+    p.n0 = ps * kBwdStates;
+    p.N = Nt - p.n0 < kBwdStates ? Nt - p.n0 : kBwdStates;
+    p.pass = passes == 1 ? 0 : ps == 0 ? 1 : ps + 1 < passes ? 2 : 3;
+    e = vec ? launch_chunks<S, true>(a, p, cpb, blocks) : launch_chunks<S, false>(a, p, cpb, blocks);
+    if (e != hipSuccess) return e;
+    const int64_t orow = (int64_t)Nt * L, o0 = (int64_t)p.n0 * L;
+    if (((int64_t)p.N * L) % 4 == 0 && orow % 4 == 0 && o0 % 4 == 0 && !((uintptr_t)a.dBs & om) &&
+        !((uintptr_t)a.dCs & om))
+      hipLaunchKernelGGL((bwd_reduce_bc4<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp,
+                         static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * 4, ngrp, (int64_t)p.N * L, orow, o0);
+    else
+      hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp,
+                         static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * 4, ngrp, p.N, (int)L, orow, o0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const uintptr_t am = sizeof(S) == 4 ? 15 : 7;
   if (L <= kMergePlaneMax && L % 4 == 0 && !((uintptr_t)a.dx & am)) {
     // threads per plane: the fewest of 64, 128, 256 that give each a group of four pixels
@@ -911,7 +951,7 @@ constexpr int64_t kBwdPairBlocks = 768;
 
 struct BwdLayout {
   int64_t L, nch, nblk, nsp, cps, cpb;
-  size_t du, hck, dBp, dCp, dAp, dbp, dDp, cdl, segP, segF, segR, xT, dyT, total;  // byte offsets
+  size_t du, hck, dBp, dCp, dAp, dbp, dDp, cdl, segP, segF, segR, ddt_acc, xT, dyT, total;  // byte offsets
 };
 
 BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
@@ -935,18 +975,20 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int 
     at = off;
     off += up(floats);
   };
+  const int64_t Nb = N < kBwdStates ? N : kBwdStates;  // states of one pass
   take(o.du, B * 4 * D * o.L);
-  take(o.hck, B * 4 * o.nch * D * N * 16);
-  take(o.dBp, B * 4 * ngrp * N * o.L);
-  take(o.dCp, B * 4 * ngrp * N * o.L);
+  take(o.hck, B * 4 * o.nch * D * Nb * 16);
+  take(o.dBp, B * 4 * ngrp * Nb * o.L);
+  take(o.dCp, B * 4 * ngrp * Nb * o.L);
   take(o.dAp, B * o.nsp * 4 * D * N);
   take(o.dbp, B * o.nsp * 4 * D);
   take(o.dDp, B * o.nsp * 4 * D);
   const bool seg = o.nsp > 1;
   take(o.cdl, seg ? B * 4 * o.nch * D * 16 : 0);
-  take(o.segP, seg ? B * 4 * o.nsp * D * N : 0);
-  take(o.segF, seg ? B * 4 * o.nsp * D * N : 0);
-  take(o.segR, seg ? B * 4 * o.nsp * D * N : 0);
+  take(o.segP, seg ? B * 4 * o.nsp * D * Nb : 0);
+  take(o.segF, seg ? B * 4 * o.nsp * D * Nb : 0);
+  take(o.segR, seg ? B * 4 * o.nsp * D * Nb : 0);
+  take(o.ddt_acc, N > kBwdStates ? B * 4 * D * o.L : 0);  // ddt summed over the passes
   take(o.xT, B * D * o.L);  // the transposed copies are sized for fp32 (bf16 uses half)
   take(o.dyT, B * D * o.L);
   o.total = off;
@@ -999,6 +1041,10 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.W = (int)a.W;
   p.L = (int)o.L;
   p.N = (int)a.N;
+  p.Nt = (int)a.N;
+  p.n0 = 0;
+  p.pass = 0;
+  p.ddt_acc = a.N > kBwdStates ? f(o.ddt_acc) : nullptr;
   p.nseg = (int)o.nch;
   p.nblk = (int)o.nblk;
   p.nsp = (int)o.nsp;

@@ -56,9 +56,12 @@ int main(void) {
   expect("backward valid", ss2d_backward(p[0], p[1], fp[2], fp[3], p[4], p[5], fp[6], p[13], p[14], p[15],
                                          (float*)p[16], (float*)p[17], p[18], p[19], (float*)p[20], 2, 3, 4, 5, 16, 0, 0),
          -7);
+  expect("backward N = 257", ss2d_backward(p[0], p[1], fp[2], fp[3], p[4], p[5], fp[6], p[13], p[14], p[15],
+                                           (float*)p[16], (float*)p[17], p[18], p[19], (float*)p[20], 2, 3, 4, 5, 257, 0,
+                                           0), -3);
   expect("backward N = 17", ss2d_backward(p[0], p[1], fp[2], fp[3], p[4], p[5], fp[6], p[13], p[14], p[15],
                                           (float*)p[16], (float*)p[17], p[18], p[19], (float*)p[20], 2, 3, 4, 5, 17, 0,
-                                          0), -3);
+                                          0), -7);
   ss2d_peaks pk;
   expect("measure_peaks bad size", ss2d_measure_peaks(&pk, 1000, 0), -2);
 

@@ -100,9 +100,10 @@ def test_lanes_per_call():
 
 
 def test_describe_state_blocks():
-    """N > 16 runs over blocks of 16 states; the backward figures are 0 (it takes N <= 16)."""
+    """N > 16 runs over blocks of 16 states, in the forward and the backward alike (the
+    backward's segments and channel blocks per workgroup do not depend on N)."""
     f = dict(kv.split("=") for kv in ss2d.describe(2, 32, 8, 8, 256).split())
-    assert f["state_blocks"] == "16" and f["backward_segments"] == "0"
+    assert f["state_blocks"] == "16" and f["backward_segments"] == "1"
     f = dict(kv.split("=") for kv in ss2d.describe(2, 32, 8, 8, 17).split())
     assert f["state_blocks"] == "2"
     f = dict(kv.split("=") for kv in ss2d.describe(2, 32, 8, 8, 16).split())
@@ -358,7 +359,8 @@ def test_backward_validation():
     p = [X, DT, AL, BI, BS, CS, DS] + GRAD
     p[0] = X + 1                          # bf16 tensors need 2-byte alignment
     assert _bwd(p, dtype=1) == -6
-    assert _bwd(N=17) == -3
+    assert _bwd(N=0) == -3
+    assert _bwd(N=257) == -3              # up to 256 states, in passes of 16
     assert _bwd(W=0) == -2
     p = [X, DT, AL, BI, BS, CS, DS] + GRAD
     p[8] = X                              # dx on top of x
@@ -375,6 +377,8 @@ def test_backward_validation():
 def test_backward_valid_calls_without_device_report_no_device():
     assert _bwd(dtype=1) == -7            # bf16 is accepted
     assert _bwd() == -7
+    assert _bwd(N=17) == -7               # more than 16 states run in passes
+    assert _bwd(N=256, dtype=1) == -7
 
 
 # the no-allocation forward: same validation, plus the static array's limit

@@ -194,6 +194,20 @@ def test_backward_full_size_batch_element(cfg, nsp, cpb):
         assert e <= (1e-2 if bf16 else TOL[k]), (k, e)
 
 
+# (B, D, H, W, N, dtype): more than 16 states run in passes of 16 states whose
+# du, ddt and ddt_bias add up in pass order: two passes (16 + 1), three with a
+# middle pass, bf16, a segmented map, and one-element accesses (L % 4 != 0)
+LARGE_N = [(1, 20, 12, 11, 17, "f32"), (2, 16, 16, 16, 40, "f32"), (1, 20, 12, 12, 24, "bf16"),
+           (1, 16, 32, 32, 20, "f32"), (1, 5, 7, 9, 33, "f32")]
+
+
+@pytest.mark.parametrize("shape", LARGE_N, ids=lambda s: "x".join(map(str, s)))
+def test_backward_large_state(shape):
+    *dims, dtype = shape
+    print(f"[backward large state] {shape}", flush=True)
+    _run(*dims, seed=sum(dims) + 13, dtype=dtype)
+
+
 def _check_batch_element_and_channels(shape, idx, seed):
     """Full GPU backward of `shape` (storage type as the shape says); the oracle on batch
     element 0 (dx, ddt, dBs, dCs) and on the channels `idx` alone (dA_log, ddt_bias, dDs,
@@ -231,6 +245,15 @@ def _check_batch_element_and_channels(shape, idx, seed):
         e = float(np.linalg.norm(g - ref[k]) / np.linalg.norm(ref[k]))
         print(k, f"{e:.2e}", flush=True)
         assert e <= TOL[k], (k, e)
+
+
+def test_backward_large_state_at_stage1_size():
+    # the VMamba-T stage-1 shape at N = 64: four passes, each with two channel
+    # blocks per workgroup, checked on batch element 0 and three channels
+    shape = ss2d_inputs.Shape("vmamba_t_stage1_n64", 32, 192, 56, 56, 64, "f32")
+    assert _plan(32, 192, 56, 56, 64) == {"backward_segments": 1, "backward_blocks_per_workgroup": 2}
+    print(f"[backward large state, full size] {shape}", flush=True)
+    _check_batch_element_and_channels(shape, [0, 77, 191], seed=21)
 
 
 @pytest.mark.parametrize("dims,dtype", [((32, 192, 16, 16, 5), "f32"), ((28, 200, 16, 16, 16), "f32"),
