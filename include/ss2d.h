@@ -36,7 +36,7 @@ typedef enum {
   SS2D_ERR_NULL = -1,           /* a required pointer is NULL                     */
   SS2D_ERR_SHAPE = -2,          /* B, D, H or W < 1, H*W > 2^25 - 1, or a size    */
                                 /* overflows int64                                */
-  SS2D_ERR_UNSUPPORTED_N = -3,  /* N outside 1..256 (forward), 1..16 (others)     */
+  SS2D_ERR_UNSUPPORTED_N = -3,  /* N outside 1..256 (1..16 for the projections)   */
   SS2D_ERR_DTYPE = -4,          /* dtype is not an ss2d_dtype value               */
   SS2D_ERR_ALIAS = -5,          /* y overlaps one of the inputs                   */
   SS2D_ERR_ALIGN = -6,          /* a pointer is not aligned to its element size   */
@@ -252,15 +252,19 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
  *           dDs     [4*D]          fp32   summed over the batch and steps
  * Every output is fully overwritten (no accumulation into existing values) and
  * must not overlap an input or another output (SS2D_ERR_ALIAS).  All arithmetic
- * is fp32; bf16 outputs are rounded once.  N is 1..16.  All sums run in a fixed
- * order, so results are deterministic.  Takes a stream-ordered temporary of at
- * most about B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*N*L + 16*B*4*D*N*ceil(L/128)
- * fp32 values (du, transposed copies of x and dy, dBs and dCs partials, one per
- * workgroup of one or two 16-channel blocks, the state entering every 8 steps)
- * and runs six kernels on `stream`.
+ * is fp32; bf16 outputs are rounded once.  N is 1..256: more than 16 states run
+ * in passes of 16 states, each writing its states' dA_log, dBs and dCs, with du,
+ * ddt and ddt_bias summed over the passes in pass order (ddt in fp32 until the
+ * last pass rounds it).  All sums run in a fixed order, so results are
+ * deterministic.  Takes a stream-ordered temporary of at most about
+ * B*4*D*L + 2*B*D*L + 2*B*4*ceil(D/16)*n*L + 16*B*4*D*n*ceil(L/128) + B*4*D*N
+ * fp32 values with n = min(N, 16) (du, transposed copies of x and dy, dBs and
+ * dCs partials, one per workgroup of one or two 16-channel blocks, the state
+ * entering every 8 steps, the dA_log partials), plus B*4*D*L for the ddt sum
+ * when N > 16, and runs four kernels per pass and three more on `stream`.
  * When B*4*ceil(D/16) is small, each sequence is cut into S segments of at least
  * 512 steps (S from ss2d_describe): two more kernels, and about
- * 16*B*4*D*ceil(L/128) + 3*B*4*S*D*N more temporary values.
+ * 16*B*4*D*ceil(L/128) + 3*B*4*S*D*n more temporary values.
  * Validation, error reporting and thread safety as for ss2d_forward; pointers
  * need element alignment: the storage type for the dtype tensors, 4 bytes for
  * the fp32 ones (SS2D_ERR_ALIGN).  With L a multiple of 4 and bases aligned to
