@@ -177,7 +177,7 @@ const char* ss2d_status_string(int status) {
     case SS2D_OK: return "ok";
     case SS2D_ERR_NULL: return "a required pointer is NULL";
     case SS2D_ERR_SHAPE: return "invalid shape: B, D, H, W must be >= 1 and sizes must fit";
-    case SS2D_ERR_UNSUPPORTED_N: return "unsupported state size N (forward: 1..256; projection and backward: 1..16)";
+    case SS2D_ERR_UNSUPPORTED_N: return "unsupported state size N (1..256; projections: 1..16)";
     case SS2D_ERR_DTYPE: return "unknown dtype (0 = fp32, 1 = bf16)";
     case SS2D_ERR_ALIAS: return "output y overlaps an input";
     case SS2D_ERR_ALIGN: return "a pointer is not aligned to its element size";
