@@ -85,3 +85,60 @@ def bidir_brute(x, dt, A_log, dt_bias, Bs, Cs, Ds):
                             acc += float(Cs[b, j, n, l]) * np.exp(A[n] * s) * delta[i] * float(Bs[b, j, n, i]) * u[i]
                     y[b, d, visited_token(j, l, L)] += acc
     return y
+
+
+def _paths(v):
+    """(B, D, L) -> (B, 2, D, L): the tokens in each path's step order."""
+    return np.stack([v, v[:, :, ::-1]], axis=1)
+
+
+def bidir_backward_f64(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy):
+    """Gradients of sum(dy * y) for the two-path scan above, by the chain rule along
+    each path (the same derivation as the four-direction backward, with the two
+    token orders as the walks):
+        u_l, g_l         x and dy at the token the path visits at step l
+        q_l            = Cs[n,l] g_l + a_{l+1} q_{l+1},  q_L = 0  (the state adjoint)
+        dCs[n,l]       = sum_d h_l g_l,        dBs[n,l] = sum_d q_l delta_l u_l
+        du_l           = sum_n q_l delta_l Bs[n,l] + Ds[c] g_l,  dx[t] = du of both paths at t
+        ddt_l          = sigmoid(dt_l + dt_bias[c]) sum_n q_l (A a_l h_{l-1} + Bs[n,l] u_l)
+        dA_log[c,n]    = A sum_{b,l} q_l delta_l a_l h_{l-1}
+        ddt_bias[c]    = sum_{b,l} ddt_l,      dDs[c] = sum_{b,l} g_l u_l.
+    Shapes as for bidir_f64, dy (B, D, L).  Returns a dict with dx, ddt, dA_log,
+    ddt_bias, dBs, dCs, dDs in float64."""
+    f = lambda a: np.asarray(a, dtype=np.float64)
+    x, dt, A_log, dt_bias, Bs, Cs, Ds, dy = (f(v) for v in (x, dt, A_log, dt_bias, Bs, Cs, Ds, dy))
+    B, D, L = x.shape
+    N = A_log.shape[1]
+    u, g = _paths(x), _paths(dy)                          # (B, 2, D, L)
+    pre = dt + dt_bias.reshape(2, D)[None, :, :, None]
+    delta = _softplus(pre)
+    A = -np.exp(A_log).reshape(2, D, N)
+    a = np.exp(delta[:, :, :, None, :] * A[None, :, :, :, None])   # (B, 2, D, N, L)
+    Bn, Cn = Bs[:, :, None], Cs[:, :, None]               # (B, 2, 1, N, L)
+    inp = (delta * u)[:, :, :, None, :] * Bn
+    h = np.empty_like(a)
+    state = np.zeros(a.shape[:-1])
+    for l in range(L):
+        state = a[..., l] * state + inp[..., l]
+        h[..., l] = state
+    h_before = np.zeros_like(h)
+    h_before[..., 1:] = h[..., :-1]
+    q = np.empty_like(a)
+    adj = np.zeros(a.shape[:-1])
+    for l in range(L - 1, -1, -1):
+        decay_next = a[..., l + 1] if l + 1 < L else 0.0
+        adj = Cn[..., l] * g[:, :, :, None, l] + decay_next * adj
+        q[..., l] = adj
+    du = (q * delta[:, :, :, None, :] * Bn).sum(axis=3) + Ds.reshape(2, D)[None, :, :, None] * g
+    ddt = (q * (A[None, :, :, :, None] * a * h_before + Bn * u[:, :, :, None, :])).sum(axis=3) / (1.0 + np.exp(-pre))
+    dA = (q * delta[:, :, :, None, :] * a * h_before).sum(axis=(0, 4))
+    dx = du[:, 0] + du[:, 1, :, ::-1]
+    return {
+        "dx": dx,
+        "ddt": ddt,
+        "dA_log": (dA * A).reshape(2 * D, N),
+        "ddt_bias": ddt.sum(axis=(0, 3)).reshape(2 * D),
+        "dBs": (q * (delta * u)[:, :, :, None, :]).sum(axis=2),
+        "dCs": (h * g[:, :, :, None, :]).sum(axis=2),
+        "dDs": (g * u).sum(axis=(0, 3)).reshape(2 * D),
+    }

@@ -6,6 +6,8 @@ summed per token.  The oracle is pinned by a hand-worked example, an O(L^2)
 unrolled form, its equality with the (separately pinned) four-direction oracle on
 a one-row map whose column directions contribute nothing, the reversal
 symmetry, the skip-only limit, and planted mistakes that these checks reject.
+Its backward is pinned by central differences through the forward oracle and by
+its equality with the (separately pinned) four-direction backward on such a map.
 """
 import importlib.util
 import json
@@ -95,6 +97,56 @@ def test_bs_zero_gives_skip_only():
     inp["Ds"] = np.array([0.5, -1.0, 2.0, 0.25])
     want = (inp["Ds"][:2] + inp["Ds"][2:])[None, :, None] * inp["x"].astype(np.float64)
     np.testing.assert_allclose(bidir.bidir_f64(**inp), want, rtol=1e-14)
+
+
+# ---- the two-path backward (bidir_backward_f64)
+
+def _dy(inp, seed):
+    return np.random.default_rng(seed).standard_normal(np.asarray(inp["x"]).shape)
+
+
+def test_backward_matches_central_differences():
+    """Every gradient against central differences of sum(dy * y) through the forward
+    oracle (pinned above), one input element at a time."""
+    inp = {k: np.asarray(v, np.float64).copy() for k, v in ss2d_inputs.bidir_random(2, 2, 6, 3, seed=5).items()}
+    dy = _dy(inp, 6)
+    got = bidir.bidir_backward_f64(**inp, dy=dy)
+    names = {"x": "dx", "dt": "ddt", "A_log": "dA_log", "dt_bias": "ddt_bias", "Bs": "dBs", "Cs": "dCs", "Ds": "dDs"}
+    eps = 1e-6
+    for name, gname in names.items():
+        v = inp[name]
+        num = np.zeros_like(v)
+        for i in np.ndindex(v.shape):
+            old = v[i]
+            v[i] = old + eps
+            up = np.sum(dy * bidir.bidir_f64(**inp))
+            v[i] = old - eps
+            down = np.sum(dy * bidir.bidir_f64(**inp))
+            v[i] = old
+            num[i] = (up - down) / (2 * eps)
+        assert got[gname].shape == v.shape, name
+        np.testing.assert_allclose(got[gname], num, rtol=1e-6, atol=1e-7 * np.max(np.abs(num)), err_msg=name)
+
+
+@pytest.mark.parametrize("L,N", [(9, 5), (40, 16)])
+def test_backward_equals_four_direction_backward_on_one_row(L, N):
+    """The two paths as directions 0 and 2 of a 1 x L map (directions 1 and 3 add
+    nothing): the (separately pinned) four-direction backward gives the same
+    gradients for the two paths' slots, and dx."""
+    from oracle import backward
+    inp = ss2d_inputs.bidir_random(2, 3, L, N, seed=L + 2 * N)
+    dy = _dy(inp, L)
+    got = bidir.bidir_backward_f64(**inp, dy=dy)
+    want = backward.ss2d_backward_f64(**_as_cross_scan(inp), dy=dy.reshape(2, 3, 1, L))
+    D = 3
+    np.testing.assert_allclose(got["dx"], want["dx"].reshape(2, D, L), rtol=1e-11, atol=1e-12)
+    for j, k in ((0, 0), (1, 2)):
+        np.testing.assert_allclose(got["ddt"][:, j], want["ddt"][:, k], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(got["dBs"][:, j], want["dBs"][:, k], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(got["dCs"][:, j], want["dCs"][:, k], rtol=1e-11, atol=1e-12)
+        for name in ("dA_log", "ddt_bias", "dDs"):
+            np.testing.assert_allclose(got[name][j * D:(j + 1) * D], want[name][k * D:(k + 1) * D], rtol=1e-11,
+                                       atol=1e-12, err_msg=name)
 
 
 def _pins_pass(mod) -> bool:
