@@ -278,6 +278,32 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
                   float* dDs, int64_t B, int64_t D, int64_t H, int64_t W, int64_t N,
                   int dtype, void* stream);
 
+/*
+ * ss2d_bidir_backward -- the gradients of ss2d_bidir_forward given dy, the
+ * gradient of a loss with respect to y: the chain rule along each of the two
+ * paths of [VSSD] page "项目概述：当视觉Transformer遇到状态空间模型" §2.2, exactly as
+ * ss2d_backward does along the cross scan's directions, with the state adjoint
+ * q_l = Cs[b,j,n,l] dy[b,d,t_j(l)] + exp(delta_{l+1} A) q_{l+1} walked from the
+ * end of each path.
+ *   inputs  x, dt, A_log, dt_bias, Bs, Cs, Ds  as for ss2d_bidir_forward;
+ *           dy      [B, D, L]      dtype
+ *   outputs dx      [B, D, L]      dtype  (both paths' terms at each token)
+ *           ddt     [B, 2, D, L]   dtype  (each path's step order)
+ *           dA_log  [2*D, N]       fp32   summed over the batch
+ *           ddt_bias[2*D]          fp32   summed over the batch and steps
+ *           dBs, dCs[B, 2, N, L]   dtype  summed over the D channels
+ *           dDs     [2*D]          fp32   summed over the batch and steps
+ *   N       1..256 (passes of 16 states, as in ss2d_backward)
+ * Overwrite, aliasing, arithmetic, determinism, temporaries (without the
+ * transposed copies: a sequence has no column walk), validation, alignment,
+ * error reporting and thread safety as for ss2d_backward with H = 1, W = L.
+ */
+int ss2d_bidir_backward(const void* x, const void* dt, const float* A_log, const float* dt_bias,
+                        const void* Bs, const void* Cs, const float* Ds, const void* dy,
+                        void* dx, void* ddt, float* dA_log, float* ddt_bias, void* dBs, void* dCs,
+                        float* dDs, int64_t B, int64_t D, int64_t L, int64_t N,
+                        int dtype, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ss2d_status_string(int status);
 

@@ -12,7 +12,7 @@ import os
 import threading
 
 __all__ = ["forward", "ss2d_forward", "project", "ss2d_project", "forward_from_x", "ss2d_forward_from_x",
-           "channel_last", "ss2d_channel_last", "backward", "ss2d_backward", "measure_peaks", "describe", "bidir_forward", "ss2d_bidir_forward", "ss2d_forward_noalloc", "trim_memory", "status_string", "version", "library_path", "lib",
+           "channel_last", "ss2d_channel_last", "backward", "ss2d_backward", "measure_peaks", "describe", "bidir_forward", "ss2d_bidir_forward", "bidir_backward", "ss2d_bidir_backward", "ss2d_forward_noalloc", "trim_memory", "status_string", "version", "library_path", "lib",
            "SS2D_F32", "SS2D_BF16", "SS2DError"]
 
 SS2D_F32 = 0
@@ -81,6 +81,8 @@ def lib():
             L.ss2d_channel_last.restype = ctypes.c_int
             L.ss2d_backward.argtypes = [vp] * 15 + [i64] * 5 + [ctypes.c_int, vp]
             L.ss2d_backward.restype = ctypes.c_int
+            L.ss2d_bidir_backward.argtypes = [vp] * 15 + [i64] * 4 + [ctypes.c_int, vp]
+            L.ss2d_bidir_backward.restype = ctypes.c_int
             L.ss2d_measure_peaks.argtypes = [ctypes.POINTER(Peaks), i64, vp]
             L.ss2d_measure_peaks.restype = ctypes.c_int
             _lib = L
@@ -280,18 +282,44 @@ def ss2d_backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bi
                                B, D, H, W, N, int(dtype), stream)
 
 
+def ss2d_bidir_backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs, B, D, L, N,
+                        dtype, stream) -> int:
+    """Raw C-ABI call with integer device addresses; returns the status code."""
+    return lib().ss2d_bidir_backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs,
+                                     dDs, B, D, L, N, int(dtype), stream)
+
+
 def backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream=None) -> dict:
     """Gradients of the forward given dy (ss2d_backward), tensors on one ROCm device.
 
     x, dt, Bs, Cs, dy: float32 or bfloat16, all the same; A_log, dt_bias, Ds: float32.
     Returns dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs (shapes and dtypes of the matching inputs)."""
+    if x.dim() != 4:
+        raise ValueError("x must be (B, D, H, W)")
+    return _backward_k(4, x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream)
+
+
+def bidir_backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream=None) -> dict:
+    """Gradients of the two-path scan given dy (ss2d_bidir_backward): x, dy (B,D,L);
+    dt (B,2,D,L), Bs/Cs (B,2,N,L) in each path's order; A_log (2D,N), dt_bias, Ds (2D,).
+    Returns dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs (shapes and dtypes of the matching inputs)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (B, D, L)")
+    return _backward_k(2, x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream)
+
+
+def _backward_k(K, x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream) -> dict:
     import torch
 
     code = _dtype_code(x)
     for t in (dt, Bs, Cs, dy):
         if t.dtype != x.dtype:
             raise TypeError("x, dt, Bs, Cs and dy must share one dtype")
-    B, D, H, W = x.shape
+    if K == 4:
+        B, D, H, W = x.shape
+    else:
+        B, D, W = x.shape
+        H = 1
     N = A_log.shape[-1]
     ins = (x, dt, A_log, dt_bias, Bs, Cs, Ds, dy)
     if tuple(dy.shape) != tuple(x.shape):
@@ -303,8 +331,12 @@ def backward(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, stream=None) -> dict:
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
-        rc = ss2d_backward(*(t.data_ptr() for t in ins), *(t.data_ptr() for t in out.values()), B, D, H, W, N,
-                           code, stream.cuda_stream)
+        if K == 4:
+            rc = ss2d_backward(*(t.data_ptr() for t in ins), *(t.data_ptr() for t in out.values()), B, D, H, W, N,
+                               code, stream.cuda_stream)
+        else:
+            rc = ss2d_bidir_backward(*(t.data_ptr() for t in ins), *(t.data_ptr() for t in out.values()), B, D, W,
+                                     N, code, stream.cuda_stream)
     if rc != 0:
         _raise(rc)
     return out

@@ -351,6 +351,59 @@ int check_projection(int64_t D, int64_t N, int64_t R, const float* wx, const flo
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The backward of ss2d_backward (K = 4) and ss2d_bidir_backward (K = 2).
+int backward_impl(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                  const void* Cs, const float* Ds, const void* dy, void* dx, void* ddt, float* dA_log,
+                  float* ddt_bias, void* dBs, void* dCs, float* dDs, int64_t B, int64_t D, int64_t H, int64_t W,
+                  int64_t N, int dtype, int K, void* stream) {
+  if (!x || !dt || !A_log || !dt_bias || !Bs || !Cs || !Ds || !dy || !dx || !ddt || !dA_log || !ddt_bias || !dBs ||
+      !dCs || !dDs)
+    return SS2D_ERR_NULL;
+  int rc = check_shape(B, D, H, W, N, dtype, ss2d::kMaxStates);
+  if (rc != SS2D_OK) return rc;
+  const int64_t L = H * W;
+  const int64_t sz = dtype == SS2D_BF16 ? 2 : 4;
+  const int64_t xb = B * D * L * sz, dtb = B * K * D * L * sz, bcb = B * K * N * L * sz, pb = K * D * N * 4,
+                vb = K * D * 4;
+  const void* ins[8] = {x, dt, A_log, dt_bias, Bs, Cs, Ds, dy};
+  const int64_t isz[8] = {xb, dtb, pb, vb, bcb, bcb, vb, xb};
+  const void* outs[7] = {dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs};
+  const int64_t osz[7] = {xb, dtb, pb, vb, bcb, bcb, vb};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return SS2D_ERR_ALIAS;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SS2D_ERR_ALIAS;
+  }
+  // storage-type tensors need element alignment, the fp32 per-channel ones 4 bytes
+  const bool io_in[8] = {true, true, false, false, true, true, false, true};
+  const bool io_out[7] = {true, true, false, false, true, true, false};
+  for (int j = 0; j < 8; ++j)
+    if ((uintptr_t)ins[j] & (uintptr_t)(io_in[j] ? sz - 1 : 3)) return SS2D_ERR_ALIGN;
+  for (int i = 0; i < 7; ++i)
+    if ((uintptr_t)outs[i] & (uintptr_t)(io_out[i] ? sz - 1 : 3)) return SS2D_ERR_ALIGN;
+  DeviceInfo di;
+  rc = device_info(&di);
+  if (rc != SS2D_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* tmp = nullptr;
+  hipError_t e = tmp_alloc(di, &tmp, ss2d::backward_scratch_bytes(B, D, H, W, N, dtype, K), st);
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  ss2d::BackwardArgs a{x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs,
+                       B, D, H, W, N, dtype, st, K};
+  e = ss2d::launch_backward(a, tmp);
+  hipError_t e2 = tmp_free(tmp, st);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) {
+    remember(e);
+    return SS2D_ERR_HIP;
+  }
+  return SS2D_OK;
+}
+
 // Largest rank for which ss2d_forward_from_x hands the scan the low-rank rows.
 constexpr int64_t kFromXLowRankUpTo = 8;
 
@@ -525,52 +578,17 @@ int ss2d_backward(const void* x, const void* dt, const float* A_log, const float
                   const void* Cs, const float* Ds, const void* dy, void* dx, void* ddt, float* dA_log,
                   float* ddt_bias, void* dBs, void* dCs, float* dDs, int64_t B, int64_t D, int64_t H, int64_t W,
                   int64_t N, int dtype, void* stream) {
-  if (!x || !dt || !A_log || !dt_bias || !Bs || !Cs || !Ds || !dy || !dx || !ddt || !dA_log || !ddt_bias || !dBs ||
-      !dCs || !dDs)
-    return SS2D_ERR_NULL;
-  int rc = check_shape(B, D, H, W, N, dtype, ss2d::kMaxStates);
-  if (rc != SS2D_OK) return rc;
-  const int64_t L = H * W;
-  const int64_t sz = dtype == SS2D_BF16 ? 2 : 4;
-  const int64_t xb = B * D * L * sz, dtb = B * 4 * D * L * sz, bcb = B * 4 * N * L * sz, pb = 4 * D * N * 4,
-                vb = 4 * D * 4;
-  const void* ins[8] = {x, dt, A_log, dt_bias, Bs, Cs, Ds, dy};
-  const int64_t isz[8] = {xb, dtb, pb, vb, bcb, bcb, vb, xb};
-  const void* outs[7] = {dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs};
-  const int64_t osz[7] = {xb, dtb, pb, vb, bcb, bcb, vb};
-  for (int i = 0; i < 7; ++i) {
-    for (int j = 0; j < 8; ++j)
-      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return SS2D_ERR_ALIAS;
-    for (int j = i + 1; j < 7; ++j)
-      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return SS2D_ERR_ALIAS;
-  }
-  // storage-type tensors need element alignment, the fp32 per-channel ones 4 bytes
-  const bool io_in[8] = {true, true, false, false, true, true, false, true};
-  const bool io_out[7] = {true, true, false, false, true, true, false};
-  for (int j = 0; j < 8; ++j)
-    if ((uintptr_t)ins[j] & (uintptr_t)(io_in[j] ? sz - 1 : 3)) return SS2D_ERR_ALIGN;
-  for (int i = 0; i < 7; ++i)
-    if ((uintptr_t)outs[i] & (uintptr_t)(io_out[i] ? sz - 1 : 3)) return SS2D_ERR_ALIGN;
-  DeviceInfo di;
-  rc = device_info(&di);
-  if (rc != SS2D_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  void* tmp = nullptr;
-  hipError_t e = tmp_alloc(di, &tmp, ss2d::backward_scratch_bytes(B, D, H, W, N, dtype), st);
-  if (e != hipSuccess) {
-    remember(e);
-    return SS2D_ERR_HIP;
-  }
-  ss2d::BackwardArgs a{x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs,
-                       B, D, H, W, N, dtype, st};
-  e = ss2d::launch_backward(a, tmp);
-  hipError_t e2 = tmp_free(tmp, st);
-  if (e == hipSuccess) e = e2;
-  if (e != hipSuccess) {
-    remember(e);
-    return SS2D_ERR_HIP;
-  }
-  return SS2D_OK;
+  return backward_impl(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs, B, D, H, W, N,
+                       dtype, 4, stream);
+}
+
+int ss2d_bidir_backward(const void* x, const void* dt, const float* A_log, const float* dt_bias, const void* Bs,
+                        const void* Cs, const float* Ds, const void* dy, void* dx, void* ddt, float* dA_log,
+                        float* ddt_bias, void* dBs, void* dCs, float* dDs, int64_t B, int64_t D, int64_t L,
+                        int64_t N, int dtype, void* stream) {
+  // one row of L tokens, as for ss2d_bidir_forward: the two paths are the row walk and its reverse
+  return backward_impl(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy, dx, ddt, dA_log, ddt_bias, dBs, dCs, dDs, B, D, 1, L, N,
+                       dtype, 2, stream);
 }
 
 }  // extern "C"

@@ -82,6 +82,7 @@ struct BwdParams {
   float* segF;  //   turns F into the state entering the segment and R into the adjoint entering it
   float* segR;
   int D, H, W, L, N;
+  int K;           // directions: 4 (the cross scan) or 2 (the two-path scan over a 1 x L sequence)
   int Nt, n0;      // all states (the row stride of A_log, Bs, Cs, dA) and this pass's first state
   int pass;        // state blocks of 16: 0 the only pass, 1 the first of several, 2 a middle one, 3 the last
   float* ddt_acc;  // (B, 4, D, L) fp32 sum of ddt over the passes so far (passes 1-3)
@@ -181,12 +182,14 @@ struct BwdChan {
   const S* xs;   // u along the direction's walk (x or its transpose)
   const S* gs;   // g likewise
   const S* dtr;  // dt row
-  int64_t row;   // start of the (b, k, d) row in (B, 4, D, L) tensors
+  int64_t row;   // start of the (b, k, d) row in (B, K, D, L) tensors
   __device__ BwdChan(const BwdParams& p, int bk, int dd) {
-    const int k = bk & 3, b = bk >> 2, D = p.D, L = p.L;
+    // slot j of K; the walk k: 0 rows, 1 columns, 2 and 3 the same reversed (K = 2: 0 and 2)
+    const int j = p.K == 4 ? (bk & 3) : (bk & 1), b = p.K == 4 ? bk >> 2 : bk >> 1;
+    const int k = p.K == 4 ? j : 2 * j, D = p.D, L = p.L;
     valid = dd < D;
     d = valid ? dd : 0;
-    c_idx = k * D + d;
+    c_idx = j * D + d;
     bias = p.dt_bias[c_idx];
     dsk = p.Ds[c_idx];
     xs = static_cast<const S*>((k & 1) ? p.xT : p.x) + ((int64_t)b * D + d) * L;
@@ -235,8 +238,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   const int grp = wid / p.nsp;
   const int ngrp = (p.nblk + CPB - 1) / CPB;
   const int blk0 = (grp % ngrp) * CPB;  // this workgroup's first channel block
-  const int bk = grp / ngrp;            // b * 4 + k
-  const int k = bk & 3, b = bk >> 2;
+  const int bk = grp / ngrp;            // b * K + the direction's slot
+  const int k = p.K == 4 ? (bk & 3) : 2 * (bk & 1), b = p.K == 4 ? bk >> 2 : bk >> 1;
   const int D = p.D, L = p.L, N = p.N, nch = p.nseg;
   const int c0 = sg * p.cps, c1 = min(nch, c0 + p.cps);
   const int j0 = s * kCT, jp0 = j0 + s;  // first step of this lane in the chunk, and its padded LDS slot
@@ -665,7 +668,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   for (int cb = 0; cb < CPB; ++cb) {
     const BwdChan<S> cn(p, bk, (blk0 + cb) * kBwdChans + ch);
     const float dbias = row_sum16(rr.dbias), dD = row_sum16(rr.dD);
-    const int64_t pc = ((int64_t)b * p.nsp + sg) * 4 * D + cn.c_idx;  // this channel's per-(batch, segment) slot
+    const int64_t pc = ((int64_t)b * p.nsp + sg) * p.K * D + cn.c_idx;  // this channel's per-(batch, segment) slot
     if (cn.valid && s < N) p.dAp[pc * p.Nt + p.n0 + s] = rr.dA;
     if (cn.valid && s == 0) {
       // ddt_bias adds every pass's ddt terms (in pass order); the g u sum of dDs
@@ -842,6 +845,28 @@ __global__ __launch_bounds__(256) void bwd_merge_plane(const float* __restrict__
   }
 }
 
+// dx of the two-path scan: dx[b, d, t] = du of path 0 at step t plus du of path 1
+// at step L-1-t (du rows (b, 0, d) and (b, 1, d)), in that order.  V4: L a
+// multiple of 4 and dx aligned, four tokens per thread with 16-byte accesses.
+template <typename S>
+__global__ __launch_bounds__(256) void bwd_merge_bidir(const float* __restrict__ du, S* __restrict__ dx, int64_t BD,
+                                                      int D, int L, bool v4) {
+  const int64_t total = v4 ? BD * L / 4 : BD * L;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t i = v4 ? 4 * e : e;
+    const int64_t bd = i / L, t = i - bd * L, b = bd / D, d = bd - b * D;
+    const float* r0 = du + ((b * 2 + 0) * D + d) * L;
+    const float* r1 = du + ((b * 2 + 1) * D + d) * L;
+    if (v4) {
+      const float4 a = *reinterpret_cast<const float4*>(r0 + t);
+      const float4 c = *reinterpret_cast<const float4*>(r1 + (L - 4 - t));  // steps L-1-t .. L-4-t, reversed
+      Io<S>::st4(dx, i, make_float4(a.x + c.w, a.y + c.z, a.z + c.y, a.w + c.x));
+    } else {
+      Io<S>::st(dx, i, r0[t] + r1[L - 1 - t]);
+    }
+  }
+}
+
 // Per-channel parameter gradients: sums over the batch in batch order.
 __global__ __launch_bounds__(256) void bwd_params(const float* __restrict__ A_log, const float* __restrict__ dAp,
                                                  const float* __restrict__ dbp, const float* __restrict__ dDp,
@@ -879,7 +904,7 @@ hipError_t launch_chunks(const BackwardArgs& a, const BwdParams& p, int cpb, uns
   } else {
     hipLaunchKernelGGL((bwd_chunk_kernel<S, kSegMaps, 1, VEC>), dim3(blocks), dim3(256), 0, a.stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t cols = a.B * 4 * a.D * p.N;
+    const int64_t cols = a.B * a.K * a.D * p.N;
     hipLaunchKernelGGL(bwd_seg_carry, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, a.stream, p.segP, p.segF,
                        p.segR, cols, a.D * p.N, p.nsp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -893,14 +918,17 @@ hipError_t launch_chunks(const BackwardArgs& a, const BwdParams& p, int cpb, uns
 // segmented map) and the dBs/dCs sums, then the dx merge.
 template <typename S>
 hipError_t launch_io(const BackwardArgs& a, BwdParams p, int64_t L, int cpb) {
-  hipError_t e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(const_cast<void*>(p.xT)),
-                                     (int)(a.B * a.D), (int)a.H, (int)a.W, a.stream);
-  if (e != hipSuccess) return e;
-  e = launch_transpose<S>(static_cast<const S*>(a.dy), static_cast<S*>(const_cast<void*>(p.dyT)), (int)(a.B * a.D),
-                          (int)a.H, (int)a.W, a.stream);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (a.K == 4) {  // the column walks read transposed copies
+    e = launch_transpose<S>(static_cast<const S*>(a.x), static_cast<S*>(const_cast<void*>(p.xT)), (int)(a.B * a.D),
+                            (int)a.H, (int)a.W, a.stream);
+    if (e != hipSuccess) return e;
+    e = launch_transpose<S>(static_cast<const S*>(a.dy), static_cast<S*>(const_cast<void*>(p.dyT)), (int)(a.B * a.D),
+                            (int)a.H, (int)a.W, a.stream);
+    if (e != hipSuccess) return e;
+  }
   const int ngrp = (p.nblk + cpb - 1) / cpb;
-  const unsigned blocks = (unsigned)(a.B * 4 * ngrp * p.nsp);
+  const unsigned blocks = (unsigned)(a.B * a.K * ngrp * p.nsp);
   // 16-byte (fp32) or 8-byte (bf16) accesses when every row the chunks read or
   // write starts aligned: L a multiple of 4 and aligned bases
   const uintptr_t vm = sizeof(S) == 4 ? 15 : 7;
@@ -919,13 +947,20 @@ hipError_t launch_io(const BackwardArgs& a, BwdParams p, int64_t L, int cpb) {
     if (((int64_t)p.N * L) % 4 == 0 && orow % 4 == 0 && o0 % 4 == 0 && !((uintptr_t)a.dBs & om) &&
         !((uintptr_t)a.dCs & om))
       hipLaunchKernelGGL((bwd_reduce_bc4<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp,
-                         static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * 4, ngrp, (int64_t)p.N * L, orow, o0);
+                         static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * a.K, ngrp, (int64_t)p.N * L, orow,
+                         o0);
     else
       hipLaunchKernelGGL((bwd_reduce_bc<S>), dim3(4096), dim3(256), 0, a.stream, p.dBp, p.dCp,
-                         static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * 4, ngrp, p.N, (int)L, orow, o0);
+                         static_cast<S*>(a.dBs), static_cast<S*>(a.dCs), a.B * a.K, ngrp, p.N, (int)L, orow, o0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const uintptr_t am = sizeof(S) == 4 ? 15 : 7;
+  if (a.K == 2) {  // dx of the two-path scan: the forward path's du plus the reversed path's, token by token
+    const bool v4 = L % 4 == 0 && !((uintptr_t)a.dx & am);
+    hipLaunchKernelGGL((bwd_merge_bidir<S>), dim3(4096), dim3(256), 0, a.stream, p.du, static_cast<S*>(a.dx),
+                       a.B * a.D, (int)a.D, (int)L, v4);
+    return hipGetLastError();
+  }
   if (L <= kMergePlaneMax && L % 4 == 0 && !((uintptr_t)a.dx & am)) {
     // threads per plane: the fewest of 64, 128, 256 that give each a group of four pixels
     const int TPP = L / 4 <= 64 ? 64 : (L / 4 <= 128 ? 128 : 256), ppw = 256 / TPP;
@@ -954,12 +989,12 @@ struct BwdLayout {
   size_t du, hck, dBp, dCp, dAp, dbp, dDp, cdl, segP, segF, segR, ddt_acc, xT, dyT, total;  // byte offsets
 };
 
-BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
+BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int K) {
   BwdLayout o;
   o.L = H * W;
   o.nch = (o.L + kChunk - 1) / kChunk;
   o.nblk = (D + kBwdChans - 1) / kBwdChans;
-  const int64_t base = B * 4 * o.nblk;
+  const int64_t base = B * K * o.nblk;
   int64_t nsp = 1;
   if (base < kBwdTargetBlocks) nsp = std::min((kBwdTargetBlocks + base - 1) / base, o.nch / kMinSegChunks);
   if (nsp < 2) nsp = 1;
@@ -967,7 +1002,7 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int 
   o.nsp = (o.nch + o.cps - 1) / o.cps;  // no empty segment
   // two channel blocks per workgroup (sharing Bs/Cs staging and the dBs/dCs
   // partial) where that still leaves a full round of workgroups
-  o.cpb = o.nsp == 1 && B * 4 * ((o.nblk + 1) / 2) >= kBwdPairBlocks ? 2 : 1;
+  o.cpb = o.nsp == 1 && B * K * ((o.nblk + 1) / 2) >= kBwdPairBlocks ? 2 : 1;
   const int64_t ngrp = (o.nblk + o.cpb - 1) / o.cpb;
   auto up = [](int64_t v) { return (size_t)((v * 4 + 255) & ~(int64_t)255); };
   size_t off = 0;
@@ -976,41 +1011,43 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int 
     off += up(floats);
   };
   const int64_t Nb = N < kBwdStates ? N : kBwdStates;  // states of one pass
-  take(o.du, B * 4 * D * o.L);
-  take(o.hck, B * 4 * o.nch * D * Nb * 16);
-  take(o.dBp, B * 4 * ngrp * Nb * o.L);
-  take(o.dCp, B * 4 * ngrp * Nb * o.L);
-  take(o.dAp, B * o.nsp * 4 * D * N);
-  take(o.dbp, B * o.nsp * 4 * D);
-  take(o.dDp, B * o.nsp * 4 * D);
+  take(o.du, B * K * D * o.L);
+  take(o.hck, B * K * o.nch * D * Nb * 16);
+  take(o.dBp, B * K * ngrp * Nb * o.L);
+  take(o.dCp, B * K * ngrp * Nb * o.L);
+  take(o.dAp, B * o.nsp * K * D * N);
+  take(o.dbp, B * o.nsp * K * D);
+  take(o.dDp, B * o.nsp * K * D);
   const bool seg = o.nsp > 1;
-  take(o.cdl, seg ? B * 4 * o.nch * D * 16 : 0);
-  take(o.segP, seg ? B * 4 * o.nsp * D * Nb : 0);
-  take(o.segF, seg ? B * 4 * o.nsp * D * Nb : 0);
-  take(o.segR, seg ? B * 4 * o.nsp * D * Nb : 0);
-  take(o.ddt_acc, N > kBwdStates ? B * 4 * D * o.L : 0);  // ddt summed over the passes
-  take(o.xT, B * D * o.L);  // the transposed copies are sized for fp32 (bf16 uses half)
-  take(o.dyT, B * D * o.L);
+  take(o.cdl, seg ? B * K * o.nch * D * 16 : 0);
+  take(o.segP, seg ? B * K * o.nsp * D * Nb : 0);
+  take(o.segF, seg ? B * K * o.nsp * D * Nb : 0);
+  take(o.segR, seg ? B * K * o.nsp * D * Nb : 0);
+  take(o.ddt_acc, N > kBwdStates ? B * K * D * o.L : 0);  // ddt summed over the passes
+  // the transposed copies (the cross scan's column walks), sized for fp32 (bf16 uses half)
+  take(o.xT, K == 4 ? B * D * o.L : 0);
+  take(o.dyT, K == 4 ? B * D * o.L : 0);
   o.total = off;
   return o;
 }
 
 }  // namespace
 
-size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
-  return bwd_layout(B, D, H, W, N, dtype).total;
+size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int K) {
+  return bwd_layout(B, D, H, W, N, dtype, K).total;
 }
 
-int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
-  return bwd_layout(B, D, H, W, N, dtype).nsp;
+int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int K) {
+  return bwd_layout(B, D, H, W, N, dtype, K).nsp;
 }
 
-int64_t backward_blocks_per_workgroup(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype) {
-  return bwd_layout(B, D, H, W, N, dtype).cpb;
+int64_t backward_blocks_per_workgroup(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int K) {
+  return bwd_layout(B, D, H, W, N, dtype, K).cpb;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
-  const BwdLayout o = bwd_layout(a.B, a.D, a.H, a.W, a.N, a.dtype);
+  if (a.K != 4 && a.K != 2) return hipErrorInvalidValue;
+  const BwdLayout o = bwd_layout(a.B, a.D, a.H, a.W, a.N, a.dtype, a.K);
   char* base = static_cast<char*>(scratch);
   auto f = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   BwdParams p;
@@ -1034,13 +1071,14 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.segP = f(o.segP);
   p.segF = f(o.segF);
   p.segR = f(o.segR);
-  p.xT = base + o.xT;
-  p.dyT = base + o.dyT;
+  p.xT = a.K == 4 ? base + o.xT : nullptr;  // the two-path scan has no column walks
+  p.dyT = a.K == 4 ? base + o.dyT : nullptr;
   p.D = (int)a.D;
   p.H = (int)a.H;
   p.W = (int)a.W;
   p.L = (int)o.L;
   p.N = (int)a.N;
+  p.K = a.K;
   p.Nt = (int)a.N;
   p.n0 = 0;
   p.pass = 0;
@@ -1050,10 +1088,10 @@ hipError_t launch_backward(const BackwardArgs& a, void* scratch) {
   p.nsp = (int)o.nsp;
   p.cps = (int)o.cps;
   const int64_t merge_tiles = ((a.H + kMergeTile - 1) / kMergeTile) * ((a.W + kMergeTile - 1) / kMergeTile);
-  if (a.B * 4 * o.nblk * o.nsp > INT32_MAX || a.B * a.D * merge_tiles > INT32_MAX) return hipErrorInvalidValue;
+  if (a.B * a.K * o.nblk * o.nsp > INT32_MAX || a.B * a.D * merge_tiles > INT32_MAX) return hipErrorInvalidValue;
   hipError_t e = a.dtype == 0 ? launch_io<float>(a, p, o.L, (int)o.cpb) : launch_io<uint16_t>(a, p, o.L, (int)o.cpb);
   if (e != hipSuccess) return e;
-  const int C4 = (int)(4 * a.D);
+  const int C4 = (int)(a.K * a.D);
   hipLaunchKernelGGL(bwd_params, dim3((unsigned)((C4 * a.N + 255) / 256)), dim3(256), 0, a.stream, a.A_log, p.dAp,
                      p.dbp, p.dDp, a.dA_log, a.ddt_bias, a.dDs, (int)(a.B * o.nsp), C4, (int)a.N);
   return hipGetLastError();

@@ -149,12 +149,13 @@ struct BackwardArgs {
   int64_t B, D, H, W, N;
   int dtype;
   hipStream_t stream;
+  int K = 4;  // 4: the cross scan of an H x W map; 2: the two-path scan of a 1 x L sequence
 };
-size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype);
+size_t backward_scratch_bytes(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int K = 4);
 // Segments each backward sequence is cut into (1: one workgroup walks the whole map).
-int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype);
+int64_t backward_segments(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int K = 4);
 // Channel blocks of 16 channels each backward workgroup takes (1 or 2).
-int64_t backward_blocks_per_workgroup(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype);
+int64_t backward_blocks_per_workgroup(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype, int K = 4);
 hipError_t launch_backward(const BackwardArgs& a, void* scratch);
 
 // x (B*D planes of H x W) -> xT (planes of W x H).

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
                             "ss2d_status_string",
                             "ss2d_last_hip_error", "ss2d_version", "ss2d_describe", "ss2d_describe_lanes",
                             "ss2d_trim_memory", "ss2d_measure_peaks", "ss2d_project", "ss2d_forward_from_x",
-                            "ss2d_channel_last", "ss2d_backward"])
+                            "ss2d_channel_last", "ss2d_backward", "ss2d_bidir_backward"])
     lib = ctypes.CDLL(ss2d.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -371,6 +371,37 @@ def test_backward_validation():
     p = [X, DT, AL, BI, BS, CS, DS] + GRAD
     p[10] = GRAD[3] + 2                   # dA_log misaligned
     assert _bwd(p) == -6
+
+
+def _bidir_bwd(ptrs=None, B=2, D=3, L=20, N=16, dtype=0):
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD if ptrs is None else ptrs
+    return ss2d.ss2d_bidir_backward(*p, B, D, L, N, dtype, None)
+
+
+def test_bidir_backward_validation():
+    for i in range(15):
+        p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+        p[i] = None
+        assert _bidir_bwd(p) == -1, i
+    assert _bidir_bwd(dtype=2) == -4
+    assert _bidir_bwd(N=0) == -3
+    assert _bidir_bwd(N=257) == -3
+    assert _bidir_bwd(L=0) == -2
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+    p[8] = X                              # dx on top of x
+    assert _bidir_bwd(p) == -5
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+    p[9] = DT + 4                         # ddt inside dt
+    assert _bidir_bwd(p) == -5
+    p = [X, DT, AL, BI, BS, CS, DS] + GRAD
+    p[0] = X + 1                          # bf16 tensors need 2-byte alignment
+    assert _bidir_bwd(p, dtype=1) == -6
+
+
+@needs_no_device
+def test_bidir_backward_valid_calls_without_device_report_no_device():
+    assert _bidir_bwd() == -7
+    assert _bidir_bwd(N=40, dtype=1) == -7
 
 
 @needs_no_device
