@@ -66,7 +66,8 @@ KERNEL_PREFIX = "ss2d_forward_kernel"
 # Kernels that one forward may launch besides the scan (transposes of x and of the merge plane).
 STEP_KERNELS = {"ss2d_forward_kernel", "transpose_small", "transpose_small4", "transpose_planes", "transpose_planes4",
                 "project_kernel", "bwd_chunk_kernel",
-                "bwd_seg_carry", "bwd_reduce_bc", "bwd_reduce_bc4", "bwd_merge", "bwd_merge_plane", "bwd_params",
+                "bwd_seg_carry", "bwd_reduce_bc", "bwd_reduce_bc4", "bwd_merge", "bwd_merge_plane", "bwd_merge_bidir",
+                "bwd_params",
                 "channel_last_kernel"}
 
 
@@ -102,11 +103,11 @@ def algorithmic_bytes(shape, K: int = 4) -> int:
     return s * shape.B * shape.L * ((2 + K) * shape.D + 2 * K * shape.N) + 4 * K * shape.D * (shape.N + 2)
 
 
-def backward_algorithmic_bytes(shape) -> int:
-    """Bytes the backward must move: x, dy, dt, Bs, Cs read once, dx, ddt, dBs, dCs written
-    once (storage type), and the fp32 parameters read and their gradients written."""
+def backward_algorithmic_bytes(shape, K: int = 4) -> int:
+    """Bytes the backward over K walks must move: x, dy, dt, Bs, Cs read once, dx, ddt, dBs,
+    dCs written once (storage type), and the fp32 parameters read and their gradients written."""
     s = shape.elem_bytes
-    return s * shape.B * shape.L * (11 * shape.D + 16 * shape.N) + 2 * 4 * 4 * shape.D * (shape.N + 2)
+    return s * shape.B * shape.L * ((3 + 2 * K) * shape.D + 4 * K * shape.N) + 2 * 4 * K * shape.D * (shape.N + 2)
 
 
 def _record(path: str):
@@ -197,7 +198,7 @@ def summarize_counters(folder: str, args) -> int:
     instruction mix per state update and the VALU's share of the CUs' busy cycles."""
     path = args.path
     shape = bench_shape(args)
-    bwd = path == "backward"
+    bwd = path in ("backward", "bidir_backward")
     kernel = "bwd_chunk_kernel" if bwd else KERNEL_PREFIX
     workload = bench_workload(shape, path)
     extra = bench_flags(args, path)
@@ -210,7 +211,7 @@ def summarize_counters(folder: str, args) -> int:
                 inst.setdefault((r["Counter_Name"], r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         for (cn, _), v in inst.items():
             vals[cn] = vals.get(cn, 0.0) + sum(v) / len(v)
-    upd = (2 if path == "bidir" else 4) * shape.B * shape.D * shape.L * shape.N
+    upd = (2 if path.startswith("bidir") else 4) * shape.B * shape.D * shape.L * shape.N
     lines = [f"# {kernel} — {workload} — shader counters (rocprofv3)", "",
              f"Workload: {shape}.  State updates per step: {upd:.4e}"
              + (" ((b,k,d,n,l) terms; the backward runs more work per term)." if bwd else "."), "",
@@ -271,12 +272,12 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
     path "scan": the scan kernel of the forward; "from_x": the projection kernel of
     the forward from x and the projection weights; "backward": the chunked backward
     kernel; "epilogue": the channel-last kernel; "bidir": the scan kernel of the
-    two-path scan."""
+    two-path scan; "bidir_backward": the chunked backward kernel of the two-path scan."""
     import csv
     shape = bench_shape(args)
     cfg = args.config
     os.makedirs(PROFILES, exist_ok=True)
-    from_x, bwd, epi = path == "from_x", path == "backward", path == "epilogue"
+    from_x, bwd, epi = path == "from_x", path in ("backward", "bidir_backward"), path == "epilogue"
     kernel = ("project_kernel" if from_x else "bwd_chunk_kernel" if bwd else "channel_last_kernel" if epi
               else KERNEL_PREFIX)
     # the kernel's template instances and variants (the epilogue has a vector and a general kernel)
@@ -310,8 +311,10 @@ def summarize_profile(folder: str, args, path: str = "scan") -> int:
         work = (f"Epilogue per launch: algorithmic bytes {alg_bytes:.4e} (y read once, the channel-last output "
                 "written once, gamma and beta).")
     elif bwd:
-        alg_bytes = backward_algorithmic_bytes(shape)
-        work = (f"Backward per launch: {shape.updates:.4e} (b,k,d,n,l) terms; algorithmic bytes {alg_bytes:.4e} "
+        K = 2 if path == "bidir_backward" else 4
+        alg_bytes = backward_algorithmic_bytes(shape, K)
+        terms = K * shape.B * shape.D * shape.L * shape.N
+        work = (f"Backward per launch: {terms:.4e} (b,k,d,n,l) terms; algorithmic bytes {alg_bytes:.4e} "
                 "(x, dy, dt, Bs, Cs read once; dx, ddt, dBs, dCs written once).")
     else:
         K = 2 if path == "bidir" else 4
@@ -480,11 +483,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = VMamba-T stage-1")
-    ap.add_argument("--path", choices=["scan", "from_x", "backward", "bidir"], default="scan",
+    ap.add_argument("--path", choices=["scan", "from_x", "backward", "bidir", "bidir_backward"], default="scan",
                     help="scan: the forward from x, dt, Bs, Cs (the headline); from_x: the forward from x and the "
                          "projection weights (projections on the matrix cores, then the scan); backward: the "
                          "gradients of the forward given dy; bidir: the two-path scan (forward and backward "
-                         "recursion over the L = H*W tokens, ss2d_bidir_forward)")
+                         "recursion over the L = H*W tokens, ss2d_bidir_forward); bidir_backward: its gradients given dy "
+                         "(ss2d_bidir_backward)")
     ap.add_argument("--n", type=int, default=0, help="state size N of the workload (0: its own, 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing and parity")
     ap.add_argument("--lanes", type=int, default=0, help="force lanes per sequence chunk (16/32/64; 0 = auto)")
@@ -495,7 +499,8 @@ def main() -> int:
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-device roofline probes")
     ap.add_argument("--epilogue", action="store_true",
                     help="also time the channel-last LayerNorm epilogue on the forward's output")
-    ap.add_argument("--summarize-kind", choices=["scan", "from_x", "backward", "epilogue", "bidir"], default=None,
+    ap.add_argument("--summarize-kind", choices=["scan", "from_x", "backward", "epilogue", "bidir", "bidir_backward"],
+                    default=None,
                     help="which kernel --summarize-profile summarises (default: --path)")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
                     help="write the SQ-counter summary (two rocprofv3 --pmc runs in DIR) into profiles/ and exit")
@@ -524,8 +529,8 @@ def main() -> int:
     shape = bench_shape(args)
     print(f"[bench] workload {shape}", file=sys.stderr, flush=True)
     from_x = args.path == "from_x"
-    bwd = args.path == "backward"
-    bidir = args.path == "bidir"
+    bwd = args.path in ("backward", "bidir_backward")
+    bidir = args.path in ("bidir", "bidir_backward")
     K = 2 if bidir else 4
     if from_x:
         inp = ss2d_inputs.generate_projected(shape, seed=0)
@@ -544,13 +549,14 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     if bwd:
-        dy = torch.from_numpy(np.random.default_rng(1).standard_normal((shape.B, shape.D, shape.H, shape.W))
-                              .astype(np.float32)).to(tdt).to(dev)
+        dshape = (shape.B, shape.D, shape.L) if bidir else (shape.B, shape.D, shape.H, shape.W)
+        dy = torch.from_numpy(np.random.default_rng(1).standard_normal(dshape).astype(np.float32)).to(tdt).to(dev)
         grads = {}
+        bwd_fn = ss2d.bidir_backward if bidir else ss2d.backward
 
         def step():
-            grads.update(ss2d.backward(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], dy,
-                                       stream=stream))
+            grads.update(bwd_fn(d["x"], d["dt"], d["A_log"], d["dt_bias"], d["Bs"], d["Cs"], d["Ds"], dy,
+                                stream=stream))
     elif from_x:
         def step():
             ss2d.forward_from_x(d["x"], d["x_proj_weight"], d["dt_projs_weight"], d["A_log"], d["dt_bias"],
@@ -690,15 +696,17 @@ def main() -> int:
     per_block = 1 if nseg == 1 else 1 + K + int(plan["plane_transposed"])  # scan, or carry + one per direction
     launches = int(plan["x_transposed"]) + blocks * per_block
     if bwd:
-        # two transposes, the chunked scan (or, on a segmented map, its two passes
-        # and the segment carry), the dBs/dCs sum, the dx merge, the parameter sums
-        launches = 6 if int(plan["backward_segments"]) == 1 else 8
+        # two transposes (the cross scan only), per block of 16 states the chunked scan
+        # (or, on a segmented map, its two passes and the segment carry) and the dBs/dCs
+        # sum, then the dx merge and the parameter sums
+        bseg = int(plan["bidir_backward_segments" if bidir else "backward_segments"])
+        launches = (0 if bidir else 2) + -(-shape.N // 16) * (2 if bseg == 1 else 4) + 2
     if from_x:
         launches += 1 + (1 - int(plan["x_transposed"]))  # the projection, and its own transpose of x
     ms_per_step = wall * 1e3 / args.steps
     step_s = ev_ms * 1e-3 / args.steps  # all launches of one step, same stream
     updates = K * shape.B * shape.D * shape.L * shape.N
-    alg_bytes = backward_algorithmic_bytes(shape) if bwd else algorithmic_bytes(shape, K)
+    alg_bytes = backward_algorithmic_bytes(shape, K) if bwd else algorithmic_bytes(shape, K)
     value = updates * args.steps / wall
     achieved = updates / step_s
     hbm_gbps = alg_bytes / step_s / 1e9
@@ -733,6 +741,8 @@ def main() -> int:
             "frac": achieved / peak,
             "traffic": traffic,
             "timed": f"HIP events around each step on the launch stream: {launches} launch(es) " + (
+                     "(the chunked backward kernel, the dBs/dCs sum, the dx merge of the two paths, the "
+                     "parameter sums; traffic is the chunked kernel's own)" if bwd and bidir else
                      "(transposes of x and dy, the chunked backward kernel, the dBs/dCs sum, the dx merge, the "
                      "parameter sums; traffic is the chunked kernel's own)" if bwd else
                      "(the scan kernel, after a transpose of x on maps of 2048+ pixels; traffic is the scan "
@@ -777,9 +787,13 @@ def main() -> int:
         nb_sample = shape.B
         if bwd:
             # a bounded sample: the float64 backward oracle on the first batch element
-            from oracle import backward as obwd
             x1 = {k: (v[:1] if k in ("x", "dt", "Bs", "Cs") else v) for k, v in x64.items()}
-            refs = obwd.ss2d_backward_f64(**x1, dy=dy[:1].double().cpu().numpy())
+            if bidir:
+                from oracle import bidir as obidir
+                refs = obidir.bidir_backward_f64(**x1, dy=dy[:1].double().cpu().numpy())
+            else:
+                from oracle import backward as obwd
+                refs = obwd.ss2d_backward_f64(**x1, dy=dy[:1].double().cpu().numpy())
             nb_sample = 1
             ref = refs["dx"]
         elif from_x:
@@ -799,7 +813,7 @@ def main() -> int:
         sample_s = time.perf_counter() - t0
         cpu_s = sample_s * shape.B / nb_sample
         got = (grads["dx"] if bwd else y).double().cpu().numpy()[:nb_sample]
-        if bidir:
+        if bidir and not bwd:
             got = got.reshape(ref.shape)
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         max_abs = float(np.max(np.abs(got - ref)))
@@ -809,8 +823,8 @@ def main() -> int:
             "unit": "state-updates/s",
             "cores": 1 if (bwd or bidir) else threads,
             "kind": "oracle",
-            "sample": (f"the float64 numpy backward oracle on 1 of {shape.B} batch elements{scaled}; "
-                       f"{sample_s:.2f} s for the sample on {cpu_model()}") if bwd else
+            "sample": (f"the float64 numpy {'two-path ' if bidir else ''}backward oracle on 1 of {shape.B} batch "
+                       f"elements{scaled}; {sample_s:.2f} s for the sample on {cpu_model()}") if bwd else
                       (f"the float64 numpy two-path oracle on {nb_sample} of {shape.B} batch elements{scaled}; "
                        f"{sample_s:.2f} s for the sample on {cpu_model()}") if bidir else
                       (f"{nb_sample} of {shape.B} batch elements ({shape.D} planes each){scaled}, "

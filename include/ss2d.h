@@ -262,7 +262,7 @@ int ss2d_channel_last(const void* y, const float* gamma, const float* beta, floa
  * dCs partials, one per workgroup of one or two 16-channel blocks, the state
  * entering every 8 steps, the dA_log partials), plus B*4*D*L for the ddt sum
  * when N > 16, and runs four kernels per pass and three more on `stream`.
- * When B*4*ceil(D/16) is small, each sequence is cut into S segments of at least
+ * When B*4*ceil(D/16) is below 768, each sequence is cut into S segments of at least
  * 512 steps (S from ss2d_describe): two more kernels, and about
  * 16*B*4*D*ceil(L/128) + 3*B*4*S*D*n more temporary values.
  * Validation, error reporting and thread safety as for ss2d_forward; pointers
@@ -319,9 +319,10 @@ int ss2d_version(void);
  * variant, lanes per sequence, channels per workgroup, grid size, LDS and
  * temporary sizes, passes over state blocks), followed by the number of
  * segments ss2d_backward cuts each sequence into and the number of 16-channel
- * blocks each of its workgroups takes (0 for N > 16, which the backward does
- * not take), into buf[0..len).  Host only; no device work.  Returns SS2D_OK or
- * a validation code.  ss2d_describe_lanes: the same for ss2d_forward_lanes.
+ * blocks each of its workgroups takes, then the same two numbers for
+ * ss2d_bidir_backward over a sequence of L = H*W tokens, into buf[0..len).
+ * Host only; no device work.  Returns SS2D_OK or a validation code.
+ * ss2d_describe_lanes: the same for ss2d_forward_lanes.
  */
 int ss2d_describe(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dtype,
                   char* buf, int64_t len);

@@ -99,7 +99,7 @@ def version() -> int:
 
 def describe(B, D, H, W, N, dtype=SS2D_F32, lanes: int = 0) -> str:
     """The launch plan of a forward of this shape (lanes: 0 = automatic, else 16/32/64)."""
-    buf = ctypes.create_string_buffer(512)
+    buf = ctypes.create_string_buffer(1024)
     if lanes:
         rc = lib().ss2d_describe_lanes(B, D, H, W, N, int(dtype), int(lanes), buf, len(buf))
     else:

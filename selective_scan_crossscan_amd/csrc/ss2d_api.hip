@@ -290,11 +290,14 @@ int describe_impl(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int dty
   snprintf(buf, (size_t)len,
            "kernel=chunked_dpp_scan lanes_per_seq=%d steps_per_lane=%d waves=%d chans_per_block=%d "
            "segments=%d x_transposed=%d plane_transposed=%d blocks=%lld lds_bytes=%zu scratch_bytes=%zu "
-           "state_blocks=%d backward_segments=%lld backward_blocks_per_workgroup=%lld",
+           "state_blocks=%d backward_segments=%lld backward_blocks_per_workgroup=%lld "
+           "bidir_backward_segments=%lld bidir_backward_blocks_per_workgroup=%lld",
            pl.lanes_per_seq, pl.steps_per_lane, pl.waves, pl.chans_per_block, pl.nseg, pl.xtrans ? 1 : 0,
            pl.transpose ? 1 : 0, (long long)pl.blocks, pl.lds_bytes, pl.scratch_bytes, pl.state_blocks,
            (long long)ss2d::backward_segments(B, D, H, W, N, dtype),
-           (long long)ss2d::backward_blocks_per_workgroup(B, D, H, W, N, dtype));
+           (long long)ss2d::backward_blocks_per_workgroup(B, D, H, W, N, dtype),
+           (long long)ss2d::backward_segments(B, D, 1, H * W, N, dtype, 2),
+           (long long)ss2d::backward_blocks_per_workgroup(B, D, 1, H * W, N, dtype, 2));
   return SS2D_OK;
 }
 

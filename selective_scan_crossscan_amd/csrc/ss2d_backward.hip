@@ -977,12 +977,15 @@ hipError_t launch_io(const BackwardArgs& a, BwdParams p, int64_t L, int cpb) {
   return hipGetLastError();
 }
 
-// Segments: a map whose channel blocks alone give fewer workgroups than about
-// six per compute unit is cut into segments of at least kMinSegChunks chunks.
-constexpr int64_t kBwdTargetBlocks = 1536;
-constexpr int64_t kMinSegChunks = 4;
 // Workgroups that fill the chip once at three per compute unit.
 constexpr int64_t kBwdPairBlocks = 768;
+// Segments: a map whose channel blocks alone give fewer workgroups than fill the
+// chip once is cut into segments of at least kMinSegChunks chunks, toward about
+// six workgroups per compute unit.  From one full round up, whole sequences are
+// faster than segments (their map and carry passes cost more than a second round
+// of workgroups saves).
+constexpr int64_t kBwdTargetBlocks = 1536;
+constexpr int64_t kMinSegChunks = 4;
 
 struct BwdLayout {
   int64_t L, nch, nblk, nsp, cps, cpb;
@@ -996,7 +999,7 @@ BwdLayout bwd_layout(int64_t B, int64_t D, int64_t H, int64_t W, int64_t N, int 
   o.nblk = (D + kBwdChans - 1) / kBwdChans;
   const int64_t base = B * K * o.nblk;
   int64_t nsp = 1;
-  if (base < kBwdTargetBlocks) nsp = std::min((kBwdTargetBlocks + base - 1) / base, o.nch / kMinSegChunks);
+  if (base < kBwdPairBlocks) nsp = std::min((kBwdTargetBlocks + base - 1) / base, o.nch / kMinSegChunks);
   if (nsp < 2) nsp = 1;
   o.cps = (o.nch + nsp - 1) / nsp;
   o.nsp = (o.nch + o.cps - 1) / o.cps;  // no empty segment

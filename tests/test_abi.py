@@ -135,6 +135,17 @@ def test_describe_backward_plan():
     assert plan(2, 192, 256, 256, 16, ss2d.SS2D_F32) == (16, 1)  # 96 blocks: 16 segments
     assert plan(1, 192, 56, 56, 16, ss2d.SS2D_F32) == (5, 1)
     assert plan(1, 16, 8, 8, 16, ss2d.SS2D_F32) == (1, 1)        # one chunk: nothing to cut
+    assert plan(16, 192, 56, 56, 16, ss2d.SS2D_F32) == (1, 1)    # 768 blocks fill the chip once: whole
+
+
+def test_describe_bidir_backward_plan():
+    # the two-path backward over L = H*W tokens: two walks per batch element
+    def plan(*a):
+        f = dict(kv.split("=") for kv in ss2d.describe(*a).split())
+        return int(f["bidir_backward_segments"]), int(f["bidir_backward_blocks_per_workgroup"])
+    assert plan(32, 192, 56, 56, 16, ss2d.SS2D_F32) == (1, 1)    # 768 blocks
+    assert plan(64, 192, 56, 56, 16, ss2d.SS2D_F32) == (1, 2)    # 1536 blocks: pairs
+    assert plan(2, 192, 256, 256, 16, ss2d.SS2D_F32) == (32, 1)  # 48 blocks: 32 segments
 
 
 # fake, well-aligned, non-overlapping addresses (never dereferenced: validation fails first)

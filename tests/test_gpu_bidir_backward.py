@@ -66,6 +66,9 @@ def test_bidir_backward_matches_oracle(shape):
 def test_bidir_backward_stage1_tokens_batch_element():
     # the token count of the VMamba-T stage-1 map (32 x 192 x 3136, N = 16), the
     # workload the two-path bench runs; batch element 0 against the oracle
+    import selective_scan_crossscan_amd as ss2d
+    f = dict(kv.split("=") for kv in ss2d.describe(32, 192, 56, 56, 16).split())
+    assert (f["bidir_backward_segments"], f["bidir_backward_blocks_per_workgroup"]) == ("1", "1")
     print("[bidir backward] 32x192x3136", flush=True)
     _run(32, 192, 3136, 16, seed=5, element=True)
 
