@@ -84,3 +84,27 @@ def ss2d_backward_f64(x, dt, A_log, dt_bias, Bs, Cs, Ds, dy):
         "dCs": dCs,
         "dDs": (g * u).sum(axis=(0, 3)).reshape(4 * D),
     }
+
+
+def ss2d_states_f64(x, dt, A_log, dt_bias, Bs, Cs, every: int = 8):
+    """The states h of the forward's recurrence (module docstring) entering every
+    `every`-th step of each direction's walk: out[b, k, d, n, p] = h_{every*p - 1}
+    (0 for p = 0), p = 0 .. ceil(L/every) - 1.  Shapes as for the forward; Cs is
+    not used (the states do not depend on it) and is taken for a uniform call."""
+    f = lambda a: np.asarray(a, dtype=np.float64)
+    x, dt, A_log, dt_bias, Bs = (f(v) for v in (x, dt, A_log, dt_bias, Bs))
+    B, D, H, W = x.shape
+    L = H * W
+    N = A_log.shape[1]
+    u = scan_sequences(x)                                            # (B, 4, D, L)
+    delta = np.logaddexp(0.0, dt + dt_bias.reshape(4, D)[None, :, :, None])
+    A = -np.exp(A_log).reshape(4, D, N)
+    P = (L + every - 1) // every
+    out = np.zeros((B, 4, D, N, P))
+    h = np.zeros((B, 4, D, N))
+    for l in range(L):
+        if l % every == 0:
+            out[..., l // every] = h
+        a = np.exp(delta[:, :, :, None, l] * A[None])
+        h = a * h + (delta[:, :, :, l] * u[:, :, :, l])[:, :, :, None] * Bs[:, :, None, :, l]
+    return out

@@ -135,3 +135,23 @@ def test_planted_mistake_is_caught(name, tmp_path):
     spec.loader.exec_module(mod)
     with np.errstate(all="ignore"):
         assert not _pins_pass(mod)
+
+
+@pytest.mark.parametrize("dims", [(2, 3, 5, 7, 4), (1, 2, 4, 4, 3)], ids=["35_steps", "16_steps"])
+def test_saved_states_match_the_c_forward(dims):
+    """ss2d_states_f64 against the (separately pinned) C forward: with Ds = 0 and Cs
+    one-hot in state n0, direction k's output at step l is h_l of state n0, so entry
+    p of the states is that output at step 8p - 1 (and entry 0 is zero)."""
+    B, D, H, W, N = dims
+    L = H * W
+    inp = ss2d_inputs.tiny_random(B, D, H, W, N, seed=sum(dims))
+    st = backward.ss2d_states_f64(**{k: inp[k] for k in ("x", "dt", "A_log", "dt_bias", "Bs", "Cs")})
+    P = (L + 7) // 8
+    assert st.shape == (B, 4, D, N, P)
+    assert np.all(st[..., 0] == 0.0)
+    for n0 in range(N):
+        Cs = np.zeros_like(inp["Cs"])
+        Cs[:, :, n0, :] = 1.0
+        _, out_k = oracle.ss2d_f64(**{**inp, "Cs": Cs, "Ds": np.zeros_like(inp["Ds"])}, want_out_k=True)
+        for p in range(1, P):
+            np.testing.assert_allclose(st[:, :, :, n0, p], out_k[:, :, :, 8 * p - 1], rtol=1e-12, atol=1e-14)
