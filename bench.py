@@ -770,13 +770,18 @@ def main() -> int:
             "update_mix_Gps": peaks["update_mix_per_s"] / 1e9, "exp_Gps": peaks["exp_per_s"] / 1e9,
             "fma_Gps": peaks["fma_per_s"] / 1e9, "hbm_read_GBps": peaks["hbm_read_Bps"] / 1e9,
             "hbm_copy_GBps": peaks["hbm_copy_Bps"] / 1e9, "lds_read_GBps": peaks["lds_read_Bps"] / 1e9,
+            "state_loop_Gps": peaks["state_loop_per_s"] / 1e9,
             "compute_units": peaks["compute_units"]}
         if not bwd:
             result["roofline_measured"] = {
                 "bound": "alu", "achieved": achieved / 1e9, "peak": peaks["update_mix_per_s"] / 1e9,
                 "unit": "Gupdates/s (peak = the probe kernel running the update's exp2 + 4 VALU mix on this device)",
                 "frac": achieved / peaks["update_mix_per_s"],
-                "hbm_frac_of_measured_copy": hbm_gbps * 1e9 / peaks["hbm_copy_Bps"]}
+                "hbm_frac_of_measured_copy": hbm_gbps * 1e9 / peaks["hbm_copy_Bps"],
+                # the scan's own state loop run alone on chip (ss2d_peaks.hip, probe_state_loop):
+                # the rate the chunked form reaches without per-step work, memory or merge
+                "state_loop_peak": peaks["state_loop_per_s"] / 1e9,
+                "frac_of_state_loop": achieved / peaks["state_loop_per_s"]}
 
     if not args.no_cpu_baseline:
         import oracle

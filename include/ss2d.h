@@ -348,6 +348,13 @@ int ss2d_trim_memory(void);
  *   hbm_copy_Bps      device copy of hbm_bytes/2, bytes read plus bytes written
  *   lds_read_Bps      16-byte LDS reads, all CUs
  *   compute_units     CUs of the device
+ *   state_loop_per_s  state updates per second of the forward's state loop
+ *                     alone (per state the fold, the DPP prefix combine over 32
+ *                     lanes, the carried state and the replay with the output FMA,
+ *                     16 steps per lane, one barrier per four states), operands in
+ *                     LDS and registers, at the forward's occupancy: what the
+ *                     chunked form reaches without its per-step work, memory
+ *                     traffic, waits or merge
  * The probes allocate hbm_bytes (1 MiB .. 64 GiB, multiple of 32) plus a small
  * sink from the device's default memory pool on `stream` and free them; the call
  * returns after synchronising `stream`.  Codes: SS2D_ERR_NULL (out), SS2D_ERR_SHAPE
@@ -362,6 +369,7 @@ typedef struct {
   double hbm_copy_Bps;
   double lds_read_Bps;
   int compute_units;
+  double state_loop_per_s;
 } ss2d_peaks;
 int ss2d_measure_peaks(ss2d_peaks* out, int64_t hbm_bytes, void* stream);
 

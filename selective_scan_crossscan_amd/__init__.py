@@ -39,7 +39,7 @@ class Peaks(ctypes.Structure):
     _fields_ = [("exp_per_s", ctypes.c_double), ("fma_per_s", ctypes.c_double),
                 ("update_mix_per_s", ctypes.c_double), ("hbm_read_Bps", ctypes.c_double),
                 ("hbm_copy_Bps", ctypes.c_double), ("lds_read_Bps", ctypes.c_double),
-                ("compute_units", ctypes.c_int)]
+                ("compute_units", ctypes.c_int), ("state_loop_per_s", ctypes.c_double)]
 
 
 def lib():

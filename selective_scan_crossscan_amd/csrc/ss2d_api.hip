@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;  // 1.1.0
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;  // 1.2.0
 thread_local char g_last_hip_error[256] = "";
 
 void remember(hipError_t e) {
@@ -169,6 +169,7 @@ int ss2d_measure_peaks(ss2d_peaks* out, int64_t hbm_bytes, void* stream) {
   out->hbm_copy_Bps = r.hbm_copy_Bps;
   out->lds_read_Bps = r.lds_read_Bps;
   out->compute_units = r.compute_units;
+  out->state_loop_per_s = r.state_loop_per_s;
   return SS2D_OK;
 }
 

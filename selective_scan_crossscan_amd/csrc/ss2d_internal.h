@@ -77,6 +77,7 @@ struct Scratch {
 struct PeakRates {
   double exp_per_s, fma_per_s, update_mix_per_s, hbm_read_Bps, hbm_copy_Bps, lds_read_Bps;
   int compute_units;
+  double state_loop_per_s;
 };
 
 // Runs the roofline probes on the current device, on `stream` (synchronises it).

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "ss2d_internal.h"
+#include "ss2d_kernels.h"
 
 namespace ss2d {
 namespace {
@@ -67,6 +68,69 @@ __global__ __launch_bounds__(kThreads) void probe_update(float* sink, int iters,
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kChains; ++j) s += u[j] + h[j];
+  if (s == kNever) sink[blockIdx.x] = s;
+}
+
+// The scan's state loop alone, every operand already on chip: the rate its
+// arithmetic form reaches at the forward's occupancy (three workgroups of four
+// waves per CU), against which the whole kernel (softplus and the other
+// per-step work, memory, waits, merge, remainders) is compared.  Each lane
+// holds 16 steps of one channel (delta, delta*u and outputs formed once) and
+// runs the states of a chunk through the forward's own state step: fold, DPP
+// prefix combine over the 32-lane group, state carried in LDS, replay with the
+// output FMA; B and C come from swizzled LDS rows read as the scan reads them, and
+// the states run in groups of four with one barrier per group, in a loop that
+// is not unrolled, as in the scan.  Every pass reads the carried state the last
+// one wrote and adds into the same outputs, so no work is loop-invariant.
+constexpr int kFormG = 32, kFormT = 16, kFormStates = 16, kFormRows = 4;
+constexpr int kFormRow = kFormG * kFormT;              // floats per LDS row (one chunk of steps)
+constexpr int kFormChans = kThreads / kFormG;           // channels per workgroup
+
+__global__ __launch_bounds__(kThreads, 3) void probe_state_loop(float* sink, int passes, int nstates, float seed) {
+  __shared__ __align__(16) float bc[2 * kFormRows * kFormRow];  // B rows, then C rows (swizzled)
+  __shared__ float a2s[kFormChans * kFormStates];
+  __shared__ float carry[kFormChans * kFormStates];
+  const int tid = threadIdx.x, seg = tid % kFormG, dl = tid / kFormG;
+  for (int i = tid; i < 2 * kFormRows * kFormRow; i += kThreads) bc[i] = 0.05f * ((i * 37) % 41 - 20);
+  for (int i = tid; i < kFormChans * kFormStates; i += kThreads) {
+    a2s[i] = -(1.f + (i % kFormStates)) * kLog2e;
+    carry[i] = 0.f;
+  }
+  __syncthreads();
+  float dtv[kFormT], u[kFormT], delta[kFormT], du[kFormT], yv[kFormT];
+#pragma unroll
+  for (int i = 0; i < kFormT; ++i) {
+    dtv[i] = 0.3f * ((i * 7 + seg) % 11 - 5);
+    u[i] = seed + 0.01f * i + 1e-6f * tid;
+  }
+  const float sdelta = prepare_steps<kFormT>(dtv, u, -4.f, 1.f, true, kFormT, delta, du, yv);
+  auto group = [&](int n0) {
+#pragma unroll
+    for (int r = 0; r < kFormRows; ++r) {
+      const int n = n0 + r;
+      __builtin_amdgcn_sched_barrier(0);
+      if (n < nstates) {  // as in the scan: each state its own block, so its FMAs stay in it
+        const char* rows = reinterpret_cast<const char*>(bc);
+        float Bv[kFormT], Cv[kFormT];
+        read_seg<float, kFormT>(rows + r * kFormRow * 4, seg, Bv);
+        read_seg<float, kFormT>(rows + (kFormRows + r) * kFormRow * 4, seg, Cv);
+        state_core<kFormG, kFormT>(Bv, Cv, a2s[dl * kFormStates + n], carry + dl * kFormStates + n, seg, delta, du,
+                                   sdelta, yv);
+      }
+    }
+    __syncthreads();
+  };
+#pragma unroll 1
+  for (int it = 0; it < passes; ++it) {
+#pragma unroll 1
+    for (int n0 = 0; n0 < nstates; n0 += 2 * kFormRows) {
+      group(n0);
+      group(n0 + kFormRows);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kFormT; ++i) s += yv[i];
   if (s == kNever) sink[blockIdx.x] = s;
 }
 
@@ -178,6 +242,13 @@ hipError_t measure_peaks(PeakRates* out, int64_t hbm_bytes, hipStream_t stream) 
   }, &t);
   if (e != hipSuccess) return done(e);
   out->update_mix_per_s = lanes / t;
+  const int form_blocks = ncu * 3, form_passes = 256;
+  e = best_time(stream, e0, e1, reps, [&] {
+    hipLaunchKernelGGL(probe_state_loop, dim3(form_blocks), dim3(kThreads), 0, stream, sink, form_passes, kFormStates,
+                       0.5f);
+  }, &t);
+  if (e != hipSuccess) return done(e);
+  out->state_loop_per_s = (double)form_blocks * kThreads * form_passes * kFormT * kFormStates / t;
 
   const float4* lo = reinterpret_cast<const float4*>(buf);
   float4* hi = reinterpret_cast<float4*>(buf + n4 * 16);
