@@ -291,7 +291,9 @@ struct Layout {
                                                                 : (kStagedBytes > kTileBytes ? kStagedBytes : kTileBytes);
   static constexpr int kDtBytes = C::kChans * kGT * (int)sizeof(S);
   static constexpr int kParFloats = 3 * C::kChans * kMaxN + 2 * C::kChans + C::kChans * kMaxLowRank;
-  static constexpr int kBytes = kRing0Bytes + kGroupBytes + kDtBytes + 4 * kParFloats;
+  // bf16 storage: the group's Bs/Cs rows widened to fp32 (widen_rows)
+  static constexpr int kWideBytes = sizeof(S) == 2 ? NG * 2 * kGT * 4 : 0;
+  static constexpr int kBytes = kRing0Bytes + kGroupBytes + kDtBytes + 4 * kParFloats + kWideBytes;
 };
 
 // ------------------------------------------------------------------ DMA staging
@@ -515,6 +517,37 @@ __device__ __forceinline__ void read_seg(const char* row, int seg, float (&v)[T]
         v[q * 8 + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
       }
     }
+  }
+}
+
+// The 2*NG Bs/Cs rows of a group, copied into the ring as bf16, rewritten once
+// per workgroup as fp32 rows with the fp32 swizzle.  The lanes of every channel
+// then read them as fp32 (read_seg<float, T>) instead of each lane unpacking
+// every bf16 value it reads, once per channel.  Element 2j of a 32-bit word is
+// its low half (little-endian).  NTH threads take 16-byte slots of the bf16
+// rows in turn; each slot (8 steps of one lane segment) becomes two fp32 slots.
+template <int T, int ROWS, int GT, int NTH>
+__device__ __forceinline__ void widen_rows(const char* src, char* dst, int tid) {
+  using Zb = Swz<uint16_t, T>;
+  using Zf = Swz<float, T>;
+  constexpr int kRowSlots = GT * 2 / 16;  // 16-byte slots of a bf16 row
+  constexpr int kSlots = ROWS * kRowSlots;
+  static_assert(kSlots % NTH == 0, "the slots of a group must divide among the threads");
+#pragma unroll 1
+  for (int k = 0; k < kSlots / NTH; ++k) {
+    const int j = tid + k * NTH;
+    const int row = j / kRowSlots, js = j - row * kRowSlots;
+    const int sg = js / Zb::kSP;
+    const int q = (js - sg * Zb::kSP) ^ Zb::swz(sg);  // holds steps 8q .. 8q+7 of segment sg
+    const uint4 w = *reinterpret_cast<const uint4*>(src + row * GT * 2 + js * 16);
+    const float4 lo = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+    const float4 hi = make_float4(__uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
+                                  __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u));
+    char* drow = dst + row * GT * 4;
+    const int sw = Zf::swz(sg);
+    *reinterpret_cast<float4*>(drow + (sg * Zf::kSP + ((2 * q) ^ sw)) * 16) = lo;
+    *reinterpret_cast<float4*>(drow + (sg * Zf::kSP + ((2 * q + 1) ^ sw)) * 16) = hi;
   }
 }
 
@@ -1027,6 +1060,7 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
   __shared__ __align__(16) char ring1[Y::kGroupBytes];
   __shared__ __align__(16) char dtb[Y::kDtBytes];
   __shared__ float par[Y::kParFloats];
+  __shared__ __align__(16) char wide[Y::kWideBytes > 0 ? Y::kWideBytes : 16];
   float* smem = reinterpret_cast<float*>(ring0);
   float* a2s = par;
   float* carry = a2s + CH * kMaxN;
@@ -1287,6 +1321,14 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
             dpl.copy(dtb, dt_rows, (c + 1) * GT);
           else if (!PART && g == 1 && tailpf)
             tail_copy_any(dtb, true);
+          // bf16 rows: widened to fp32 once for all channels (cur is complete: the
+          // previous group waited for its copy; wide was last read before that
+          // group's closing barrier)
+          constexpr bool kWiden = sizeof(S) == 2 && MODE != kCarry;
+          if constexpr (kWiden) {
+            widen_rows<T, 2 * NG, GT, NTH>(cur, wide, ln.tid);
+            __syncthreads();
+          }
           // Unrolled, so the LDS offsets of each state are immediates; the barrier keeps
           // the states apart (interleaved, their registers would not fit).
 #pragma unroll
@@ -1299,8 +1341,13 @@ __global__ __launch_bounds__(kWaves * 64, T == 8 ? 4 : 3) void ss2d_forward_kern
                                      carry + ln.dl * kMaxN + n, aprod + ln.dl * kMaxN + n, delta, du, sdelta);
               } else {
                 float Bv[T], Cv[T];
-                read_seg<S, T>(cur + nn * GT * (int)sizeof(S), ln.seg, Bv);
-                read_seg<S, T>(cur + (NG + nn) * GT * (int)sizeof(S), ln.seg, Cv);
+                if constexpr (kWiden) {
+                  read_seg<float, T>(wide + nn * GT * 4, ln.seg, Bv);
+                  read_seg<float, T>(wide + (NG + nn) * GT * 4, ln.seg, Cv);
+                } else {
+                  read_seg<S, T>(cur + nn * GT * (int)sizeof(S), ln.seg, Bv);
+                  read_seg<S, T>(cur + (NG + nn) * GT * (int)sizeof(S), ln.seg, Cv);
+                }
                 state_core<G, T>(Bv, Cv, a2s[ln.dl * kMaxN + n], carry + ln.dl * kMaxN + n, ln.seg, delta, du,
                                  sdelta, yv);
               }
