@@ -184,6 +184,11 @@ LANE_CASES = [
     (16, (1, 3, 24, 32, 16, "bf16")),
     (16, (1, 3, 40, 40, 16, "f32")),   # 16 x 16, 6 chunks + a 64-step remainder (not prefetched)
     (16, (1, 4, 28, 28, 16, "bf16")),  # 16 x 16, 3 chunks + a 16-step remainder
+    # bf16 rows widened to fp32 in LDS once per workgroup, in every variant
+    (32, (2, 5, 24, 32, 16, "bf16")),  # 32 x 8, 3 chunks
+    (32, (1, 3, 40, 40, 16, "bf16")),  # 32 x 16, 3 chunks + 64-step remainder
+    (64, (1, 2, 64, 64, 16, "bf16")),  # 64 x 16, 4 chunks
+    (32, (1, 3, 40, 40, 5, "bf16")),   # 32 x 16, N = 5: rows of absent states widened too, not read
 ]
 
 
