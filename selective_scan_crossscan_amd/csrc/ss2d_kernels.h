@@ -176,6 +176,9 @@ __device__ __forceinline__ void scan_inclusive(float& A, float& B) {
 // to the group's carried state, h = A_prev * carry + B_prev; the group's first
 // lane takes the carry itself.  One asm block: the add reads B (last written by
 // the scan, well before) through DPP and the product through its plain operand.
+// With 16 lanes a group is one DPP row, and row_shr:1 does not write a row's
+// first lane (its source lies outside the row), so that lane keeps the carry
+// with no select.
 template <int G>
 __device__ __forceinline__ float incoming_state(float A, float B, float carry, int seg) {
   float h = carry;
@@ -186,6 +189,7 @@ __device__ __forceinline__ float incoming_state(float A, float B, float carry, i
         "v_add_f32_dpp %0, %2, %0 row_shr:1 row_mask:0xf bank_mask:0xf"
         : "+v"(h)
         : "v"(A), "v"(B));
+    return h;
   } else {
     asm volatile(
         "s_nop 1\n\t"
